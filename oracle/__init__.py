@@ -1,0 +1,248 @@
+"""CPU oracle for the bf16 -> NVFP4 block-scaled cast (numpy front end).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` import this package; the product library
+never does.  It shares no code with the HIP path: the arithmetic lives in
+``nvfp4_oracle.c`` (plain C, one IEEE binary32 op per step), loaded here with
+ctypes.  Inputs are bf16 bit patterns held as numpy ``uint16`` arrays.
+
+Modes: 0 = per-tensor outer amax, 1 = per-token (per-row amax for rowwise
+output, per-column amax for columnwise output), 2 = 16x16 tiles with the
+per-tensor amax, emitted in the per-token layout.  See ``nvfp4_oracle.c`` for
+the step-by-step definition and the pages each step follows.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnvfp4_oracle.so")
+_lib = None
+
+PER_TENSOR, PER_TOKEN, TILE_16x16 = 0, 1, 2
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "orc_e4m3_encode_array": (None, [_p, _i64, _p]),
+        "orc_e2m1_encode_array": (None, [_p, _i64, _p]),
+        "orc_e4m3_decode": (ctypes.c_float, [ctypes.c_uint8]),
+        "orc_e2m1_decode": (ctypes.c_float, [ctypes.c_uint8]),
+        "orc_quantize_vector": (None, [_p, _i64, ctypes.c_float, _p, _p]),
+        "orc_amax_tensor": (ctypes.c_float, [_p, _i64, _i64, _i64]),
+        "orc_amax_rows": (None, [_p, _i64, _i64, _i64, _p]),
+        "orc_amax_cols": (None, [_p, _i64, _i64, _i64, _p]),
+        "orc_encode_rowwise": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.c_int, _p, _p, _p]),
+        "orc_encode_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.c_int, _p, _p, _p]),
+        "orc_quantize": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_int, _p, _p, _p, _p, _p, _p]),
+        "orc_quantize_grouped": (ctypes.c_int, [_p, _i64, ctypes.c_int32, _p, _p, _p, _p, _p, _p, _p]),
+        "orc_dequantize": (ctypes.c_int, [_p, _p, _p, _i64, _i64, ctypes.c_int, _p]),
+        "orc_amax_accumulate": (None, [_p, _p, _i64, ctypes.c_float]),
+        "orc_amax_accumulate_reduce": (None, [_p, _p, _i64, ctypes.c_float]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _bf16(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are bf16 bit patterns (numpy uint16)")
+    return x
+
+
+# ------------------------------------------------------------------ codecs
+
+def e4m3_encode(s):
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    out = np.empty(s.shape, np.uint8)
+    _load().orc_e4m3_encode_array(_ptr(s), s.size, _ptr(out))
+    return out
+
+
+def e2m1_encode(q):
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.empty(q.shape, np.uint8)
+    _load().orc_e2m1_encode_array(_ptr(q), q.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(code):
+    return float(_load().orc_e4m3_decode(int(code)))
+
+
+def e2m1_decode(nibble):
+    return float(_load().orc_e2m1_decode(int(nibble)))
+
+
+def quantize_vector(v, A):
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    n = v.size
+    q = np.empty(n // 2, np.uint8)
+    sf = np.empty(n // 16, np.uint8)
+    _load().orc_quantize_vector(_ptr(v), n, float(np.float32(A)), _ptr(q), _ptr(sf))
+    return q, sf
+
+
+# -------------------------------------------------------------------- amax
+
+def amax_tensor(x):
+    x = _bf16(x)
+    M, K = x.shape
+    return np.float32(_load().orc_amax_tensor(_ptr(x), M, K, K))
+
+
+def amax_rows(x):
+    x = _bf16(x)
+    M, K = x.shape
+    out = np.empty(M, np.float32)
+    _load().orc_amax_rows(_ptr(x), M, K, K, _ptr(out))
+    return out
+
+
+def amax_cols(x):
+    x = _bf16(x)
+    M, K = x.shape
+    out = np.empty(K, np.float32)
+    _load().orc_amax_cols(_ptr(x), M, K, K, _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------------ casts
+
+def encode_rowwise(x, amax, per_vector, ld=None, rows=None, cols=None):
+    """Rowwise encode with caller-supplied outer amax (scalar or per row).
+
+    ``x`` may be a view into a wider row-major array when ``ld`` is given
+    (used by the CPU baseline to split work into bands)."""
+    amax = np.ascontiguousarray(np.atleast_1d(amax), dtype=np.float32)
+    if ld is None:
+        x = _bf16(x)
+        M, K = x.shape
+        ld = K
+        base = x
+        off = 0
+    else:
+        base, off = x
+        M, K = rows, cols
+    q = np.empty((M, K // 2), np.uint8)
+    sf = np.empty((M, K // 16), np.uint8)
+    rc = _load().orc_encode_rowwise(base.ctypes.data + 2 * off, M, K, ld, int(per_vector),
+                                    _ptr(amax), _ptr(q), _ptr(sf))
+    if rc != 0:
+        raise ValueError("oracle: rowwise needs K % 16 == 0")
+    return q, sf
+
+
+def encode_colwise(x, amax, per_vector, ld=None, rows=None, cols=None):
+    """Columnwise encode (quantization of the transpose) with caller amax."""
+    amax = np.ascontiguousarray(np.atleast_1d(amax), dtype=np.float32)
+    if ld is None:
+        x = _bf16(x)
+        M, K = x.shape
+        ld = K
+        base = x
+        off = 0
+    else:
+        base, off = x
+        M, K = rows, cols
+    q = np.empty((K, M // 2), np.uint8)
+    sf = np.empty((K, M // 16), np.uint8)
+    rc = _load().orc_encode_colwise(base.ctypes.data + 2 * off, M, K, ld, int(per_vector),
+                                    _ptr(amax), _ptr(q), _ptr(sf))
+    if rc != 0:
+        raise ValueError("oracle: columnwise needs M % 16 == 0")
+    return q, sf
+
+
+def quantize(x, mode, rowwise=True, columnwise=True):
+    """Whole cast; returns a dict with row_q/row_sf/row_amax and/or col_*."""
+    x = _bf16(x)
+    M, K = x.shape
+    out = {}
+    if rowwise:
+        out["row_q"] = np.empty((M, K // 2), np.uint8)
+        out["row_sf"] = np.empty((M, K // 16), np.uint8)
+        out["row_amax"] = np.empty(1 if mode == PER_TENSOR else M, np.float32)
+    if columnwise:
+        out["col_q"] = np.empty((K, M // 2), np.uint8)
+        out["col_sf"] = np.empty((K, M // 16), np.uint8)
+        out["col_amax"] = np.empty(1 if mode == PER_TENSOR else K, np.float32)
+    g = out.get
+    rc = _load().orc_quantize(_ptr(x), M, K, int(mode),
+                              _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
+                              _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")))
+    if rc != 0:
+        raise ValueError("oracle: shape not supported by this mode")
+    return out
+
+
+def quantize_grouped(x, counts, rowwise=True, columnwise=True):
+    x = _bf16(x)
+    T, K = x.shape
+    counts = np.ascontiguousarray(counts, dtype=np.int64)
+    G = counts.size
+    if int(counts.sum()) != T:
+        raise ValueError("oracle: counts must sum to the row count")
+    out = {}
+    if rowwise:
+        out["row_q"] = np.empty((T, K // 2), np.uint8)
+        out["row_sf"] = np.empty((T, K // 16), np.uint8)
+        out["row_amax"] = np.empty(T, np.float32)
+    if columnwise:
+        out["col_q"] = np.empty(T * K // 2, np.uint8)
+        out["col_sf"] = np.empty(T * K // 16, np.uint8)
+        out["col_amax"] = np.empty((G, K), np.float32)
+    g = out.get
+    rc = _load().orc_quantize_grouped(_ptr(x), K, G, _ptr(counts),
+                                      _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
+                                      _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")))
+    if rc != 0:
+        raise ValueError("oracle: bad grouped shape")
+    return out
+
+
+def dequantize(q, sf, amax, R, C, amax_per_row):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sf = np.ascontiguousarray(sf, dtype=np.uint8)
+    amax = np.ascontiguousarray(np.atleast_1d(amax), dtype=np.float32)
+    out = np.empty((R, C), np.float32)
+    rc = _load().orc_dequantize(_ptr(q), _ptr(sf), _ptr(amax), R, C, int(amax_per_row), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: dequantize needs C % 16 == 0")
+    return out
+
+
+def amax_accumulate(buf, obs, decay):
+    buf = np.array(buf, dtype=np.float32, copy=True)
+    obs = np.ascontiguousarray(obs, dtype=np.float32)
+    assert buf.shape == obs.shape
+    _load().orc_amax_accumulate(_ptr(buf), _ptr(obs), buf.size, float(np.float32(decay)))
+    return buf
+
+
+def amax_accumulate_reduce(buf, obs_vec, decay):
+    buf = np.array(np.atleast_1d(buf), dtype=np.float32, copy=True)
+    obs_vec = np.ascontiguousarray(obs_vec, dtype=np.float32)
+    _load().orc_amax_accumulate_reduce(_ptr(buf), _ptr(obs_vec), obs_vec.size,
+                                       float(np.float32(decay)))
+    return buf

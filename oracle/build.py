@@ -1,0 +1,29 @@
+"""Build the CPU oracle (plain C) into oracle/libnvfp4_oracle.so.
+
+Test infrastructure only.  Flags keep every float operation a single IEEE
+binary32 op: no fused multiply-add contraction, no fast-math.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "nvfp4_oracle.c")
+LIB = os.path.join(HERE, "libnvfp4_oracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+          "-fexcess-precision=standard", "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,420 @@
+/*
+ * nvfp4_oracle.c -- plain, slow CPU reference for the bf16 -> NVFP4
+ * block-scaled cast.  TEST INFRASTRUCTURE ONLY (tests, smoke check, the
+ * benchmark's CPU-baseline leg).  It shares no code with the HIP library.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math (oracle/build.py).
+ *
+ * What is computed, for one vector v of n values (n % 16 == 0) with outer
+ * amax A (the steps follow the per-token recipe page, TransformerEngine
+ * PR #3045, "Description"/"Changes" and the sequence diagram, and the block
+ * scale discussion on Model-Optimizer PR #2598):
+ *   S    = A / 2688                (2688 = 6 * 448: E2M1 max times E4M3 max)
+ *   b_j  = max |v| over block j of 16 values
+ *   sf_j = (b_j / 6) / S           two divisions, in this order
+ *   c_j  = E4M3(sf_j), D_j = decode(c_j)
+ *   r_j  = D_j * S
+ *   nib  = E2M1(v_i / r_j)         division, then RNE onto the E2M1 grid
+ * with S == 0 or r_j == 0 giving scale code 0 and sign-only nibbles.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - block-scale op order (b/6)/S: the Model-Optimizer review shows two
+ *     orders disagree on ~0.1% of blocks; this one is fixed by convention
+ *     (parity of that choice is unpinned by the pages).
+ *   - sign of zero copied into the nibble; even element in the low nibble;
+ *     zero outer amax or zero block scale gives code 0 and sign-only
+ *     nibbles (conventions, unpinned).
+ */
+#include "nvfp4_oracle.h"
+
+#include <math.h>
+#include <string.h>
+#include <stdlib.h>
+
+/* ---------------------------------------------------------------- codecs */
+
+float orc_bf16_to_f32(uint16_t b)
+{
+    /* bf16 is the high half of a binary32: widening is exact */
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* round a non-negative float that holds an exact value to the nearest
+ * integer, ties to even (written out rather than relying on the FP
+ * environment's rounding mode) */
+static float round_half_even(float y)
+{
+    float fl = floorf(y);
+    float frac = y - fl;            /* exact: y and fl share the binade scale */
+    if (frac > 0.5f) return fl + 1.0f;
+    if (frac < 0.5f) return fl;
+    /* tie: pick the even neighbour */
+    return (fmodf(fl, 2.0f) == 0.0f) ? fl : fl + 1.0f;
+}
+
+/* OCP FP8 E4M3 ("fn"): bias 7, 3 mantissa bits, no infinities, 0x7F is NaN,
+ * largest finite value 448 (0x7E), subnormals m * 2^-9. */
+float orc_e4m3_decode(uint8_t code)
+{
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    float mag;
+    if (e == 0)
+        mag = ldexpf((float)m, -9);
+    else
+        mag = ldexpf((float)(8 + m), e - 10);   /* (1 + m/8) * 2^(e-7) */
+    if (e == 0xF && m == 0x7) mag = NAN;
+    return (code & 0x80) ? -mag : mag;
+}
+
+uint8_t orc_e4m3_encode(float s)
+{
+    /* s >= 0 by construction (a ratio of magnitudes).  Values at or above the
+     * largest finite code saturate to it; (448, 464] would round there anyway. */
+    if (!(s < 448.0f)) return 0x7E;
+    if (s <= 0.0f) return 0x00;
+    if (s < ldexpf(1.0f, -6)) {
+        /* subnormal range: quantum 2^-9, code == integer multiple */
+        float m = round_half_even(ldexpf(s, 9));  /* exact scaling by 2^9 */
+        return (uint8_t)m;                         /* m == 8 is code 0x08 = 2^-6 */
+    }
+    int fe;
+    (void)frexpf(s, &fe);          /* s = f * 2^fe, f in [0.5, 1) */
+    int e = fe - 1;                /* floor(log2 s), in [-6, 8] here */
+    float m = round_half_even(ldexpf(s, 3 - e));   /* significand * 8, in [8, 16] */
+    if (m >= 16.0f) { m = 8.0f; e += 1; }
+    int code = ((e + 7) << 3) | ((int)m - 8);
+    if (code > 0x7E) code = 0x7E;
+    return (uint8_t)code;
+}
+
+/* E2M1 magnitudes, code 0..7 */
+static const float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+float orc_e2m1_decode(uint8_t nibble)
+{
+    float g = kE2M1[nibble & 7];
+    return (nibble & 8) ? -g : g;
+}
+
+uint8_t orc_e2m1_encode(float q)
+{
+    /* round to nearest, ties to the even code, saturating at 6; the
+     * comparison list is the grid's midpoints with the tie direction of each */
+    uint8_t s = signbit(q) ? 8 : 0;
+    float a = fabsf(q);
+    uint8_t c;
+    if (a <= 0.25f)      c = 0;   /* tie 0.25 -> 0 (even) */
+    else if (a < 0.75f)  c = 1;   /* tie 0.75 -> 1.0 (code 2) */
+    else if (a <= 1.25f) c = 2;   /* tie 1.25 -> 1.0 */
+    else if (a < 1.75f)  c = 3;   /* tie 1.75 -> 2.0 (code 4) */
+    else if (a <= 2.5f)  c = 4;   /* tie 2.5  -> 2.0 */
+    else if (a < 3.5f)   c = 5;   /* tie 3.5  -> 4.0 (code 6) */
+    else if (a <= 5.0f)  c = 6;   /* tie 5.0  -> 4.0 */
+    else                 c = 7;   /* beyond: saturate at 6 (also +inf) */
+    return (uint8_t)(s | c);
+}
+
+void orc_e4m3_encode_array(const float* s, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(s[i]);
+}
+
+void orc_e2m1_encode_array(const float* q, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode(q[i]);
+}
+
+/* ------------------------------------------------------------ core routine */
+
+static const float kE2M1Max = 6.0f;
+static const float kOuterDiv = 2688.0f;   /* 6 * 448, exact */
+
+/* quantize the 16 values of one block given its decoded ratio r = D * S */
+static void encode_block(const float* v, int64_t count, float r, uint8_t* nibbles)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        if (r == 0.0f)
+            nibbles[i] = signbit(v[i]) ? 8 : 0;
+        else
+            nibbles[i] = orc_e2m1_encode(v[i] / r);
+    }
+}
+
+void orc_quantize_vector(const float* v, int64_t n, float A, uint8_t* q, uint8_t* sf)
+{
+    float S = A / kOuterDiv;
+    uint8_t nib[16];
+    for (int64_t j = 0; j < n / 16; ++j) {
+        const float* blk = v + 16 * j;
+        float r;
+        if (S == 0.0f) {
+            sf[j] = 0x00;
+            r = 0.0f;
+        } else {
+            float b = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                float a = fabsf(blk[i]);
+                if (a > b) b = a;
+            }
+            float t = b / kE2M1Max;
+            float s = t / S;
+            uint8_t code = orc_e4m3_encode(s);
+            sf[j] = code;
+            r = orc_e4m3_decode(code) * S;
+        }
+        encode_block(blk, 16, r, nib);
+        for (int i = 0; i < 8; ++i)
+            q[8 * j + i] = (uint8_t)(nib[2 * i] | (nib[2 * i + 1] << 4));
+    }
+}
+
+/* ------------------------------------------------------------------ amax */
+
+float orc_amax_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ld)
+{
+    float A = 0.0f;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(orc_bf16_to_f32(x[m * ld + k]));
+            if (a > A) A = a;
+        }
+    return A;
+}
+
+void orc_amax_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ld, float* out)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float A = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(orc_bf16_to_f32(x[m * ld + k]));
+            if (a > A) A = a;
+        }
+        out[m] = A;
+    }
+}
+
+void orc_amax_cols(const uint16_t* x, int64_t M, int64_t K, int64_t ld, float* out)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        float A = 0.0f;
+        for (int64_t m = 0; m < M; ++m) {
+            float a = fabsf(orc_bf16_to_f32(x[m * ld + k]));
+            if (a > A) A = a;
+        }
+        out[k] = A;
+    }
+}
+
+/* ---------------------------------------------------------------- modes */
+
+int orc_encode_rowwise(const uint16_t* x, int64_t M, int64_t K, int64_t ld,
+                       int per_vector, const float* amax, uint8_t* q, uint8_t* sf)
+{
+    if (M < 0 || K < 0 || K % 16 != 0) return -1;
+    float* v = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) v[k] = orc_bf16_to_f32(x[m * ld + k]);
+        float A = per_vector ? amax[m] : amax[0];
+        orc_quantize_vector(v, K, A, q + m * (K / 2), sf + m * (K / 16));
+    }
+    free(v);
+    return 0;
+}
+
+int orc_encode_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ld,
+                       int per_vector, const float* amax, uint8_t* q, uint8_t* sf)
+{
+    if (M < 0 || K < 0 || M % 16 != 0) return -1;
+    float* v = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t m = 0; m < M; ++m) v[m] = orc_bf16_to_f32(x[m * ld + k]);
+        float A = per_vector ? amax[k] : amax[0];
+        orc_quantize_vector(v, M, A, q + k * (M / 2), sf + k * (M / 16));
+    }
+    free(v);
+    return 0;
+}
+
+/* 16x16 tiles: one E4M3 code per tile relative to the per-tensor outer
+ * scale, so the rowwise and columnwise codes are the same numbers; emitted
+ * in the per-token layout (scale replicated along each row / column of the
+ * tile, amax vectors filled with the tensor amax).  Follows the opt-in 2D
+ * weight mode described in the "Changes" list of the per-token recipe page. */
+static int quantize_2d(const uint16_t* x, int64_t M, int64_t K,
+                       uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                       uint8_t* col_q, uint8_t* col_sf, float* col_amax)
+{
+    if (M % 16 != 0 || K % 16 != 0) return -1;
+    float A = orc_amax_tensor(x, M, K, K);
+    float S = A / kOuterDiv;
+    int64_t TI = M / 16, TJ = K / 16;
+    for (int64_t I = 0; I < TI; ++I) {
+        for (int64_t J = 0; J < TJ; ++J) {
+            float tile[16][16];
+            for (int a = 0; a < 16; ++a)
+                for (int b = 0; b < 16; ++b)
+                    tile[a][b] = orc_bf16_to_f32(x[(16 * I + a) * K + 16 * J + b]);
+            uint8_t code;
+            float r;
+            if (S == 0.0f) {
+                code = 0x00;
+                r = 0.0f;
+            } else {
+                float bmax = 0.0f;
+                for (int a = 0; a < 16; ++a)
+                    for (int b = 0; b < 16; ++b) {
+                        float m = fabsf(tile[a][b]);
+                        if (m > bmax) bmax = m;
+                    }
+                float t = bmax / kE2M1Max;
+                float s = t / S;
+                code = orc_e4m3_encode(s);
+                r = orc_e4m3_decode(code) * S;
+            }
+            uint8_t nib[16][16];
+            for (int a = 0; a < 16; ++a) encode_block(tile[a], 16, r, nib[a]);
+            for (int a = 0; a < 16; ++a) {
+                int64_t m = 16 * I + a;
+                for (int b = 0; b < 16; b += 2) {
+                    int64_t k = 16 * J + b;
+                    if (row_q) row_q[m * (K / 2) + k / 2] = (uint8_t)(nib[a][b] | (nib[a][b + 1] << 4));
+                }
+                if (row_sf) row_sf[m * (K / 16) + J] = code;
+            }
+            for (int b = 0; b < 16; ++b) {
+                int64_t k = 16 * J + b;
+                for (int a = 0; a < 16; a += 2) {
+                    int64_t m = 16 * I + a;
+                    if (col_q) col_q[k * (M / 2) + m / 2] = (uint8_t)(nib[a][b] | (nib[a + 1][b] << 4));
+                }
+                if (col_sf) col_sf[k * (M / 16) + I] = code;
+            }
+        }
+    }
+    if (row_amax) for (int64_t m = 0; m < M; ++m) row_amax[m] = A;
+    if (col_amax) for (int64_t k = 0; k < K; ++k) col_amax[k] = A;
+    return 0;
+}
+
+int orc_quantize(const uint16_t* x, int64_t M, int64_t K, int mode,
+                 uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                 uint8_t* col_q, uint8_t* col_sf, float* col_amax)
+{
+    int want_row = row_q != NULL, want_col = col_q != NULL;
+    if (M < 0 || K < 0) return -1;
+    if (want_row && K % 16 != 0) return -1;
+    if (want_col && M % 16 != 0) return -1;
+    if (mode == 2)
+        return quantize_2d(x, M, K, row_q, row_sf, row_amax, col_q, col_sf, col_amax);
+    if (mode == 0) {
+        /* per-tensor: one outer amax for the whole tensor (the recipe's default) */
+        float A = orc_amax_tensor(x, M, K, K);
+        if (want_row) {
+            if (row_amax) row_amax[0] = A;
+            orc_encode_rowwise(x, M, K, K, 0, &A, row_q, row_sf);
+        }
+        if (want_col) {
+            if (col_amax) col_amax[0] = A;
+            orc_encode_colwise(x, M, K, K, 0, &A, col_q, col_sf);
+        }
+        return 0;
+    }
+    if (mode == 1) {
+        /* per-token: a per-row amax (length M) for rowwise data and a per-col
+         * amax (length K) for columnwise data */
+        if (want_row) {
+            float* ra = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+            orc_amax_rows(x, M, K, K, ra);
+            orc_encode_rowwise(x, M, K, K, 1, ra, row_q, row_sf);
+            if (row_amax) memcpy(row_amax, ra, sizeof(float) * (size_t)M);
+            free(ra);
+        }
+        if (want_col) {
+            float* ca = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+            orc_amax_cols(x, M, K, K, ca);
+            orc_encode_colwise(x, M, K, K, 1, ca, col_q, col_sf);
+            if (col_amax) memcpy(col_amax, ca, sizeof(float) * (size_t)K);
+            free(ca);
+        }
+        return 0;
+    }
+    return -1;
+}
+
+int orc_quantize_grouped(const uint16_t* x, int64_t K, int32_t G, const int64_t* counts,
+                         uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                         uint8_t* col_q, uint8_t* col_sf, float* col_amax)
+{
+    int64_t total = 0;
+    for (int32_t e = 0; e < G; ++e) {
+        if (counts[e] < 0 || counts[e] % 16 != 0) return -1;
+        total += counts[e];
+    }
+    if (row_q) {
+        if (K % 16 != 0) return -1;
+        /* rowwise: per-token rowwise of the concatenated experts */
+        if (orc_quantize(x, total, K, 1, row_q, row_sf, row_amax, NULL, NULL, NULL) != 0) return -1;
+    }
+    if (col_q) {
+        int64_t off = 0;
+        for (int32_t e = 0; e < G; ++e) {
+            int64_t me = counts[e];
+            const uint16_t* xe = x + off * K;
+            float* ca = col_amax + (int64_t)e * K;
+            orc_amax_cols(xe, me, K, K, ca);   /* an empty expert gives 0 */
+            orc_encode_colwise(xe, me, K, K, 1, ca, col_q + K * off / 2, col_sf + K * off / 16);
+            off += me;
+        }
+    }
+    return 0;
+}
+
+/* ----------------------------------------------------------- dequantize */
+
+int orc_dequantize(const uint8_t* q, const uint8_t* sf, const float* amax,
+                   int64_t R, int64_t C, int amax_per_row, float* out)
+{
+    if (R < 0 || C < 0 || C % 16 != 0) return -1;
+    for (int64_t r = 0; r < R; ++r) {
+        float A = amax_per_row ? amax[r] : amax[0];
+        float S = A / kOuterDiv;
+        for (int64_t j = 0; j < C / 16; ++j) {
+            float ratio = orc_e4m3_decode(sf[r * (C / 16) + j]) * S;
+            for (int i = 0; i < 16; ++i) {
+                int64_t c = 16 * j + i;
+                uint8_t byte = q[r * (C / 2) + c / 2];
+                uint8_t nib = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+                float val = kE2M1[nib & 7] * ratio;
+                out[r * C + c] = (nib & 8) ? -val : val;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ decayed accumulate */
+
+/* New = max(Old * Decay, Observed), from the PTQ scaling-factor buffering
+ * page (TransformerEngine PR #3296, "Description"): decay 0 keeps only the
+ * latest value, decay 1 keeps the maximum over the whole history. */
+void orc_amax_accumulate(float* buf, const float* obs, int64_t n, float decay)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float t = buf[i] * decay;
+        buf[i] = (obs[i] > t) ? obs[i] : t;
+    }
+}
+
+/* the same page max-reduces the row-wise vector to a scalar before it is
+ * kept; an empty vector observes 0 */
+void orc_amax_accumulate_reduce(float* buf, const float* obs, int64_t n, float decay)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i)
+        if (obs[i] > m) m = obs[i];
+    orc_amax_accumulate(buf, &m, 1, decay);
+}

@@ -1,0 +1,300 @@
+"""Pins for the oracle's whole cast (CPU only).
+
+The oracle is checked against: hand-worked examples (tests/golden), an
+independent brute-force quantizer on tiny inputs (tests/bruteforce.py),
+exact round trips of representable values, structural invariants that hold
+for any correct implementation, an error bound, and the decay limits stated
+on the PTQ scaling-factor buffering page.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from nvfp4_block_scaled_bf16_amd import workloads as W
+from tests import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _f(v):
+    return -0.0 if v == "-0.0" else float(v)
+
+
+def _golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)
+
+
+# ------------------------------------------------------------ golden files
+
+@pytest.mark.parametrize("ex", _golden()["vectors"], ids=lambda e: e["name"])
+def test_golden_vectors(oracle, ex):
+    if "v" in ex:
+        v = [_f(a) for a in ex["v"]]
+    else:
+        key = [k for k in ex if k.startswith("v_times_2^")][0]
+        p = int(key.split("^")[1])
+        v = [_f(a) * 2.0 ** p if _f(a) != 0 else _f(a) for a in ex[key]]
+    v = np.array(v, np.float32)
+    # every value must be a bf16 number
+    assert np.array_equal(W.bf16_to_f32(W.bf16_from_f32(v)), v)
+    q, sf = oracle.quantize_vector(v, ex["A"])
+    assert q.tolist() == ex["q"]
+    assert sf.tolist() == ex["sf"]
+    # the independent brute force agrees too
+    bq, bsf = bf.quantize_vector_brute(v, np.float32(ex["A"]))
+    assert bq.tolist() == ex["q"] and bsf.tolist() == ex["sf"]
+
+
+@pytest.mark.parametrize("ex", _golden()["tensors"], ids=lambda e: e["name"])
+def test_golden_tensors(oracle, ex):
+    x = W.bf16_from_f32(np.array([_f(a) for a in ex["x"]], np.float32).reshape(ex["M"], ex["K"]))
+    out = oracle.quantize(x, ex["mode"], rowwise=True, columnwise=False)
+    assert out["row_q"].reshape(-1).tolist() == ex["row_q"]
+    assert out["row_sf"].reshape(-1).tolist() == ex["row_sf"]
+    assert out["row_amax"].tolist() == ex["row_amax"]
+
+
+# ---------------------------------------------------- brute force, tiny sizes
+
+def _crafted(M, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= np.exp(rng.normal(0, 2, size=(M, 1))).astype(np.float32)
+    x[0, :] = 0.0                          # an all-zero row
+    x[1, :16] = -0.0                       # a negative-zero block
+    if M > 2:
+        x[2, 3] = 2688.0                   # one huge element: tiny block scales elsewhere
+        x[2, 16:32] = 1e-4
+    if M > 3:
+        x[3, 5] = 6.0 * 2.0 ** -130        # bf16 subnormal territory
+    return W.bf16_from_f32(x)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("shape,seed", [((16, 16), 1), ((32, 48), 2), ((48, 32), 3), ((64, 64), 4)])
+def test_bruteforce_tiny(oracle, mode, shape, seed):
+    x = _crafted(*shape, seed)
+    got = oracle.quantize(x, mode)
+    exp = bf.quantize_brute(x, mode)
+    for key in ("row_q", "row_sf", "col_q", "col_sf", "row_amax", "col_amax"):
+        np.testing.assert_array_equal(got[key], exp[key], err_msg=key)
+
+
+def test_bruteforce_random_vectors(oracle):
+    rng = np.random.default_rng(11)
+    for i in range(200):
+        n = 16 * int(rng.integers(1, 5))
+        v = W.bf16_to_f32(W.bf16_from_f32(
+            (rng.standard_normal(n) * np.exp(rng.normal(0, 8))).astype(np.float32)))
+        A = np.float32(np.abs(v).max() * np.float32(rng.choice([1.0, 1.0, 0.5, 0.01, 3.0])))
+        q, sf = oracle.quantize_vector(v, A)
+        bq, bsf = bf.quantize_vector_brute(v, A)
+        np.testing.assert_array_equal(q, bq)
+        np.testing.assert_array_equal(sf, bsf)
+
+
+# -------------------------------------------------------- exact round trip
+
+def test_exact_roundtrip_of_representable_values(oracle):
+    """x = g * D * 2^e with a +/-6 in every block and one block at D = 448:
+    then A = 2688 * 2^e, S = 2^e exactly, and quantize(x) must give back the
+    chosen codes, scales and amax bit for bit, and dequantize must give x."""
+    rng = np.random.default_rng(21)
+    for e in (-20, -7, 0, 3, 12):
+        M, K = 32, 64
+        codes = rng.integers(0x08, 0x7E, size=(M, K // 16)).astype(np.uint8)  # normal E4M3
+        codes[:, 0] = 0x7E
+        nib = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+        nib[:, ::16] = np.where(rng.integers(0, 2, size=(M, K // 16)) == 1, 15, 7)  # a +/-6 per block
+        D = np.array([bf.E4M3_VALUES[c] for c in codes.reshape(-1)]).reshape(codes.shape)
+        g = np.array([bf.E2M1_GRID[n & 7] * (-1 if n & 8 else 1) for n in nib.reshape(-1)]).reshape(nib.shape)
+        x = (g * np.repeat(D, 16, axis=1) * 2.0 ** e).astype(np.float32)
+        assert np.array_equal(W.bf16_to_f32(W.bf16_from_f32(x)), x)
+        xb = W.bf16_from_f32(x)
+        out = oracle.quantize(xb, 1, rowwise=True, columnwise=False)
+        # nibbles for +/-0 keep the sign the construction gave them
+        exp_q = nib[:, 0::2] | (nib[:, 1::2] << 4)
+        np.testing.assert_array_equal(out["row_sf"], codes)
+        np.testing.assert_array_equal(out["row_q"], exp_q)
+        np.testing.assert_array_equal(out["row_amax"], np.full(M, 2688.0 * 2.0 ** e, np.float32))
+        back = oracle.dequantize(out["row_q"], out["row_sf"], out["row_amax"], M, K, True)
+        np.testing.assert_array_equal(back, x)
+
+
+# -------------------------------------------------------------- invariants
+
+def _c2_like(M, K, seed):
+    return W.row_scaled_with_outliers(M, K, seed)
+
+
+def test_amax_invariants(oracle):
+    x = _c2_like(96, 160, 5)
+    xf = W.bf16_to_f32(x)
+    A = oracle.amax_tensor(x)
+    ra, ca = oracle.amax_rows(x), oracle.amax_cols(x)
+    assert A == np.abs(xf).max()
+    np.testing.assert_array_equal(ra, np.abs(xf).max(axis=1))
+    np.testing.assert_array_equal(ca, np.abs(xf).max(axis=0))
+    assert ra.max() == ca.max() == A
+
+
+def test_columnwise_is_rowwise_of_transpose(oracle):
+    x = _c2_like(64, 96, 6)
+    for mode in (0, 1):
+        a = oracle.quantize(x, mode)
+        b = oracle.quantize(np.ascontiguousarray(x.T), mode)
+        np.testing.assert_array_equal(a["col_q"], b["row_q"])
+        np.testing.assert_array_equal(a["col_sf"], b["row_sf"])
+        np.testing.assert_array_equal(a["col_amax"], b["row_amax"])
+
+
+def test_per_tensor_single_row_equals_per_token(oracle):
+    x = _c2_like(16, 256, 7)
+    for r in range(16):
+        a = oracle.quantize(np.ascontiguousarray(x[r:r + 1]), 0, columnwise=False)
+        b = oracle.quantize(x, 1, columnwise=False)
+        np.testing.assert_array_equal(a["row_q"][0], b["row_q"][r])
+        np.testing.assert_array_equal(a["row_sf"][0], b["row_sf"][r])
+
+
+def test_block_holding_the_amax_gets_the_top_code(oracle):
+    """(A/6)/(A/2688) is within an ulp of 448, which E4M3 rounds to 0x7E."""
+    x = _c2_like(128, 256, 8)
+    out = oracle.quantize(x, 1)
+    xf = np.abs(W.bf16_to_f32(x))
+    arg = xf.argmax(axis=1)
+    for r in range(128):
+        assert out["row_sf"][r, arg[r] // 16] == 0x7E
+    assert out["row_sf"].max() <= 0x7E and out["col_sf"].max() <= 0x7E
+
+
+def test_2d_transposition_invariance(oracle):
+    x = W.weight_with_outliers(64, 96, 9)
+    a = oracle.quantize(x, 2)
+    b = oracle.quantize(np.ascontiguousarray(x.T), 2)
+    np.testing.assert_array_equal(a["row_q"], b["col_q"])
+    np.testing.assert_array_equal(a["col_q"], b["row_q"])
+    np.testing.assert_array_equal(a["row_sf"], b["col_sf"])
+    # nibble (m, k) of the rowwise data equals nibble (k, m) of the columnwise data
+    def nibbles(q):
+        return np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+    np.testing.assert_array_equal(nibbles(a["row_q"]), nibbles(a["col_q"]).T)
+    # the scale is constant over each 16 x 16 tile
+    t = a["row_sf"].reshape(4, 16, 6)
+    assert (t == t[:, :1, :]).all()
+
+
+def test_grouped_equals_per_expert_calls(oracle):
+    rng = np.random.default_rng(12)
+    counts = np.array([32, 0, 16, 48, 0, 16], np.int64)
+    K = 64
+    x = W.bf16_from_f32(rng.standard_normal((counts.sum(), K)).astype(np.float32))
+    g = oracle.quantize_grouped(x, counts)
+    ung = oracle.quantize(x, 1, columnwise=False)
+    np.testing.assert_array_equal(g["row_q"], ung["row_q"])
+    np.testing.assert_array_equal(g["row_sf"], ung["row_sf"])
+    np.testing.assert_array_equal(g["row_amax"], ung["row_amax"])
+    off = 0
+    for e, m in enumerate(counts):
+        if m == 0:
+            assert (g["col_amax"][e] == 0).all()
+            continue
+        one = oracle.quantize(np.ascontiguousarray(x[off:off + m]), 1, rowwise=False)
+        np.testing.assert_array_equal(g["col_q"][K * off // 2:K * (off + m) // 2],
+                                      one["col_q"].reshape(-1))
+        np.testing.assert_array_equal(g["col_sf"][K * off // 16:K * (off + m) // 16],
+                                      one["col_sf"].reshape(-1))
+        np.testing.assert_array_equal(g["col_amax"][e], one["col_amax"])
+        off += m
+
+
+def test_zero_tensor(oracle):
+    x = np.zeros((32, 32), np.uint16)
+    x[5, 7] = 0x8000  # -0.0
+    for mode in (0, 1, 2):
+        out = oracle.quantize(x, mode)
+        assert (out["row_sf"] == 0).all() and (out["col_sf"] == 0).all()
+        assert (out["row_amax"] == 0).all()
+        exp = np.zeros((32, 16), np.uint8)
+        exp[5, 3] = 0x80  # element 7 is the high nibble of byte 3
+        np.testing.assert_array_equal(out["row_q"], exp)
+
+
+def test_saturation_with_undersized_amax(oracle):
+    x = _c2_like(16, 64, 13)
+    true_amax = oracle.amax_rows(x)
+    q, sf = oracle.encode_rowwise(x, true_amax / np.float32(64.0), True)
+    assert (sf[true_amax > 0].max(axis=1) == 0x7E).all()
+    nib = np.stack([q & 0xF, q >> 4], -1).reshape(16, -1)
+    assert ((nib & 7) == 7).any(axis=1)[true_amax > 0].all()
+
+
+def test_error_bound(oracle):
+    """|x - dequant(quant(x))| <= r * max(1, |x|/r - 6) + 2^-22 |x|: rounding
+    to the E2M1 grid moves a value by at most one grid unit of r (the widest
+    gap is 2, half of it 1), saturation costs |q| - 6."""
+    x = _c2_like(64, 128, 14)
+    xf = W.bf16_to_f32(x).astype(np.float64)
+    out = oracle.quantize(x, 1)
+    back = oracle.dequantize(out["row_q"], out["row_sf"], out["row_amax"], 64, 128, True)
+    S = out["row_amax"].astype(np.float64) / 2688.0
+    D = np.array([bf.E4M3_VALUES[c] for c in out["row_sf"].reshape(-1)]).reshape(64, 8)
+    r = np.repeat(D, 16, axis=1) * S[:, None]
+    q = np.where(r > 0, np.abs(xf) / np.where(r > 0, r, 1), 0)
+    bound = r * np.maximum(1.0, q - 6.0) + 2.0 ** -22 * np.abs(xf) + 1e-45
+    assert (np.abs(xf - back) <= bound).all()
+
+
+# ------------------------------------------------------------------ decay
+
+def test_decay_zero_keeps_latest_and_one_keeps_history_max(oracle):
+    """The buffering page: decay 0 takes only the most recent value, decay 1
+    the maximum over the whole history."""
+    rng = np.random.default_rng(15)
+    obs = np.abs(rng.standard_normal((20, 7))).astype(np.float32) * 10
+    b0 = np.zeros(7, np.float32)
+    b1 = np.zeros(7, np.float32)
+    for t in range(20):
+        b0 = oracle.amax_accumulate(b0, obs[t], 0.0)
+        b1 = oracle.amax_accumulate(b1, obs[t], 1.0)
+        np.testing.assert_array_equal(b0, obs[t])
+        np.testing.assert_array_equal(b1, obs[:t + 1].max(axis=0))
+
+
+def test_decay_09_close_to_float64_closed_form(oracle):
+    """New = max(Old*d, Obs) unrolls to max_s obs_s * d^(t-s); the fp32 loop
+    stays within a few ulps of that float64 closed form."""
+    rng = np.random.default_rng(16)
+    obs = (np.abs(rng.standard_normal(16)) * np.exp(rng.normal(0, 1, 16))).astype(np.float32)
+    buf = np.zeros(1, np.float32)
+    for t in range(16):
+        buf = oracle.amax_accumulate_reduce(buf, obs[t:t + 1], 0.9)
+        closed = max(float(obs[s]) * 0.9 ** (t - s) for s in range(t + 1))
+        assert abs(float(buf[0]) - closed) <= 8 * np.spacing(np.float32(closed)), (t, buf, closed)
+
+
+def test_decay_reduce_uses_vector_max(oracle):
+    v = np.array([0.5, 3.0, 2.0], np.float32)
+    assert oracle.amax_accumulate_reduce(np.array([10.0], np.float32), v, 0.5)[0] == 5.0
+    assert oracle.amax_accumulate_reduce(np.array([1.0], np.float32), v, 0.5)[0] == 3.0
+    assert oracle.amax_accumulate_reduce(np.array([1.0], np.float32), v[:0], 0.5)[0] == 0.5
+
+
+def test_decay_checkpoint_resume(oracle):
+    """8 + 8 iterations with the buffer saved and restored equal 16 straight."""
+    rng = np.random.default_rng(17)
+    obs = np.abs(rng.standard_normal((16, 5))).astype(np.float32)
+    a = np.zeros(5, np.float32)
+    for t in range(16):
+        a = oracle.amax_accumulate(a, obs[t], 0.9)
+    b = np.zeros(5, np.float32)
+    for t in range(8):
+        b = oracle.amax_accumulate(b, obs[t], 0.9)
+    saved = b.tobytes()
+    c = np.frombuffer(saved, np.float32).copy()
+    for t in range(8, 16):
+        c = oracle.amax_accumulate(c, obs[t], 0.9)
+    np.testing.assert_array_equal(a, c)

@@ -1,0 +1,181 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4: the bf16 -> NVFP4 block-scaled cast on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (TransformerEngine PR #3045, "Add NVFP4 per-token
+ * quantization recipe": Description, Changes, and the sequence diagram of its
+ * review summary):
+ *   - an outer fp32 amax: one per tensor (the NVFP4BlockScaling default), or
+ *     per token -- a vector of length M for rowwise output and a vector of
+ *     length K for columnwise output;
+ *   - per 16-element block, an FP8 E4M3 block scale relative to the outer
+ *     scale S = amax / (6 * 448);
+ *   - each element encoded to E2M1 and packed two per byte.
+ * Exact arithmetic, for a vector v with outer amax A and block j:
+ *   S = A/2688;  sf_j = (max|v in j| / 6) / S;  c_j = E4M3_rne_sat(sf_j);
+ *   r_j = decode(c_j) * S;  nibble_i = E2M1_rne_sat(v_i / r_j)
+ * with every step one IEEE binary32 operation rounded to nearest-even, and
+ * S == 0 or r_j == 0 giving scale code 0 and sign-only nibbles.  The fp32
+ * order of the block-scale formula follows the reading of the FP8 block-scale
+ * discussion on Model-Optimizer PR #2598 (amax/6 relative to the global
+ * scale); results are bit-identical to the library's CPU reference.
+ *
+ * Conventions shared by every entry point
+ *   - x is bf16, contiguous row-major [M][K] (or [T][K] for grouped), on the
+ *     device.  All other arrays are device memory owned by the caller; the
+ *     library allocates nothing, keeps no state between calls (beyond a
+ *     thread-local error string) and never reads outputs before writing them.
+ *   - Rowwise output ("row_*"): row_q [M][K/2] bytes, row_sf [M][K/16] E4M3
+ *     codes, row_amax fp32.  Columnwise output ("col_*") is the quantization
+ *     of the transpose: col_q [K][M/2], col_sf [K][M/16], col_amax fp32.
+ *     Element 2i sits in the low nibble of its byte; a nibble is
+ *     sign<<3 | E2M1 magnitude code; scales are row-major and unswizzled.
+ *   - amax lengths: per-tensor [1]; per-token rowwise [M], columnwise [K];
+ *     16x16 tiles [M] and [K] filled with the tensor amax.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work and return; results are ready when the stream reaches them.
+ *   - Validation runs on the host before anything is enqueued.  On any
+ *     non-OK status nothing was launched and nvfp4_last_error() names the
+ *     problem.  NVFP4_EINVAL: NULL input, no direction requested, a NULL
+ *     output in a requested direction, bad mode, decay outside [0,1],
+ *     negative size.  NVFP4_ESHAPE: K % 16 (rowwise), M % 16 (columnwise),
+ *     both for 16x16 tiles, group counts negative / not % 16 / not summing.
+ *     NVFP4_EALIGN: a pointer not 16-byte aligned (amax/observed arrays need
+ *     4-byte alignment).  NVFP4_EDEVICE: a HIP call or launch failed.
+ *   - Outputs must not overlap the input or each other.  Inputs are assumed
+ *     finite; a NaN or Inf input gives unspecified codes.
+ *   - Any shape meeting the % 16 rules is accepted; all shapes give results
+ *     bit-identical to the CPU reference.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define NVFP4_API __attribute__((visibility("default")))
+#else
+#define NVFP4_API
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_EINVAL = 1,
+    NVFP4_ESHAPE = 2,
+    NVFP4_EALIGN = 3,
+    NVFP4_EDEVICE = 4
+} nvfp4_status;
+
+typedef enum {
+    NVFP4_PER_TENSOR = 0,   /* one outer amax per tensor */
+    NVFP4_PER_TOKEN = 1,    /* per-row amax (rowwise), per-column amax (columnwise) */
+    NVFP4_TILE_16x16 = 2    /* one E4M3 scale per 16x16 tile, per-tensor amax */
+} nvfp4_scaling;
+
+NVFP4_API int nvfp4_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+NVFP4_API const char* nvfp4_last_error(void);
+
+/*
+ * Whole cast, one read of x serving both directions.  Pass NULL for all three
+ * pointers of a direction that is not wanted (at least one must be wanted).
+ * PER_TENSOR / PER_TOKEN follow the Description of the per-token recipe page;
+ * TILE_16x16 is its opt-in 2D weight mode ("Changes": transposition-invariant
+ * 16x16 cast emitted in per-token layout): one E4M3 code per tile relative to
+ * the per-tensor outer scale, row_sf[m][J] = col_sf[k][I] = code of tile (I,J)
+ * with I = m/16, J = k/16; nibbles identical in both directions.
+ */
+NVFP4_API nvfp4_status nvfp4_quantize(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                            uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                            uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                            void* stream);
+
+/* One direction only (same as nvfp4_quantize with the other direction NULL). */
+NVFP4_API nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                    uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                    void* stream);
+NVFP4_API nvfp4_status nvfp4_quantize_columnwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                       uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                                       void* stream);
+
+/*
+ * Split form, first half: outer amax only ("K1 vector amax" on the per-token
+ * page).  PER_TENSOR writes the tensor amax to whichever of row_amax /
+ * col_amax is non-NULL ([1] each); PER_TOKEN writes row_amax [M] and/or
+ * col_amax [K].  TILE_16x16 is not accepted here (it is PER_TENSOR's amax).
+ */
+NVFP4_API nvfp4_status nvfp4_amax(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                        float* row_amax, float* col_amax, void* stream);
+
+/*
+ * Split form, second half ("K2 encode"): block scales and E2M1 data from
+ * caller-supplied outer amax (e.g. calibrated values kept by
+ * nvfp4_amax_accumulate).  PER_TENSOR reads row_amax[0] / col_amax[0];
+ * PER_TOKEN reads row_amax [M] / col_amax [K].  An amax smaller than the
+ * data's saturates: the block scale clamps to 448 (0x7E) and elements to 6.
+ * A direction is requested by non-NULL q and sf (its amax must then be
+ * non-NULL too).
+ */
+NVFP4_API nvfp4_status nvfp4_encode(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                          const float* row_amax, const float* col_amax,
+                          uint8_t* row_q, uint8_t* row_sf,
+                          uint8_t* col_q, uint8_t* col_sf, void* stream);
+
+/*
+ * Grouped (MoE) per-token cast in one call: x holds T = sum(h_counts) rows of
+ * K values, expert e owning rows [o_e, o_e + h_counts[e]) (the grouped
+ * helper on the per-token page; zero-count experts are accepted -- they are
+ * common under dynamic routing, as that page's review notes).
+ *   rowwise  : per-token rowwise of all T rows: row_q [T][K/2], row_sf
+ *              [T][K/16], row_amax [T];
+ *   columnwise: per expert e, the columnwise quantization of its slice at
+ *              byte offsets K*o_e/2 (col_q, [K][m_e/2]) and K*o_e/16
+ *              (col_sf, [K][m_e/16]); col_amax is [num_groups][K] (a zero
+ *              row for an empty expert).
+ * h_counts is a HOST array of num_groups int64 values, each >= 0 and % 16.
+ */
+NVFP4_API nvfp4_status nvfp4_quantize_grouped(const void* x, int64_t K, int32_t num_groups,
+                                    const int64_t* h_counts,
+                                    uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                    uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                                    void* stream);
+
+/*
+ * Dequantize R vectors of C values (C % 16 == 0) from q [R][C/2], sf
+ * [R][C/16] and amax ([1] if amax_per_row == 0, else [R]) to fp32 out [R][C]:
+ * out = (+/-) g * (decode(sf) * (amax / 2688)), the product computed exactly
+ * as in the cast.  Columnwise buffers are passed with R = K, C = M.  This is
+ * the reference dequantization the per-token page pairs with its quantizer.
+ */
+NVFP4_API nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* amax,
+                              int64_t R, int64_t C, int amax_per_row, float* out,
+                              void* stream);
+
+/*
+ * Decayed calibration accumulator from the PTQ scaling-factor page
+ * (TransformerEngine PR #3296, Description): buf[i] = max(buf[i] * decay,
+ * observed[i]) for i < n, in fp32.  decay 0 keeps the latest value, decay 1
+ * the maximum over the whole history.  decay must lie in [0, 1].
+ */
+NVFP4_API nvfp4_status nvfp4_amax_accumulate(float* buf, const float* observed, int64_t n, float decay,
+                                   void* stream);
+
+/*
+ * Scalar form for per-token recipes: the same page max-reduces the row-wise
+ * vector to a scalar, so buf[0] = max(buf[0] * decay, max_i observed[i]) (an
+ * empty vector observes 0).
+ */
+NVFP4_API nvfp4_status nvfp4_amax_accumulate_reduce(float* buf, const float* observed, int64_t n,
+                                          float decay, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

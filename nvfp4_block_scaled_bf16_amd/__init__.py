@@ -1,0 +1,222 @@
+"""bf16 -> NVFP4 block-scaled cast on AMD MI355X (gfx950).
+
+Thin Python binding of ``libnvfp4.so`` (the C ABI declared in
+``include/nvfp4.h``).  This module only marshals arguments: it allocates the
+output tensors with torch on the input's device, passes raw device pointers
+and the current HIP stream, and raises on a non-OK status.  Every step of the
+cast runs in the library's HIP kernels; there is no fallback, so a missing or
+unloadable library is an error.
+
+Layouts (see the header): rowwise ``row_q`` [M, K/2] uint8 (element 2i in the
+low nibble), ``row_sf`` [M, K/16] E4M3 codes, ``row_amax`` fp32; columnwise
+(the quantization of the transpose) ``col_q`` [K, M/2], ``col_sf`` [K, M/16],
+``col_amax``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PER_TENSOR, PER_TOKEN, TILE_16x16 = 0, 1, 2
+_MODES = {"per_tensor": PER_TENSOR, "per_token": PER_TOKEN, "tile_16x16": TILE_16x16,
+          PER_TENSOR: PER_TENSOR, PER_TOKEN: PER_TOKEN, TILE_16x16: TILE_16x16}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+
+EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_quantize_rowwise",
+           "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
+           "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce")
+
+STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"nvfp4 {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnvfp4.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, f32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int
+    sig = {
+        "nvfp4_abi_version": (ctypes.c_int, []),
+        "nvfp4_last_error": (ctypes.c_char_p, []),
+        "nvfp4_quantize": (st, [p, i64, i64, st, p, p, p, p, p, p, p]),
+        "nvfp4_quantize_rowwise": (st, [p, i64, i64, st, p, p, p, p]),
+        "nvfp4_quantize_columnwise": (st, [p, i64, i64, st, p, p, p, p]),
+        "nvfp4_amax": (st, [p, i64, i64, st, p, p, p]),
+        "nvfp4_encode": (st, [p, i64, i64, st, p, p, p, p, p, p, p]),
+        "nvfp4_quantize_grouped": (st, [p, i64, i32, p, p, p, p, p, p, p, p]),
+        "nvfp4_dequantize": (st, [p, p, p, i64, i64, ctypes.c_int, p, p]),
+        "nvfp4_amax_accumulate": (st, [p, p, i64, f32, p]),
+        "nvfp4_amax_accumulate_reduce": (st, [p, p, i64, f32, p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise NVFP4Error(status, lib().nvfp4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _input(x):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 CUDA tensor")
+    return x
+
+
+def _mode(mode):
+    try:
+        return _MODES[mode]
+    except KeyError:
+        raise ValueError(f"unknown scaling mode {mode!r}") from None
+
+
+def _u8(shape, dev):
+    return torch.empty(shape, dtype=torch.uint8, device=dev)
+
+
+def _f32(shape, dev):
+    return torch.empty(shape, dtype=torch.float32, device=dev)
+
+
+def _amax_len(mode, n):
+    return 1 if mode == PER_TENSOR else n
+
+
+def quantize(x: torch.Tensor, mode="per_token", rowwise: bool = True, columnwise: bool = True) -> dict:
+    """Whole cast (one read of x for both directions)."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    dev = x.device
+    out = {}
+    if rowwise:
+        out.update(row_q=_u8((M, K // 2), dev), row_sf=_u8((M, K // 16), dev), row_amax=_f32(_amax_len(mode, M), dev))
+    if columnwise:
+        out.update(col_q=_u8((K, M // 2), dev), col_sf=_u8((K, M // 16), dev), col_amax=_f32(_amax_len(mode, K), dev))
+    g = out.get
+    _check(lib().nvfp4_quantize(_ptr(x), M, K, mode, _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
+                                _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")), _stream(dev)))
+    return out
+
+
+def quantize_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, col_sf=None, col_amax=None):
+    """Whole cast into caller-provided buffers (no allocation)."""
+    x = _input(x)
+    M, K = x.shape
+    _check(lib().nvfp4_quantize(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
+                                _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _stream(x.device)))
+
+
+def quantize_rowwise(x, mode="per_token"):
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    q, sf, a = _u8((M, K // 2), x.device), _u8((M, K // 16), x.device), _f32(_amax_len(mode, M), x.device)
+    _check(lib().nvfp4_quantize_rowwise(_ptr(x), M, K, mode, _ptr(q), _ptr(sf), _ptr(a), _stream(x.device)))
+    return {"row_q": q, "row_sf": sf, "row_amax": a}
+
+
+def quantize_columnwise(x, mode="per_token"):
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    q, sf, a = _u8((K, M // 2), x.device), _u8((K, M // 16), x.device), _f32(_amax_len(mode, K), x.device)
+    _check(lib().nvfp4_quantize_columnwise(_ptr(x), M, K, mode, _ptr(q), _ptr(sf), _ptr(a), _stream(x.device)))
+    return {"col_q": q, "col_sf": sf, "col_amax": a}
+
+
+def amax(x, mode="per_token", rowwise=True, columnwise=True):
+    """Outer amax only (split form, first half)."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    ra = _f32(_amax_len(mode, M), x.device) if rowwise else None
+    ca = _f32(_amax_len(mode, K), x.device) if columnwise else None
+    _check(lib().nvfp4_amax(_ptr(x), M, K, mode, _ptr(ra), _ptr(ca), _stream(x.device)))
+    return {"row_amax": ra, "col_amax": ca}
+
+
+def encode(x, mode="per_token", row_amax=None, col_amax=None):
+    """Block scales + E2M1 data from caller-supplied amax (split form)."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    out = {}
+    if row_amax is not None:
+        out.update(row_q=_u8((M, K // 2), x.device), row_sf=_u8((M, K // 16), x.device))
+    if col_amax is not None:
+        out.update(col_q=_u8((K, M // 2), x.device), col_sf=_u8((K, M // 16), x.device))
+    g = out.get
+    _check(lib().nvfp4_encode(_ptr(x), M, K, mode, _ptr(row_amax), _ptr(col_amax), _ptr(g("row_q")),
+                              _ptr(g("row_sf")), _ptr(g("col_q")), _ptr(g("col_sf")), _stream(x.device)))
+    return out
+
+
+def quantize_grouped(x, counts, rowwise=True, columnwise=True):
+    """Grouped (MoE) per-token cast; counts: host sequence of per-expert rows."""
+    x = _input(x)
+    T, K = x.shape
+    counts_t = torch.as_tensor(list(counts), dtype=torch.int64).contiguous()
+    G = counts_t.numel()
+    dev = x.device
+    out = {}
+    if rowwise:
+        out.update(row_q=_u8((T, K // 2), dev), row_sf=_u8((T, K // 16), dev), row_amax=_f32(T, dev))
+    if columnwise:
+        out.update(col_q=_u8(T * K // 2, dev), col_sf=_u8(T * K // 16, dev), col_amax=_f32((G, K), dev))
+    g = out.get
+    _check(lib().nvfp4_quantize_grouped(_ptr(x), K, G, ctypes.c_void_p(counts_t.data_ptr()),
+                                        _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
+                                        _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")), _stream(dev)))
+    return out
+
+
+def dequantize(q, sf, amax, amax_per_row: bool):
+    """fp32 [R, C] from q [R, C/2], sf [R, C/16] and amax ([1] or [R])."""
+    R, C2 = q.shape
+    C = 2 * C2
+    out = _f32((R, C), q.device)
+    _check(lib().nvfp4_dequantize(_ptr(q), _ptr(sf), _ptr(amax), R, C, int(bool(amax_per_row)), _ptr(out),
+                                  _stream(q.device)))
+    return out
+
+
+def amax_accumulate(buf, observed, decay: float):
+    """In place: buf = max(buf * decay, observed), fp32."""
+    if buf.numel() != observed.numel():
+        raise ValueError("buf and observed must have the same length")
+    _check(lib().nvfp4_amax_accumulate(_ptr(buf), _ptr(observed), buf.numel(), float(decay), _stream(buf.device)))
+    return buf
+
+
+def amax_accumulate_reduce(buf, observed, decay: float):
+    """In place: buf[0] = max(buf[0] * decay, max(observed))."""
+    _check(lib().nvfp4_amax_accumulate_reduce(_ptr(buf), _ptr(observed), observed.numel(), float(decay),
+                                              _stream(buf.device)))
+    return buf

@@ -1,0 +1,294 @@
+// nvfp4_api.cpp -- the C ABI of libnvfp4 (declared in include/nvfp4.h):
+// host-side validation, then stream-ordered launches.  Nothing is enqueued
+// unless every check passes; the library allocates no memory.
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "nvfp4_device.hpp"
+#include "nvfp4_fused.h"
+#include "nvfp4_internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+nvfp4_status ok() {
+    g_last_error.clear();
+    return NVFP4_OK;
+}
+
+nvfp4_status check_hip(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(NVFP4_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return NVFP4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Dir {
+    bool want;
+    nvfp4_status st;
+};
+
+// a direction is requested when any of its pointers is given; then all of
+// them must be given
+Dir direction(const char* name, const void* q, const void* sf, const void* amax) {
+    int given = (q != nullptr) + (sf != nullptr) + (amax != nullptr);
+    if (given == 0) return {false, NVFP4_OK};
+    if (given != 3) return {true, fail(NVFP4_EINVAL, "%s output: q, sf and amax must all be given (or all NULL)", name)};
+    if (!aligned(q, 16)) return {true, fail(NVFP4_EALIGN, "%s_q must be 16-byte aligned", name)};
+    if (!aligned(amax, 4)) return {true, fail(NVFP4_EALIGN, "%s_amax must be 4-byte aligned", name)};
+    return {true, NVFP4_OK};
+}
+
+nvfp4_status check_shape(int64_t M, int64_t K, bool row, bool col, int mode) {
+    if (M < 0 || K < 0) return fail(NVFP4_EINVAL, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (row && K % 16 != 0) return fail(NVFP4_ESHAPE, "rowwise output needs K %% 16 == 0 (K=%lld)", (long long)K);
+    if (col && M % 16 != 0) return fail(NVFP4_ESHAPE, "columnwise output needs M %% 16 == 0 (M=%lld)", (long long)M);
+    if (col && K % 8 != 0) return fail(NVFP4_ESHAPE, "columnwise output needs K %% 8 == 0 (K=%lld)", (long long)K);
+    if (mode == NVFP4_TILE_16x16 && (M % 16 != 0 || K % 16 != 0))
+        return fail(NVFP4_ESHAPE, "16x16 tiles need M and K multiples of 16 (M=%lld K=%lld)", (long long)M, (long long)K);
+    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 40)) return fail(NVFP4_ESHAPE, "size too large");
+    return NVFP4_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+GroupTable empty_table() {
+    GroupTable gt;
+    gt.n = 0;
+    gt.first = 0;
+    return gt;
+}
+
+// zero-fill up to two fp32 arrays before an atomic-max pass
+nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
+    nvfp4_status s;
+    if (a && na > 0 && (s = check_hip(launch_fill(a, na, 0.0f, st), "fill")) != NVFP4_OK) return s;
+    if (b && nb > 0 && (s = check_hip(launch_fill(b, nb, 0.0f, st), "fill")) != NVFP4_OK) return s;
+    return NVFP4_OK;
+}
+
+nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode,
+                           uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                           uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+    if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN && mode != NVFP4_TILE_16x16)
+        return fail(NVFP4_EINVAL, "unknown scaling mode %d", (int)mode);
+    Dir r = direction("row", row_q, row_sf, row_amax);
+    if (r.st != NVFP4_OK) return r.st;
+    Dir c = direction("col", col_q, col_sf, col_amax);
+    if (c.st != NVFP4_OK) return c.st;
+    if (!r.want && !c.want) return fail(NVFP4_EINVAL, "no output direction requested");
+    nvfp4_status s = check_shape(M, K, r.want, c.want, mode);
+    if (s != NVFP4_OK) return s;
+    if (xv == nullptr) return fail(NVFP4_EINVAL, "x is NULL");
+    if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
+    const uint16_t* x = static_cast<const uint16_t*>(xv);
+    hipStream_t st = as_stream(stream);
+    float* ra = r.want ? row_amax : nullptr;
+    float* ca = c.want ? col_amax : nullptr;
+    const GroupTable gt = empty_table();
+
+    if (mode == NVFP4_PER_TOKEN) {
+        if ((s = zero(ra, M, ca, K, st)) != NVFP4_OK) return s;
+        if (M == 0 || K == 0) return ok();
+        if (fused_per_token_supported(M, K, r.want, c.want)) {
+            if ((s = check_hip(fused_per_token(x, M, K, row_q, row_sf, ra, col_q, col_sf, ca, st), "fused cast")) != NVFP4_OK) return s;
+            return ok();
+        }
+        if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if ((s = check_hip(launch_encode(ENC_TOKEN, r.want, c.want, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                         nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
+        return ok();
+    }
+    // per-tensor and 16x16 tiles: one tensor amax
+    if ((s = zero(ra, ra ? (mode == NVFP4_TILE_16x16 ? M : 1) : 0, ca, ca ? (mode == NVFP4_TILE_16x16 ? K : 1) : 0, st)) != NVFP4_OK) return s;
+    if (M == 0 || K == 0) return ok();
+    if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, st), "amax")) != NVFP4_OK) return s;
+    const int emode = mode == NVFP4_TILE_16x16 ? ENC_TILE : ENC_TENSOR;
+    if ((s = check_hip(launch_encode(emode, r.want, c.want, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st),
+                       "encode")) != NVFP4_OK)
+        return s;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+nvfp4_status nvfp4_quantize(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                            uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                            uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+    return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream);
+}
+
+nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                    uint8_t* row_q, uint8_t* row_sf, float* row_amax, void* stream) {
+    if (!row_q || !row_sf || !row_amax) return fail(NVFP4_EINVAL, "rowwise outputs must not be NULL");
+    return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, nullptr, nullptr, nullptr, stream);
+}
+
+nvfp4_status nvfp4_quantize_columnwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                       uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+    if (!col_q || !col_sf || !col_amax) return fail(NVFP4_EINVAL, "columnwise outputs must not be NULL");
+    return quantize_impl(x, M, K, mode, nullptr, nullptr, nullptr, col_q, col_sf, col_amax, stream);
+}
+
+nvfp4_status nvfp4_amax(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode,
+                        float* row_amax, float* col_amax, void* stream) {
+    if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN)
+        return fail(NVFP4_EINVAL, "nvfp4_amax takes PER_TENSOR or PER_TOKEN (mode %d)", (int)mode);
+    if (!row_amax && !col_amax) return fail(NVFP4_EINVAL, "no amax output given");
+    if ((row_amax && !aligned(row_amax, 4)) || (col_amax && !aligned(col_amax, 4)))
+        return fail(NVFP4_EALIGN, "amax outputs must be 4-byte aligned");
+    if (M < 0 || K < 0) return fail(NVFP4_EINVAL, "negative size");
+    if (K % 8 != 0) return fail(NVFP4_ESHAPE, "nvfp4_amax needs K %% 8 == 0 (K=%lld)", (long long)K);
+    if (!xv) return fail(NVFP4_EINVAL, "x is NULL");
+    if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
+    const uint16_t* x = static_cast<const uint16_t*>(xv);
+    hipStream_t st = as_stream(stream);
+    const GroupTable gt = empty_table();
+    nvfp4_status s;
+    if (mode == NVFP4_PER_TOKEN) {
+        if ((s = zero(row_amax, M, col_amax, K, st)) != NVFP4_OK) return s;
+        if (M == 0 || K == 0) return ok();
+        if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, row_amax, col_amax, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        return ok();
+    }
+    if ((s = zero(row_amax, row_amax ? 1 : 0, col_amax, col_amax ? 1 : 0, st)) != NVFP4_OK) return s;
+    if (M == 0 || K == 0) return ok();
+    if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, row_amax, col_amax, gt, st), "amax")) != NVFP4_OK) return s;
+    return ok();
+}
+
+nvfp4_status nvfp4_encode(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode,
+                          const float* row_amax, const float* col_amax,
+                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf, void* stream) {
+    if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN)
+        return fail(NVFP4_EINVAL, "nvfp4_encode takes PER_TENSOR or PER_TOKEN (mode %d)", (int)mode);
+    Dir r = direction("row", row_q, row_sf, row_amax);
+    if (r.st != NVFP4_OK) return r.st;
+    Dir c = direction("col", col_q, col_sf, col_amax);
+    if (c.st != NVFP4_OK) return c.st;
+    if (!r.want && !c.want) return fail(NVFP4_EINVAL, "no output direction requested");
+    nvfp4_status s = check_shape(M, K, r.want, c.want, mode);
+    if (s != NVFP4_OK) return s;
+    if (!xv) return fail(NVFP4_EINVAL, "x is NULL");
+    if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
+    if (M == 0 || K == 0) return ok();
+    const GroupTable gt = empty_table();
+    if ((s = check_hip(launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want,
+                                     static_cast<const uint16_t*>(xv), M, K, 0, M, row_amax, col_amax,
+                                     row_q, row_sf, col_q, col_sf, nullptr, nullptr, gt, as_stream(stream)),
+                       "encode")) != NVFP4_OK)
+        return s;
+    return ok();
+}
+
+nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_groups, const int64_t* h_counts,
+                                    uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                    uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+    if (num_groups < 0) return fail(NVFP4_EINVAL, "num_groups < 0");
+    if (num_groups > 0 && !h_counts) return fail(NVFP4_EINVAL, "h_counts is NULL");
+    Dir r = direction("row", row_q, row_sf, row_amax);
+    if (r.st != NVFP4_OK) return r.st;
+    Dir c = direction("col", col_q, col_sf, col_amax);
+    if (c.st != NVFP4_OK) return c.st;
+    if (!r.want && !c.want) return fail(NVFP4_EINVAL, "no output direction requested");
+    int64_t T = 0;
+    for (int32_t e = 0; e < num_groups; ++e) {
+        if (h_counts[e] < 0 || h_counts[e] % 16 != 0)
+            return fail(NVFP4_ESHAPE, "group %d has %lld rows; counts must be >= 0 and multiples of 16", e, (long long)h_counts[e]);
+        T += h_counts[e];
+    }
+    nvfp4_status s = check_shape(T, K, r.want, c.want, NVFP4_PER_TOKEN);
+    if (s != NVFP4_OK) return s;
+    if (!xv && T > 0) return fail(NVFP4_EINVAL, "x is NULL");
+    if (xv && !aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
+    const uint16_t* x = static_cast<const uint16_t*>(xv);
+    hipStream_t st = as_stream(stream);
+    float* ra = r.want ? row_amax : nullptr;
+    float* ca = c.want ? col_amax : nullptr;
+    if ((s = zero(ra, T, ca, (int64_t)num_groups * K, st)) != NVFP4_OK) return s;
+    if (T == 0 || K == 0) return ok();
+    if (!c.want) {
+        const GroupTable gt = empty_table();
+        if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, T, ra, nullptr, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if ((s = check_hip(launch_encode(ENC_TOKEN, true, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
+                                         nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
+        return ok();
+    }
+    // experts travel in the kernel arguments, a bounded number per launch
+    int64_t off = 0;
+    for (int32_t e0 = 0; e0 < num_groups; e0 += kMaxGroupsPerLaunch) {
+        GroupTable gt;
+        gt.n = 0;
+        gt.first = e0;
+        const int64_t begin = off;
+        for (int32_t e = e0; e < num_groups && e < e0 + kMaxGroupsPerLaunch; ++e) {
+            gt.off[gt.n] = off;
+            gt.cnt[gt.n] = h_counts[e];
+            off += h_counts[e];
+            ++gt.n;
+        }
+        const int64_t end = off;
+        if (end == begin) continue;
+        if ((s = check_hip(launch_amax(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if ((s = check_hip(launch_encode(ENC_GROUPED, r.want, true, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
+                                         nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
+    }
+    return ok();
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
+                              int amax_per_row, float* out, void* stream) {
+    if (R < 0 || C < 0) return fail(NVFP4_EINVAL, "negative size");
+    if (C % 16 != 0) return fail(NVFP4_ESHAPE, "dequantize needs C %% 16 == 0 (C=%lld)", (long long)C);
+    if (R == 0 || C == 0) return ok();
+    if (!q || !sf || !amax || !out) return fail(NVFP4_EINVAL, "NULL argument");
+    if (!aligned(q, 8) || !aligned(out, 16) || !aligned(amax, 4)) return fail(NVFP4_EALIGN, "q needs 8-byte, out 16-byte, amax 4-byte alignment");
+    nvfp4_status s = check_hip(launch_dequant(q, sf, amax, R, C, amax_per_row ? 1 : 0, out, as_stream(stream)), "dequantize");
+    return s != NVFP4_OK ? s : ok();
+}
+
+nvfp4_status nvfp4_amax_accumulate(float* buf, const float* observed, int64_t n, float decay, void* stream) {
+    if (n < 0) return fail(NVFP4_EINVAL, "n < 0");
+    if (!(decay >= 0.0f && decay <= 1.0f)) return fail(NVFP4_EINVAL, "decay must lie in [0, 1]");
+    if (n == 0) return ok();
+    if (!buf || !observed) return fail(NVFP4_EINVAL, "NULL argument");
+    if (!aligned(buf, 4) || !aligned(observed, 4)) return fail(NVFP4_EALIGN, "buffers must be 4-byte aligned");
+    nvfp4_status s = check_hip(launch_accumulate(buf, observed, n, decay, as_stream(stream)), "accumulate");
+    return s != NVFP4_OK ? s : ok();
+}
+
+nvfp4_status nvfp4_amax_accumulate_reduce(float* buf, const float* observed, int64_t n, float decay, void* stream) {
+    if (n < 0) return fail(NVFP4_EINVAL, "n < 0");
+    if (!(decay >= 0.0f && decay <= 1.0f)) return fail(NVFP4_EINVAL, "decay must lie in [0, 1]");
+    if (!buf || (n > 0 && !observed)) return fail(NVFP4_EINVAL, "NULL argument");
+    if (!aligned(buf, 4) || (observed && !aligned(observed, 4))) return fail(NVFP4_EALIGN, "buffers must be 4-byte aligned");
+    nvfp4_status s = check_hip(launch_accumulate_reduce(buf, observed, n, decay, as_stream(stream)), "accumulate");
+    return s != NVFP4_OK ? s : ok();
+}
+
+}  // extern "C"

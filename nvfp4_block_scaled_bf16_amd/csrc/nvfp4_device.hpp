@@ -1,0 +1,156 @@
+// nvfp4_device.hpp -- device-side building blocks of the bf16 -> NVFP4 cast
+// for gfx950 (CDNA4).  Every floating-point step is one IEEE binary32 op
+// rounded to nearest-even (the library is built with -ffp-contract=off and
+// fp32 denormals preserved); fused multiply-adds appear only where written.
+//
+// The arithmetic follows the per-token NVFP4 recipe page (TransformerEngine
+// PR #3045, "Add NVFP4 per-token quantization recipe": outer amax per tensor
+// or per row/column, 16-element E4M3 block scale relative to the outer scale,
+// E2M1 data two per byte) with the block-scale order read from the FP8
+// block-scale discussion on Model-Optimizer PR #2598:
+//   S = A / 2688;  sf = (b / 6) / S;  code = E4M3(sf);  r = decode(code) * S;
+//   nibble = E2M1(v / r)   (S == 0 or r == 0: code 0, sign-only nibble).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ bf16 helpers
+
+// a 32-bit word holds two bf16 values: element 2i in the low half
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// elementwise max of two packed pairs of bf16 magnitudes (sign bits cleared
+// by the caller): magnitude bit patterns order like the values they encode
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    u16x2 x = __builtin_bit_cast(u16x2, a), y = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+__device__ __forceinline__ uint32_t abs2(uint32_t w) { return w & 0x7fff7fffu; }
+__device__ __forceinline__ uint32_t max_halves(uint32_t w) {
+    uint32_t lo = w & 0xffffu, hi = w >> 16;
+    return lo > hi ? lo : hi;
+}
+// magnitude bits (16-bit) -> fp32 value
+__device__ __forceinline__ float mag_to_f32(uint32_t m16) { return __uint_as_float(m16 << 16); }
+
+// --------------------------------------------------------------- E4M3 code
+
+// RNE onto OCP E4M3 (bias 7, 3 mantissa bits), saturating at 448 (0x7E);
+// s >= 0.  Written from the format definition with integer rounding of the
+// fp32 encoding; independent of the CPU reference's formulation.
+__device__ __forceinline__ uint32_t e4m3_code(float s) {
+    if (!(s < 448.0f)) return 0x7Eu;
+    uint32_t u = __float_as_uint(s);
+    if (u < 0x3C800000u) {
+        // below 2^-6: code = RNE(s * 2^9), s * 2^9 < 8 exact; adding 2^23
+        // leaves a unit spacing, so the addition performs the rounding
+        float t = s * 512.0f + 8388608.0f;
+        return __float_as_uint(t) - 0x4B000000u;
+    }
+    // round the 23-bit mantissa to 3 bits, ties to even; a carry moves into
+    // the exponent as it should
+    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    return (r >> 20) - 0x3C0u;  // rebias 127 -> 7 (120 << 3)
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+    // code < 8: subnormal m * 2^-9; otherwise exponent field + 120 in fp32
+    return code < 8u ? (float)code * 0.001953125f : __uint_as_float((code << 20) + 0x3C000000u);
+}
+
+// ------------------------------------------------------------ block state
+
+struct BlockScale {
+    float r;        // decode(code) * S: the divisor of every element
+    float y;        // RN(1 / r), for the FMA-corrected quotient
+    uint32_t code;  // E4M3 byte
+    bool zero;      // r == 0: sign-only nibbles
+    bool fast;      // the FMA-corrected quotient is exact for this block
+};
+
+// S: outer scale of the vector (A / 2688); bmag: block max magnitude bits
+__device__ __forceinline__ BlockScale block_scale(uint32_t bmag, float S) {
+    BlockScale bs;
+    if (S == 0.0f) {
+        bs.r = 0.0f; bs.y = 0.0f; bs.code = 0u; bs.zero = true; bs.fast = true;
+        return bs;
+    }
+    float b = mag_to_f32(bmag);
+    float t = b / 6.0f;
+    float sf = t / S;
+    bs.code = e4m3_code(sf);
+    bs.r = e4m3_value(bs.code) * S;
+    bs.zero = bs.r == 0.0f;
+    bs.y = 1.0f / bs.r;
+    // the three-op quotient below equals IEEE division whenever r and the
+    // quotients stay in this range (checked exhaustively on the host)
+    bs.fast = bs.zero || (bs.r >= 0x1p-64f && bs.r <= 0x1p64f && b * bs.y <= 0x1p64f);
+    return bs;
+}
+
+// q = RN(a / r).  fast: Markstein's correction of a * (1/r) with one fma for
+// the residual (written r*q0 - a so that -0 keeps its sign) and one for the
+// update; otherwise IEEE division.  zero: a signed zero.
+__device__ __forceinline__ float quotient(float a, const BlockScale& bs) {
+    if (bs.zero) return a * 0.0f;
+    if (bs.fast) {
+        float q0 = a * bs.y;
+        float e = __builtin_fmaf(bs.r, q0, -a);
+        return __builtin_fmaf(-e, bs.y, q0);
+    }
+    return a / bs.r;
+}
+
+// E2M1 of two quotients into byte SEL of `old`: gfx950's scaled FP4
+// conversion with scale 1.0 rounds to nearest-even on the E2M1 grid and
+// saturates at 6 (verified against the rounding table over every fp32 input);
+// src0 lands in the low nibble.
+template <int SEL>
+__device__ __forceinline__ uint32_t put_fp4x2(uint32_t old, float q0, float q1) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, 1.0f, SEL);
+}
+
+// encode 8 bf16 values held in 4 words (elements 0..7 in order) -> 32 bits
+__device__ __forceinline__ uint32_t encode8(u32x4 w, const BlockScale& bs) {
+    uint32_t o = 0;
+    o = put_fp4x2<0>(o, quotient(bf_lo(w.x), bs), quotient(bf_hi(w.x), bs));
+    o = put_fp4x2<1>(o, quotient(bf_lo(w.y), bs), quotient(bf_hi(w.y), bs));
+    o = put_fp4x2<2>(o, quotient(bf_lo(w.z), bs), quotient(bf_hi(w.z), bs));
+    o = put_fp4x2<3>(o, quotient(bf_lo(w.w), bs), quotient(bf_hi(w.w), bs));
+    return o;
+}
+
+// outer scale from an outer amax
+__device__ __forceinline__ float outer_scale(float A) { return A / 2688.0f; }
+
+// ----------------------------------------------------------- grouped table
+
+// Experts for the grouped cast travel in the kernel arguments: row offsets
+// (multiples of 16) and counts.
+constexpr int kMaxGroupsPerLaunch = 128;
+struct GroupTable {
+    int32_t n;
+    int32_t first;                        // index of table entry 0 among all experts
+    int64_t off[kMaxGroupsPerLaunch];     // first row of each expert
+    int64_t cnt[kMaxGroupsPerLaunch];     // rows of each expert
+};
+
+// expert owning row r (r inside the table's span): the last entry whose
+// offset is <= r, which skips empty experts sharing that offset
+__device__ __forceinline__ int group_of_row(const GroupTable& gt, int64_t r) {
+    int lo = 0, hi = gt.n - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (gt.off[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,27 @@
+// nvfp4_internal.h -- launchers shared between the C ABI (nvfp4_api.cpp) and
+// the kernel translation units.  Not part of the public interface.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct GroupTable;
+
+enum AmaxKind { AMAX_TENSOR = 0, AMAX_TOKEN = 1, AMAX_GROUPED = 2 };
+enum EncodeMode { ENC_TENSOR = 0, ENC_TOKEN = 1, ENC_TILE = 2, ENC_GROUPED = 3 };
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
+                       float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
+                       hipStream_t st);
+hipError_t launch_encode(int mode, bool row, bool col, const uint16_t* x, int64_t M, int64_t K,
+                         int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
+                         uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
+                         float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st);
+hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
+                          int amax_per_row, float* out, hipStream_t st);
+hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);
+hipError_t launch_accumulate_reduce(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);
+
+}  // namespace nvfp4

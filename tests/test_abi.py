@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/nvfp4.h declares, and its host-side validation rejects bad arguments
+with the documented status before anything is launched (only argument sets
+that fail validation are passed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_bf16_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+EINVAL, ESHAPE, EALIGN = 1, 2, 3
+FAKE = 0x10000  # an aligned address that is never dereferenced: validation fails first
+
+
+def declared():
+    with open(HEADER) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]*?\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared() == sorted(nv.EXPORTS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = nv.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+    assert L.nvfp4_abi_version() == 1
+
+
+def _q(*args):
+    return nv.lib().nvfp4_quantize(*args)
+
+
+P = ctypes.c_void_p
+
+
+def test_quantize_validation():
+    L = nv.lib()
+    f = P(FAKE)
+    # no direction requested
+    assert _q(f, 16, 16, 1, None, None, None, None, None, None, None) == EINVAL
+    assert b"direction" in L.nvfp4_last_error()
+    # partial direction
+    assert _q(f, 16, 16, 1, f, None, f, None, None, None, None) == EINVAL
+    # bad mode
+    assert _q(f, 16, 16, 7, f, f, f, None, None, None, None) == EINVAL
+    # negative size
+    assert _q(f, -16, 16, 1, f, f, f, None, None, None, None) == EINVAL
+    # rowwise needs K % 16
+    assert _q(f, 16, 24, 1, f, f, f, None, None, None, None) == ESHAPE
+    # columnwise needs M % 16 and K % 8
+    assert _q(f, 20, 16, 1, None, None, None, f, f, f, None) == ESHAPE
+    assert _q(f, 16, 12, 1, None, None, None, f, f, f, None) == ESHAPE
+    # 16x16 tiles need both
+    assert _q(f, 16, 24, 2, None, None, None, f, f, f, None) == ESHAPE
+    # NULL input
+    assert _q(None, 16, 16, 1, f, f, f, None, None, None, None) == EINVAL
+    # misaligned input / outputs / amax
+    assert _q(P(FAKE + 2), 16, 16, 1, f, f, f, None, None, None, None) == EALIGN
+    assert _q(f, 16, 16, 1, P(FAKE + 8), f, f, None, None, None, None) == EALIGN
+    assert _q(f, 16, 16, 1, f, f, P(FAKE + 2), None, None, None, None) == EALIGN
+
+
+def test_other_entry_points_validation():
+    L = nv.lib()
+    f = P(FAKE)
+    assert L.nvfp4_quantize_rowwise(f, 16, 16, 1, None, f, f, None) == EINVAL
+    assert L.nvfp4_quantize_columnwise(f, 16, 16, 1, f, None, f, None) == EINVAL
+    assert L.nvfp4_amax(f, 16, 16, 2, f, f, None) == EINVAL          # tiles not accepted
+    assert L.nvfp4_amax(f, 16, 16, 1, None, None, None) == EINVAL
+    assert L.nvfp4_amax(f, 16, 12, 1, f, None, None) == ESHAPE
+    assert L.nvfp4_encode(f, 16, 16, 2, f, None, f, f, None, None, None) == EINVAL
+    assert L.nvfp4_encode(f, 16, 16, 1, None, None, f, f, None, None, None) == EINVAL
+    assert L.nvfp4_dequantize(f, f, f, 4, 24, 1, f, None) == ESHAPE
+    assert L.nvfp4_dequantize(None, f, f, 4, 32, 1, f, None) == EINVAL
+    assert L.nvfp4_amax_accumulate(f, f, 4, ctypes.c_float(1.5), None) == EINVAL
+    assert L.nvfp4_amax_accumulate(f, f, 4, ctypes.c_float(-0.1), None) == EINVAL
+    assert L.nvfp4_amax_accumulate(f, f, 4, ctypes.c_float(float("nan")), None) == EINVAL
+    assert L.nvfp4_amax_accumulate(f, f, -1, ctypes.c_float(0.5), None) == EINVAL
+    assert L.nvfp4_amax_accumulate_reduce(None, f, 4, ctypes.c_float(0.5), None) == EINVAL
+
+
+def test_grouped_validation():
+    L = nv.lib()
+    f = P(FAKE)
+    bad = (ctypes.c_int64 * 3)(16, 8, 0)
+    assert L.nvfp4_quantize_grouped(f, 32, 3, bad, f, f, f, f, f, f, None) == ESHAPE
+    neg = (ctypes.c_int64 * 2)(16, -16)
+    assert L.nvfp4_quantize_grouped(f, 32, 2, neg, f, f, f, f, f, f, None) == ESHAPE
+    good = (ctypes.c_int64 * 2)(16, 32)
+    assert L.nvfp4_quantize_grouped(f, 24, 2, good, f, f, f, None, None, None, None) == ESHAPE
+    assert L.nvfp4_quantize_grouped(f, 32, -1, good, f, f, f, None, None, None, None) == EINVAL
+    assert L.nvfp4_quantize_grouped(f, 32, 2, None, f, f, f, None, None, None, None) == EINVAL
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        nv.quantize(torch.zeros(16, 16, dtype=torch.bfloat16))

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact on every output byte (packed E2M1 data, E4M3 scale codes) and on
+the fp32 amax bit patterns.  Small shapes span several workgroup tiles and a
+ragged tail; the full-size workloads are compared in full where the oracle
+finishes in seconds, otherwise on sampled rows / columns / tiles that the
+oracle computes one by one, plus the complete amax vectors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_bf16_amd as nv
+from nvfp4_block_scaled_bf16_amd import workloads as W
+from tests.gpu_util import assert_bytes_equal, compare_cast, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MODES = [nv.PER_TENSOR, nv.PER_TOKEN, nv.TILE_16x16]
+# several 512-column tiles and 64/256-row tiles, with ragged tails
+SHAPES = [(16, 16), (32, 512), (48, 1040), (272, 528), (1072, 544), (64, 8192), (2048, 48)]
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _x(M, K, seed):
+    return W.row_scaled_with_outliers(M, K, seed)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_cast_small_shapes(oracle, mode, shape):
+    M, K = shape
+    x = _x(M, K, 100 + M + K)
+    _announce(f"quantize mode={mode} shape={shape}")
+    out = nv.quantize(to_dev(x), mode)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, mode))
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+def test_rowwise_only_ragged_rows(oracle, mode):
+    x = _x(37, 96, 7)
+    _announce(f"rowwise 37x96 mode={mode}")
+    out = nv.quantize_rowwise(to_dev(x), mode)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, mode, rowwise=True, columnwise=False))
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+def test_columnwise_only_narrow(oracle, mode):
+    x = _x(48, 24, 8)
+    _announce(f"columnwise 48x24 mode={mode}")
+    out = nv.quantize_columnwise(to_dev(x), mode)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, mode, rowwise=False, columnwise=True))
+
+
+def _crafted(M=64, K=1024, seed=3):
+    """Zeros, negative zeros, bf16 subnormals, huge values, exact grid ties,
+    blocks whose scale rounds to a subnormal or to zero."""
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal((M, K)).astype(np.float32)
+    f[0] = 0.0
+    f[1, :64] = -0.0
+    f[2, 5] = 2688.0
+    f[2, 16:32] = 1e-4
+    f[2, 32:48] = 3e-7
+    f[3] = (rng.integers(-12, 13, K) * 0.25).astype(np.float32)   # exact ties with S = 1
+    f[3, 0] = 2688.0
+    f[4] = np.float32(2.0 ** -130) * rng.integers(-3, 4, K)       # bf16 subnormals
+    f[5] = np.float32(3.0e38) * rng.choice([-1.0, 1.0], K).astype(np.float32)
+    f[6, ::2] = -0.0
+    f[7] = rng.standard_normal(K).astype(np.float32) * np.float32(1e-38)
+    f[:, 7] = 0.0
+    f[:, 9] = -0.0
+    f[8:24, 100] = 6.0 * 448.0
+    return W.bf16_from_f32(f)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_crafted_edges(oracle, mode):
+    x = _crafted()
+    _announce(f"crafted 64x1024 mode={mode}")
+    out = nv.quantize(to_dev(x), mode)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, mode))
+
+
+def test_all_zero_and_single_row(oracle):
+    for shape in [(16, 32), (1, 16)]:
+        x = np.zeros(shape, np.uint16)
+        x.reshape(-1)[3] = 0x8000
+        for mode in (nv.PER_TENSOR, nv.PER_TOKEN):
+            _announce(f"zeros {shape} mode={mode}")
+            col = shape[0] % 16 == 0
+            out = nv.quantize(to_dev(x), mode, rowwise=True, columnwise=col)
+            torch.cuda.synchronize()
+            compare_cast(out, oracle.quantize(x, mode, rowwise=True, columnwise=col))
+
+
+def test_encode_with_supplied_amax_saturates(oracle):
+    x = _x(64, 512, 9)
+    true_r, true_c = oracle.amax_rows(x), oracle.amax_cols(x)
+    for fr, fc in [(1 / 64.0, 1 / 16.0), (3.0, 0.5), (1.0, 1.0)]:
+        ra = (true_r * np.float32(fr)).astype(np.float32)
+        ca = (true_c * np.float32(fc)).astype(np.float32)
+        _announce(f"encode per-token factors {fr} {fc}")
+        out = nv.encode(to_dev(x), nv.PER_TOKEN, torch.from_numpy(ra).cuda(), torch.from_numpy(ca).cuda())
+        torch.cuda.synchronize()
+        q, sf = oracle.encode_rowwise(x, ra, True)
+        assert_bytes_equal(host(out["row_q"]), q, "row_q")
+        assert_bytes_equal(host(out["row_sf"]), sf, "row_sf")
+        q, sf = oracle.encode_colwise(x, ca, True)
+        assert_bytes_equal(host(out["col_q"]), q, "col_q")
+        assert_bytes_equal(host(out["col_sf"]), sf, "col_sf")
+    # per-tensor with different rowwise / columnwise scalars
+    ra = np.array([oracle.amax_tensor(x) * np.float32(0.25)], np.float32)
+    ca = np.array([oracle.amax_tensor(x) * np.float32(2.0)], np.float32)
+    _announce("encode per-tensor, different scalars")
+    out = nv.encode(to_dev(x), nv.PER_TENSOR, torch.from_numpy(ra).cuda(), torch.from_numpy(ca).cuda())
+    torch.cuda.synchronize()
+    q, sf = oracle.encode_rowwise(x, ra, False)
+    assert_bytes_equal(host(out["row_q"]), q, "row_q")
+    assert_bytes_equal(host(out["row_sf"]), sf, "row_sf")
+    q, sf = oracle.encode_colwise(x, ca, False)
+    assert_bytes_equal(host(out["col_q"]), q, "col_q")
+    assert_bytes_equal(host(out["col_sf"]), sf, "col_sf")
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+def test_split_amax(oracle, mode):
+    x = _x(272, 1040, 10)
+    _announce(f"amax 272x1040 mode={mode}")
+    out = nv.amax(to_dev(x), mode)
+    torch.cuda.synchronize()
+    if mode == nv.PER_TOKEN:
+        assert_bytes_equal(host(out["row_amax"]), oracle.amax_rows(x), "row_amax")
+        assert_bytes_equal(host(out["col_amax"]), oracle.amax_cols(x), "col_amax")
+    else:
+        A = np.array([oracle.amax_tensor(x)], np.float32)
+        assert_bytes_equal(host(out["row_amax"]), A, "row_amax")
+        assert_bytes_equal(host(out["col_amax"]), A, "col_amax")
+
+
+def _grouped_case(counts, K, seed):
+    rng = np.random.default_rng(seed)
+    T = int(sum(counts))
+    scales = rng.uniform(0.5, 4.0, len(counts)).astype(np.float32)
+    f = rng.standard_normal((T, K)).astype(np.float32) * np.repeat(scales, counts)[:, None]
+    return W.bf16_from_f32(f)
+
+
+@pytest.mark.parametrize("counts,K", [([32, 0, 16, 48, 0, 16, 128], 96),
+                                      ([0, 0, 64], 512),
+                                      ([16] * 70 + [0] * 40 + [32] * 30, 48),
+                                      ([256, 512, 0, 128], 1040)])
+def test_grouped_small(oracle, counts, K):
+    x = _grouped_case(counts, K, len(counts))
+    _announce(f"grouped experts={len(counts)} T={sum(counts)} K={K}")
+    out = nv.quantize_grouped(to_dev(x), counts)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_grouped(x, np.array(counts, np.int64)))
+
+
+def test_dequantize_roundtrip(oracle):
+    x = W.c1()
+    _announce("C1 dequantize")
+    d = to_dev(x)
+    out = nv.quantize(d, nv.PER_TENSOR)
+    back = nv.dequantize(out["row_q"], out["row_sf"], out["row_amax"], amax_per_row=False)
+    backc = nv.dequantize(out["col_q"], out["col_sf"], out["col_amax"], amax_per_row=False)
+    tok = nv.quantize(d, nv.PER_TOKEN)
+    backt = nv.dequantize(tok["col_q"], tok["col_sf"], tok["col_amax"], amax_per_row=True)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(x, nv.PER_TENSOR)
+    assert_bytes_equal(host(back), oracle.dequantize(ref["row_q"], ref["row_sf"], ref["row_amax"], 256, 1024, False), "row deq")
+    assert_bytes_equal(host(backc), oracle.dequantize(ref["col_q"], ref["col_sf"], ref["col_amax"], 1024, 256, False), "col deq")
+    reft = oracle.quantize(x, nv.PER_TOKEN)
+    assert_bytes_equal(host(backt), oracle.dequantize(reft["col_q"], reft["col_sf"], reft["col_amax"], 1024, 256, True), "tok deq")
+
+
+@pytest.mark.parametrize("decay", [0.0, 0.9, 1.0])
+def test_accumulate(oracle, decay):
+    rng = np.random.default_rng(int(decay * 10) + 1)
+    obs = (np.abs(rng.standard_normal((12, 1000))) * np.exp(rng.normal(0, 2, (12, 1)))).astype(np.float32)
+    buf = torch.zeros(1000, dtype=torch.float32, device="cuda:0")
+    sbuf = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    ref = np.zeros(1000, np.float32)
+    sref = np.zeros(1, np.float32)
+    _announce(f"accumulate decay={decay}")
+    for t in range(12):
+        o = torch.from_numpy(obs[t]).cuda()
+        nv.amax_accumulate(buf, o, decay)
+        nv.amax_accumulate_reduce(sbuf, o, decay)
+        ref = oracle.amax_accumulate(ref, obs[t], decay)
+        sref = oracle.amax_accumulate_reduce(sref, obs[t], decay)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(buf), ref, "buf")
+    assert_bytes_equal(host(sbuf), sref, "sbuf")
+
+
+# ------------------------------------------------------- named workloads
+
+def test_c1_per_tensor_rowwise(oracle):
+    x = W.c1()
+    _announce("C1 256x1024 per-tensor rowwise")
+    out = nv.quantize(to_dev(x), nv.PER_TENSOR, rowwise=True, columnwise=False)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.PER_TENSOR, rowwise=True, columnwise=False))
+
+
+def test_c2_per_token_full(oracle):
+    x = W.c2()
+    _announce("C2 4096x4096 per-token row+col")
+    d = to_dev(x)
+    out = nv.quantize(d, nv.PER_TOKEN)
+    again = nv.quantize(d, nv.PER_TOKEN)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
+    for k in out:
+        assert torch.equal(out[k], again[k]), f"run-to-run difference in {k}"
+
+
+def _sample_vectors(x, out, mode, rows, cols, oracle):
+    xf = W.bf16_to_f32(x)
+    if mode == nv.PER_TOKEN:
+        ra = host(out["row_amax"])
+        ca = host(out["col_amax"])
+        assert_bytes_equal(ra, oracle.amax_rows(x), "row_amax")
+        assert_bytes_equal(ca, oracle.amax_cols(x), "col_amax")
+    else:
+        A = np.float32(oracle.amax_tensor(x))
+        assert_bytes_equal(host(out["row_amax"]), np.array([A], np.float32), "row_amax")
+        ra = np.full(x.shape[0], A, np.float32)
+        ca = np.full(x.shape[1], A, np.float32)
+    rq, rs = host(out["row_q"]), host(out["row_sf"])
+    cq, cs = host(out["col_q"]), host(out["col_sf"])
+    for r in rows:
+        q, sf = oracle.quantize_vector(xf[r], ra[r])
+        assert_bytes_equal(rq[r], q, f"row_q[{r}]")
+        assert_bytes_equal(rs[r], sf, f"row_sf[{r}]")
+    for c in cols:
+        q, sf = oracle.quantize_vector(np.ascontiguousarray(xf[:, c]), ca[c])
+        assert_bytes_equal(cq[c], q, f"col_q[{c}]")
+        assert_bytes_equal(cs[c], sf, f"col_sf[{c}]")
+
+
+def test_c3_per_token_full(oracle):
+    x = W.c3(0)
+    _announce("C3 16384x8192 per-token row+col (full compare)")
+    out = nv.quantize(to_dev(x), nv.PER_TOKEN)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
+
+
+def test_c3_sixteen_iterations_with_decay(oracle):
+    """Per-tensor and per-token casts of 16 seeded tensors; the per-tensor
+    amax (= max of the per-token row amax) feeds buf = max(buf*0.9, A)."""
+    rng = np.random.default_rng(33)
+    buf = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    buf_tok = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    ref = np.zeros(1, np.float32)
+    for t in range(16):
+        x = W.c3(t)
+        _announce(f"C3 iteration {t}")
+        d = to_dev(x)
+        pt = nv.quantize(d, nv.PER_TENSOR)
+        tok = nv.quantize(d, nv.PER_TOKEN)
+        nv.amax_accumulate(buf, pt["row_amax"], 0.9)
+        nv.amax_accumulate_reduce(buf_tok, tok["row_amax"], 0.9)
+        torch.cuda.synchronize()
+        ref = oracle.amax_accumulate(ref, np.array([oracle.amax_tensor(x)], np.float32), 0.9)
+        assert_bytes_equal(host(buf), ref, f"decayed buffer after iteration {t}")
+        assert_bytes_equal(host(buf_tok), ref, f"decayed buffer (per-token feed) after iteration {t}")
+        if t in (0, 15):
+            rows = list(rng.choice(16384, 24, replace=False)) + [0, 16383]
+            cols = list(rng.choice(8192, 24, replace=False)) + [0, 8191]
+            _sample_vectors(x, pt, nv.PER_TENSOR, rows, cols, oracle)
+            _sample_vectors(x, tok, nv.PER_TOKEN, rows, cols, oracle)
+
+
+def test_c4_grouped_moe(oracle):
+    x, counts = W.c4()
+    assert int(counts.sum()) == 32768 and (counts % 128 == 0).all()
+    _announce(f"C4 grouped 64 experts, zero-count experts: {int((counts == 0).sum())}")
+    out = nv.quantize_grouped(to_dev(x), counts.tolist())
+    torch.cuda.synchronize()
+    ref = oracle.quantize_grouped(x, counts)
+    compare_cast(out, ref)
+
+
+def test_c5_tile_16x16_full(oracle):
+    x = W.c5()
+    _announce("C5 8192x28672 16x16 tiles (full compare)")
+    out = nv.quantize(to_dev(x), nv.TILE_16x16)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.TILE_16x16))

@@ -113,7 +113,7 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
             return ok();
         }
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = check_hip(launch_encode(ENC_TOKEN, r.want, c.want, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+        if ((s = check_hip(launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
                                          nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
         return ok();
     }
@@ -122,7 +122,7 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (M == 0 || K == 0) return ok();
     if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, st), "amax")) != NVFP4_OK) return s;
     const int emode = mode == NVFP4_TILE_16x16 ? ENC_TILE : ENC_TENSOR;
-    if ((s = check_hip(launch_encode(emode, r.want, c.want, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+    if ((s = check_hip(launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
                                      emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st),
                        "encode")) != NVFP4_OK)
         return s;
@@ -198,7 +198,7 @@ nvfp4_status nvfp4_encode(const void* xv, int64_t M, int64_t K, nvfp4_scaling mo
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     if (M == 0 || K == 0) return ok();
     const GroupTable gt = empty_table();
-    if ((s = check_hip(launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want,
+    if ((s = check_hip(launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want, true,
                                      static_cast<const uint16_t*>(xv), M, K, 0, M, row_amax, col_amax,
                                      row_q, row_sf, col_q, col_sf, nullptr, nullptr, gt, as_stream(stream)),
                        "encode")) != NVFP4_OK)
@@ -235,7 +235,7 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
     if (!c.want) {
         const GroupTable gt = empty_table();
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, T, ra, nullptr, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = check_hip(launch_encode(ENC_TOKEN, true, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
+        if ((s = check_hip(launch_encode(ENC_TOKEN, true, false, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
                                          nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
         return ok();
     }
@@ -255,7 +255,7 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
         const int64_t end = off;
         if (end == begin) continue;
         if ((s = check_hip(launch_amax(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = check_hip(launch_encode(ENC_GROUPED, r.want, true, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
+        if ((s = check_hip(launch_encode(ENC_GROUPED, r.want, true, false, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
                                          nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
     }
     return ok();

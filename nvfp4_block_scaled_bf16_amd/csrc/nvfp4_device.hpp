@@ -130,6 +130,89 @@ __device__ __forceinline__ uint32_t encode8(u32x4 w, const BlockScale& bs) {
 // outer scale from an outer amax
 __device__ __forceinline__ float outer_scale(float A) { return A / 2688.0f; }
 
+// ------------------------------------------------------------- fast path
+//
+// The hot loops avoid IEEE division.  Facts, each checked exhaustively (1 and
+// 1b on the host by tests/native/div_identity_check.c, 2 and 3 on the GPU):
+//  1. for a bf16 numerator a and divisor r with y = RN(1/r), the sequence
+//     q0 = a*y; e = fma(r, q0, -a); q = fma(-e, y, q0) returns RN(a/r)
+//     (Markstein's correction) whenever r is in [2^-64, 2^64] and |a|*y <=
+//     2^64, signed zeros included;
+//  1b. the same sequence returns RN(t/S) for t = RN(b/6), b bf16, and any
+//     normal S (t has only 128 significands, each checked against every
+//     significand of S);
+//  2. v_rcp_f32 followed by one Newton step, fma(fma(-r, y0, 1), y0, y0),
+//     returns RN(1/r) for every normal r in [2^-64, 2^64];
+//  3. the scaled FP4 conversion rounds like the E2M1 table (put_fp4x2).
+// Blocks outside these ranges, or whose scale falls in the E4M3 subnormal
+// range, take an exact slow path chosen per wave.
+
+// RN(1/r) for normal r in [2^-64, 2^64]
+__device__ __forceinline__ float rcp_rn(float r) {
+    float y0 = __builtin_amdgcn_rcpf(r);
+    float e = __builtin_fmaf(-r, y0, 1.0f);
+    return __builtin_fmaf(e, y0, y0);
+}
+
+// RN(a / r) given y = RN(1/r), under the range conditions of fact 1
+__device__ __forceinline__ float div_fast(float a, float r, float y) {
+    float q0 = a * y;
+    float e = __builtin_fmaf(r, q0, -a);
+    return __builtin_fmaf(-e, y, q0);
+}
+
+// outer scale of one vector with its reciprocal
+struct Outer {
+    float S, yS;
+    bool slow;   // A outside [2^-40, 2^60] (or tiny enough for S to underflow): exact path
+};
+
+// A == 0 uses S = yS = 1: every block of such a vector is all zeros and the
+// fast block below encodes it as code 0 with sign-only nibbles.
+__device__ __forceinline__ Outer make_outer(float A) {
+    Outer o;
+    const bool zero = A == 0.0f;
+    o.S = zero ? 1.0f : outer_scale(A);
+    o.yS = rcp_rn(o.S);
+    o.slow = !zero && !(A >= 0x1p-40f && A <= 0x1p60f);
+    return o;
+}
+
+// Per-block parameters on the fast path: r = decode(code) * S and y = RN(1/r).
+// slow: this block needs the exact path.
+struct FastBlock {
+    float r, y;
+    uint32_t code;
+    bool slow;
+};
+
+constexpr float kRcp6 = 0x1.555556p-3f;   // RN(1/6)
+
+// SAT: the outer amax may be smaller than the data (caller-supplied amax),
+// so the block scale may saturate and quotients exceed 6.4.
+template <bool SAT>
+__device__ __forceinline__ FastBlock fast_block(uint32_t bmag, const Outer& o) {
+    FastBlock fb;
+    const float b = mag_to_f32(bmag);
+    const float t = div_fast(b, 6.0f, kRcp6);   // RN(b / 6)   (fact 1: b is bf16)
+    const float sf = div_fast(t, o.S, o.yS);    // RN(t / S)   (fact 1b: t = RN(b/6))
+    const uint32_t u = __float_as_uint(sf);
+    // E4M3 code of sf: round the mantissa to 3 bits, ties to even, then clamp
+    // to [code 0, 0x7E].  The lower clamp gives code 0 for all-zero blocks
+    // (their elements are +/-0, so the divisor's value does not matter); the
+    // upper one saturates at 448.
+    uint32_t c = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
+    c = c < 0x3C0u ? 0x3C0u : (c > 0x43Eu ? 0x43Eu : c);
+    fb.code = c - 0x3C0u;
+    fb.r = __uint_as_float(c << 20) * o.S;     // decode(code) * S; 2^-7 * S for code 0
+    fb.y = rcp_rn(fb.r);
+    // sf in the E4M3 subnormal range (and not an all-zero block): exact path
+    bool slow = (u - 1u) < (0x3C800000u - 1u);
+    if (SAT) slow |= !(fb.r <= 0x1p64f && b * fb.y <= 0x1p64f);
+    fb.slow = slow || o.slow;
+    return fb;
+}
+
 // ----------------------------------------------------------- grouped table
 
 // Experts for the grouped cast travel in the kernel arguments: row offsets

@@ -15,7 +15,7 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
                        float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
                        hipStream_t st);
-hipError_t launch_encode(int mode, bool row, bool col, const uint16_t* x, int64_t M, int64_t K,
+hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const uint16_t* x, int64_t M, int64_t K,
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st);

@@ -17,7 +17,7 @@ namespace nvfp4 {
 
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
 constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass
-constexpr int kEncRows = 64;       // rows per workgroup tile in the encode pass
+constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass
 
 // --------------------------------------------------------------- utilities
 
@@ -195,80 +195,83 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
 
 // -------------------------------------------------------------- encode pass
 
-// MODE: ENC_TENSOR (amax[0] for every vector), ENC_TOKEN (row_amax[r],
-// col_amax[c]), ENC_TILE (16x16 tiles, tensor amax in row_amax[0]; also fills
-// row_amax[1..M) and col_amax[1..K) with it), ENC_GROUPED (rowwise per-token;
-// columnwise per expert with col_amax[e][K] and per-expert output slabs).
-template <int MODE, bool ROW, bool COL>
-__global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                int64_t row_begin, int64_t row_end,
-                                                const float* __restrict__ row_amax, const float* __restrict__ col_amax,
-                                                uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_sf,
-                                                uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,
-                                                float* __restrict__ fill_row, float* __restrict__ fill_col,
-                                                GroupTable gt) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * kTileCols + lane * 8;
-    const int64_t r0 = row_begin + (int64_t)blockIdx.y * kEncRows + wave * 16;
-    const bool col_ok = c0 < K;
-    if (MODE == ENC_TILE) {
-        // broadcast the tensor amax into the per-token-layout vectors
-        const float A = row_amax ? row_amax[0] : col_amax[0];
-        const int64_t gid = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-        const int64_t gsz = (int64_t)gridDim.x * gridDim.y * blockDim.x;
-        if (fill_row) for (int64_t i = 1 + gid; i < M; i += gsz) fill_row[i] = A;
-        if (fill_col) for (int64_t i = 1 + gid; i < K; i += gsz) fill_col[i] = A;
+// exact per-element quotient for the slow path
+__device__ __forceinline__ float quotient_exact(float a, const BlockScale& bs) {
+    return bs.zero ? a * 0.0f : a / bs.r;
+}
+
+// element k (0..7) of a 16x8 sub-block row held as 4 words
+__device__ __forceinline__ float elem(const u32x4& w, int k) {
+    const uint32_t word = (k >> 1) == 0 ? w.x : (k >> 1) == 1 ? w.y : (k >> 1) == 2 ? w.z : w.w;
+    return (k & 1) ? bf_hi(word) : bf_lo(word);
+}
+
+// DPP: value of the neighbouring lane (lane ^ 1)
+__device__ __forceinline__ uint32_t from_pair(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t rowmax_word(const u32x4& w) {
+    return pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
+}
+
+// Where a lane's sub-block results go.  Columnwise data of column c, rows
+// [r0, r0+16) of a vector of length m_len starting at row grow0.
+struct SubDst {
+    uint8_t* row_q; uint8_t* row_sf; uint8_t* col_q; uint8_t* col_sf;
+    int64_t K, r0, c0, row_end, m_len, grow0;
+    bool col_ok, even;
+};
+
+__device__ __forceinline__ void store_row(const SubDst& d, int i, uint32_t q, uint32_t code) {
+    const int64_t r = d.r0 + i;
+    if (d.col_ok && r < d.row_end) {
+        *reinterpret_cast<uint32_t*>(d.row_q + r * (d.K / 2) + d.c0 / 2) = q;
+        if (d.even) d.row_sf[r * (d.K / 16) + d.c0 / 16] = (uint8_t)code;
     }
-    if (r0 >= row_end || !col_ok) return;
+}
 
-    u32x4 v[16];
-    load_subblock(x, K, r0, row_end, c0, true, v);
+__device__ __forceinline__ void store_row_pair(const SubDst& d, int i, uint32_t q0, uint32_t q1, uint32_t own_code) {
+    if (!d.col_ok) return;
+    const int64_t r = d.r0 + i;
+    if (r < d.row_end) *reinterpret_cast<uint32_t*>(d.row_q + r * (d.K / 2) + d.c0 / 2) = q0;
+    if (r + 1 < d.row_end) *reinterpret_cast<uint32_t*>(d.row_q + (r + 1) * (d.K / 2) + d.c0 / 2) = q1;
+    const int64_t ro = d.even ? r : r + 1;
+    if (ro < d.row_end) d.row_sf[ro * (d.K / 16) + d.c0 / 16] = (uint8_t)own_code;
+}
 
-    // per-tensor outer scales (the split encode may carry different rowwise
-    // and columnwise amax values); 16x16 tiles use the single tensor amax
-    float S_row = 0.0f, S_col = 0.0f, S_tensor = 0.0f;
-    if (MODE == ENC_TENSOR) {
-        if (ROW) S_row = outer_scale(row_amax[0]);
-        if (COL) S_col = outer_scale(col_amax[0]);
-    }
-    if (MODE == ENC_TILE) S_tensor = outer_scale(row_amax ? row_amax[0] : col_amax[0]);
+__device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, uint32_t hi, uint32_t code) {
+    if (!d.col_ok) return;
+    const int64_t c = d.c0 + j;
+    uint8_t* qb = d.col_q + d.grow0 * d.K / 2;
+    uint8_t* sb = d.col_sf + d.grow0 * d.K / 16;
+    *reinterpret_cast<u32x2*>(qb + c * (d.m_len / 2) + (d.r0 - d.grow0) / 2) = u32x2{lo, hi};
+    sb[c * (d.m_len / 16) + (d.r0 - d.grow0) / 16] = (uint8_t)code;
+}
 
-    // 16x16 tile: one scale from the max over the tile (this lane's 16x8 half
-    // and the neighbour's)
-    BlockScale tile_bs;
-    if (MODE == ENC_TILE) {
-        uint32_t a = 0u;
+// Fast encode and store of one lane's 16x8 sub-block.  Row outer scales are
+// wave-uniform (rowS/rowYS per row, a bit mask of rows needing the exact
+// path); colO are this lane's 8 columns; tileO the tensor's (16x16 tiles).
+// The two lanes of a pair share every rowwise block: each computes the
+// parameters of one row of every row pair (row 2s + parity) and the pair
+// swaps them.  Returns true if some block needs the exact path, in which
+// case the caller re-encodes the sub-block exactly over what was stored.
+template <bool ROW, bool COL, bool TILE, bool SAT>
+__device__ __forceinline__ bool encode_fast(const u32x4 v[16], const float* rowS, const float* rowYS,
+                                            uint32_t row_slow, const Outer* colO, const Outer& tileO,
+                                            const SubDst& d) {
+    const bool odd = !d.even;
+    bool slow = false;
+    FastBlock cb[8];
+    FastBlock tb;
+    if (TILE) {
+        uint32_t m = 0u;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            a = pk_max_u16(a, pk_max_u16(pk_max_u16(abs2(v[i].x), abs2(v[i].y)), pk_max_u16(abs2(v[i].z), abs2(v[i].w))));
-        uint32_t m = max_halves(a);
-        uint32_t o = (uint32_t)__shfl_xor((int)m, 1);
-        tile_bs = block_scale(m > o ? m : o, S_tensor);
-    }
-
-    if (ROW) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t r = r0 + i;
-            uint32_t a = pk_max_u16(pk_max_u16(abs2(v[i].x), abs2(v[i].y)), pk_max_u16(abs2(v[i].z), abs2(v[i].w)));
-            uint32_t hm = max_halves(a);
-            uint32_t other = (uint32_t)__shfl_xor((int)hm, 1);
-            if (r >= row_end) continue;
-            BlockScale bs;
-            if (MODE == ENC_TILE) {
-                bs = tile_bs;
-            } else {
-                float S = (MODE == ENC_TENSOR) ? S_row : outer_scale(row_amax[r]);
-                bs = block_scale(hm > other ? hm : other, S);
-            }
-            uint32_t packed = encode8(v[i], bs);
-            *reinterpret_cast<uint32_t*>(row_q + r * (K / 2) + c0 / 2) = packed;
-            if ((lane & 1) == 0) row_sf[r * (K / 16) + c0 / 16] = (uint8_t)bs.code;
-        }
-    }
-
-    if (COL) {
-        // column maxima over the 16 rows, packed pairs of columns
+        for (int i = 0; i < 16; ++i) m = pk_max_u16(m, rowmax_word(v[i]));
+        m = pk_max_u16(m, from_pair(m));
+        tb = fast_block<SAT>(max_halves(m), tileO);
+        slow = tb.slow;
+    } else if (COL) {
         uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -277,46 +280,226 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             cm[2] = pk_max_u16(cm[2], abs2(v[i].z));
             cm[3] = pk_max_u16(cm[3], abs2(v[i].w));
         }
-        // where this sub-block's columnwise output goes
-        int64_t m_len = M, row0 = 0, amax_row = 0;
-        if (MODE == ENC_GROUPED) {
-            int g = group_of_row(gt, r0);
-            m_len = gt.cnt[g];
-            row0 = gt.off[g];
-            amax_row = (int64_t)(gt.first + g) * K;
-        }
-        uint8_t* qbase = col_q + row0 * K / 2;
-        uint8_t* sbase = col_sf + row0 * K / 16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t c = c0 + j;
-            const uint32_t w = cm[j >> 1];
-            const uint32_t bmag = (j & 1) ? (w >> 16) : (w & 0xffffu);
-            BlockScale bs;
-            if (MODE == ENC_TILE) {
-                bs = tile_bs;
+            cb[j] = fast_block<SAT>((j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xffffu), colO[j]);
+            slow |= cb[j].slow;
+        }
+    }
+    uint32_t cq[8][2];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        float a[2][8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { a[0][k] = elem(v[i], k); a[1][k] = elem(v[i + 1], k); }
+        if (ROW) {
+            float rr[2], ry[2];
+            uint32_t own_code;
+            if (TILE) {
+                rr[0] = rr[1] = tb.r; ry[0] = ry[1] = tb.y; own_code = tb.code;
             } else {
-                float S = (MODE == ENC_TENSOR) ? S_col : outer_scale(col_amax[amax_row + c]);
-                bs = block_scale(bmag, S);
+                uint32_t f0 = rowmax_word(v[i]), f1 = rowmax_word(v[i + 1]);
+                f0 = pk_max_u16(f0, from_pair(f0));
+                f1 = pk_max_u16(f1, from_pair(f1));
+                Outer ro;
+                ro.S = odd ? rowS[i + 1] : rowS[i];
+                ro.yS = odd ? rowYS[i + 1] : rowYS[i];
+                ro.slow = (row_slow >> (i + (odd ? 1 : 0))) & 1u;
+                const FastBlock f = fast_block<SAT>(max_halves(odd ? f1 : f0), ro);
+                slow |= f.slow;
+                const float pr = __uint_as_float(from_pair(__float_as_uint(f.r)));
+                const float py = __uint_as_float(from_pair(__float_as_uint(f.y)));
+                rr[0] = odd ? pr : f.r; ry[0] = odd ? py : f.y;
+                rr[1] = odd ? f.r : pr; ry[1] = odd ? f.y : py;
+                own_code = f.code;
             }
-            float e[16];
+            uint32_t w[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t q = 0u;
+                q = put_fp4x2<0>(q, div_fast(a[h][0], rr[h], ry[h]), div_fast(a[h][1], rr[h], ry[h]));
+                q = put_fp4x2<1>(q, div_fast(a[h][2], rr[h], ry[h]), div_fast(a[h][3], rr[h], ry[h]));
+                q = put_fp4x2<2>(q, div_fast(a[h][4], rr[h], ry[h]), div_fast(a[h][5], rr[h], ry[h]));
+                q = put_fp4x2<3>(q, div_fast(a[h][6], rr[h], ry[h]), div_fast(a[h][7], rr[h], ry[h]));
+                w[h] = q;
+            }
+            store_row_pair(d, i, w[0], w[1], own_code);
+        }
+        if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const FastBlock& f = TILE ? tb : cb[j];
+                const float q0 = div_fast(a[0][j], f.r, f.y), q1 = div_fast(a[1][j], f.r, f.y);
+                uint32_t& w = cq[j][i >> 3];
+                const int byte = (i >> 1) & 3;
+                if (byte == 0) w = put_fp4x2<0>(0u, q0, q1);
+                else if (byte == 1) w = put_fp4x2<1>(w, q0, q1);
+                else if (byte == 2) w = put_fp4x2<2>(w, q0, q1);
+                else w = put_fp4x2<3>(w, q0, q1);
+            }
+        }
+    }
+    if (COL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) store_col(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
+    }
+    return slow;
+}
+
+// Exact encode and store of a sub-block with IEEE divisions throughout,
+// re-reading the data.  rowA: amax of row r0+i for lanes 0..15 (lane i holds
+// row i's), broadcast here; colA: this lane's 8 column amax; tileA: tensor's.
+template <bool ROW, bool COL, bool TILE>
+__device__ __noinline__ void encode_exact(const uint16_t* __restrict__ x, float rowA_lane, float colA0, float colA1,
+                                          float colA2, float colA3, float colA4, float colA5, float colA6,
+                                          float colA7, float tileA, SubDst d) {
+    u32x4 v[16];
+    load_subblock(x, d.K, d.r0, d.row_end, d.c0, d.col_ok, v);
+    const float colA[8] = {colA0, colA1, colA2, colA3, colA4, colA5, colA6, colA7};
+    if (TILE) {
+        uint32_t m = 0u;
+        for (int i = 0; i < 16; ++i) m = pk_max_u16(m, rowmax_word(v[i]));
+        m = pk_max_u16(m, from_pair(m));
+        const BlockScale bs = block_scale(max_halves(m), outer_scale(tileA));
+        for (int i = 0; i < 16; ++i) {
+            uint32_t w = 0u;
+            for (int k = 0; k < 8; k += 2)
+                w |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], k), bs),
+                                                              quotient_exact(elem(v[i], k + 1), bs), 1.0f, 0) & 0xffu) << (4 * k);
+            if (ROW) store_row(d, i, w, bs.code);
+        }
+        if (COL)
+            for (int j = 0; j < 8; ++j) {
+                uint32_t lohi[2] = {0u, 0u};
+                for (int i = 0; i < 16; i += 2)
+                    lohi[i >> 3] |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], j), bs),
+                                                                         quotient_exact(elem(v[i + 1], j), bs), 1.0f, 0) & 0xffu) << (8 * ((i >> 1) & 3));
+                store_col(d, j, lohi[0], lohi[1], bs.code);
+            }
+        return;
+    }
+    if (ROW) {
+        for (int i = 0; i < 16; ++i) {
+            const float A = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rowA_lane), i));
+            uint32_t hw = rowmax_word(v[i]);
+            hw = pk_max_u16(hw, from_pair(hw));
+            const BlockScale bs = block_scale(max_halves(hw), outer_scale(A));
+            uint32_t w = 0u;
+            for (int k = 0; k < 8; k += 2)
+                w |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], k), bs),
+                                                              quotient_exact(elem(v[i], k + 1), bs), 1.0f, 0) & 0xffu) << (4 * k);
+            store_row(d, i, w, bs.code);
+        }
+    }
+    if (COL) {
+        for (int j = 0; j < 8; ++j) {
+            uint32_t m = 0u;
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t e = (__float_as_uint(elem(v[i], j)) >> 16) & 0x7fffu;
+                m = e > m ? e : m;
+            }
+            const BlockScale bs = block_scale(m, outer_scale(colA[j]));
+            uint32_t lohi[2] = {0u, 0u};
+            for (int i = 0; i < 16; i += 2)
+                lohi[i >> 3] |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], j), bs),
+                                                                     quotient_exact(elem(v[i + 1], j), bs), 1.0f, 0) & 0xffu) << (8 * ((i >> 1) & 3));
+            store_col(d, j, lohi[0], lohi[1], bs.code);
+        }
+    }
+}
+
+// MODE: ENC_TENSOR (row_amax[0] / col_amax[0] for every vector), ENC_TOKEN
+// (row_amax[r], col_amax[c]), ENC_TILE (16x16 tiles, tensor amax in
+// row_amax[0] or col_amax[0]; also fills row_amax[1..M) and col_amax[1..K)
+// with it), ENC_GROUPED (rowwise per-token; columnwise per expert with
+// col_amax[e][K] and per-expert output slabs).  A workgroup covers 256 rows
+// x 512 columns; each wave walks four 16-row sub-blocks.
+template <int MODE, bool ROW, bool COL, bool SAT>
+__global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                int64_t row_begin, int64_t row_end,
+                                                const float* __restrict__ row_amax, const float* __restrict__ col_amax,
+                                                uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_sf,
+                                                uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,
+                                                float* __restrict__ fill_row, float* __restrict__ fill_col,
+                                                GroupTable gt) {
+    constexpr bool TILE = MODE == ENC_TILE;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    SubDst d;
+    d.row_q = row_q; d.row_sf = row_sf; d.col_q = col_q; d.col_sf = col_sf;
+    d.K = K; d.c0 = (int64_t)blockIdx.x * kTileCols + lane * 8; d.row_end = row_end;
+    d.m_len = M; d.grow0 = 0; d.col_ok = d.c0 < K; d.even = (lane & 1) == 0;
+    const int64_t rbase = row_begin + (int64_t)blockIdx.y * kEncRows + wave * (kEncRows / 4);
+    float tileA = 0.0f;
+    if (TILE) {
+        tileA = row_amax ? row_amax[0] : col_amax[0];
+        const int64_t gid = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+        const int64_t gsz = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+        if (fill_row) for (int64_t i = 1 + gid; i < M; i += gsz) fill_row[i] = tileA;
+        if (fill_col) for (int64_t i = 1 + gid; i < K; i += gsz) fill_col[i] = tileA;
+    }
+    const Outer tileO = make_outer(tileA);
+
+    // columnwise outer scales of this lane's 8 columns
+    float colA[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    Outer colO[8];
+    int cur_group = -1;
+    if (COL && !TILE && MODE != ENC_GROUPED) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            colA[j] = (MODE == ENC_TENSOR) ? col_amax[0] : (d.col_ok ? col_amax[d.c0 + j] : 0.0f);
+            colO[j] = make_outer(colA[j]);
+        }
+    }
+    // per-tensor rowwise outer scale
+    float rowA_t = 0.0f;
+    Outer rowO_t;
+    if (ROW && MODE == ENC_TENSOR) { rowA_t = row_amax[0]; }
+    rowO_t = make_outer(rowA_t);
+
+    for (int sb = 0; sb < kEncRows / 64; ++sb) {
+        d.r0 = rbase + 16 * sb;
+        if (d.r0 >= row_end) break;
+        if (COL && MODE == ENC_GROUPED) {
+            const int g = group_of_row(gt, d.r0);
+            if (g != cur_group) {
+                cur_group = g;
+                d.m_len = gt.cnt[g];
+                d.grow0 = gt.off[g];
+                const int64_t base = (int64_t)(gt.first + g) * K;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    colA[j] = d.col_ok ? col_amax[base + d.c0 + j] : 0.0f;
+                    colO[j] = make_outer(colA[j]);
+                }
+            }
+        }
+        u32x4 v[16];
+        load_subblock(x, K, d.r0, row_end, d.c0, d.col_ok, v);
+
+        // rowwise outer scales of the 16 rows: lanes 0..15 compute one row
+        // each; S and 1/S are broadcast through readlane, flags through ballot
+        float rowS[16], rowYS[16];
+        uint32_t row_slow = 0u;
+        float rowA_lane = rowA_t;
+        if (ROW && !TILE) {
+            Outer mine = rowO_t;
+            if (MODE != ENC_TENSOR) {
+                const int64_t rr = d.r0 + (lane & 15);
+                rowA_lane = rr < row_end ? row_amax[rr] : 0.0f;
+                mine = make_outer(rowA_lane);
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                uint32_t word = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
-                e[i] = (j & 1) ? bf_hi(word) : bf_lo(word);
+                rowS[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.S), i));
+                rowYS[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.yS), i));
             }
-            uint32_t lo = 0u, hi = 0u;
-            lo = put_fp4x2<0>(lo, quotient(e[0], bs), quotient(e[1], bs));
-            lo = put_fp4x2<1>(lo, quotient(e[2], bs), quotient(e[3], bs));
-            lo = put_fp4x2<2>(lo, quotient(e[4], bs), quotient(e[5], bs));
-            lo = put_fp4x2<3>(lo, quotient(e[6], bs), quotient(e[7], bs));
-            hi = put_fp4x2<0>(hi, quotient(e[8], bs), quotient(e[9], bs));
-            hi = put_fp4x2<1>(hi, quotient(e[10], bs), quotient(e[11], bs));
-            hi = put_fp4x2<2>(hi, quotient(e[12], bs), quotient(e[13], bs));
-            hi = put_fp4x2<3>(hi, quotient(e[14], bs), quotient(e[15], bs));
-            *reinterpret_cast<u32x2*>(qbase + c * (m_len / 2) + (r0 - row0) / 2) = u32x2{lo, hi};
-            sbase[c * (m_len / 16) + (r0 - row0) / 16] = (uint8_t)bs.code;
+            row_slow = (uint32_t)__builtin_amdgcn_ballot_w64(mine.slow) & 0xffffu;
         }
+
+        const bool slow = encode_fast<ROW, COL, TILE, SAT>(v, rowS, rowYS, row_slow, colO, tileO, d);
+        if (__builtin_amdgcn_ballot_w64(slow) != 0ull)
+            encode_exact<ROW, COL, TILE>(x, rowA_lane, colA[0], colA[1], colA[2], colA[3], colA[4], colA[5],
+                                         colA[6], colA[7], tileA, d);
     }
 }
 
@@ -414,38 +597,38 @@ hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin
     return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool SAT>
 static void launch_encode_mode(bool row, bool col, dim3 grid, hipStream_t st, const uint16_t* x, int64_t M, int64_t K,
                                int64_t rb, int64_t re, const float* ra, const float* ca, uint8_t* rq, uint8_t* rs,
                                uint8_t* cq, uint8_t* cs, float* fr, float* fc, const GroupTable& gt) {
     if (row && col)
-        hipLaunchKernelGGL((k_encode<MODE, true, true>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
+        hipLaunchKernelGGL((k_encode<MODE, true, true, SAT>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
     else if (row)
-        hipLaunchKernelGGL((k_encode<MODE, true, false>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
+        hipLaunchKernelGGL((k_encode<MODE, true, false, SAT>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
     else
-        hipLaunchKernelGGL((k_encode<MODE, false, true>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
+        hipLaunchKernelGGL((k_encode<MODE, false, true, SAT>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
 }
 
-hipError_t launch_encode(int mode, bool row, bool col, const uint16_t* x, int64_t M, int64_t K,
+hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const uint16_t* x, int64_t M, int64_t K,
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st) {
     if (row_end <= row_begin || K <= 0 || (!row && !col)) return hipSuccess;
     dim3 grid(cdiv(K, kTileCols), cdiv(row_end - row_begin, kEncRows));
-    switch (mode) {
-    case ENC_TENSOR:
-        launch_encode_mode<ENC_TENSOR>(row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt);
-        break;
-    case ENC_TOKEN:
-        launch_encode_mode<ENC_TOKEN>(row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt);
-        break;
-    case ENC_TILE:
-        launch_encode_mode<ENC_TILE>(row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt);
-        break;
-    default:
-        launch_encode_mode<ENC_GROUPED>(row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt);
-        break;
+#define NVFP4_ENC_ARGS row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt
+    if (caller_amax) {
+        // amax from the caller: scales may saturate
+        if (mode == ENC_TENSOR) launch_encode_mode<ENC_TENSOR, true>(NVFP4_ENC_ARGS);
+        else launch_encode_mode<ENC_TOKEN, true>(NVFP4_ENC_ARGS);
+    } else {
+        switch (mode) {
+        case ENC_TENSOR: launch_encode_mode<ENC_TENSOR, false>(NVFP4_ENC_ARGS); break;
+        case ENC_TOKEN: launch_encode_mode<ENC_TOKEN, false>(NVFP4_ENC_ARGS); break;
+        case ENC_TILE: launch_encode_mode<ENC_TILE, false>(NVFP4_ENC_ARGS); break;
+        default: launch_encode_mode<ENC_GROUPED, false>(NVFP4_ENC_ARGS); break;
+        }
     }
+#undef NVFP4_ENC_ARGS
     return hipGetLastError();
 }
 

@@ -15,7 +15,10 @@
  * is written as r*q0 - a (not a - r*q0) so that a = -0 keeps its sign.
  *
  * Claim checked here: q == RN(a / r) bit for bit for every bf16 significand
- * of a (both signs) and every fp32 significand of r.  The three steps are
+ * of a (both signs) and every fp32 significand of r.  A second family checks
+ * the same sequence for the block-scale quotient sf = RN(t / S), whose
+ * numerator t = RN(b / 6) (b bf16) takes only 128 distinct significands:
+ * every one of them against every fp32 significand of S.  The three steps are
  * exact under scaling by powers of two while every intermediate is a normal
  * number, so one exponent pair covers the whole range the kernels allow
  * (r in [2^-64, 2^64] and |a| * y <= 2^64); the run also samples other
@@ -85,6 +88,29 @@ static void* run_exhaustive(void* p)
     return NULL;
 }
 
+/* block-scale family: t = RN(b/6) for the 128 bf16 significands of b in
+ * [1, 2), divided by every significand of S in [1, 2) */
+static void* run_scale_family(void* p)
+{
+    job_t* j = (job_t*)p;
+    float b = f_of(((uint32_t)127 << 23) | ((uint32_t)j->task << 16));
+    float t = b / 6.0f;
+    for (uint32_t ms = 0; ms < (1u << 23); ++ms) {
+        float S = f_of(((uint32_t)127 << 23) | ms);
+        float y = 1.0f / S;
+        float q = shortcut(t, S, y);
+        float ref = t / S;
+        j->checked++;
+        if (u_of(q) != u_of(ref)) {
+            if (j->bad < 4)
+                fprintf(stderr, "scale mismatch t=%08x S=%08x got=%08x want=%08x\n",
+                        u_of(t), u_of(S), u_of(q), u_of(ref));
+            j->bad++;
+        }
+    }
+    return NULL;
+}
+
 /* tiny and subnormal a against r at the ends of the allowed range: the
  * E2M1 code (magnitude and sign) must agree */
 static void check_tiny(uint64_t* checked, uint64_t* bad)
@@ -136,6 +162,17 @@ int main(void)
         for (int t = base; t < base + 16; ++t) {
             jobs[t].task = t; jobs[t].checked = 0; jobs[t].bad = 0;
             pthread_create(&th[t], NULL, run_exhaustive, &jobs[t]);
+        }
+        for (int t = base; t < base + 16; ++t) {
+            pthread_join(th[t], NULL);
+            checked += jobs[t].checked;
+            bad += jobs[t].bad;
+        }
+    }
+    for (int base = 0; base < 128; base += 16) {
+        for (int t = base; t < base + 16; ++t) {
+            jobs[t].task = t; jobs[t].checked = 0; jobs[t].bad = 0;
+            pthread_create(&th[t], NULL, run_scale_family, &jobs[t]);
         }
         for (int t = base; t < base + 16; ++t) {
             pthread_join(th[t], NULL);

@@ -18,6 +18,11 @@ namespace nvfp4 {
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
 constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass
 constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass
+// LDS staging of a workgroup's columnwise output: per column, 256 rows give
+// 128 bytes of data and 16 scale bytes; padded pitches spread the lanes'
+// writes over the banks
+constexpr int kStageQPitch = 132;
+constexpr int kStageSfPitch = 20;
 
 // --------------------------------------------------------------- utilities
 
@@ -215,52 +220,62 @@ __device__ __forceinline__ uint32_t rowmax_word(const u32x4& w) {
     return pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
 }
 
-// Where a lane's sub-block results go.  Columnwise data of column c, rows
+// Where a lane's sub-block results go.  Row and column bases are per
+// sub-block; lane offsets are 32-bit.  Columnwise data of column c, rows
 // [r0, r0+16) of a vector of length m_len starting at row grow0.
 struct SubDst {
-    uint8_t* row_q; uint8_t* row_sf; uint8_t* col_q; uint8_t* col_sf;
-    int64_t K, r0, c0, row_end, m_len, grow0;
-    bool col_ok, even;
+    uint8_t* row_q; uint8_t* row_sf;     // at row r0, column 0
+    uint8_t* col_q; uint8_t* col_sf;     // at column 0 of this vector's slab, row r0
+    uint32_t row_q_stride, row_sf_stride; // bytes per row: K/2, K/16
+    uint32_t col_q_stride, col_sf_stride; // bytes per column: m_len/2, m_len/16
+    uint32_t c0;                          // first column of this lane
+    int nrows;                            // valid rows in the sub-block (<= 16)
+    bool col_ok, odd;
+    // columnwise output staged in LDS (when non-null): the lane's 8 columns
+    // start at lds_q (pitch kStageQPitch bytes per column, this sub-block's
+    // 8 bytes at the right offset) and lds_sf (pitch kStageSfPitch)
+    uint8_t* lds_q; uint8_t* lds_sf;
 };
-
-__device__ __forceinline__ void store_row(const SubDst& d, int i, uint32_t q, uint32_t code) {
-    const int64_t r = d.r0 + i;
-    if (d.col_ok && r < d.row_end) {
-        *reinterpret_cast<uint32_t*>(d.row_q + r * (d.K / 2) + d.c0 / 2) = q;
-        if (d.even) d.row_sf[r * (d.K / 16) + d.c0 / 16] = (uint8_t)code;
-    }
-}
 
 __device__ __forceinline__ void store_row_pair(const SubDst& d, int i, uint32_t q0, uint32_t q1, uint32_t own_code) {
     if (!d.col_ok) return;
-    const int64_t r = d.r0 + i;
-    if (r < d.row_end) *reinterpret_cast<uint32_t*>(d.row_q + r * (d.K / 2) + d.c0 / 2) = q0;
-    if (r + 1 < d.row_end) *reinterpret_cast<uint32_t*>(d.row_q + (r + 1) * (d.K / 2) + d.c0 / 2) = q1;
-    const int64_t ro = d.even ? r : r + 1;
-    if (ro < d.row_end) d.row_sf[ro * (d.K / 16) + d.c0 / 16] = (uint8_t)own_code;
+    if (i < d.nrows) *reinterpret_cast<uint32_t*>(d.row_q + i * d.row_q_stride + d.c0 / 2) = q0;
+    if (i + 1 < d.nrows) *reinterpret_cast<uint32_t*>(d.row_q + (i + 1) * d.row_q_stride + d.c0 / 2) = q1;
+    const int io = d.odd ? i + 1 : i;
+    if (io < d.nrows) d.row_sf[io * d.row_sf_stride + d.c0 / 16] = (uint8_t)own_code;
+}
+
+__device__ __forceinline__ void store_row(const SubDst& d, int i, uint32_t q, uint32_t code) {
+    if (d.col_ok && i < d.nrows) {
+        *reinterpret_cast<uint32_t*>(d.row_q + i * d.row_q_stride + d.c0 / 2) = q;
+        if (!d.odd) d.row_sf[i * d.row_sf_stride + d.c0 / 16] = (uint8_t)code;
+    }
 }
 
 __device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, uint32_t hi, uint32_t code) {
     if (!d.col_ok) return;
-    const int64_t c = d.c0 + j;
-    uint8_t* qb = d.col_q + d.grow0 * d.K / 2;
-    uint8_t* sb = d.col_sf + d.grow0 * d.K / 16;
-    *reinterpret_cast<u32x2*>(qb + c * (d.m_len / 2) + (d.r0 - d.grow0) / 2) = u32x2{lo, hi};
-    sb[c * (d.m_len / 16) + (d.r0 - d.grow0) / 16] = (uint8_t)code;
+    if (d.lds_q != nullptr) {
+        *reinterpret_cast<u32x2*>(d.lds_q + j * kStageQPitch) = u32x2{lo, hi};
+        d.lds_sf[j * kStageSfPitch] = (uint8_t)code;
+        return;
+    }
+    const uint32_t c = d.c0 + j;
+    *reinterpret_cast<u32x2*>(d.col_q + c * d.col_q_stride) = u32x2{lo, hi};
+    d.col_sf[c * d.col_sf_stride] = (uint8_t)code;
 }
 
-// Fast encode and store of one lane's 16x8 sub-block.  Row outer scales are
-// wave-uniform (rowS/rowYS per row, a bit mask of rows needing the exact
-// path); colO are this lane's 8 columns; tileO the tensor's (16x16 tiles).
-// The two lanes of a pair share every rowwise block: each computes the
-// parameters of one row of every row pair (row 2s + parity) and the pair
-// swaps them.  Returns true if some block needs the exact path, in which
-// case the caller re-encodes the sub-block exactly over what was stored.
+// Fast encode and store of one lane's 16x8 sub-block.  rowO[s] is the outer
+// scale of this lane's own row 2s + parity (the two lanes of a pair share
+// every rowwise block: each computes the parameters of one row of every row
+// pair and the pair swaps them); colO are this lane's 8 columns; tileO the
+// tensor's (16x16 tiles).  Returns true if some block needs the exact path,
+// in which case the caller re-encodes the sub-block exactly over what was
+// stored here.
 template <bool ROW, bool COL, bool TILE, bool SAT>
-__device__ __forceinline__ bool encode_fast(const u32x4 v[16], const float* rowS, const float* rowYS,
-                                            uint32_t row_slow, const Outer* colO, const Outer& tileO,
+__device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale)[2], const Outer& rowO_t,
+                                            bool per_tensor_rows, const Outer* colO, const Outer& tileO,
                                             const SubDst& d) {
-    const bool odd = !d.even;
+    const bool odd = d.odd;
     bool slow = false;
     FastBlock cb[8];
     FastBlock tb;
@@ -286,50 +301,15 @@ __device__ __forceinline__ bool encode_fast(const u32x4 v[16], const float* rowS
             slow |= cb[j].slow;
         }
     }
-    uint32_t cq[8][2];
+    // columnwise pass
+    if (COL) {
+        uint32_t cq[8][2];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-        float a[2][8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { a[0][k] = elem(v[i], k); a[1][k] = elem(v[i + 1], k); }
-        if (ROW) {
-            float rr[2], ry[2];
-            uint32_t own_code;
-            if (TILE) {
-                rr[0] = rr[1] = tb.r; ry[0] = ry[1] = tb.y; own_code = tb.code;
-            } else {
-                uint32_t f0 = rowmax_word(v[i]), f1 = rowmax_word(v[i + 1]);
-                f0 = pk_max_u16(f0, from_pair(f0));
-                f1 = pk_max_u16(f1, from_pair(f1));
-                Outer ro;
-                ro.S = odd ? rowS[i + 1] : rowS[i];
-                ro.yS = odd ? rowYS[i + 1] : rowYS[i];
-                ro.slow = (row_slow >> (i + (odd ? 1 : 0))) & 1u;
-                const FastBlock f = fast_block<SAT>(max_halves(odd ? f1 : f0), ro);
-                slow |= f.slow;
-                const float pr = __uint_as_float(from_pair(__float_as_uint(f.r)));
-                const float py = __uint_as_float(from_pair(__float_as_uint(f.y)));
-                rr[0] = odd ? pr : f.r; ry[0] = odd ? py : f.y;
-                rr[1] = odd ? f.r : pr; ry[1] = odd ? f.y : py;
-                own_code = f.code;
-            }
-            uint32_t w[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t q = 0u;
-                q = put_fp4x2<0>(q, div_fast(a[h][0], rr[h], ry[h]), div_fast(a[h][1], rr[h], ry[h]));
-                q = put_fp4x2<1>(q, div_fast(a[h][2], rr[h], ry[h]), div_fast(a[h][3], rr[h], ry[h]));
-                q = put_fp4x2<2>(q, div_fast(a[h][4], rr[h], ry[h]), div_fast(a[h][5], rr[h], ry[h]));
-                q = put_fp4x2<3>(q, div_fast(a[h][6], rr[h], ry[h]), div_fast(a[h][7], rr[h], ry[h]));
-                w[h] = q;
-            }
-            store_row_pair(d, i, w[0], w[1], own_code);
-        }
-        if (COL) {
+        for (int i = 0; i < 16; i += 2) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const FastBlock& f = TILE ? tb : cb[j];
-                const float q0 = div_fast(a[0][j], f.r, f.y), q1 = div_fast(a[1][j], f.r, f.y);
+                const float q0 = div_fast(elem(v[i], j), f.r, f.y), q1 = div_fast(elem(v[i + 1], j), f.r, f.y);
                 uint32_t& w = cq[j][i >> 3];
                 const int byte = (i >> 1) & 3;
                 if (byte == 0) w = put_fp4x2<0>(0u, q0, q1);
@@ -338,24 +318,72 @@ __device__ __forceinline__ bool encode_fast(const u32x4 v[16], const float* rowS
                 else w = put_fp4x2<3>(w, q0, q1);
             }
         }
-    }
-    if (COL) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) store_col(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
+    }
+    // rowwise pass, one row pair at a time: each lane computes the block of
+    // its own row (2s + parity) and swaps the parameters with the pair.  The
+    // empty register barrier keeps the compiler from carrying the 128
+    // unpacked values of the columnwise pass over into this one (unpacking
+    // again costs one op per element; keeping them live costs occupancy).
+    if (ROW && COL) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[i]));
+    }
+    if (ROW) {
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+            const int i = 2 * s2;
+            float rr[2], ry[2];
+            uint32_t own_code;
+            if (TILE) {
+                rr[0] = rr[1] = tb.r; ry[0] = ry[1] = tb.y; own_code = tb.code;
+            } else {
+                uint32_t f0 = rowmax_word(v[i]), f1 = rowmax_word(v[i + 1]);
+                f0 = pk_max_u16(f0, from_pair(f0));
+                f1 = pk_max_u16(f1, from_pair(f1));
+                Outer ro = rowO_t;
+                if (!per_tensor_rows) {
+                    const int own = i + (odd ? 1 : 0);
+                    const float S = row_scale[own][0];
+                    ro.S = S < 0.0f ? 1.0f : S;
+                    ro.yS = row_scale[own][1];
+                    ro.slow = S < 0.0f;
+                }
+                const FastBlock f = fast_block<SAT>(max_halves(odd ? f1 : f0), ro);
+                slow |= f.slow;
+                own_code = f.code;
+                const float pr = __uint_as_float(from_pair(__float_as_uint(f.r)));
+                const float py = __uint_as_float(from_pair(__float_as_uint(f.y)));
+                rr[0] = odd ? pr : f.r; ry[0] = odd ? py : f.y;
+                rr[1] = odd ? f.r : pr; ry[1] = odd ? f.y : py;
+            }
+            uint32_t w[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4& vv = v[i + h];
+                uint32_t q = 0u;
+                q = put_fp4x2<0>(q, div_fast(bf_lo(vv.x), rr[h], ry[h]), div_fast(bf_hi(vv.x), rr[h], ry[h]));
+                q = put_fp4x2<1>(q, div_fast(bf_lo(vv.y), rr[h], ry[h]), div_fast(bf_hi(vv.y), rr[h], ry[h]));
+                q = put_fp4x2<2>(q, div_fast(bf_lo(vv.z), rr[h], ry[h]), div_fast(bf_hi(vv.z), rr[h], ry[h]));
+                q = put_fp4x2<3>(q, div_fast(bf_lo(vv.w), rr[h], ry[h]), div_fast(bf_hi(vv.w), rr[h], ry[h]));
+                w[h] = q;
+            }
+            store_row_pair(d, i, w[0], w[1], own_code);
+        }
     }
     return slow;
 }
 
 // Exact encode and store of a sub-block with IEEE divisions throughout,
-// re-reading the data.  rowA: amax of row r0+i for lanes 0..15 (lane i holds
-// row i's), broadcast here; colA: this lane's 8 column amax; tileA: tensor's.
+// re-reading the data from xr (row r0, column 0; row stride K).  rowA[i]:
+// amax of row i; colA: this lane's 8 column amax; tileA: the tensor's.
 template <bool ROW, bool COL, bool TILE>
-__device__ __noinline__ void encode_exact(const uint16_t* __restrict__ x, float rowA_lane, float colA0, float colA1,
-                                          float colA2, float colA3, float colA4, float colA5, float colA6,
-                                          float colA7, float tileA, SubDst d) {
+__device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64_t K, const float* rowA,
+                                          const float* colA, float tileA, SubDst d) {
     u32x4 v[16];
-    load_subblock(x, d.K, d.r0, d.row_end, d.c0, d.col_ok, v);
-    const float colA[8] = {colA0, colA1, colA2, colA3, colA4, colA5, colA6, colA7};
+    for (int i = 0; i < 16; ++i)
+        v[i] = (d.col_ok && i < d.nrows) ? *reinterpret_cast<const u32x4*>(xr + i * K + d.c0) : u32x4{0u, 0u, 0u, 0u};
     if (TILE) {
         uint32_t m = 0u;
         for (int i = 0; i < 16; ++i) m = pk_max_u16(m, rowmax_word(v[i]));
@@ -380,10 +408,9 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ x, float 
     }
     if (ROW) {
         for (int i = 0; i < 16; ++i) {
-            const float A = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rowA_lane), i));
             uint32_t hw = rowmax_word(v[i]);
             hw = pk_max_u16(hw, from_pair(hw));
-            const BlockScale bs = block_scale(max_halves(hw), outer_scale(A));
+            const BlockScale bs = block_scale(max_halves(hw), outer_scale(rowA[i]));
             uint32_t w = 0u;
             for (int k = 0; k < 8; k += 2)
                 w |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], k), bs),
@@ -413,7 +440,8 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ x, float 
 // row_amax[0] or col_amax[0]; also fills row_amax[1..M) and col_amax[1..K)
 // with it), ENC_GROUPED (rowwise per-token; columnwise per expert with
 // col_amax[e][K] and per-expert output slabs).  A workgroup covers 256 rows
-// x 512 columns; each wave walks four 16-row sub-blocks.
+// x 512 columns; each wave walks four 16-row sub-blocks.  SAT: the amax
+// comes from the caller and may be smaller than the data.
 template <int MODE, bool ROW, bool COL, bool SAT>
 __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                 int64_t row_begin, int64_t row_end,
@@ -423,11 +451,15 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                                                 float* __restrict__ fill_row, float* __restrict__ fill_col,
                                                 GroupTable gt) {
     constexpr bool TILE = MODE == ENC_TILE;
+    __shared__ float row_scale[4][16][2];    // per wave: S and 1/S of its 16 rows (S < 0: exact path)
+    // columnwise output of the workgroup tile, written out in whole lines
+    constexpr bool STAGE = COL && MODE != ENC_GROUPED;
+    __shared__ __attribute__((aligned(16))) uint8_t stage_q[STAGE ? kTileCols * kStageQPitch : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_sf[STAGE ? kTileCols * kStageSfPitch : 16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    SubDst d;
-    d.row_q = row_q; d.row_sf = row_sf; d.col_q = col_q; d.col_sf = col_sf;
-    d.K = K; d.c0 = (int64_t)blockIdx.x * kTileCols + lane * 8; d.row_end = row_end;
-    d.m_len = M; d.grow0 = 0; d.col_ok = d.c0 < K; d.even = (lane & 1) == 0;
+    const uint32_t c0 = (uint32_t)blockIdx.x * kTileCols + lane * 8;
+    const bool col_ok = c0 < K;
+    const bool odd = lane & 1;
     const int64_t rbase = row_begin + (int64_t)blockIdx.y * kEncRows + wave * (kEncRows / 4);
     float tileA = 0.0f;
     if (TILE) {
@@ -440,66 +472,139 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     const Outer tileO = make_outer(tileA);
 
     // columnwise outer scales of this lane's 8 columns
-    float colA[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     Outer colO[8];
     int cur_group = -1;
+    int64_t m_len = M, grow0 = 0;
     if (COL && !TILE && MODE != ENC_GROUPED) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            colA[j] = (MODE == ENC_TENSOR) ? col_amax[0] : (d.col_ok ? col_amax[d.c0 + j] : 0.0f);
-            colO[j] = make_outer(colA[j]);
-        }
+        for (int j = 0; j < 8; ++j)
+            colO[j] = make_outer((MODE == ENC_TENSOR) ? col_amax[0] : (col_ok ? col_amax[c0 + j] : 0.0f));
     }
     // per-tensor rowwise outer scale
-    float rowA_t = 0.0f;
-    Outer rowO_t;
-    if (ROW && MODE == ENC_TENSOR) { rowA_t = row_amax[0]; }
-    rowO_t = make_outer(rowA_t);
+    const float rowA_t = (ROW && MODE == ENC_TENSOR) ? row_amax[0] : 0.0f;
+    const Outer rowO_t = make_outer(rowA_t);
 
+    // destinations of a sub-block
+    auto make_dst = [&](int64_t r0, int nrows, int64_t mlen, int64_t g0) {
+        SubDst d;
+        d.row_q = row_q + r0 * (K / 2);
+        d.row_sf = row_sf + r0 * (K / 16);
+        d.col_q = col_q + g0 * K / 2 + (r0 - g0) / 2;
+        d.col_sf = col_sf + g0 * K / 16 + (r0 - g0) / 16;
+        d.row_q_stride = (uint32_t)(K / 2);
+        d.row_sf_stride = (uint32_t)(K / 16);
+        d.col_q_stride = (uint32_t)(mlen / 2);
+        d.col_sf_stride = (uint32_t)(mlen / 16);
+        d.c0 = c0; d.nrows = nrows; d.col_ok = col_ok; d.odd = odd;
+        d.lds_q = nullptr; d.lds_sf = nullptr;
+        if (STAGE) {
+            const int rl = (int)(r0 - (row_begin + (int64_t)blockIdx.y * kEncRows));   // row within the tile
+            d.lds_q = stage_q + (lane * 8) * kStageQPitch + rl / 2;
+            d.lds_sf = stage_sf + (lane * 8) * kStageSfPitch + rl / 16;
+        }
+        return d;
+    };
+
+    uint32_t slow_mask = 0u;
+#pragma unroll 1
     for (int sb = 0; sb < kEncRows / 64; ++sb) {
-        d.r0 = rbase + 16 * sb;
-        if (d.r0 >= row_end) break;
+        const int64_t r0 = rbase + 16 * sb;
+        if (r0 >= row_end) break;
         if (COL && MODE == ENC_GROUPED) {
-            const int g = group_of_row(gt, d.r0);
+            const int g = group_of_row(gt, r0);
             if (g != cur_group) {
                 cur_group = g;
-                d.m_len = gt.cnt[g];
-                d.grow0 = gt.off[g];
+                m_len = gt.cnt[g];
+                grow0 = gt.off[g];
                 const int64_t base = (int64_t)(gt.first + g) * K;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    colA[j] = d.col_ok ? col_amax[base + d.c0 + j] : 0.0f;
-                    colO[j] = make_outer(colA[j]);
-                }
+                for (int j = 0; j < 8; ++j) colO[j] = make_outer(col_ok ? col_amax[base + c0 + j] : 0.0f);
             }
         }
+        const int nrows = (int)(row_end - r0 < 16 ? row_end - r0 : 16);
+        const uint16_t* xr = x + r0 * K;
         u32x4 v[16];
-        load_subblock(x, K, d.r0, row_end, d.c0, d.col_ok, v);
-
-        // rowwise outer scales of the 16 rows: lanes 0..15 compute one row
-        // each; S and 1/S are broadcast through readlane, flags through ballot
-        float rowS[16], rowYS[16];
-        uint32_t row_slow = 0u;
-        float rowA_lane = rowA_t;
-        if (ROW && !TILE) {
-            Outer mine = rowO_t;
-            if (MODE != ENC_TENSOR) {
-                const int64_t rr = d.r0 + (lane & 15);
-                rowA_lane = rr < row_end ? row_amax[rr] : 0.0f;
-                mine = make_outer(rowA_lane);
-            }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                rowS[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.S), i));
-                rowYS[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.yS), i));
-            }
-            row_slow = (uint32_t)__builtin_amdgcn_ballot_w64(mine.slow) & 0xffffu;
-        }
+        for (int i = 0; i < 16; ++i)
+            v[i] = (col_ok && i < nrows) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + i * K + c0))
+                                         : u32x4{0u, 0u, 0u, 0u};
+        const SubDst d = make_dst(r0, nrows, m_len, grow0);
 
-        const bool slow = encode_fast<ROW, COL, TILE, SAT>(v, rowS, rowYS, row_slow, colO, tileO, d);
-        if (__builtin_amdgcn_ballot_w64(slow) != 0ull)
-            encode_exact<ROW, COL, TILE>(x, rowA_lane, colA[0], colA[1], colA[2], colA[3], colA[4], colA[5],
-                                         colA[6], colA[7], tileA, d);
+        // rowwise outer scales: lanes 0..15 compute one row each into LDS
+        if (ROW && !TILE && MODE != ENC_TENSOR) {
+            if (lane < 16) {
+                const Outer o = make_outer(lane < nrows ? row_amax[r0 + lane] : 0.0f);
+                row_scale[wave][lane][0] = o.slow ? -1.0f : o.S;
+                row_scale[wave][lane][1] = o.yS;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        const bool slow = encode_fast<ROW, COL, TILE, SAT>(v, row_scale[wave], rowO_t, MODE == ENC_TENSOR, colO,
+                                                           tileO, d);
+        if (__builtin_amdgcn_ballot_w64(slow) != 0ull) slow_mask |= 1u << sb;
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // sub-blocks with a block outside the fast path's range: encode again,
+    // exactly, over what the fast path stored
+    while (slow_mask != 0u) {
+        const int sb = __builtin_ctz(slow_mask);
+        slow_mask &= slow_mask - 1u;
+        const int64_t r0 = rbase + 16 * sb;
+        const int nrows = (int)(row_end - r0 < 16 ? row_end - r0 : 16);
+        int64_t mlen = M, g0 = 0, cbase = 0;
+        if (COL && MODE == ENC_GROUPED) {
+            const int g = group_of_row(gt, r0);
+            mlen = gt.cnt[g];
+            g0 = gt.off[g];
+            cbase = (int64_t)(gt.first + g) * K;
+        }
+        float rowA[16], colA[8];
+        for (int i = 0; i < 16; ++i)
+            rowA[i] = (ROW && !TILE) ? (MODE == ENC_TENSOR ? rowA_t : (i < nrows ? row_amax[r0 + i] : 0.0f)) : 0.0f;
+        for (int j = 0; j < 8; ++j)
+            colA[j] = (COL && !TILE) ? (MODE == ENC_TENSOR ? col_amax[0] : (col_ok ? col_amax[cbase + c0 + j] : 0.0f)) : 0.0f;
+        encode_exact<ROW, COL, TILE>(x + r0 * K, K, rowA, colA, tileA, make_dst(r0, nrows, mlen, g0));
+    }
+
+    if (STAGE) {
+        // every wave's columnwise bytes are in LDS: write whole 128-byte
+        // lines (8 lanes per column), then the scale bytes
+        __syncthreads();
+        const int64_t tile_r0 = row_begin + (int64_t)blockIdx.y * kEncRows;
+        const int64_t tile_rows = row_end - tile_r0 < kEncRows ? row_end - tile_r0 : kEncRows;
+        const uint32_t qbytes = (uint32_t)(tile_rows / 2), sbytes = (uint32_t)(tile_rows / 16);
+        const uint32_t cbase = (uint32_t)blockIdx.x * kTileCols;
+        const uint32_t ncols = (uint32_t)(K - cbase < kTileCols ? K - cbase : kTileCols);
+        uint8_t* gq = col_q + tile_r0 / 2;
+        uint8_t* gs = col_sf + tile_r0 / 16;
+        const uint32_t t = threadIdx.x;
+        // qbytes is a multiple of 8: the last chunk of a short tile may be 8 bytes
+        for (uint32_t k = 0; k < (kTileCols * 8) / 256; ++k) {
+            const uint32_t c = (t >> 3) + 32 * k, chunk = (t & 7) * 16;
+            if (c >= ncols || chunk >= qbytes) continue;
+            const uint8_t* src = stage_q + c * kStageQPitch + chunk;
+            uint8_t* dst = gq + (int64_t)(cbase + c) * (M / 2) + chunk;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+            if (chunk + 16 <= qbytes) {
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+                *reinterpret_cast<u32x4*>(dst) = u32x4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                *reinterpret_cast<u32x2*>(dst) = lo;
+            }
+        }
+        // scale bytes: whole words when the destination allows it
+        const bool words = ((M / 16) % 4 == 0) && ((tile_r0 / 16) % 4 == 0) && (sbytes % 4 == 0);
+        for (uint32_t c = t; c < ncols; c += 256) {
+            const uint8_t* src = stage_sf + c * kStageSfPitch;
+            uint8_t* dst = gs + (int64_t)(cbase + c) * (M / 16);
+            if (words) {
+                for (uint32_t b = 0; b < sbytes; b += 4)
+                    *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
+            } else {
+                for (uint32_t b = 0; b < sbytes; ++b) dst[b] = src[b];
+            }
+        }
     }
 }
 

@@ -77,12 +77,9 @@ GroupTable empty_table() {
     return gt;
 }
 
-// zero-fill up to two fp32 arrays before an atomic-max pass
+// zero-fill up to two fp32 arrays (one launch) before an atomic-max pass
 nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
-    nvfp4_status s;
-    if (a && na > 0 && (s = check_hip(launch_fill(a, na, 0.0f, st), "fill")) != NVFP4_OK) return s;
-    if (b && nb > 0 && (s = check_hip(launch_fill(b, nb, 0.0f, st), "fill")) != NVFP4_OK) return s;
-    return NVFP4_OK;
+    return check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
 }
 
 nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode,

@@ -143,7 +143,9 @@ __device__ __forceinline__ float outer_scale(float A) { return A / 2688.0f; }
 //     significand of S);
 //  2. v_rcp_f32 followed by one Newton step, fma(fma(-r, y0, 1), y0, y0),
 //     returns RN(1/r) for every normal r in [2^-64, 2^64];
-//  3. the scaled FP4 conversion rounds like the E2M1 table (put_fp4x2).
+//  3. the scaled FP4 conversion rounds like the E2M1 table (put_fp4x2);
+//  4. the two-op element quotient below (quot2) gives the E2M1 code of
+//     RN(a/r) for bf16 a (host check, with one excluded divisor pattern).
 // Blocks outside these ranges, or whose scale falls in the E4M3 subnormal
 // range, take an exact slow path chosen per wave.
 
@@ -178,13 +180,23 @@ __device__ __forceinline__ Outer make_outer(float A) {
     return o;
 }
 
-// Per-block parameters on the fast path: r = decode(code) * S and y = RN(1/r).
-// slow: this block needs the exact path.
+// Per-block parameters on the fast path: r = decode(code) * S, and the
+// split reciprocal yh = RD(1/r), yl = RN((1 - r*yh) * yh) >= 0 used by the
+// two-op element quotient.  slow: this block needs the exact path.
 struct FastBlock {
-    float r, y;
+    float r, yh, yl;
     uint32_t code;
     bool slow;
 };
+
+// Element quotient for the E2M1 code: fma(a, yh, a*yl).  Its E2M1 code
+// equals that of RN(a/r) for every bf16 a and every r in the fast range
+// except r with all mantissa bits set (fact 4, checked exhaustively on the
+// host; fast_block sends those blocks to the exact path).  yl >= 0 keeps the
+// sign of a zero numerator.
+__device__ __forceinline__ float quot2(float a, const FastBlock& f) {
+    return __builtin_fmaf(a, f.yh, a * f.yl);
+}
 
 constexpr float kRcp6 = 0x1.555556p-3f;   // RN(1/6)
 
@@ -205,10 +217,14 @@ __device__ __forceinline__ FastBlock fast_block(uint32_t bmag, const Outer& o) {
     c = c < 0x3C0u ? 0x3C0u : (c > 0x43Eu ? 0x43Eu : c);
     fb.code = c - 0x3C0u;
     fb.r = __uint_as_float(c << 20) * o.S;     // decode(code) * S; 2^-7 * S for code 0
-    fb.y = rcp_rn(fb.r);
-    // sf in the E4M3 subnormal range (and not an all-zero block): exact path
-    bool slow = (u - 1u) < (0x3C800000u - 1u);
-    if (SAT) slow |= !(fb.r <= 0x1p64f && b * fb.y <= 0x1p64f);
+    const float y = rcp_rn(fb.r);               // RN(1/r)
+    const float e = __builtin_fmaf(-fb.r, y, 1.0f);
+    fb.yh = e < 0.0f ? __uint_as_float(__float_as_uint(y) - 1u) : y;   // RD(1/r)
+    fb.yl = __builtin_fmaf(-fb.r, fb.yh, 1.0f) * fb.yh;
+    // exact path: sf in the E4M3 subnormal range (and not an all-zero
+    // block), or an r with all mantissa bits set (fact 4's exception)
+    bool slow = (u - 1u) < (0x3C800000u - 1u) || (__float_as_uint(fb.r) & 0x7FFFFFu) == 0x7FFFFFu;
+    if (SAT) slow |= !(fb.r <= 0x1p64f && b * fb.yh <= 0x1p64f);
     fb.slow = slow || o.slow;
     return fb;
 }

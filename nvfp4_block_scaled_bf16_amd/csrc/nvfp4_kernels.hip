@@ -18,6 +18,8 @@ namespace nvfp4 {
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
 constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass
 constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass
+constexpr int kEncCols = 256;      // columns per workgroup tile in the encode pass: a wave is
+                                   // two row groups of 32 lanes, each 16 rows x 256 columns
 // LDS staging of a workgroup's columnwise output: per column, 256 rows give
 // 128 bytes of data and 16 scale bytes; padded pitches spread the lanes'
 // writes over the banks
@@ -26,10 +28,14 @@ constexpr int kStageSfPitch = 20;
 
 // --------------------------------------------------------------- utilities
 
-__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+// fill two arrays (either may be empty) in one launch
+__global__ void k_fill2_u32(uint32_t* __restrict__ p, int64_t n, uint32_t* __restrict__ q, int64_t m, uint32_t v) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t s = (int64_t)gridDim.x * blockDim.x;
-    for (; i < n; i += s) p[i] = v;
+    const int64_t s = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n + m; i += s) {
+        if (i < n) p[i] = v;
+        else q[i - n] = v;
+    }
 }
 
 // max of non-negative floats through their bit patterns
@@ -38,14 +44,16 @@ __device__ __forceinline__ void atomic_max_mag(float* p, uint32_t mag16) {
 }
 
 // load 16 rows x 8 bf16 (one 16-byte word per row) of a lane's sub-block;
-// rows at or beyond row_end, or a lane past the last column, read zeros
+// rows at or beyond row_end, or a lane past the last column, read zeros.
+// Ordinary (cached) loads: the amax pass leaves x in the last-level cache for
+// the encode pass that follows.
 __device__ __forceinline__ void load_subblock(const uint16_t* __restrict__ x, int64_t K, int64_t r0,
                                               int64_t row_end, int64_t c0, bool col_ok, u32x4 v[16]) {
     const u32x4* base = reinterpret_cast<const u32x4*>(x + r0 * K + c0);
     const int64_t stride = K / 8;  // in 16-byte words
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        if (col_ok && r0 + i < row_end) v[i] = __builtin_nontemporal_load(base + i * stride);
+        if (col_ok && r0 + i < row_end) v[i] = base[i * stride];
         else v[i] = u32x4{0u, 0u, 0u, 0u};
     }
 }
@@ -108,12 +116,21 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
                                               float* __restrict__ t0, float* __restrict__ t1, GroupTable gt) {
     __shared__ uint32_t red[4][64][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * kTileCols + lane * 8;
+    // tile order: each XCD takes a contiguous run of tiles (row band major),
+    // the order the encode pass walks backwards
+    const uint32_t ntiles = gridDim.x * gridDim.y;
+    const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const uint32_t tile = ((ntiles & 7u) == 0u) ? (lin & 7u) * (ntiles >> 3) + (lin >> 3) : lin;
+    const uint32_t bx = tile % gridDim.x, by = tile / gridDim.x;
+    const int64_t c0 = (int64_t)bx * kTileCols + lane * 8;
     const bool col_ok = c0 < K;
-    const int64_t rb = row_begin + (int64_t)blockIdx.y * kAmaxRows + wave * (kAmaxRows / 4);
+    const int64_t rb = row_begin + (int64_t)by * kAmaxRows + wave * (kAmaxRows / 4);
     uint32_t cm[4] = {0u, 0u, 0u, 0u};
     uint32_t tm = 0u;
     int cur_group = -1;
+    u32x4 vnext[16];
+    if (rb < row_end) load_subblock(x, K, rb, row_end, c0, col_ok, vnext);
+#pragma unroll 1
     for (int s = 0; s < kAmaxRows / 4; s += 16) {
         const int64_t r0 = rb + s;
         if (r0 >= row_end) break;
@@ -133,7 +150,9 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
             }
         }
         u32x4 v[16];
-        load_subblock(x, K, r0, row_end, c0, col_ok, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = vnext[i];
+        if (s + 16 < kAmaxRows / 4 && r0 + 16 < row_end) load_subblock(x, K, r0 + 16, row_end, c0, col_ok, vnext);
         uint32_t rm[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -239,8 +258,8 @@ struct SubDst {
 
 __device__ __forceinline__ void store_row_pair(const SubDst& d, int i, uint32_t q0, uint32_t q1, uint32_t own_code) {
     if (!d.col_ok) return;
-    if (i < d.nrows) *reinterpret_cast<uint32_t*>(d.row_q + i * d.row_q_stride + d.c0 / 2) = q0;
-    if (i + 1 < d.nrows) *reinterpret_cast<uint32_t*>(d.row_q + (i + 1) * d.row_q_stride + d.c0 / 2) = q1;
+    if (i < d.nrows) __builtin_nontemporal_store(q0, reinterpret_cast<uint32_t*>(d.row_q + i * d.row_q_stride + d.c0 / 2));
+    if (i + 1 < d.nrows) __builtin_nontemporal_store(q1, reinterpret_cast<uint32_t*>(d.row_q + (i + 1) * d.row_q_stride + d.c0 / 2));
     const int io = d.odd ? i + 1 : i;
     if (io < d.nrows) d.row_sf[io * d.row_sf_stride + d.c0 / 16] = (uint8_t)own_code;
 }
@@ -252,9 +271,10 @@ __device__ __forceinline__ void store_row(const SubDst& d, int i, uint32_t q, ui
     }
 }
 
+template <bool STAGE>
 __device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, uint32_t hi, uint32_t code) {
     if (!d.col_ok) return;
-    if (d.lds_q != nullptr) {
+    if (STAGE) {
         *reinterpret_cast<u32x2*>(d.lds_q + j * kStageQPitch) = u32x2{lo, hi};
         d.lds_sf[j * kStageSfPitch] = (uint8_t)code;
         return;
@@ -271,7 +291,7 @@ __device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, u
 // tensor's (16x16 tiles).  Returns true if some block needs the exact path,
 // in which case the caller re-encodes the sub-block exactly over what was
 // stored here.
-template <bool ROW, bool COL, bool TILE, bool SAT>
+template <bool ROW, bool COL, bool TILE, bool SAT, bool STAGE>
 __device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale)[2], const Outer& rowO_t,
                                             bool per_tensor_rows, const Outer* colO, const Outer& tileO,
                                             const SubDst& d) {
@@ -309,7 +329,7 @@ __device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const FastBlock& f = TILE ? tb : cb[j];
-                const float q0 = div_fast(elem(v[i], j), f.r, f.y), q1 = div_fast(elem(v[i + 1], j), f.r, f.y);
+                const float q0 = quot2(elem(v[i], j), f), q1 = quot2(elem(v[i + 1], j), f);
                 uint32_t& w = cq[j][i >> 3];
                 const int byte = (i >> 1) & 3;
                 if (byte == 0) w = put_fp4x2<0>(0u, q0, q1);
@@ -319,7 +339,7 @@ __device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) store_col(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
+        for (int j = 0; j < 8; ++j) store_col<STAGE>(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
     }
     // rowwise pass, one row pair at a time: each lane computes the block of
     // its own row (2s + parity) and swaps the parameters with the pair.  The
@@ -334,10 +354,10 @@ __device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) {
             const int i = 2 * s2;
-            float rr[2], ry[2];
+            FastBlock rf[2];
             uint32_t own_code;
             if (TILE) {
-                rr[0] = rr[1] = tb.r; ry[0] = ry[1] = tb.y; own_code = tb.code;
+                rf[0] = rf[1] = tb; own_code = tb.code;
             } else {
                 uint32_t f0 = rowmax_word(v[i]), f1 = rowmax_word(v[i + 1]);
                 f0 = pk_max_u16(f0, from_pair(f0));
@@ -353,20 +373,22 @@ __device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale
                 const FastBlock f = fast_block<SAT>(max_halves(odd ? f1 : f0), ro);
                 slow |= f.slow;
                 own_code = f.code;
-                const float pr = __uint_as_float(from_pair(__float_as_uint(f.r)));
-                const float py = __uint_as_float(from_pair(__float_as_uint(f.y)));
-                rr[0] = odd ? pr : f.r; ry[0] = odd ? py : f.y;
-                rr[1] = odd ? f.r : pr; ry[1] = odd ? f.y : py;
+                FastBlock pf;
+                pf.yh = __uint_as_float(from_pair(__float_as_uint(f.yh)));
+                pf.yl = __uint_as_float(from_pair(__float_as_uint(f.yl)));
+                rf[0].yh = odd ? pf.yh : f.yh; rf[0].yl = odd ? pf.yl : f.yl;
+                rf[1].yh = odd ? f.yh : pf.yh; rf[1].yl = odd ? f.yl : pf.yl;
             }
             uint32_t w[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const u32x4& vv = v[i + h];
+                const FastBlock& f = rf[h];
                 uint32_t q = 0u;
-                q = put_fp4x2<0>(q, div_fast(bf_lo(vv.x), rr[h], ry[h]), div_fast(bf_hi(vv.x), rr[h], ry[h]));
-                q = put_fp4x2<1>(q, div_fast(bf_lo(vv.y), rr[h], ry[h]), div_fast(bf_hi(vv.y), rr[h], ry[h]));
-                q = put_fp4x2<2>(q, div_fast(bf_lo(vv.z), rr[h], ry[h]), div_fast(bf_hi(vv.z), rr[h], ry[h]));
-                q = put_fp4x2<3>(q, div_fast(bf_lo(vv.w), rr[h], ry[h]), div_fast(bf_hi(vv.w), rr[h], ry[h]));
+                q = put_fp4x2<0>(q, quot2(bf_lo(vv.x), f), quot2(bf_hi(vv.x), f));
+                q = put_fp4x2<1>(q, quot2(bf_lo(vv.y), f), quot2(bf_hi(vv.y), f));
+                q = put_fp4x2<2>(q, quot2(bf_lo(vv.z), f), quot2(bf_hi(vv.z), f));
+                q = put_fp4x2<3>(q, quot2(bf_lo(vv.w), f), quot2(bf_hi(vv.w), f));
                 w[h] = q;
             }
             store_row_pair(d, i, w[0], w[1], own_code);
@@ -378,7 +400,7 @@ __device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale
 // Exact encode and store of a sub-block with IEEE divisions throughout,
 // re-reading the data from xr (row r0, column 0; row stride K).  rowA[i]:
 // amax of row i; colA: this lane's 8 column amax; tileA: the tensor's.
-template <bool ROW, bool COL, bool TILE>
+template <bool ROW, bool COL, bool TILE, bool STAGE>
 __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64_t K, const float* rowA,
                                           const float* colA, float tileA, SubDst d) {
     u32x4 v[16];
@@ -402,7 +424,7 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
                 for (int i = 0; i < 16; i += 2)
                     lohi[i >> 3] |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], j), bs),
                                                                          quotient_exact(elem(v[i + 1], j), bs), 1.0f, 0) & 0xffu) << (8 * ((i >> 1) & 3));
-                store_col(d, j, lohi[0], lohi[1], bs.code);
+                store_col<STAGE>(d, j, lohi[0], lohi[1], bs.code);
             }
         return;
     }
@@ -430,7 +452,7 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
             for (int i = 0; i < 16; i += 2)
                 lohi[i >> 3] |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], j), bs),
                                                                      quotient_exact(elem(v[i + 1], j), bs), 1.0f, 0) & 0xffu) << (8 * ((i >> 1) & 3));
-            store_col(d, j, lohi[0], lohi[1], bs.code);
+            store_col<STAGE>(d, j, lohi[0], lohi[1], bs.code);
         }
     }
 }
@@ -451,16 +473,31 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                                                 float* __restrict__ fill_row, float* __restrict__ fill_col,
                                                 GroupTable gt) {
     constexpr bool TILE = MODE == ENC_TILE;
-    __shared__ float row_scale[4][16][2];    // per wave: S and 1/S of its 16 rows (S < 0: exact path)
+    __shared__ float row_scale[4][32][2];    // per wave: S and 1/S of its 32 rows (S < 0: exact path)
     // columnwise output of the workgroup tile, written out in whole lines
     constexpr bool STAGE = COL && MODE != ENC_GROUPED;
-    __shared__ __attribute__((aligned(16))) uint8_t stage_q[STAGE ? kTileCols * kStageQPitch : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_sf[STAGE ? kTileCols * kStageSfPitch : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_q[STAGE ? kEncCols * kStageQPitch : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_sf[STAGE ? kEncCols * kStageSfPitch : 16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t c0 = (uint32_t)blockIdx.x * kTileCols + lane * 8;
+    // Workgroups are dispatched round-robin over the 8 XCDs (each with its
+    // own L2).  Give XCD x a contiguous run of tiles, row band major, so the
+    // scale bytes that share a cache line (rowwise: 4 adjacent column tiles,
+    // columnwise: 8 adjacent row bands) are written through one L2; and walk
+    // the tiles in the reverse of the amax pass's order, whose last tiles are
+    // the ones most likely still in the last-level cache.
+    const uint32_t ntiles = gridDim.x * gridDim.y;
+    const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
+    uint32_t tile = lin;
+    if ((ntiles & 7u) == 0u) tile = (lin & 7u) * (ntiles >> 3) + (lin >> 3);
+    tile = ntiles - 1u - tile;
+    const uint32_t bx = tile % gridDim.x, by = tile / gridDim.x;
+    const int rg = lane >> 5;                     // row group within the wave
+    const uint32_t c0 = bx * kEncCols + (lane & 31) * 8;
     const bool col_ok = c0 < K;
     const bool odd = lane & 1;
-    const int64_t rbase = row_begin + (int64_t)blockIdx.y * kEncRows + wave * (kEncRows / 4);
+    const int64_t tile_r0 = row_begin + (int64_t)by * kEncRows;
+    const int64_t wbase = tile_r0 + wave * (kEncRows / 4);   // a wave covers 64 rows in 2 steps
+    const int64_t rbase = wbase + 16 * rg;
     float tileA = 0.0f;
     if (TILE) {
         tileA = row_amax ? row_amax[0] : col_amax[0];
@@ -476,9 +513,13 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     int cur_group = -1;
     int64_t m_len = M, grow0 = 0;
     if (COL && !TILE && MODE != ENC_GROUPED) {
+        // unconditional loads (a lane past the last column reads column 0 and
+        // ignores it) so the eight requests are in flight together
+        float ca[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            colO[j] = make_outer((MODE == ENC_TENSOR) ? col_amax[0] : (col_ok ? col_amax[c0 + j] : 0.0f));
+        for (int j = 0; j < 8; ++j) ca[j] = col_amax[(MODE == ENC_TENSOR) ? 0 : (col_ok ? c0 + j : 0)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
     }
     // per-tensor rowwise outer scale
     const float rowA_t = (ROW && MODE == ENC_TENSOR) ? row_amax[0] : 0.0f;
@@ -498,18 +539,47 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         d.c0 = c0; d.nrows = nrows; d.col_ok = col_ok; d.odd = odd;
         d.lds_q = nullptr; d.lds_sf = nullptr;
         if (STAGE) {
-            const int rl = (int)(r0 - (row_begin + (int64_t)blockIdx.y * kEncRows));   // row within the tile
-            d.lds_q = stage_q + (lane * 8) * kStageQPitch + rl / 2;
-            d.lds_sf = stage_sf + (lane * 8) * kStageSfPitch + rl / 16;
+            const int rl = (int)(r0 - tile_r0);   // row within the tile
+            d.lds_q = stage_q + ((lane & 31) * 8) * kStageQPitch + rl / 2;
+            d.lds_sf = stage_sf + ((lane & 31) * 8) * kStageSfPitch + rl / 16;
         }
         return d;
     };
 
     uint32_t slow_mask = 0u;
+    // unconditional loads: a lane past the last column reads column 0 and a
+    // row past the end (rowwise-only calls with M % 16 != 0) repeats the last
+    // row; neither is stored, and column maxima are only formed when M % 16
+    // == 0, i.e. when every row is real.  The next sub-block's loads are
+    // issued before the current one is encoded.
+    const uint32_t cl = col_ok ? c0 : 0u;
+    auto load16 = [&](int64_t r0, u32x4* v) {
+        const int nr = (int)(row_end - r0 < 16 ? row_end - r0 : 16);
+        const uint16_t* xr = x + r0 * K;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int ii = i < nr ? i : nr - 1;
+            v[i] = *reinterpret_cast<const u32x4*>(xr + ii * K + cl);
+        }
+    };
+    constexpr int kSteps = kEncRows / 4 / 32;   // 32-row steps per wave
 #pragma unroll 1
-    for (int sb = 0; sb < kEncRows / 64; ++sb) {
-        const int64_t r0 = rbase + 16 * sb;
-        if (r0 >= row_end) break;
+    for (int sb = 0; sb < kSteps; ++sb) {
+        const int64_t wr0 = wbase + 32 * sb;     // first row of the wave's step
+        if (wr0 >= row_end) break;
+        // a row group past the end only occurs when M % 32 != 0; it loads
+        // the last row again and stores nothing
+        const int64_t r0 = wr0 + 16 * rg < row_end ? wr0 + 16 * rg : wr0;
+        const bool group_ok = wr0 + 16 * rg < row_end;
+        // the step's rowwise amax first, so that waiting for it does not also
+        // wait for the 16 data loads issued after it
+        float ra = 0.0f;
+        if (ROW && !TILE && MODE != ENC_TENSOR) {
+            ra = row_amax[wr0 + (lane & 31) < row_end ? wr0 + (lane & 31) : row_begin];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        u32x4 v[16];
+        load16(r0, v);
         if (COL && MODE == ENC_GROUPED) {
             const int g = group_of_row(gt, r0);
             if (g != cur_group) {
@@ -517,30 +587,29 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 m_len = gt.cnt[g];
                 grow0 = gt.off[g];
                 const int64_t base = (int64_t)(gt.first + g) * K;
+                float ca[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) colO[j] = make_outer(col_ok ? col_amax[base + c0 + j] : 0.0f);
+                for (int j = 0; j < 8; ++j) ca[j] = col_amax[base + (col_ok ? c0 + j : 0)];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
             }
         }
-        const int nrows = (int)(row_end - r0 < 16 ? row_end - r0 : 16);
-        const uint16_t* xr = x + r0 * K;
-        u32x4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            v[i] = (col_ok && i < nrows) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + i * K + c0))
-                                         : u32x4{0u, 0u, 0u, 0u};
-        const SubDst d = make_dst(r0, nrows, m_len, grow0);
+        const int nrows = group_ok ? (int)(row_end - r0 < 16 ? row_end - r0 : 16) : 0;
+        SubDst d = make_dst(r0, nrows > 0 ? nrows : 1, m_len, grow0);
+        if (!group_ok) { d.nrows = 0; d.col_ok = false; }
 
-        // rowwise outer scales: lanes 0..15 compute one row each into LDS
+        // rowwise outer scales: lanes 0..31 compute one row of the step each
+        // into LDS
         if (ROW && !TILE && MODE != ENC_TENSOR) {
-            if (lane < 16) {
-                const Outer o = make_outer(lane < nrows ? row_amax[r0 + lane] : 0.0f);
+            const Outer o = make_outer(wr0 + (lane & 31) < row_end ? ra : 0.0f);
+            if (lane < 32) {
                 row_scale[wave][lane][0] = o.slow ? -1.0f : o.S;
                 row_scale[wave][lane][1] = o.yS;
             }
             __builtin_amdgcn_wave_barrier();
         }
-        const bool slow = encode_fast<ROW, COL, TILE, SAT>(v, row_scale[wave], rowO_t, MODE == ENC_TENSOR, colO,
-                                                           tileO, d);
+        const bool slow = encode_fast<ROW, COL, TILE, SAT, STAGE>(v, row_scale[wave] + 16 * rg, rowO_t, MODE == ENC_TENSOR,
+                                                           colO, tileO, d);
         if (__builtin_amdgcn_ballot_w64(slow) != 0ull) slow_mask |= 1u << sb;
         __builtin_amdgcn_wave_barrier();
     }
@@ -550,8 +619,10 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     while (slow_mask != 0u) {
         const int sb = __builtin_ctz(slow_mask);
         slow_mask &= slow_mask - 1u;
-        const int64_t r0 = rbase + 16 * sb;
-        const int nrows = (int)(row_end - r0 < 16 ? row_end - r0 : 16);
+        const int64_t wr0 = wbase + 32 * sb;
+        const bool group_ok = wr0 + 16 * rg < row_end;
+        const int64_t r0 = group_ok ? wr0 + 16 * rg : wr0;
+        const int nrows = group_ok ? (int)(row_end - r0 < 16 ? row_end - r0 : 16) : 1;
         int64_t mlen = M, g0 = 0, cbase = 0;
         if (COL && MODE == ENC_GROUPED) {
             const int g = group_of_row(gt, r0);
@@ -564,23 +635,24 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             rowA[i] = (ROW && !TILE) ? (MODE == ENC_TENSOR ? rowA_t : (i < nrows ? row_amax[r0 + i] : 0.0f)) : 0.0f;
         for (int j = 0; j < 8; ++j)
             colA[j] = (COL && !TILE) ? (MODE == ENC_TENSOR ? col_amax[0] : (col_ok ? col_amax[cbase + c0 + j] : 0.0f)) : 0.0f;
-        encode_exact<ROW, COL, TILE>(x + r0 * K, K, rowA, colA, tileA, make_dst(r0, nrows, mlen, g0));
+        SubDst d = make_dst(r0, nrows, mlen, g0);
+        if (!group_ok) { d.nrows = 0; d.col_ok = false; }
+        encode_exact<ROW, COL, TILE, STAGE>(x + r0 * K, K, rowA, colA, tileA, d);
     }
 
     if (STAGE) {
         // every wave's columnwise bytes are in LDS: write whole 128-byte
         // lines (8 lanes per column), then the scale bytes
         __syncthreads();
-        const int64_t tile_r0 = row_begin + (int64_t)blockIdx.y * kEncRows;
         const int64_t tile_rows = row_end - tile_r0 < kEncRows ? row_end - tile_r0 : kEncRows;
         const uint32_t qbytes = (uint32_t)(tile_rows / 2), sbytes = (uint32_t)(tile_rows / 16);
-        const uint32_t cbase = (uint32_t)blockIdx.x * kTileCols;
-        const uint32_t ncols = (uint32_t)(K - cbase < kTileCols ? K - cbase : kTileCols);
+        const uint32_t cbase = bx * kEncCols;
+        const uint32_t ncols = (uint32_t)(K - cbase < kEncCols ? K - cbase : kEncCols);
         uint8_t* gq = col_q + tile_r0 / 2;
         uint8_t* gs = col_sf + tile_r0 / 16;
         const uint32_t t = threadIdx.x;
         // qbytes is a multiple of 8: the last chunk of a short tile may be 8 bytes
-        for (uint32_t k = 0; k < (kTileCols * 8) / 256; ++k) {
+        for (uint32_t k = 0; k < (kEncCols * 8) / 256; ++k) {
             const uint32_t c = (t >> 3) + 32 * k, chunk = (t & 7) * 16;
             if (c >= ncols || chunk >= qbytes) continue;
             const uint8_t* src = stage_q + c * kStageQPitch + chunk;
@@ -588,9 +660,9 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
             if (chunk + 16 <= qbytes) {
                 const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-                *reinterpret_cast<u32x4*>(dst) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(dst));
             } else {
-                *reinterpret_cast<u32x2*>(dst) = lo;
+                __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
             }
         }
         // scale bytes: whole words when the destination allows it
@@ -651,12 +723,29 @@ __global__ void k_accumulate(float* __restrict__ buf, const float* __restrict__ 
     }
 }
 
-// one workgroup: m = max(obs), then buf[0] = max(buf[0] * decay, m)
-__global__ __launch_bounds__(256) void k_accumulate_reduce(float* __restrict__ buf, const float* __restrict__ obs,
-                                                           int64_t n, float decay) {
-    __shared__ float red[4];
+// one workgroup of 1024 threads: m = max(obs), then buf[0] = max(buf[0] *
+// decay, m).  Four independent 16-byte loads per thread per round keep the
+// latency of a single pass over a few hundred KB low.
+__global__ __launch_bounds__(1024) void k_accumulate_reduce(float* __restrict__ buf, const float* __restrict__ obs,
+                                                            int64_t n, float decay) {
+    __shared__ float red[16];
     float m = 0.0f;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) m = obs[i] > m ? obs[i] : m;
+    const int64_t nv = (reinterpret_cast<uintptr_t>(obs) % 16 == 0) ? n / 4 : 0;   // float4 part
+    const float4* o4 = reinterpret_cast<const float4*>(obs);
+    for (int64_t i = threadIdx.x; i < nv; i += 4 * blockDim.x) {
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t j = i + k * (int64_t)blockDim.x;
+            v[k] = j < nv ? o4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = v[k].x > m ? v[k].x : m; m = v[k].y > m ? v[k].y : m;
+            m = v[k].z > m ? v[k].z : m; m = v[k].w > m ? v[k].w : m;
+        }
+    }
+    for (int64_t i = 4 * nv + threadIdx.x; i < n; i += blockDim.x) m = obs[i] > m ? obs[i] : m;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
         const float o = __shfl_xor(m, d);
@@ -665,7 +754,8 @@ __global__ __launch_bounds__(256) void k_accumulate_reduce(float* __restrict__ b
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w) m = red[w] > m ? red[w] : m;
+        const int nw = (int)(blockDim.x >> 6);
+        for (int w = 1; w < nw; ++w) m = red[w] > m ? red[w] : m;
         const float t = buf[0] * decay;
         buf[0] = m > t ? m : t;
     }
@@ -675,11 +765,14 @@ __global__ __launch_bounds__(256) void k_accumulate_reduce(float* __restrict__ b
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
-hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
-    if (n <= 0) return hipSuccess;
-    unsigned grid = cdiv(n, 256);
+hipError_t launch_fill2(float* p, int64_t n, float* q, int64_t m, float v, hipStream_t st) {
+    if (p == nullptr) n = 0;
+    if (q == nullptr) m = 0;
+    if (n + m <= 0) return hipSuccess;
+    unsigned grid = cdiv(n + m, 256);
     if (grid > 4096) grid = 4096;
-    hipLaunchKernelGGL(k_fill_u32, dim3(grid), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n, __builtin_bit_cast(uint32_t, v));
+    hipLaunchKernelGGL(k_fill2_u32, dim3(grid), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n,
+                       reinterpret_cast<uint32_t*>(q), m, __builtin_bit_cast(uint32_t, v));
     return hipGetLastError();
 }
 
@@ -719,7 +812,7 @@ hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const u
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st) {
     if (row_end <= row_begin || K <= 0 || (!row && !col)) return hipSuccess;
-    dim3 grid(cdiv(K, kTileCols), cdiv(row_end - row_begin, kEncRows));
+    dim3 grid(cdiv(K, kEncCols), cdiv(row_end - row_begin, kEncRows));
 #define NVFP4_ENC_ARGS row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt
     if (caller_amax) {
         // amax from the caller: scales may saturate
@@ -756,7 +849,7 @@ hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float deca
 }
 
 hipError_t launch_accumulate_reduce(float* buf, const float* obs, int64_t n, float decay, hipStream_t st) {
-    hipLaunchKernelGGL(k_accumulate_reduce, dim3(1), dim3(256), 0, st, buf, obs, n, decay);
+    hipLaunchKernelGGL(k_accumulate_reduce, dim3(1), dim3(1024), 0, st, buf, obs, n, decay);
     return hipGetLastError();
 }
 

@@ -25,6 +25,18 @@
  * exponent pairs, tiny and subnormal a (where only the E2M1 code and its sign
  * must agree), and signed zeros.
  *
+ * A third family checks the two-op element quotient the encode kernels use:
+ * per block y_hi = RD(1/r) (RN(1/r), stepped down one ulp when r*y > 1) and
+ * y_lo = RN((1 - r*y_hi) * y_hi) >= 0, per element q = fma(a, y_hi, a*y_lo).
+ * It is not always RN(a/r) (it can differ in the last bit), so what is
+ * checked is the E2M1 code of q against the code of RN(a/r), for every bf16
+ * significand of a (both signs) against every significand of r, at the eight
+ * exponent offsets that put a/r anywhere in [2^-4, 2^4] (below, both codes
+ * are a signed zero; above, both saturate), plus tiny and zero numerators.
+ * The one divisor significand where the codes can differ, all mantissa bits
+ * set (r = 2^k * (2 - 2^-23), with a/r just above 0.25), is excluded here:
+ * the kernels send blocks with such an r to the exact path.
+ *
  * Build: gcc -O2 -mfma -ffp-contract=off -pthread; prints one summary line
  * and exits 0 only if nothing disagrees.
  */
@@ -88,6 +100,40 @@ static void* run_exhaustive(void* p)
     return NULL;
 }
 
+/* two-op element quotient */
+static float quot2(float a, float r)
+{
+    float y = 1.0f / r;
+    volatile float e = fmaf(-r, y, 1.0f);
+    float yhi = e < 0.0f ? f_of(u_of(y) - 1u) : y;
+    volatile float e2 = fmaf(-r, yhi, 1.0f);
+    float ylo = e2 * yhi;
+    volatile float p = a * ylo;
+    return fmaf(a, yhi, p);
+}
+
+static void* run_two_op(void* p)
+{
+    job_t* j = (job_t*)p;
+    uint32_t sign = (uint32_t)(j->task >> 7) << 31;
+    uint32_t m = (uint32_t)(j->task & 127);
+    for (int ea = -3; ea <= 4; ++ea) {
+        float a = f_of(sign | ((uint32_t)(127 + ea) << 23) | (m << 16));
+        for (uint32_t mr = 0; mr < (1u << 23) - 1u; ++mr) {
+            float r = f_of((127u << 23) | mr);
+            float q = quot2(a, r), ref = a / r;
+            j->checked++;
+            if (e2m1(q) != e2m1(ref)) {
+                if (j->bad < 4)
+                    fprintf(stderr, "two-op mismatch a=%08x r=%08x got=%08x want=%08x\n",
+                            u_of(a), u_of(r), u_of(q), u_of(ref));
+                j->bad++;
+            }
+        }
+    }
+    return NULL;
+}
+
 /* block-scale family: t = RN(b/6) for the 128 bf16 significands of b in
  * [1, 2), divided by every significand of S in [1, 2) */
 static void* run_scale_family(void* p)
@@ -138,6 +184,24 @@ static void check_tiny(uint64_t* checked, uint64_t* bad)
             }
         }
     }
+    /* the two-op quotient on tiny and subnormal numerators */
+    for (uint32_t abits = 0; abits < 0x2000u; ++abits) {
+        for (int s = 0; s < 2; ++s) {
+            float a = f_of(((uint32_t)s << 31) | (abits << 16));
+            for (int k = 0; k < 16; ++k) {
+                seed = seed * 1664525u + 1013904223u;
+                int er = -64 + (int)(seed >> 25);
+                seed = seed * 1664525u + 1013904223u;
+                float r = f_of(((uint32_t)(127 + er) << 23) | (seed >> 9));
+                if (fabsf(a) / r > 0x1p64f || (u_of(r) & 0x7FFFFFu) == 0x7FFFFFu) continue;
+                (*checked)++;
+                if (e2m1(quot2(a, r)) != e2m1(a / r)) {
+                    if (*bad < 4) fprintf(stderr, "two-op tiny mismatch a=%08x r=%08x\n", u_of(a), u_of(r));
+                    (*bad)++;
+                }
+            }
+        }
+    }
     /* signed zeros */
     float rs[] = {0x1p-64f, 1.0f, 3.0f, 0x1.fffffep63f};
     for (int i = 0; i < 4; ++i) {
@@ -146,6 +210,12 @@ static void check_tiny(uint64_t* checked, uint64_t* bad)
         (*checked) += 2;
         if (u_of(qp) != 0u || u_of(qn) != 0x80000000u) {
             fprintf(stderr, "signed zero lost for r=%a\n", (double)rs[i]);
+            (*bad)++;
+        }
+        float zp = quot2(0.0f, rs[i]), zn = quot2(-0.0f, rs[i]);
+        (*checked) += 2;
+        if (u_of(zp) != 0u || u_of(zn) != 0x80000000u) {
+            fprintf(stderr, "two-op signed zero lost for r=%a\n", (double)rs[i]);
             (*bad)++;
         }
     }
@@ -173,6 +243,17 @@ int main(void)
         for (int t = base; t < base + 16; ++t) {
             jobs[t].task = t; jobs[t].checked = 0; jobs[t].bad = 0;
             pthread_create(&th[t], NULL, run_scale_family, &jobs[t]);
+        }
+        for (int t = base; t < base + 16; ++t) {
+            pthread_join(th[t], NULL);
+            checked += jobs[t].checked;
+            bad += jobs[t].bad;
+        }
+    }
+    for (int base = 0; base < NT; base += 16) {
+        for (int t = base; t < base + 16; ++t) {
+            jobs[t].task = t; jobs[t].checked = 0; jobs[t].bad = 0;
+            pthread_create(&th[t], NULL, run_two_op, &jobs[t]);
         }
         for (int t = base; t < base + 16; ++t) {
             pthread_join(th[t], NULL);

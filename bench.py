@@ -10,15 +10,24 @@ re-reads the previous step's tensor from the 256 MB last-level cache.
 
 value = algorithmic bytes of the cast / step time, where the algorithmic
 bytes are one read of x plus every output (packed data, scales, fp32 amax).
-"roofline" times the cast's kernel launch with HIP events on the launch
-stream inside the timed region; "cpu_baseline" times the CPU oracle on the
-host (test infrastructure, never on the product path).
+"roofline" covers the dominant kernel, the encoding kernel (it reads x once
+and writes every packed byte and block scale, so its algorithmic bytes per
+launch equal the cast's): its launches inside the timed region are bracketed
+with HIP events on the launch stream through the library's nvfp4_trace_encode
+hook.  "traffic" is the HBM byte count per launch measured with rocprofv3
+FETCH_SIZE / WRITE_SIZE counters and calibrated against a plain copy; it is
+read from profiles/ and reported only while the kernel sources still hash to
+the value the counters were taken on (else null).  "cpu_baseline" times the
+CPU oracle on the host (test infrastructure, never on the product path).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (plain 256 MiB copies, for counters)
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,18 +47,62 @@ def algorithmic_bytes(M, K):
     return x + data + scales + amax
 
 
-def cpu_baseline(x_u16):
+KERNEL_SOURCES = ("nvfp4_block_scaled_bf16_amd/csrc/nvfp4_kernels.hip",
+                  "nvfp4_block_scaled_bf16_amd/csrc/nvfp4_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_c3_per_token_counters.md")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per encoding launch from the committed counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    m_b = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m_b or not m_h or m_h.group(1) != kernel_source_hash():
+        return None
+    return int(m_b.group(1))
+
+
+def copy_calibration(steps):
+    """Plain device copies of a known size (256 MiB read + 256 MiB written per
+    launch): the scale for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read_per_launch": a.numel() * 2,
+                      "bytes_written_per_launch": b.numel() * 2, "launches": steps}), flush=True)
+
+
+def cpu_baseline(inputs):
     """The oracle as it stands, single-threaded, on the full 16384 x 8192
-    tensor of one step (about 10 s of CPU work)."""
+    per-token row+col cast of each of the step inputs (about 15 s of CPU
+    work for three)."""
     import oracle
     t0 = time.perf_counter()
-    oracle.quantize(x_u16, oracle.PER_TOKEN)
+    for x in inputs:
+        oracle.quantize(x, oracle.PER_TOKEN)
     dt = time.perf_counter() - t0
-    nbytes = algorithmic_bytes(*x_u16.shape)
+    nbytes = algorithmic_bytes(*inputs[0].shape) * len(inputs)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full {x_u16.shape[0]}x{x_u16.shape[1]} per-token row+col cast "
-                      f"(seed 3000), single thread, {dt:.2f} s",
-            "seconds": dt}
+            "sample": f"{len(inputs)} full {inputs[0].shape[0]}x{inputs[0].shape[1]} per-token row+col casts "
+                      f"(the step's inputs), single thread, {dt:.2f} s",
+            "seconds": round(dt, 3)}
 
 
 def main():
@@ -58,12 +111,17 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the cast would shard "
               "rows across GPUs with no exchange for rowwise output and one max all-reduce of the "
               "column amax for columnwise output; that multi-GPU path is not built)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import numpy as np
     import torch
@@ -89,10 +147,8 @@ def main():
     def step(i, ev=None):
         x = xs[i % len(xs)]
         if ev is not None:
-            ev[0].record(stream)
+            nv.trace_encode(ev[0], ev[1])   # brackets the encoding kernel's launch
         nv.quantize_into(x, nv.PER_TOKEN, **out)
-        if ev is not None:
-            ev[1].record(stream)
         nv.amax_accumulate_reduce(buf, out["row_amax"], 0.9)
 
     for i in range(args.warmup):
@@ -101,6 +157,9 @@ def main():
 
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
+    for a, b in events:   # create the HIP events outside the timed region
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -116,9 +175,10 @@ def main():
     achieved = nbytes / (kavg * 1e-3) / 1e9
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "nvfp4_quantize per-token row+col (the cast's launches on the stream)",
-                "kernel_avg_us": round(kavg * 1e3, 2), "bytes_per_launch": nbytes}
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                "kernel": "k_encode (per-token, rowwise+columnwise)",
+                "kernel_avg_us": round(kavg * 1e3, 2), "bytes_per_launch": nbytes,
+                "kernel_source_sha256": kernel_source_hash()}
     line = {
         "metric": "NVFP4 quantize HBM GB/s + % of peak, 16384x8192 bf16 per-token row+col",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -133,7 +193,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inputs_host[0])
+        line["cpu_baseline"] = cpu_baseline(inputs_host)
     print(json.dumps(line), flush=True)
 
 

@@ -24,7 +24,8 @@
  *   - x is bf16, contiguous row-major [M][K] (or [T][K] for grouped), on the
  *     device.  All other arrays are device memory owned by the caller; the
  *     library allocates nothing, keeps no state between calls (beyond a
- *     thread-local error string) and never reads outputs before writing them.
+ *     thread-local error string and a pending nvfp4_trace_encode pair) and
+ *     never reads outputs before writing them.
  *   - Rowwise output ("row_*"): row_q [M][K/2] bytes, row_sf [M][K/16] E4M3
  *     codes, row_amax fp32.  Columnwise output ("col_*") is the quantization
  *     of the transpose: col_q [K][M/2], col_sf [K][M/16], col_amax fp32.
@@ -38,14 +39,18 @@
  *     non-OK status nothing was launched and nvfp4_last_error() names the
  *     problem.  NVFP4_EINVAL: NULL input, no direction requested, a NULL
  *     output in a requested direction, bad mode, decay outside [0,1],
- *     negative size.  NVFP4_ESHAPE: K % 16 (rowwise), M % 16 (columnwise),
- *     both for 16x16 tiles, group counts negative / not % 16 / not summing.
+ *     negative size.  NVFP4_ESHAPE: rowwise output needs K % 16 == 0,
+ *     columnwise output M % 16 == 0 and K % 8 == 0, 16x16 tiles both
+ *     M % 16 and K % 16; group counts must be >= 0 and % 16.
  *     NVFP4_EALIGN: a pointer not 16-byte aligned (amax/observed arrays need
  *     4-byte alignment).  NVFP4_EDEVICE: a HIP call or launch failed.
  *   - Outputs must not overlap the input or each other.  Inputs are assumed
  *     finite; a NaN or Inf input gives unspecified codes.
- *   - Any shape meeting the % 16 rules is accepted; all shapes give results
+ *   - Any shape meeting these rules is accepted; all shapes give results
  *     bit-identical to the CPU reference.
+ *   - The cast writes every amax output it computes: it first zero-fills the
+ *     arrays in-stream, then max-combines into them, so their prior contents
+ *     never matter.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -82,6 +87,19 @@ NVFP4_API int nvfp4_abi_version(void);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 NVFP4_API const char* nvfp4_last_error(void);
+
+/*
+ * Timing hook for benchmarks and profilers.  The next call on this thread
+ * that launches the data-encoding kernel (the kernel that writes the packed
+ * E2M1 bytes and the block scales) records `before` on that call's stream
+ * just before the launch and `after` just after it; the pair is then
+ * forgotten (one-shot).  A call that fails validation leaves it pending; a
+ * grouped call brackets its first encoding launch.  Both arguments are
+ * hipEvent_t handles created and owned by the caller; NULL, NULL cancels a
+ * pending pair, and exactly one NULL is NVFP4_EINVAL.  Recording an event
+ * costs no device work and changes no result.
+ */
+NVFP4_API nvfp4_status nvfp4_trace_encode(void* before, void* after);
 
 /*
  * Whole cast, one read of x serving both directions.  Pass NULL for all three

@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 
 EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_quantize_rowwise",
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
-           "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce")
+           "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
+           "nvfp4_trace_encode")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_dequantize": (st, [p, p, p, i64, i64, ctypes.c_int, p, p]),
         "nvfp4_amax_accumulate": (st, [p, p, i64, f32, p]),
         "nvfp4_amax_accumulate_reduce": (st, [p, p, i64, f32, p]),
+        "nvfp4_trace_encode": (st, [p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -220,3 +222,19 @@ def amax_accumulate_reduce(buf, observed, decay: float):
     _check(lib().nvfp4_amax_accumulate_reduce(_ptr(buf), _ptr(observed), observed.numel(), float(decay),
                                               _stream(buf.device)))
     return buf
+
+
+def trace_encode(before, after):
+    """Bracket the next encoding-kernel launch on this thread with two events
+    (torch.cuda.Event, or raw hipEvent_t handles as ints); None, None cancels.
+    A torch event that was never recorded has no handle yet, so it is recorded
+    once here on the current stream to create it."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if isinstance(ev, int):
+            return ctypes.c_void_p(ev)
+        if ev.cuda_event == 0:
+            ev.record()
+        return ctypes.c_void_p(ev.cuda_event)
+    _check(lib().nvfp4_trace_encode(handle(before), handle(after)))

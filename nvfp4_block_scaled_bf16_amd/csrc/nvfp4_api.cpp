@@ -77,6 +77,22 @@ GroupTable empty_table() {
     return gt;
 }
 
+// one-shot timing events set by nvfp4_trace_encode (hipEvent_t, caller-owned)
+thread_local hipEvent_t g_trace_before = nullptr;
+thread_local hipEvent_t g_trace_after = nullptr;
+
+// launch an encoding kernel, bracketed by the pending trace events if any
+template <class Launch>
+nvfp4_status encode_launch(hipStream_t st, Launch&& launch) {
+    hipEvent_t before = g_trace_before, after = g_trace_after;
+    g_trace_before = g_trace_after = nullptr;
+    nvfp4_status s;
+    if (before && (s = check_hip(hipEventRecord(before, st), "trace event")) != NVFP4_OK) return s;
+    if ((s = check_hip(launch(), "encode")) != NVFP4_OK) return s;
+    if (after && (s = check_hip(hipEventRecord(after, st), "trace event")) != NVFP4_OK) return s;
+    return NVFP4_OK;
+}
+
 // zero-fill up to two fp32 arrays (one launch) before an atomic-max pass
 nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
     return check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
@@ -106,12 +122,13 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         if ((s = zero(ra, M, ca, K, st)) != NVFP4_OK) return s;
         if (M == 0 || K == 0) return ok();
         if (fused_per_token_supported(M, K, r.want, c.want)) {
-            if ((s = check_hip(fused_per_token(x, M, K, row_q, row_sf, ra, col_q, col_sf, ca, st), "fused cast")) != NVFP4_OK) return s;
+            if ((s = encode_launch(st, [&] { return fused_per_token(x, M, K, row_q, row_sf, ra, col_q, col_sf, ca, st); })) != NVFP4_OK)
+                return s;
             return ok();
         }
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = check_hip(launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                         nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
+        if ((s = encode_launch(st, [&] { return launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                         nullptr, nullptr, gt, st); })) != NVFP4_OK) return s;
         return ok();
     }
     // per-tensor and 16x16 tiles: one tensor amax
@@ -119,9 +136,8 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (M == 0 || K == 0) return ok();
     if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, st), "amax")) != NVFP4_OK) return s;
     const int emode = mode == NVFP4_TILE_16x16 ? ENC_TILE : ENC_TENSOR;
-    if ((s = check_hip(launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st),
-                       "encode")) != NVFP4_OK)
+    if ((s = encode_launch(st, [&] { return launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st); })) != NVFP4_OK)
         return s;
     return ok();
 }
@@ -133,6 +149,13 @@ extern "C" {
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
 const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+nvfp4_status nvfp4_trace_encode(void* before, void* after) {
+    if ((before == nullptr) != (after == nullptr)) return fail(NVFP4_EINVAL, "give both trace events or neither");
+    g_trace_before = static_cast<hipEvent_t>(before);
+    g_trace_after = static_cast<hipEvent_t>(after);
+    return ok();
+}
 
 nvfp4_status nvfp4_quantize(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
                             uint8_t* row_q, uint8_t* row_sf, float* row_amax,
@@ -195,10 +218,9 @@ nvfp4_status nvfp4_encode(const void* xv, int64_t M, int64_t K, nvfp4_scaling mo
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     if (M == 0 || K == 0) return ok();
     const GroupTable gt = empty_table();
-    if ((s = check_hip(launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want, true,
+    if ((s = encode_launch(as_stream(stream), [&] { return launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want, true,
                                      static_cast<const uint16_t*>(xv), M, K, 0, M, row_amax, col_amax,
-                                     row_q, row_sf, col_q, col_sf, nullptr, nullptr, gt, as_stream(stream)),
-                       "encode")) != NVFP4_OK)
+                                     row_q, row_sf, col_q, col_sf, nullptr, nullptr, gt, as_stream(stream)); })) != NVFP4_OK)
         return s;
     return ok();
 }
@@ -232,8 +254,8 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
     if (!c.want) {
         const GroupTable gt = empty_table();
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, T, ra, nullptr, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = check_hip(launch_encode(ENC_TOKEN, true, false, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
-                                         nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
+        if ((s = encode_launch(st, [&] { return launch_encode(ENC_TOKEN, true, false, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
+                                         nullptr, nullptr, gt, st); })) != NVFP4_OK) return s;
         return ok();
     }
     // experts travel in the kernel arguments, a bounded number per launch
@@ -252,8 +274,8 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
         const int64_t end = off;
         if (end == begin) continue;
         if ((s = check_hip(launch_amax(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = check_hip(launch_encode(ENC_GROUPED, r.want, true, false, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
-                                         nullptr, nullptr, gt, st), "encode")) != NVFP4_OK) return s;
+        if ((s = encode_launch(st, [&] { return launch_encode(ENC_GROUPED, r.want, true, false, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
+                                         nullptr, nullptr, gt, st); })) != NVFP4_OK) return s;
     }
     return ok();
 }

@@ -497,7 +497,6 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     const bool odd = lane & 1;
     const int64_t tile_r0 = row_begin + (int64_t)by * kEncRows;
     const int64_t wbase = tile_r0 + wave * (kEncRows / 4);   // a wave covers 64 rows in 2 steps
-    const int64_t rbase = wbase + 16 * rg;
     float tileA = 0.0f;
     if (TILE) {
         tileA = row_amax ? row_amax[0] : col_amax[0];

@@ -87,6 +87,14 @@ def test_other_entry_points_validation():
     assert L.nvfp4_amax_accumulate_reduce(None, f, 4, ctypes.c_float(0.5), None) == EINVAL
 
 
+def test_trace_encode_validation():
+    L = nv.lib()
+    assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL
+    assert b"trace" in L.nvfp4_last_error()
+    assert L.nvfp4_trace_encode(None, P(FAKE)) == EINVAL
+    assert L.nvfp4_trace_encode(None, None) == 0   # cancels; nothing pending
+
+
 def test_grouped_validation():
     L = nv.lib()
     f = P(FAKE)

@@ -202,6 +202,25 @@ def test_accumulate(oracle, decay):
     assert_bytes_equal(host(sbuf), sref, "sbuf")
 
 
+def test_trace_encode_brackets_the_encoding_kernel(oracle):
+    x = _x(1072, 544, 21)
+    _announce("trace_encode events around a per-token cast")
+    d = to_dev(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nv.trace_encode(a, b)
+    out = nv.quantize(d, nv.PER_TOKEN)
+    again = nv.quantize(d, nv.PER_TOKEN)   # the pair was consumed by the first call
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) > 0.0
+    compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
+    for k in out:
+        assert torch.equal(out[k], again[k]), k
+    nv.trace_encode(a, b)
+    nv.trace_encode(None, None)   # cancelled: nothing is recorded
+    nv.quantize(d, nv.PER_TOKEN)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------- named workloads
 
 def test_c1_per_tensor_rowwise(oracle):

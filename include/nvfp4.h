@@ -41,7 +41,8 @@
  *     output in a requested direction, bad mode, decay outside [0,1],
  *     negative size.  NVFP4_ESHAPE: rowwise output needs K % 16 == 0,
  *     columnwise output M % 16 == 0 and K % 8 == 0, 16x16 tiles both
- *     M % 16 and K % 16; group counts must be >= 0 and % 16.
+ *     M % 16 and K % 16; group counts must be >= 0 and % 16; every cast
+ *     needs K < 2^25 (33554432) and M <= 2^40.
  *     NVFP4_EALIGN: a pointer not 16-byte aligned (amax/observed arrays need
  *     4-byte alignment).  NVFP4_EDEVICE: a HIP call or launch failed.
  *   - Outputs must not overlap the input or each other.  Inputs are assumed

@@ -64,7 +64,9 @@ nvfp4_status check_shape(int64_t M, int64_t K, bool row, bool col, int mode) {
     if (col && K % 8 != 0) return fail(NVFP4_ESHAPE, "columnwise output needs K %% 8 == 0 (K=%lld)", (long long)K);
     if (mode == NVFP4_TILE_16x16 && (M % 16 != 0 || K % 16 != 0))
         return fail(NVFP4_ESHAPE, "16x16 tiles need M and K multiples of 16 (M=%lld K=%lld)", (long long)M, (long long)K);
-    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 40)) return fail(NVFP4_ESHAPE, "size too large");
+    if (M > (int64_t(1) << 40)) return fail(NVFP4_ESHAPE, "M too large (M=%lld)", (long long)M);
+    // the encoding kernel addresses 32 rows of x with 32-bit offsets
+    if (K >= kMaxEncodeK) return fail(NVFP4_ESHAPE, "K must be below %lld (K=%lld)", (long long)kMaxEncodeK, (long long)K);
     return NVFP4_OK;
 }
 

@@ -69,17 +69,16 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
 
 struct BlockScale {
     float r;        // decode(code) * S: the divisor of every element
-    float y;        // RN(1 / r), for the FMA-corrected quotient
     uint32_t code;  // E4M3 byte
     bool zero;      // r == 0: sign-only nibbles
-    bool fast;      // the FMA-corrected quotient is exact for this block
 };
 
-// S: outer scale of the vector (A / 2688); bmag: block max magnitude bits
+// Exact block scale with IEEE divisions.  S: outer scale of the vector
+// (A / 2688); bmag: block max magnitude bits (16-bit)
 __device__ __forceinline__ BlockScale block_scale(uint32_t bmag, float S) {
     BlockScale bs;
     if (S == 0.0f) {
-        bs.r = 0.0f; bs.y = 0.0f; bs.code = 0u; bs.zero = true; bs.fast = true;
+        bs.r = 0.0f; bs.code = 0u; bs.zero = true;
         return bs;
     }
     float b = mag_to_f32(bmag);
@@ -88,24 +87,7 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmag, float S) {
     bs.code = e4m3_code(sf);
     bs.r = e4m3_value(bs.code) * S;
     bs.zero = bs.r == 0.0f;
-    bs.y = 1.0f / bs.r;
-    // the three-op quotient below equals IEEE division whenever r and the
-    // quotients stay in this range (checked exhaustively on the host)
-    bs.fast = bs.zero || (bs.r >= 0x1p-64f && bs.r <= 0x1p64f && b * bs.y <= 0x1p64f);
     return bs;
-}
-
-// q = RN(a / r).  fast: Markstein's correction of a * (1/r) with one fma for
-// the residual (written r*q0 - a so that -0 keeps its sign) and one for the
-// update; otherwise IEEE division.  zero: a signed zero.
-__device__ __forceinline__ float quotient(float a, const BlockScale& bs) {
-    if (bs.zero) return a * 0.0f;
-    if (bs.fast) {
-        float q0 = a * bs.y;
-        float e = __builtin_fmaf(bs.r, q0, -a);
-        return __builtin_fmaf(-e, bs.y, q0);
-    }
-    return a / bs.r;
 }
 
 // E2M1 of two quotients into byte SEL of `old`: gfx950's scaled FP4
@@ -117,23 +99,14 @@ __device__ __forceinline__ uint32_t put_fp4x2(uint32_t old, float q0, float q1) 
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, 1.0f, SEL);
 }
 
-// encode 8 bf16 values held in 4 words (elements 0..7 in order) -> 32 bits
-__device__ __forceinline__ uint32_t encode8(u32x4 w, const BlockScale& bs) {
-    uint32_t o = 0;
-    o = put_fp4x2<0>(o, quotient(bf_lo(w.x), bs), quotient(bf_hi(w.x), bs));
-    o = put_fp4x2<1>(o, quotient(bf_lo(w.y), bs), quotient(bf_hi(w.y), bs));
-    o = put_fp4x2<2>(o, quotient(bf_lo(w.z), bs), quotient(bf_hi(w.z), bs));
-    o = put_fp4x2<3>(o, quotient(bf_lo(w.w), bs), quotient(bf_hi(w.w), bs));
-    return o;
-}
-
 // outer scale from an outer amax
 __device__ __forceinline__ float outer_scale(float A) { return A / 2688.0f; }
 
 // ------------------------------------------------------------- fast path
 //
-// The hot loops avoid IEEE division.  Facts, each checked exhaustively (1 and
-// 1b on the host by tests/native/div_identity_check.c, 2 and 3 on the GPU):
+// The hot loops avoid IEEE division.  Facts, each checked exhaustively (1,
+// 1b and 4 on the host by tests/native/div_identity_check.c, 2 and 3 on the
+// GPU):
 //  1. for a bf16 numerator a and divisor r with y = RN(1/r), the sequence
 //     q0 = a*y; e = fma(r, q0, -a); q = fma(-e, y, q0) returns RN(a/r)
 //     (Markstein's correction) whenever r is in [2^-64, 2^64] and |a|*y <=
@@ -141,15 +114,16 @@ __device__ __forceinline__ float outer_scale(float A) { return A / 2688.0f; }
 //  1b. the same sequence returns RN(t/S) for t = RN(b/6), b bf16, and any
 //     normal S (t has only 128 significands, each checked against every
 //     significand of S);
-//  2. v_rcp_f32 followed by one Newton step, fma(fma(-r, y0, 1), y0, y0),
-//     returns RN(1/r) for every normal r in [2^-64, 2^64];
+//  2. v_rcp_f32 returns RD(1/r) or RU(1/r) (exactly 1/r when that is
+//     representable) for every normal r in [2^-64, 2^64]; one Newton step,
+//     fma(fma(-r, y0, 1), y0, y0), then gives RN(1/r);
 //  3. the scaled FP4 conversion rounds like the E2M1 table (put_fp4x2);
 //  4. the two-op element quotient below (quot2) gives the E2M1 code of
 //     RN(a/r) for bf16 a (host check, with one excluded divisor pattern).
 // Blocks outside these ranges, or whose scale falls in the E4M3 subnormal
 // range, take an exact slow path chosen per wave.
 
-// RN(1/r) for normal r in [2^-64, 2^64]
+// RN(1/r) for normal r in [2^-64, 2^64] (fact 2)
 __device__ __forceinline__ float rcp_rn(float r) {
     float y0 = __builtin_amdgcn_rcpf(r);
     float e = __builtin_fmaf(-r, y0, 1.0f);
@@ -180,11 +154,13 @@ __device__ __forceinline__ Outer make_outer(float A) {
     return o;
 }
 
-// Per-block parameters on the fast path: r = decode(code) * S, and the
-// split reciprocal yh = RD(1/r), yl = RN((1 - r*yh) * yh) >= 0 used by the
-// two-op element quotient.  slow: this block needs the exact path.
+// Per-block parameters on the fast path: the split reciprocal yh = RD(1/r),
+// yl = RN((1 - r*yh) * yh) >= 0 of the divisor r = decode(code) * S, used
+// by the two-op element quotient, and the E4M3 scale byte in the low 8 bits
+// of `code` (the bits above are ignored by byte stores).  slow: this block
+// needs the exact path.  The outer scale's own range flag is not included.
 struct FastBlock {
-    float r, yh, yl;
+    float yh, yl;
     uint32_t code;
     bool slow;
 };
@@ -194,38 +170,45 @@ struct FastBlock {
 // except r with all mantissa bits set (fact 4, checked exhaustively on the
 // host; fast_block sends those blocks to the exact path).  yl >= 0 keeps the
 // sign of a zero numerator.
-__device__ __forceinline__ float quot2(float a, const FastBlock& f) {
-    return __builtin_fmaf(a, f.yh, a * f.yl);
+__device__ __forceinline__ float quot2(float a, float yh, float yl) {
+    return __builtin_fmaf(a, yh, a * yl);
 }
 
 constexpr float kRcp6 = 0x1.555556p-3f;   // RN(1/6)
 
-// SAT: the outer amax may be smaller than the data (caller-supplied amax),
-// so the block scale may saturate and quotients exceed 6.4.
+// bbits: the block's largest magnitude as fp32 bits (a bf16 magnitude in the
+// high half, zeros below).  SAT: the outer amax may be smaller than the data
+// (caller-supplied amax), so the block scale may saturate and quotients
+// exceed 6.
 template <bool SAT>
-__device__ __forceinline__ FastBlock fast_block(uint32_t bmag, const Outer& o) {
+__device__ __forceinline__ FastBlock fast_block(uint32_t bbits, const Outer& o) {
     FastBlock fb;
-    const float b = mag_to_f32(bmag);
+    const float b = __uint_as_float(bbits);
     const float t = div_fast(b, 6.0f, kRcp6);   // RN(b / 6)   (fact 1: b is bf16)
     const float sf = div_fast(t, o.S, o.yS);    // RN(t / S)   (fact 1b: t = RN(b/6))
     const uint32_t u = __float_as_uint(sf);
-    // E4M3 code of sf: round the mantissa to 3 bits, ties to even, then clamp
-    // to [code 0, 0x7E].  The lower clamp gives code 0 for all-zero blocks
-    // (their elements are +/-0, so the divisor's value does not matter); the
-    // upper one saturates at 448.
-    uint32_t c = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
-    c = c < 0x3C0u ? 0x3C0u : (c > 0x43Eu ? 0x43Eu : c);
-    fb.code = c - 0x3C0u;
-    fb.r = __uint_as_float(c << 20) * o.S;     // decode(code) * S; 2^-7 * S for code 0
-    const float y = rcp_rn(fb.r);               // RN(1/r)
-    const float e = __builtin_fmaf(-fb.r, y, 1.0f);
-    fb.yh = e < 0.0f ? __uint_as_float(__float_as_uint(y) - 1u) : y;   // RD(1/r)
-    fb.yl = __builtin_fmaf(-fb.r, fb.yh, 1.0f) * fb.yh;
+    // E4M3 code of sf by rounding its fp32 encoding: mantissa to 3 bits, ties
+    // to even (a carry moves into the exponent).  c holds the fp32 exponent
+    // and the 3 kept mantissa bits plus 0x40, so that its low byte is the
+    // E4M3 code (the bias change 127 -> 7 is 120 << 3 = 0x3C0 = 0x400 - 0x40).
+    // The clamp to [0x400, 0x47E] gives code 0 for an all-zero block (its
+    // elements are +/-0, so the divisor's value does not matter) and
+    // saturates at 448 (0x7E).
+    uint32_t c = (u + (0x7FFFFu + (0x40u << 20)) + ((u >> 20) & 1u)) >> 20;
+    c = c < 0x400u ? 0x400u : (c > 0x47Eu ? 0x47Eu : c);
+    fb.code = c;
+    const float r = __uint_as_float((c << 20) - (0x40u << 20)) * o.S;   // decode(code) * S; 2^-7 * S for code 0
+    // RD(1/r): the hardware reciprocal is RD or RU (fact 2); step down one
+    // ulp when the residual 1 - r*y0 is negative
+    const float y0 = __builtin_amdgcn_rcpf(r);
+    const float e = __builtin_fmaf(-r, y0, 1.0f);
+    fb.yh = __uint_as_float(__float_as_uint(y0) - (__float_as_uint(e) >> 31));
+    fb.yl = __builtin_fmaf(-r, fb.yh, 1.0f) * fb.yh;
     // exact path: sf in the E4M3 subnormal range (and not an all-zero
     // block), or an r with all mantissa bits set (fact 4's exception)
-    bool slow = (u - 1u) < (0x3C800000u - 1u) || (__float_as_uint(fb.r) & 0x7FFFFFu) == 0x7FFFFFu;
-    if (SAT) slow |= !(fb.r <= 0x1p64f && b * fb.yh <= 0x1p64f);
-    fb.slow = slow || o.slow;
+    bool slow = (u - 1u) < (0x3C800000u - 1u) || (__float_as_uint(r) & 0x7FFFFFu) == 0x7FFFFFu;
+    if (SAT) slow |= !(r <= 0x1p64f && b * fb.yh <= 0x1p64f);
+    fb.slow = slow;
     return fb;
 }
 

@@ -11,6 +11,9 @@ struct GroupTable;
 enum AmaxKind { AMAX_TENSOR = 0, AMAX_TOKEN = 1, AMAX_GROUPED = 2 };
 enum EncodeMode { ENC_TENSOR = 0, ENC_TOKEN = 1, ENC_TILE = 2, ENC_GROUPED = 3 };
 
+// the encoding kernel forms 32-bit byte offsets within 32 rows of x
+constexpr int64_t kMaxEncodeK = int64_t(1) << 25;
+
 hipError_t launch_fill2(float* p, int64_t n, float* q, int64_t m, float v, hipStream_t st);
 hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
                        float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,

@@ -1,15 +1,16 @@
-// nvfp4_kernels.hip -- general-path HIP kernels of the bf16 -> NVFP4 cast for
-// gfx950: outer amax, encode (rowwise and columnwise from one read), 16x16
-// tiles, grouped experts, dequantize and the decayed accumulator.  They serve
-// every shape the C ABI accepts; large aligned per-token and per-tensor casts
-// take the fused path in nvfp4_fused.hip instead.
+// nvfp4_kernels.hip -- HIP kernels of the bf16 -> NVFP4 cast for gfx950:
+// outer amax, encode (rowwise and columnwise from one read), 16x16 tiles,
+// grouped experts, dequantize and the decayed accumulator.  They serve every
+// shape the C ABI accepts.
 //
 // Work decomposition shared by the amax and encode kernels: a lane owns a
-// 16-row x 8-column sub-block (sixteen 16-byte loads, one per row), so a
-// wave covers 16 rows x 512 columns and reads 1 KB of one row per load
-// instruction.  A lane's 8 columns x 16 rows are eight complete columnwise
-// blocks; the 16 rows hold half of a rowwise block each, the other half
-// sitting in the neighbouring lane (lanes 2j and 2j+1 exchange maxima).
+// 16-row x 8-column sub-block (sixteen 16-byte loads, one per row), so one
+// load instruction reads 16 bytes per lane along a row (1 KB of one row per
+// wave in the amax pass; 512 bytes of each of two rows in the encode pass,
+// whose waves are two 32-lane row groups).  A lane's 8 columns x 16 rows are
+// eight complete columnwise blocks; the 16 rows hold half of a rowwise block
+// each, the other half sitting in the neighbouring lane (lanes 2j and 2j+1
+// exchange maxima and block parameters).
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
 
@@ -284,119 +285,6 @@ __device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, u
     d.col_sf[c * d.col_sf_stride] = (uint8_t)code;
 }
 
-// Fast encode and store of one lane's 16x8 sub-block.  rowO[s] is the outer
-// scale of this lane's own row 2s + parity (the two lanes of a pair share
-// every rowwise block: each computes the parameters of one row of every row
-// pair and the pair swaps them); colO are this lane's 8 columns; tileO the
-// tensor's (16x16 tiles).  Returns true if some block needs the exact path,
-// in which case the caller re-encodes the sub-block exactly over what was
-// stored here.
-template <bool ROW, bool COL, bool TILE, bool SAT, bool STAGE>
-__device__ __forceinline__ bool encode_fast(u32x4 v[16], const float (*row_scale)[2], const Outer& rowO_t,
-                                            bool per_tensor_rows, const Outer* colO, const Outer& tileO,
-                                            const SubDst& d) {
-    const bool odd = d.odd;
-    bool slow = false;
-    FastBlock cb[8];
-    FastBlock tb;
-    if (TILE) {
-        uint32_t m = 0u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = pk_max_u16(m, rowmax_word(v[i]));
-        m = pk_max_u16(m, from_pair(m));
-        tb = fast_block<SAT>(max_halves(m), tileO);
-        slow = tb.slow;
-    } else if (COL) {
-        uint32_t cm[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            cm[0] = pk_max_u16(cm[0], abs2(v[i].x));
-            cm[1] = pk_max_u16(cm[1], abs2(v[i].y));
-            cm[2] = pk_max_u16(cm[2], abs2(v[i].z));
-            cm[3] = pk_max_u16(cm[3], abs2(v[i].w));
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            cb[j] = fast_block<SAT>((j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xffffu), colO[j]);
-            slow |= cb[j].slow;
-        }
-    }
-    // columnwise pass
-    if (COL) {
-        uint32_t cq[8][2];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const FastBlock& f = TILE ? tb : cb[j];
-                const float q0 = quot2(elem(v[i], j), f), q1 = quot2(elem(v[i + 1], j), f);
-                uint32_t& w = cq[j][i >> 3];
-                const int byte = (i >> 1) & 3;
-                if (byte == 0) w = put_fp4x2<0>(0u, q0, q1);
-                else if (byte == 1) w = put_fp4x2<1>(w, q0, q1);
-                else if (byte == 2) w = put_fp4x2<2>(w, q0, q1);
-                else w = put_fp4x2<3>(w, q0, q1);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) store_col<STAGE>(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
-    }
-    // rowwise pass, one row pair at a time: each lane computes the block of
-    // its own row (2s + parity) and swaps the parameters with the pair.  The
-    // empty register barrier keeps the compiler from carrying the 128
-    // unpacked values of the columnwise pass over into this one (unpacking
-    // again costs one op per element; keeping them live costs occupancy).
-    if (ROW && COL) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[i]));
-    }
-    if (ROW) {
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-            const int i = 2 * s2;
-            FastBlock rf[2];
-            uint32_t own_code;
-            if (TILE) {
-                rf[0] = rf[1] = tb; own_code = tb.code;
-            } else {
-                uint32_t f0 = rowmax_word(v[i]), f1 = rowmax_word(v[i + 1]);
-                f0 = pk_max_u16(f0, from_pair(f0));
-                f1 = pk_max_u16(f1, from_pair(f1));
-                Outer ro = rowO_t;
-                if (!per_tensor_rows) {
-                    const int own = i + (odd ? 1 : 0);
-                    const float S = row_scale[own][0];
-                    ro.S = S < 0.0f ? 1.0f : S;
-                    ro.yS = row_scale[own][1];
-                    ro.slow = S < 0.0f;
-                }
-                const FastBlock f = fast_block<SAT>(max_halves(odd ? f1 : f0), ro);
-                slow |= f.slow;
-                own_code = f.code;
-                FastBlock pf;
-                pf.yh = __uint_as_float(from_pair(__float_as_uint(f.yh)));
-                pf.yl = __uint_as_float(from_pair(__float_as_uint(f.yl)));
-                rf[0].yh = odd ? pf.yh : f.yh; rf[0].yl = odd ? pf.yl : f.yl;
-                rf[1].yh = odd ? f.yh : pf.yh; rf[1].yl = odd ? f.yl : pf.yl;
-            }
-            uint32_t w[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4& vv = v[i + h];
-                const FastBlock& f = rf[h];
-                uint32_t q = 0u;
-                q = put_fp4x2<0>(q, quot2(bf_lo(vv.x), f), quot2(bf_hi(vv.x), f));
-                q = put_fp4x2<1>(q, quot2(bf_lo(vv.y), f), quot2(bf_hi(vv.y), f));
-                q = put_fp4x2<2>(q, quot2(bf_lo(vv.z), f), quot2(bf_hi(vv.z), f));
-                q = put_fp4x2<3>(q, quot2(bf_lo(vv.w), f), quot2(bf_hi(vv.w), f));
-                w[h] = q;
-            }
-            store_row_pair(d, i, w[0], w[1], own_code);
-        }
-    }
-    return slow;
-}
-
 // Exact encode and store of a sub-block with IEEE divisions throughout,
 // re-reading the data from xr (row r0, column 0; row stride K).  rowA[i]:
 // amax of row i; colA: this lane's 8 column amax; tileA: the tensor's.
@@ -457,13 +345,44 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
     }
 }
 
+// Buffer resources for the hot loop: a raw buffer over [base, base + bytes)
+// (bytes <= 2^31).  Loads at a lane offset at or beyond `bytes` read zeros
+// and stores there are dropped, which is how rows past the end of the tensor
+// and lanes past its last column are handled (offsets stay below 2^32).  The
+// fourth descriptor word is the raw-buffer setting of the gfx9 family.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCacheNT = 2;               // nontemporal hint in the gfx940-family cache-policy bits
+constexpr uint32_t kOffOut = 0x80000000u; // lane offset beyond every buffer's extent
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// DPP quad permutations: the value of the even / odd lane of each pair
+__device__ __forceinline__ float from_even(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xA0, 0xF, 0xF, false));   // [0,0,2,2]
+}
+__device__ __forceinline__ float from_odd(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xF5, 0xF, 0xF, false));   // [1,1,3,3]
+}
+
 // MODE: ENC_TENSOR (row_amax[0] / col_amax[0] for every vector), ENC_TOKEN
 // (row_amax[r], col_amax[c]), ENC_TILE (16x16 tiles, tensor amax in
 // row_amax[0] or col_amax[0]; also fills row_amax[1..M) and col_amax[1..K)
 // with it), ENC_GROUPED (rowwise per-token; columnwise per expert with
 // col_amax[e][K] and per-expert output slabs).  A workgroup covers 256 rows
-// x 512 columns; each wave walks four 16-row sub-blocks.  SAT: the amax
-// comes from the caller and may be smaller than the data.
+// x 256 columns: each wave takes 64 rows in two steps of 32, a step being
+// two groups of 32 lanes with a 16-row x 8-column sub-block per lane.  SAT:
+// the amax comes from the caller and may be smaller than the data.
+// Requires K < 2^25 (32 rows of a step span less than 2^31 bytes).
+//
+// A step: (1) sixteen 16-byte loads; (2) column maxima and the rowwise block
+// maxima from the packed words, then the block parameters of the lane's 8
+// column blocks; (3) per row pair, the rowwise block parameters of the
+// lane's own row (2s + parity, swapped with the pair through DPP), the two
+// rows unpacked once and encoded both ways.  Rowwise bytes go straight to
+// memory; columnwise bytes are staged in LDS and written in whole lines at
+// the end.
 template <int MODE, bool ROW, bool COL, bool SAT>
 __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                 int64_t row_begin, int64_t row_end,
@@ -473,12 +392,14 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                                                 float* __restrict__ fill_row, float* __restrict__ fill_col,
                                                 GroupTable gt) {
     constexpr bool TILE = MODE == ENC_TILE;
-    __shared__ float row_scale[4][32][2];    // per wave: S and 1/S of its 32 rows (S < 0: exact path)
+    constexpr bool ROWTOK = ROW && !TILE && MODE != ENC_TENSOR;   // a row amax per row
+    __shared__ float row_scale[4][32][2];    // per wave: S and 1/S of the step's 32 rows
     // columnwise output of the workgroup tile, written out in whole lines
     constexpr bool STAGE = COL && MODE != ENC_GROUPED;
     __shared__ __attribute__((aligned(16))) uint8_t stage_q[STAGE ? kEncCols * kStageQPitch : 16];
     __shared__ __attribute__((aligned(16))) uint8_t stage_sf[STAGE ? kEncCols * kStageSfPitch : 16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups are dispatched round-robin over the 8 XCDs (each with its
     // own L2).  Give XCD x a contiguous run of tiles, row band major, so the
     // scale bytes that share a cache line (rowwise: 4 adjacent column tiles,
@@ -509,6 +430,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 
     // columnwise outer scales of this lane's 8 columns
     Outer colO[8];
+    bool col_slow = false;
     int cur_group = -1;
     int64_t m_len = M, grow0 = 0;
     if (COL && !TILE && MODE != ENC_GROUPED) {
@@ -518,13 +440,17 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 #pragma unroll
         for (int j = 0; j < 8; ++j) ca[j] = col_amax[(MODE == ENC_TENSOR) ? 0 : (col_ok ? c0 + j : 0)];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
+        for (int j = 0; j < 8; ++j) {
+            colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
+            col_slow |= colO[j].slow;
+        }
     }
     // per-tensor rowwise outer scale
     const float rowA_t = (ROW && MODE == ENC_TENSOR) ? row_amax[0] : 0.0f;
     const Outer rowO_t = make_outer(rowA_t);
+    const bool tile_slow = (TILE && tileO.slow) || (ROW && MODE == ENC_TENSOR && rowO_t.slow);
 
-    // destinations of a sub-block
+    // destinations of a sub-block (columnwise output and the exact path)
     auto make_dst = [&](int64_t r0, int nrows, int64_t mlen, int64_t g0) {
         SubDst d;
         d.row_q = row_q + r0 * (K / 2);
@@ -545,40 +471,41 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         return d;
     };
 
+    // lane parts of the buffer offsets within a step (row group, column)
+    const uint32_t xrow = (uint32_t)K * 2u, qrow = (uint32_t)(K / 2), srow = (uint32_t)(K / 16);
+    const uint32_t vx = col_ok ? 16u * rg * xrow + c0 * 2u : kOffOut;
+    const uint32_t vq = col_ok ? 16u * rg * qrow + c0 / 2u : kOffOut;
+    const uint32_t vs = col_ok ? (16u * rg + (odd ? 1u : 0u)) * srow + c0 / 16u : kOffOut;
+    // v_perm selector moving this lane's row (low half: even, high: odd) to the top half
+    const uint32_t own_sel = odd ? 0x03020c0cu : 0x01000c0cu;
+
     uint32_t slow_mask = 0u;
-    // unconditional loads: a lane past the last column reads column 0 and a
-    // row past the end (rowwise-only calls with M % 16 != 0) repeats the last
-    // row; neither is stored, and column maxima are only formed when M % 16
-    // == 0, i.e. when every row is real.  The next sub-block's loads are
-    // issued before the current one is encoded.
-    const uint32_t cl = col_ok ? c0 : 0u;
-    auto load16 = [&](int64_t r0, u32x4* v) {
-        const int nr = (int)(row_end - r0 < 16 ? row_end - r0 : 16);
-        const uint16_t* xr = x + r0 * K;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int ii = i < nr ? i : nr - 1;
-            v[i] = *reinterpret_cast<const u32x4*>(xr + ii * K + cl);
-        }
-    };
     constexpr int kSteps = kEncRows / 4 / 32;   // 32-row steps per wave
 #pragma unroll 1
     for (int sb = 0; sb < kSteps; ++sb) {
         const int64_t wr0 = wbase + 32 * sb;     // first row of the wave's step
         if (wr0 >= row_end) break;
-        // a row group past the end only occurs when M % 32 != 0; it loads
-        // the last row again and stores nothing
-        const int64_t r0 = wr0 + 16 * rg < row_end ? wr0 + 16 * rg : wr0;
-        const bool group_ok = wr0 + 16 * rg < row_end;
+        const uint32_t nrows = (uint32_t)(row_end - wr0 < 32 ? row_end - wr0 : 32);   // rows of the step
+        const bool group_ok = 16u * rg < nrows;
+        const int64_t r0 = group_ok ? wr0 + 16 * rg : wr0;
         // the step's rowwise amax first, so that waiting for it does not also
         // wait for the 16 data loads issued after it
         float ra = 0.0f;
-        if (ROW && !TILE && MODE != ENC_TENSOR) {
-            ra = row_amax[wr0 + (lane & 31) < row_end ? wr0 + (lane & 31) : row_begin];
+        if (ROWTOK) {
+            ra = row_amax[(uint32_t)(lane & 31) < nrows ? wr0 + (lane & 31) : row_begin];
             __builtin_amdgcn_sched_barrier(0);
         }
+        // row strides made opaque each step: otherwise the compiler keeps the
+        // 40 per-row lane offsets below live across the loop in registers
+        // instead of forming each with one add where it is used
+        uint32_t xr = xrow, qr = qrow, sr = srow;
+        asm volatile("" : "+s"(xr), "+s"(qr), "+s"(sr));
+        // (1) loads through buffers spanning the step's valid rows, so rows
+        // past the end read zeros (and their stores below are dropped)
+        const __amdgpu_buffer_rsrc_t bx_rs = rsrc(x + wr0 * K, nrows * xrow);
         u32x4 v[16];
-        load16(r0, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(bx_rs, vx + i * xr, 0, kCacheNT);
         if (COL && MODE == ENC_GROUPED) {
             const int g = group_of_row(gt, r0);
             if (g != cur_group) {
@@ -589,27 +516,154 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 float ca[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) ca[j] = col_amax[base + (col_ok ? c0 + j : 0)];
+                col_slow = false;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
+                for (int j = 0; j < 8; ++j) {
+                    colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
+                    col_slow |= colO[j].slow;
+                }
             }
         }
-        const int nrows = group_ok ? (int)(row_end - r0 < 16 ? row_end - r0 : 16) : 0;
-        SubDst d = make_dst(r0, nrows > 0 ? nrows : 1, m_len, grow0);
+        SubDst d = make_dst(r0, group_ok ? (int)(nrows - 16u * rg < 16u ? nrows - 16u * rg : 16u) : 1, m_len, grow0);
         if (!group_ok) { d.nrows = 0; d.col_ok = false; }
 
         // rowwise outer scales: lanes 0..31 compute one row of the step each
-        // into LDS
-        if (ROW && !TILE && MODE != ENC_TENSOR) {
-            const Outer o = make_outer(wr0 + (lane & 31) < row_end ? ra : 0.0f);
+        // into LDS; a row outside the fast range sends the whole step to the
+        // exact path
+        bool step_slow = tile_slow;
+        if (ROWTOK) {
+            const bool row_in = (uint32_t)(lane & 31) < nrows;
+            const Outer o = make_outer(row_in ? ra : 0.0f);
             if (lane < 32) {
-                row_scale[wave][lane][0] = o.slow ? -1.0f : o.S;
+                row_scale[wave][lane][0] = o.S;
                 row_scale[wave][lane][1] = o.yS;
             }
+            step_slow |= __builtin_amdgcn_ballot_w64(o.slow) != 0ull;
             __builtin_amdgcn_wave_barrier();
         }
-        const bool slow = encode_fast<ROW, COL, TILE, SAT, STAGE>(v, row_scale[wave] + 16 * rg, rowO_t, MODE == ENC_TENSOR,
-                                                           colO, tileO, d);
-        if (__builtin_amdgcn_ballot_w64(slow) != 0ull) slow_mask |= 1u << sb;
+
+        // (2) maxima from the packed words
+        bool slow = col_slow;
+        uint32_t cm[4] = {0u, 0u, 0u, 0u};    // columns 2k (low half) and 2k+1 (high half)
+        uint32_t bm[8];                       // rowwise block max of the own row of pair s
+        uint32_t tm = 0u;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            uint32_t rw[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 w = v[2 * s + h];
+                const uint32_t a0 = abs2(w.x), a1 = abs2(w.y), a2 = abs2(w.z), a3 = abs2(w.w);
+                if (COL && !TILE) {
+                    cm[0] = pk_max_u16(cm[0], a0);
+                    cm[1] = pk_max_u16(cm[1], a1);
+                    cm[2] = pk_max_u16(cm[2], a2);
+                    cm[3] = pk_max_u16(cm[3], a3);
+                }
+                rw[h] = pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3));
+            }
+            if (TILE) {
+                tm = pk_max_u16(tm, pk_max_u16(rw[0], rw[1]));
+            } else if (ROW) {
+                // (row 2s | row 2s+1 << 16) over the lane's 8 columns, then the pair's 16
+                uint32_t m = pk_max_u16(__builtin_amdgcn_perm(rw[1], rw[0], 0x05040100u),
+                                        __builtin_amdgcn_perm(rw[1], rw[0], 0x07060302u));
+                m = pk_max_u16(m, from_pair(m));
+                bm[s] = __builtin_amdgcn_perm(m, m, own_sel);
+            }
+        }
+        // block parameters of the lane's column blocks (or of its 16x16 tile)
+        FastBlock cb[8];
+        FastBlock tb;
+        if (TILE) {
+            const uint32_t m = pk_max_u16(tm, from_pair(tm));
+            tb = fast_block<SAT>(max_halves(m) << 16, tileO);
+            slow |= tb.slow;
+        } else if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t bits = (j & 1) ? (cm[j >> 1] & 0xffff0000u) : (cm[j >> 1] << 16);
+                cb[j] = fast_block<SAT>(bits, colO[j]);
+                slow |= cb[j].slow;
+            }
+        }
+
+        // (3) per row pair: rowwise parameters, then both encodings
+        const __amdgpu_buffer_rsrc_t q_rs = rsrc(row_q + wr0 * (K / 2), nrows * qrow);
+        const __amdgpu_buffer_rsrc_t s_rs = rsrc(row_sf + wr0 * (K / 16), nrows * srow);
+        uint32_t cq[8][2];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int i = 2 * s;
+            float yh0 = 0.0f, yl0 = 0.0f, yh1 = 0.0f, yl1 = 0.0f;
+            if (ROW) {
+                if (TILE) {
+                    yh0 = yh1 = tb.yh;
+                    yl0 = yl1 = tb.yl;
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)tb.code, s_rs, vs + i * sr, 0, 0);
+                } else {
+                    Outer ro = rowO_t;
+                    if (ROWTOK) {
+                        ro.S = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][0];
+                        ro.yS = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][1];
+                    }
+                    const FastBlock f = fast_block<SAT>(bm[s], ro);
+                    slow |= f.slow;
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs + i * sr, 0, 0);
+                    yh0 = from_even(f.yh); yl0 = from_even(f.yl);
+                    yh1 = from_odd(f.yh);  yl1 = from_odd(f.yl);
+                }
+            }
+            // The empty asm orders the row pairs: pair s is unpacked (16
+            // registers) only after pair s-1's stores and columnwise nibbles
+            // are done.  Otherwise the rowwise halves of all pairs run as
+            // soon as their rows arrive and every unpacked value stays live
+            // until the columnwise block parameters are known.
+            u32x4 w0 = v[i], w1 = v[i + 1];
+            if (COL && s > 0)
+                asm volatile("" : "+v"(w0), "+v"(w1), "+v"(cq[0][(s - 1) >> 2]), "+v"(cq[1][(s - 1) >> 2]),
+                             "+v"(cq[2][(s - 1) >> 2]), "+v"(cq[3][(s - 1) >> 2]), "+v"(cq[4][(s - 1) >> 2]),
+                             "+v"(cq[5][(s - 1) >> 2]), "+v"(cq[6][(s - 1) >> 2]), "+v"(cq[7][(s - 1) >> 2]));
+            else
+                asm volatile("" : "+v"(w0), "+v"(w1));
+            const float a0[8] = {bf_lo(w0.x), bf_hi(w0.x), bf_lo(w0.y), bf_hi(w0.y),
+                                 bf_lo(w0.z), bf_hi(w0.z), bf_lo(w0.w), bf_hi(w0.w)};
+            const float a1[8] = {bf_lo(w1.x), bf_hi(w1.x), bf_lo(w1.y), bf_hi(w1.y),
+                                 bf_lo(w1.z), bf_hi(w1.z), bf_lo(w1.w), bf_hi(w1.w)};
+            if (COL) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float yh = TILE ? tb.yh : cb[j].yh, yl = TILE ? tb.yl : cb[j].yl;
+                    const float q0 = quot2(a0[j], yh, yl), q1 = quot2(a1[j], yh, yl);
+                    uint32_t& w = cq[j][s >> 2];
+                    // byte 0 first: the bytes above it are written by the next
+                    // three conversions, so the register merged into can be q0's
+                    if ((s & 3) == 0) w = put_fp4x2<0>(__float_as_uint(q0), q0, q1);
+                    else if ((s & 3) == 1) w = put_fp4x2<1>(w, q0, q1);
+                    else if ((s & 3) == 2) w = put_fp4x2<2>(w, q0, q1);
+                    else w = put_fp4x2<3>(w, q0, q1);
+                }
+            }
+            if (ROW) {
+                // as above: bytes 1..3 overwrite whatever byte 0's conversion kept
+                const float p00 = quot2(a0[0], yh0, yl0), p10 = quot2(a1[0], yh1, yl1);
+                uint32_t o0 = put_fp4x2<0>(__float_as_uint(p00), p00, quot2(a0[1], yh0, yl0));
+                o0 = put_fp4x2<1>(o0, quot2(a0[2], yh0, yl0), quot2(a0[3], yh0, yl0));
+                o0 = put_fp4x2<2>(o0, quot2(a0[4], yh0, yl0), quot2(a0[5], yh0, yl0));
+                o0 = put_fp4x2<3>(o0, quot2(a0[6], yh0, yl0), quot2(a0[7], yh0, yl0));
+                uint32_t o1 = put_fp4x2<0>(__float_as_uint(p10), p10, quot2(a1[1], yh1, yl1));
+                o1 = put_fp4x2<1>(o1, quot2(a1[2], yh1, yl1), quot2(a1[3], yh1, yl1));
+                o1 = put_fp4x2<2>(o1, quot2(a1[4], yh1, yl1), quot2(a1[5], yh1, yl1));
+                o1 = put_fp4x2<3>(o1, quot2(a1[6], yh1, yl1), quot2(a1[7], yh1, yl1));
+                __builtin_amdgcn_raw_buffer_store_b32(o0, q_rs, vq + i * qr, 0, kCacheNT);
+                __builtin_amdgcn_raw_buffer_store_b32(o1, q_rs, vq + (i + 1) * qr, 0, kCacheNT);
+            }
+        }
+        if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) store_col<STAGE>(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
+        }
+        if (step_slow || __builtin_amdgcn_ballot_w64(slow) != 0ull) slow_mask |= 1u << sb;
         __builtin_amdgcn_wave_barrier();
     }
 

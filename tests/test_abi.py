@@ -60,6 +60,9 @@ def test_quantize_validation():
     assert _q(f, 16, 12, 1, None, None, None, f, f, f, None) == ESHAPE
     # 16x16 tiles need both
     assert _q(f, 16, 24, 2, None, None, None, f, f, f, None) == ESHAPE
+    # K at the encoding kernel's limit (2^25)
+    assert _q(f, 16, 1 << 25, 1, f, f, f, None, None, None, None) == ESHAPE
+    assert b"K must be below" in L.nvfp4_last_error()
     # NULL input
     assert _q(None, 16, 16, 1, f, f, f, None, None, None, None) == EINVAL
     # misaligned input / outputs / amax

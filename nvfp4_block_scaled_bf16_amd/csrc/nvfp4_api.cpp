@@ -186,6 +186,7 @@ nvfp4_status nvfp4_amax(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode
         return fail(NVFP4_EALIGN, "amax outputs must be 4-byte aligned");
     if (M < 0 || K < 0) return fail(NVFP4_EINVAL, "negative size");
     if (K % 8 != 0) return fail(NVFP4_ESHAPE, "nvfp4_amax needs K %% 8 == 0 (K=%lld)", (long long)K);
+    if (K >= kMaxEncodeK) return fail(NVFP4_ESHAPE, "K must be below %lld (K=%lld)", (long long)kMaxEncodeK, (long long)K);
     if (!xv) return fail(NVFP4_EINVAL, "x is NULL");
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     const uint16_t* x = static_cast<const uint16_t*>(xv);

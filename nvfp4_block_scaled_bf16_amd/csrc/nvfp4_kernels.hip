@@ -18,14 +18,14 @@ namespace nvfp4 {
 
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
 constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass
-constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass
+constexpr int kEncRows = 512;      // rows per workgroup tile in the encode pass
 constexpr int kEncCols = 256;      // columns per workgroup tile in the encode pass: a wave is
                                    // two row groups of 32 lanes, each 16 rows x 256 columns
-// LDS staging of a workgroup's columnwise output: per column, 256 rows give
-// 128 bytes of data and 16 scale bytes; padded pitches spread the lanes'
-// writes over the banks
-constexpr int kStageQPitch = 132;
-constexpr int kStageSfPitch = 20;
+// LDS staging of a workgroup's columnwise output: per column, kEncRows rows
+// give kEncRows/2 bytes of data and kEncRows/16 scale bytes; padded pitches
+// spread the lanes' writes over the banks
+constexpr int kStageQPitch = kEncRows / 2 + 4;
+constexpr int kStageSfPitch = kEncRows / 16 + 4;
 
 // --------------------------------------------------------------- utilities
 
@@ -44,19 +44,32 @@ __device__ __forceinline__ void atomic_max_mag(float* p, uint32_t mag16) {
     if (mag16 != 0u) atomicMax(reinterpret_cast<uint32_t*>(p), mag16 << 16);
 }
 
+// Buffer resources: a raw buffer over [base, base + bytes) (bytes <= 2^31).
+// Loads at a lane offset at or beyond `bytes` read zeros and stores there are
+// dropped, which is how rows past the end of the tensor and lanes past its
+// last column are handled (offsets stay below 2^32).  The fourth descriptor
+// word is the raw-buffer setting of the gfx9 family.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCacheNT = 2;               // nontemporal hint in the gfx940-family cache-policy bits
+constexpr uint32_t kOffOut = 0x80000000u; // lane offset beyond every buffer's extent
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
 // load 16 rows x 8 bf16 (one 16-byte word per row) of a lane's sub-block;
-// rows at or beyond row_end, or a lane past the last column, read zeros.
-// Ordinary (cached) loads: the amax pass leaves x in the last-level cache for
-// the encode pass that follows.
+// rows at or beyond row_end, and lanes past the last column (lane_off ==
+// kOffOut), read zeros.  lane_off: the lane's byte offset within a row; xr:
+// the row stride in bytes.  Ordinary (cached) loads: the amax pass leaves
+// part of x in the last-level cache for the encode pass that follows, which
+// measurably shortens it (nontemporal loads here make the amax pass a few
+// microseconds faster and the encode pass more than that slower).
 __device__ __forceinline__ void load_subblock(const uint16_t* __restrict__ x, int64_t K, int64_t r0,
-                                              int64_t row_end, int64_t c0, bool col_ok, u32x4 v[16]) {
-    const u32x4* base = reinterpret_cast<const u32x4*>(x + r0 * K + c0);
-    const int64_t stride = K / 8;  // in 16-byte words
+                                              int64_t row_end, uint32_t lane_off, uint32_t xr, u32x4 v[16]) {
+    const uint32_t nrows = (uint32_t)(row_end - r0 < 16 ? row_end - r0 : 16);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(x + r0 * K, nrows * xr);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        if (col_ok && r0 + i < row_end) v[i] = base[i * stride];
-        else v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + i * xr, 0, 0);
 }
 
 // Max over the wave of 16 per-lane 16-bit values (one per row), by halving
@@ -126,11 +139,14 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     const int64_t c0 = (int64_t)bx * kTileCols + lane * 8;
     const bool col_ok = c0 < K;
     const int64_t rb = row_begin + (int64_t)by * kAmaxRows + wave * (kAmaxRows / 4);
+    const uint32_t lane_off = col_ok ? (uint32_t)c0 * 2u : kOffOut;
+    uint32_t xr = (uint32_t)K * 2u;
+    asm volatile("" : "+s"(xr));   // keeps the 16 row offsets from being held in registers
     uint32_t cm[4] = {0u, 0u, 0u, 0u};
     uint32_t tm = 0u;
     int cur_group = -1;
     u32x4 vnext[16];
-    if (rb < row_end) load_subblock(x, K, rb, row_end, c0, col_ok, vnext);
+    if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, vnext);
 #pragma unroll 1
     for (int s = 0; s < kAmaxRows / 4; s += 16) {
         const int64_t r0 = rb + s;
@@ -153,7 +169,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         u32x4 v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = vnext[i];
-        if (s + 16 < kAmaxRows / 4 && r0 + 16 < row_end) load_subblock(x, K, r0 + 16, row_end, c0, col_ok, vnext);
+        if (s + 16 < kAmaxRows / 4 && r0 + 16 < row_end) load_subblock(x, K, r0 + 16, row_end, lane_off, xr, vnext);
         uint32_t rm[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -345,19 +361,6 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
     }
 }
 
-// Buffer resources for the hot loop: a raw buffer over [base, base + bytes)
-// (bytes <= 2^31).  Loads at a lane offset at or beyond `bytes` read zeros
-// and stores there are dropped, which is how rows past the end of the tensor
-// and lanes past its last column are handled (offsets stay below 2^32).  The
-// fourth descriptor word is the raw-buffer setting of the gfx9 family.
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kCacheNT = 2;               // nontemporal hint in the gfx940-family cache-policy bits
-constexpr uint32_t kOffOut = 0x80000000u; // lane offset beyond every buffer's extent
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
 // DPP quad permutations: the value of the even / odd lane of each pair
 __device__ __forceinline__ float from_even(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xA0, 0xF, 0xF, false));   // [0,0,2,2]
@@ -370,9 +373,10 @@ __device__ __forceinline__ float from_odd(float v) {
 // (row_amax[r], col_amax[c]), ENC_TILE (16x16 tiles, tensor amax in
 // row_amax[0] or col_amax[0]; also fills row_amax[1..M) and col_amax[1..K)
 // with it), ENC_GROUPED (rowwise per-token; columnwise per expert with
-// col_amax[e][K] and per-expert output slabs).  A workgroup covers 256 rows
-// x 256 columns: each wave takes 64 rows in two steps of 32, a step being
-// two groups of 32 lanes with a 16-row x 8-column sub-block per lane.  SAT:
+// col_amax[e][K] and per-expert output slabs).  A workgroup covers kEncRows
+// (512) rows x 256 columns: each wave takes a quarter of the rows in steps of
+// 32, a step being two groups of 32 lanes with a 16-row x 8-column sub-block
+// per lane.  SAT:
 // the amax comes from the caller and may be smaller than the data.
 // Requires K < 2^25 (32 rows of a step span less than 2^31 bytes).
 //
@@ -382,7 +386,7 @@ __device__ __forceinline__ float from_odd(float v) {
 // lane's own row (2s + parity, swapped with the pair through DPP), the two
 // rows unpacked once and encoded both ways.  Rowwise bytes go straight to
 // memory; columnwise bytes are staged in LDS and written in whole lines at
-// the end.
+// the end of the workgroup's tile.
 template <int MODE, bool ROW, bool COL, bool SAT>
 __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                 int64_t row_begin, int64_t row_end,
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     const bool col_ok = c0 < K;
     const bool odd = lane & 1;
     const int64_t tile_r0 = row_begin + (int64_t)by * kEncRows;
-    const int64_t wbase = tile_r0 + wave * (kEncRows / 4);   // a wave covers 64 rows in 2 steps
+    const int64_t wbase = tile_r0 + wave * (kEncRows / 4);   // a wave covers kEncRows/4 rows in 32-row steps
     float tileA = 0.0f;
     if (TILE) {
         tileA = row_amax ? row_amax[0] : col_amax[0];
@@ -481,31 +485,37 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 
     uint32_t slow_mask = 0u;
     constexpr int kSteps = kEncRows / 4 / 32;   // 32-row steps per wave
-#pragma unroll 1
+    // loads of a step: its rowwise amax, then the 16 data words, through
+    // buffers spanning the step's valid rows, so that rows past the end read
+    // zeros (and their stores below are dropped)
+    auto issue = [&](int sb, u32x4* v, float& ra) {
+        const int64_t wr0 = wbase + 32 * sb;
+        const uint32_t nrows = (uint32_t)(row_end - wr0 < 32 ? row_end - wr0 : 32);
+        if (ROWTOK) ra = row_amax[(uint32_t)(lane & 31) < nrows ? wr0 + (lane & 31) : row_begin];
+        // the row stride is made opaque: otherwise the compiler keeps the 16
+        // per-row lane offsets live in registers instead of forming each with
+        // one add where it is used
+        uint32_t xr = xrow;
+        asm volatile("" : "+s"(xr));
+        const __amdgpu_buffer_rsrc_t bx_rs = rsrc(x + wr0 * K, nrows * xrow);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(bx_rs, vx + i * xr, 0, kCacheNT);
+    };
+    // Loads are issued at the top of each step.  (Issuing the next step's
+    // before this step's work needs a second set of 64 data registers, which
+    // costs a wave per SIMD of occupancy and measured slower.)
+#pragma unroll
     for (int sb = 0; sb < kSteps; ++sb) {
         const int64_t wr0 = wbase + 32 * sb;     // first row of the wave's step
         if (wr0 >= row_end) break;
         const uint32_t nrows = (uint32_t)(row_end - wr0 < 32 ? row_end - wr0 : 32);   // rows of the step
         const bool group_ok = 16u * rg < nrows;
         const int64_t r0 = group_ok ? wr0 + 16 * rg : wr0;
-        // the step's rowwise amax first, so that waiting for it does not also
-        // wait for the 16 data loads issued after it
-        float ra = 0.0f;
-        if (ROWTOK) {
-            ra = row_amax[(uint32_t)(lane & 31) < nrows ? wr0 + (lane & 31) : row_begin];
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // row strides made opaque each step: otherwise the compiler keeps the
-        // 40 per-row lane offsets below live across the loop in registers
-        // instead of forming each with one add where it is used
-        uint32_t xr = xrow, qr = qrow, sr = srow;
-        asm volatile("" : "+s"(xr), "+s"(qr), "+s"(sr));
-        // (1) loads through buffers spanning the step's valid rows, so rows
-        // past the end read zeros (and their stores below are dropped)
-        const __amdgpu_buffer_rsrc_t bx_rs = rsrc(x + wr0 * K, nrows * xrow);
         u32x4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(bx_rs, vx + i * xr, 0, kCacheNT);
+        float ra = 0.0f;
+        issue(sb, v, ra);
+        uint32_t qr = qrow, sr = srow;
+        asm volatile("" : "+s"(qr), "+s"(sr));
         if (COL && MODE == ENC_GROUPED) {
             const int g = group_of_row(gt, r0);
             if (g != cur_group) {
@@ -704,9 +714,11 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         uint8_t* gq = col_q + tile_r0 / 2;
         uint8_t* gs = col_sf + tile_r0 / 16;
         const uint32_t t = threadIdx.x;
-        // qbytes is a multiple of 8: the last chunk of a short tile may be 8 bytes
-        for (uint32_t k = 0; k < (kEncCols * 8) / 256; ++k) {
-            const uint32_t c = (t >> 3) + 32 * k, chunk = (t & 7) * 16;
+        // 16-byte chunks, consecutive threads along a column; qbytes is a
+        // multiple of 8, so the last chunk of a short tile may be 8 bytes
+        constexpr uint32_t kChunks = kEncRows / 32;   // per column
+        for (uint32_t k = t; k < kEncCols * kChunks; k += 256) {
+            const uint32_t c = k / kChunks, chunk = (k % kChunks) * 16;
             if (c >= ncols || chunk >= qbytes) continue;
             const uint8_t* src = stage_q + c * kStageQPitch + chunk;
             uint8_t* dst = gq + (int64_t)(cbase + c) * (M / 2) + chunk;
@@ -718,16 +730,27 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
             }
         }
-        // scale bytes: whole words when the destination allows it
-        const bool words = ((M / 16) % 4 == 0) && ((tile_r0 / 16) % 4 == 0) && (sbytes % 4 == 0);
-        for (uint32_t c = t; c < ncols; c += 256) {
-            const uint8_t* src = stage_sf + c * kStageSfPitch;
-            uint8_t* dst = gs + (int64_t)(cbase + c) * (M / 16);
-            if (words) {
-                for (uint32_t b = 0; b < sbytes; b += 4)
-                    *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
-            } else {
-                for (uint32_t b = 0; b < sbytes; ++b) dst[b] = src[b];
+        // scale bytes: 16-byte pieces with consecutive threads along a
+        // column when the destination is aligned for them, else words or bytes
+        if (sbytes % 16 == 0 && (tile_r0 / 16) % 16 == 0 && (M / 16) % 16 == 0) {
+            const uint32_t per = sbytes / 16;
+            for (uint32_t k = t; k < ncols * per; k += 256) {
+                const uint32_t c = k / per, part = (k % per) * 16;
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + c * kStageSfPitch + part);
+                __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
+                                            reinterpret_cast<u32x4*>(gs + (int64_t)(cbase + c) * (M / 16) + part));
+            }
+        } else {
+            const bool words = ((M / 16) % 4 == 0) && ((tile_r0 / 16) % 4 == 0) && (sbytes % 4 == 0);
+            for (uint32_t c = t; c < ncols; c += 256) {
+                const uint8_t* src = stage_sf + c * kStageSfPitch;
+                uint8_t* dst = gs + (int64_t)(cbase + c) * (M / 16);
+                if (words) {
+                    for (uint32_t b = 0; b < sbytes; b += 4)
+                        *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
+                } else {
+                    for (uint32_t b = 0; b < sbytes; ++b) dst[b] = src[b];
+                }
             }
         }
     }

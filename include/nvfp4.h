@@ -92,13 +92,13 @@ NVFP4_API const char* nvfp4_last_error(void);
 /*
  * Timing hook for benchmarks and profilers.  The next call on this thread
  * that launches the data-encoding kernel (the kernel that writes the packed
- * E2M1 bytes and the block scales) records `before` on that call's stream
- * just before the launch and `after` just after it; the pair is then
- * forgotten (one-shot).  A call that fails validation leaves it pending; a
- * grouped call brackets its first encoding launch.  Both arguments are
- * hipEvent_t handles created and owned by the caller; NULL, NULL cancels a
- * pending pair, and exactly one NULL is NVFP4_EINVAL.  Recording an event
- * costs no device work and changes no result.
+ * E2M1 bytes and the block scales) has that launch record `before` when the
+ * kernel starts and `after` when it ends, so that hipEventElapsedTime gives
+ * the kernel's own duration; the pair is then forgotten (one-shot).  A call
+ * that fails validation leaves it pending; a grouped call times its first
+ * encoding launch.  Both arguments are hipEvent_t handles created and owned
+ * by the caller; NULL, NULL cancels a pending pair, and exactly one NULL is
+ * NVFP4_EINVAL.  Recording the events changes no result.
  */
 NVFP4_API nvfp4_status nvfp4_trace_encode(void* before, void* after);
 
@@ -115,6 +115,21 @@ NVFP4_API nvfp4_status nvfp4_quantize(const void* x, int64_t M, int64_t K, nvfp4
                             uint8_t* row_q, uint8_t* row_sf, float* row_amax,
                             uint8_t* col_q, uint8_t* col_sf, float* col_amax,
                             void* stream);
+
+/*
+ * nvfp4_quantize followed by the decayed calibration update of the PTQ
+ * scaling-factor page (TransformerEngine PR #3296, Description) on a scalar
+ * buffer, in one call:  buf[0] = max(buf[0] * decay, A)  in fp32, where A is
+ * the tensor amax this cast observed (the maximum of row_amax or col_amax
+ * for PER_TOKEN, the tensor amax otherwise; 0 for an empty tensor).  The
+ * result equals nvfp4_quantize then nvfp4_amax_accumulate_reduce on the
+ * amax vector, without the second launch.  buf: one fp32 value in device
+ * memory, finite and >= 0; decay in [0, 1].
+ */
+NVFP4_API nvfp4_status nvfp4_quantize_calibrate(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                      uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                      uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                                      float* buf, float decay, void* stream);
 
 /* One direction only (same as nvfp4_quantize with the other direction NULL). */
 NVFP4_API nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_quantize_rowwise",
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
-           "nvfp4_trace_encode")
+           "nvfp4_trace_encode", "nvfp4_quantize_calibrate")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_amax_accumulate": (st, [p, p, i64, f32, p]),
         "nvfp4_amax_accumulate_reduce": (st, [p, p, i64, f32, p]),
         "nvfp4_trace_encode": (st, [p, p]),
+        "nvfp4_quantize_calibrate": (st, [p, i64, i64, st, p, p, p, p, p, p, p, f32, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -133,6 +134,20 @@ def quantize_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, c
     M, K = x.shape
     _check(lib().nvfp4_quantize(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                 _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _stream(x.device)))
+
+
+def quantize_calibrate_into(x, mode, buf, decay: float, row_q=None, row_sf=None, row_amax=None,
+                            col_q=None, col_sf=None, col_amax=None):
+    """Whole cast into caller-provided buffers plus the decayed calibration
+    update buf[0] = max(buf[0] * decay, tensor amax) (fp32 tensor of one
+    element on the same device)."""
+    x = _input(x)
+    M, K = x.shape
+    if buf.dtype != torch.float32 or buf.device != x.device or buf.numel() < 1:
+        raise ValueError("buf must be a float32 tensor on the input's device")
+    _check(lib().nvfp4_quantize_calibrate(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
+                                          _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _ptr(buf),
+                                          ctypes.c_float(decay), _stream(x.device)))
 
 
 def quantize_rowwise(x, mode="per_token"):

@@ -10,7 +10,6 @@
 #include <string>
 
 #include "nvfp4_device.hpp"
-#include "nvfp4_fused.h"
 #include "nvfp4_internal.h"
 
 using namespace nvfp4;
@@ -83,16 +82,13 @@ GroupTable empty_table() {
 thread_local hipEvent_t g_trace_before = nullptr;
 thread_local hipEvent_t g_trace_after = nullptr;
 
-// launch an encoding kernel, bracketed by the pending trace events if any
+// launch an encoding kernel with the pending trace events if any: the
+// kernel's dispatch records them at its start and end
 template <class Launch>
-nvfp4_status encode_launch(hipStream_t st, Launch&& launch) {
+nvfp4_status encode_launch(Launch&& launch) {
     hipEvent_t before = g_trace_before, after = g_trace_after;
     g_trace_before = g_trace_after = nullptr;
-    nvfp4_status s;
-    if (before && (s = check_hip(hipEventRecord(before, st), "trace event")) != NVFP4_OK) return s;
-    if ((s = check_hip(launch(), "encode")) != NVFP4_OK) return s;
-    if (after && (s = check_hip(hipEventRecord(after, st), "trace event")) != NVFP4_OK) return s;
-    return NVFP4_OK;
+    return check_hip(launch(before, after), "encode");
 }
 
 // zero-fill up to two fp32 arrays (one launch) before an atomic-max pass
@@ -100,9 +96,12 @@ nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
     return check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
 }
 
+// cal_buf (may be null): buf[0] = max(buf[0] * decay, tensor amax), done by
+// the encoding kernel from the amax it has just read
 nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode,
                            uint8_t* row_q, uint8_t* row_sf, float* row_amax,
-                           uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+                           uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream,
+                           float* cal_buf = nullptr, float decay = 0.0f) {
     if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN && mode != NVFP4_TILE_16x16)
         return fail(NVFP4_EINVAL, "unknown scaling mode %d", (int)mode);
     Dir r = direction("row", row_q, row_sf, row_amax);
@@ -112,7 +111,7 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (!r.want && !c.want) return fail(NVFP4_EINVAL, "no output direction requested");
     nvfp4_status s = check_shape(M, K, r.want, c.want, mode);
     if (s != NVFP4_OK) return s;
-    if (xv == nullptr) return fail(NVFP4_EINVAL, "x is NULL");
+    if (xv == nullptr && M > 0 && K > 0) return fail(NVFP4_EINVAL, "x is NULL");
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     const uint16_t* x = static_cast<const uint16_t*>(xv);
     hipStream_t st = as_stream(stream);
@@ -120,17 +119,23 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     float* ca = c.want ? col_amax : nullptr;
     const GroupTable gt = empty_table();
 
+    if (cal_buf && (M == 0 || K == 0)) {
+        // nothing observed: buf = max(buf * decay, 0)
+        if ((s = check_hip(launch_accumulate_reduce(cal_buf, nullptr, 0, decay, st), "calibration")) != NVFP4_OK) return s;
+    }
+    // what the calibration observes: the tensor amax, as the max of the
+    // per-column (else per-row) vector, or the per-tensor value
+    Calib cal{cal_buf, nullptr, 0, decay};
+    if (cal_buf) {
+        if (mode == NVFP4_PER_TOKEN) { cal.obs = ca ? ca : ra; cal.n = ca ? K : M; }
+        else { cal.obs = ra ? ra : ca; cal.n = 1; }
+    }
     if (mode == NVFP4_PER_TOKEN) {
         if ((s = zero(ra, M, ca, K, st)) != NVFP4_OK) return s;
         if (M == 0 || K == 0) return ok();
-        if (fused_per_token_supported(M, K, r.want, c.want)) {
-            if ((s = encode_launch(st, [&] { return fused_per_token(x, M, K, row_q, row_sf, ra, col_q, col_sf, ca, st); })) != NVFP4_OK)
-                return s;
-            return ok();
-        }
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = encode_launch(st, [&] { return launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                         nullptr, nullptr, gt, st); })) != NVFP4_OK) return s;
+        if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                         nullptr, nullptr, gt, st, b, a, cal); })) != NVFP4_OK) return s;
         return ok();
     }
     // per-tensor and 16x16 tiles: one tensor amax
@@ -138,8 +143,8 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (M == 0 || K == 0) return ok();
     if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, st), "amax")) != NVFP4_OK) return s;
     const int emode = mode == NVFP4_TILE_16x16 ? ENC_TILE : ENC_TENSOR;
-    if ((s = encode_launch(st, [&] { return launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st); })) != NVFP4_OK)
+    if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st, b, a, cal); })) != NVFP4_OK)
         return s;
     return ok();
 }
@@ -163,6 +168,16 @@ nvfp4_status nvfp4_quantize(const void* x, int64_t M, int64_t K, nvfp4_scaling m
                             uint8_t* row_q, uint8_t* row_sf, float* row_amax,
                             uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
     return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream);
+}
+
+nvfp4_status nvfp4_quantize_calibrate(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                      uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                      uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                                      float* buf, float decay, void* stream) {
+    if (!buf) return fail(NVFP4_EINVAL, "buf is NULL");
+    if (!aligned(buf, 4)) return fail(NVFP4_EALIGN, "buf must be 4-byte aligned");
+    if (!(decay >= 0.0f && decay <= 1.0f)) return fail(NVFP4_EINVAL, "decay must lie in [0, 1]");
+    return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream, buf, decay);
 }
 
 nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
@@ -221,9 +236,9 @@ nvfp4_status nvfp4_encode(const void* xv, int64_t M, int64_t K, nvfp4_scaling mo
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     if (M == 0 || K == 0) return ok();
     const GroupTable gt = empty_table();
-    if ((s = encode_launch(as_stream(stream), [&] { return launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want, true,
+    if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, r.want, c.want, true,
                                      static_cast<const uint16_t*>(xv), M, K, 0, M, row_amax, col_amax,
-                                     row_q, row_sf, col_q, col_sf, nullptr, nullptr, gt, as_stream(stream)); })) != NVFP4_OK)
+                                     row_q, row_sf, col_q, col_sf, nullptr, nullptr, gt, as_stream(stream), b, a); })) != NVFP4_OK)
         return s;
     return ok();
 }
@@ -257,8 +272,8 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
     if (!c.want) {
         const GroupTable gt = empty_table();
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, T, ra, nullptr, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = encode_launch(st, [&] { return launch_encode(ENC_TOKEN, true, false, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
-                                         nullptr, nullptr, gt, st); })) != NVFP4_OK) return s;
+        if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_TOKEN, true, false, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
+                                         nullptr, nullptr, gt, st, b, a); })) != NVFP4_OK) return s;
         return ok();
     }
     // experts travel in the kernel arguments, a bounded number per launch
@@ -277,8 +292,8 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
         const int64_t end = off;
         if (end == begin) continue;
         if ((s = check_hip(launch_amax(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = encode_launch(st, [&] { return launch_encode(ENC_GROUPED, r.want, true, false, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
-                                         nullptr, nullptr, gt, st); })) != NVFP4_OK) return s;
+        if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_GROUPED, r.want, true, false, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
+                                         nullptr, nullptr, gt, st, b, a); })) != NVFP4_OK) return s;
     }
     return ok();
 }

@@ -18,10 +18,20 @@ hipError_t launch_fill2(float* p, int64_t n, float* q, int64_t m, float v, hipSt
 hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
                        float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
                        hipStream_t st);
+// optional calibration update done by the encoding kernel: buf[0] =
+// max(buf[0] * decay, max(obs[0..n))); buf == nullptr: none
+struct Calib {
+    float* buf;
+    const float* obs;
+    int64_t n;
+    float decay;
+};
+
 hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const uint16_t* x, int64_t M, int64_t K,
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
-                         float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st);
+                         float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, const Calib& cal = Calib{nullptr, nullptr, 0, 0.0f});
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
                           int amax_per_row, float* out, hipStream_t st);
 hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);

@@ -11,6 +11,8 @@
 // eight complete columnwise blocks; the 16 rows hold half of a rowwise block
 // each, the other half sitting in the neighbouring lane (lanes 2j and 2j+1
 // exchange maxima and block parameters).
+#include <hip/hip_ext.h>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
 
@@ -361,6 +363,44 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
     }
 }
 
+// One workgroup (blockDim.x a multiple of 64, at most 1024): m = max(obs),
+// then buf[0] = max(buf[0] * decay, m), in fp32.  red: 16 floats of LDS.
+// Four independent 16-byte loads per thread per round keep the latency of a
+// single pass over a few hundred KB low.
+__device__ void wg_accumulate_reduce(float* __restrict__ buf, const float* __restrict__ obs, int64_t n, float decay,
+                                     float* red) {
+    float m = 0.0f;
+    const int64_t nv = (reinterpret_cast<uintptr_t>(obs) % 16 == 0) ? n / 4 : 0;   // float4 part
+    const float4* o4 = reinterpret_cast<const float4*>(obs);
+    for (int64_t i = threadIdx.x; i < nv; i += 4 * blockDim.x) {
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t j = i + k * (int64_t)blockDim.x;
+            v[k] = j < nv ? o4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = v[k].x > m ? v[k].x : m; m = v[k].y > m ? v[k].y : m;
+            m = v[k].z > m ? v[k].z : m; m = v[k].w > m ? v[k].w : m;
+        }
+    }
+    for (int64_t i = 4 * nv + threadIdx.x; i < n; i += blockDim.x) m = obs[i] > m ? obs[i] : m;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float o = __shfl_xor(m, d);
+        m = o > m ? o : m;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nw = (int)(blockDim.x >> 6);
+        for (int w = 1; w < nw; ++w) m = red[w] > m ? red[w] : m;
+        const float t = buf[0] * decay;
+        buf[0] = m > t ? m : t;
+    }
+}
+
 // DPP quad permutations: the value of the even / odd lane of each pair
 __device__ __forceinline__ float from_even(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xA0, 0xF, 0xF, false));   // [0,0,2,2]
@@ -394,7 +434,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                                                 uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_sf,
                                                 uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,
                                                 float* __restrict__ fill_row, float* __restrict__ fill_col,
-                                                GroupTable gt) {
+                                                GroupTable gt, Calib cal) {
     constexpr bool TILE = MODE == ENC_TILE;
     constexpr bool ROWTOK = ROW && !TILE && MODE != ENC_TENSOR;   // a row amax per row
     __shared__ float row_scale[4][32][2];    // per wave: S and 1/S of the step's 32 rows
@@ -431,6 +471,12 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         if (fill_col) for (int64_t i = 1 + gid; i < K; i += gsz) fill_col[i] = tileA;
     }
     const Outer tileO = make_outer(tileA);
+    // the calibration update, folded into the cast: one workgroup reduces the
+    // finished amax vector into the decayed buffer
+    if (cal.buf != nullptr && lin == 0u) {
+        wg_accumulate_reduce(cal.buf, cal.obs, cal.n, cal.decay, &row_scale[0][0][0]);
+        __syncthreads();
+    }
 
     // columnwise outer scales of this lane's 8 columns
     Outer colO[8];
@@ -799,42 +845,10 @@ __global__ void k_accumulate(float* __restrict__ buf, const float* __restrict__ 
     }
 }
 
-// one workgroup of 1024 threads: m = max(obs), then buf[0] = max(buf[0] *
-// decay, m).  Four independent 16-byte loads per thread per round keep the
-// latency of a single pass over a few hundred KB low.
 __global__ __launch_bounds__(1024) void k_accumulate_reduce(float* __restrict__ buf, const float* __restrict__ obs,
                                                             int64_t n, float decay) {
     __shared__ float red[16];
-    float m = 0.0f;
-    const int64_t nv = (reinterpret_cast<uintptr_t>(obs) % 16 == 0) ? n / 4 : 0;   // float4 part
-    const float4* o4 = reinterpret_cast<const float4*>(obs);
-    for (int64_t i = threadIdx.x; i < nv; i += 4 * blockDim.x) {
-        float4 v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int64_t j = i + k * (int64_t)blockDim.x;
-            v[k] = j < nv ? o4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            m = v[k].x > m ? v[k].x : m; m = v[k].y > m ? v[k].y : m;
-            m = v[k].z > m ? v[k].z : m; m = v[k].w > m ? v[k].w : m;
-        }
-    }
-    for (int64_t i = 4 * nv + threadIdx.x; i < n; i += blockDim.x) m = obs[i] > m ? obs[i] : m;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const float o = __shfl_xor(m, d);
-        m = o > m ? o : m;
-    }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int nw = (int)(blockDim.x >> 6);
-        for (int w = 1; w < nw; ++w) m = red[w] > m ? red[w] : m;
-        const float t = buf[0] * decay;
-        buf[0] = m > t ? m : t;
-    }
+    wg_accumulate_reduce(buf, obs, n, decay, red);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -871,25 +885,32 @@ hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin
     return hipGetLastError();
 }
 
+// ev0 / ev1 (may be null): events the kernel's own dispatch records at its
+// start and end, for timing it alone
 template <int MODE, bool SAT>
-static void launch_encode_mode(bool row, bool col, dim3 grid, hipStream_t st, const uint16_t* x, int64_t M, int64_t K,
+static void launch_encode_mode(bool row, bool col, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                               const uint16_t* x, int64_t M, int64_t K,
                                int64_t rb, int64_t re, const float* ra, const float* ca, uint8_t* rq, uint8_t* rs,
-                               uint8_t* cq, uint8_t* cs, float* fr, float* fc, const GroupTable& gt) {
+                               uint8_t* cq, uint8_t* cs, float* fr, float* fc, const GroupTable& gt, const Calib& cal) {
     if (row && col)
-        hipLaunchKernelGGL((k_encode<MODE, true, true, SAT>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
+        hipExtLaunchKernelGGL((k_encode<MODE, true, true, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
+                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal);
     else if (row)
-        hipLaunchKernelGGL((k_encode<MODE, true, false, SAT>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
+        hipExtLaunchKernelGGL((k_encode<MODE, true, false, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
+                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal);
     else
-        hipLaunchKernelGGL((k_encode<MODE, false, true, SAT>), grid, dim3(256), 0, st, x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt);
+        hipExtLaunchKernelGGL((k_encode<MODE, false, true, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
+                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal);
 }
 
 hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const uint16_t* x, int64_t M, int64_t K,
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
-                         float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st) {
+                         float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st,
+                         hipEvent_t ev0, hipEvent_t ev1, const Calib& cal) {
     if (row_end <= row_begin || K <= 0 || (!row && !col)) return hipSuccess;
     dim3 grid(cdiv(K, kEncCols), cdiv(row_end - row_begin, kEncRows));
-#define NVFP4_ENC_ARGS row, col, grid, st, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt
+#define NVFP4_ENC_ARGS row, col, grid, st, ev0, ev1, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt, cal
     if (caller_amax) {
         // amax from the caller: scales may saturate
         if (mode == ENC_TENSOR) launch_encode_mode<ENC_TENSOR, true>(NVFP4_ENC_ARGS);

@@ -90,6 +90,19 @@ def test_other_entry_points_validation():
     assert L.nvfp4_amax_accumulate_reduce(None, f, 4, ctypes.c_float(0.5), None) == EINVAL
 
 
+def test_quantize_calibrate_validation():
+    L = nv.lib()
+    f = P(FAKE)
+    q = L.nvfp4_quantize_calibrate
+    assert q(f, 16, 16, 1, f, f, f, None, None, None, None, ctypes.c_float(0.9), None) == EINVAL   # no buf
+    assert q(f, 16, 16, 1, f, f, f, None, None, None, P(FAKE + 2), ctypes.c_float(0.9), None) == EALIGN
+    assert q(f, 16, 16, 1, f, f, f, None, None, None, f, ctypes.c_float(1.5), None) == EINVAL
+    assert q(f, 16, 16, 1, f, f, f, None, None, None, f, ctypes.c_float(float("nan")), None) == EINVAL
+    # the cast's own checks still apply
+    assert q(f, 16, 24, 1, f, f, f, None, None, None, f, ctypes.c_float(0.9), None) == ESHAPE
+    assert q(f, 16, 16, 1, None, None, None, None, None, None, f, ctypes.c_float(0.9), None) == EINVAL
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

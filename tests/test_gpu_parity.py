@@ -202,6 +202,58 @@ def test_accumulate(oracle, decay):
     assert_bytes_equal(host(sbuf), sref, "sbuf")
 
 
+@pytest.mark.parametrize("mode,shape,dirs", [(nv.PER_TOKEN, (272, 528), (True, True)),
+                                             (nv.PER_TOKEN, (96, 1040), (True, False)),
+                                             (nv.PER_TOKEN, (48, 24), (False, True)),
+                                             (nv.PER_TENSOR, (272, 528), (True, True)),
+                                             (nv.TILE_16x16, (64, 512), (False, True))])
+def test_quantize_calibrate_matches_cast_then_accumulate(oracle, mode, shape, dirs):
+    """The folded calibration update equals the oracle's decayed accumulate
+    of the tensor amax, over several calls, and the cast is unchanged."""
+    M, K = shape
+    row, col = dirs
+    _announce(f"quantize_calibrate mode={mode} shape={shape} row={row} col={col}")
+    buf = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    ref = np.zeros(1, np.float32)
+    for it, decay in enumerate([0.9, 0.9, 0.5, 1.0, 0.0, 0.9]):
+        x = _x(M, K, 500 + it)
+        if it == 3:
+            x = (x & np.uint16(0x8000)) | ((x & np.uint16(0x7FFF)) >> np.uint16(1))   # smaller amax: decay shows
+        d = to_dev(x)
+        out = {}
+        if row:
+            out.update(row_q=torch.empty(M, K // 2, dtype=torch.uint8, device="cuda:0"),
+                       row_sf=torch.empty(M, K // 16, dtype=torch.uint8, device="cuda:0"),
+                       row_amax=torch.empty(M if mode == nv.PER_TOKEN else (M if mode == nv.TILE_16x16 else 1),
+                                            dtype=torch.float32, device="cuda:0"))
+        if col:
+            out.update(col_q=torch.empty(K, M // 2, dtype=torch.uint8, device="cuda:0"),
+                       col_sf=torch.empty(K, M // 16, dtype=torch.uint8, device="cuda:0"),
+                       col_amax=torch.empty(K if mode == nv.PER_TOKEN else (K if mode == nv.TILE_16x16 else 1),
+                                            dtype=torch.float32, device="cuda:0"))
+        nv.quantize_calibrate_into(d, mode, buf, decay, **out)
+        torch.cuda.synchronize()
+        exp = oracle.quantize(x, mode, rowwise=row, columnwise=col)
+        compare_cast(out, exp)
+        A = np.array([oracle.amax_tensor(x)], np.float32)
+        ref = oracle.amax_accumulate(ref, A, decay)
+        assert_bytes_equal(host(buf), ref, f"buf after call {it}")
+
+
+def test_quantize_calibrate_empty_tensor(oracle):
+    """An empty tensor observes amax 0: buf = max(buf * decay, 0).  (Output
+    buffers are non-empty allocations: a NULL pointer means 'direction not
+    requested'.)"""
+    _announce("quantize_calibrate of a 0 x 32 tensor")
+    buf = torch.full((1,), 3.0, dtype=torch.float32, device="cuda:0")
+    x = torch.empty(0, 32, dtype=torch.bfloat16, device="cuda:0")
+    dummy = lambda dt: torch.empty(16, dtype=dt, device="cuda:0")
+    nv.quantize_calibrate_into(x, nv.PER_TOKEN, buf, 0.5, row_q=dummy(torch.uint8), row_sf=dummy(torch.uint8),
+                               row_amax=dummy(torch.float32))
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(buf), np.array([1.5], np.float32), "buf")
+
+
 def test_trace_encode_brackets_the_encoding_kernel(oracle):
     x = _x(1072, 544, 21)
     _announce("trace_encode events around a per-token cast")

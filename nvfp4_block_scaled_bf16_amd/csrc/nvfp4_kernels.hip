@@ -20,7 +20,7 @@ namespace nvfp4 {
 
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
 constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass
-constexpr int kEncRows = 512;      // rows per workgroup tile in the encode pass
+constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass
 constexpr int kEncCols = 256;      // columns per workgroup tile in the encode pass: a wave is
                                    // two row groups of 32 lanes, each 16 rows x 256 columns
 // LDS staging of a workgroup's columnwise output: per column, kEncRows rows
@@ -47,10 +47,13 @@ __device__ __forceinline__ void atomic_max_mag(float* p, uint32_t mag16) {
 }
 
 // Buffer resources: a raw buffer over [base, base + bytes) (bytes <= 2^31).
-// Loads at a lane offset at or beyond `bytes` read zeros and stores there are
+// Loads at an offset at or beyond `bytes` read zeros and stores there are
 // dropped, which is how rows past the end of the tensor and lanes past its
-// last column are handled (offsets stay below 2^32).  The fourth descriptor
-// word is the raw-buffer setting of the gfx9 family.
+// last column are handled.  The offset checked is the lane offset plus the
+// scalar offset (checked on gfx950 with an in-bounds probe), so the per-row
+// part of an address goes in the scalar offset at no vector-ALU cost; sums
+// stay below 2^32.  The fourth descriptor word is the raw-buffer setting of
+// the gfx9 family.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kCacheNT = 2;               // nontemporal hint in the gfx940-family cache-policy bits
 constexpr uint32_t kOffOut = 0x80000000u; // lane offset beyond every buffer's extent
@@ -71,7 +74,7 @@ __device__ __forceinline__ void load_subblock(const uint16_t* __restrict__ x, in
     const uint32_t nrows = (uint32_t)(row_end - r0 < 16 ? row_end - r0 : 16);
     const __amdgpu_buffer_rsrc_t rs = rsrc(x + r0 * K, nrows * xr);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + i * xr, 0, 0);
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, i * xr, 0);
 }
 
 // Max over the wave of 16 per-lane 16-bit values (one per row), by halving
@@ -414,7 +417,7 @@ __device__ __forceinline__ float from_odd(float v) {
 // row_amax[0] or col_amax[0]; also fills row_amax[1..M) and col_amax[1..K)
 // with it), ENC_GROUPED (rowwise per-token; columnwise per expert with
 // col_amax[e][K] and per-expert output slabs).  A workgroup covers kEncRows
-// (512) rows x 256 columns: each wave takes a quarter of the rows in steps of
+// (256) rows x 256 columns: each wave takes a quarter of the rows in steps of
 // 32, a step being two groups of 32 lanes with a 16-row x 8-column sub-block
 // per lane.  SAT:
 // the amax comes from the caller and may be smaller than the data.
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         asm volatile("" : "+s"(xr));
         const __amdgpu_buffer_rsrc_t bx_rs = rsrc(x + wr0 * K, nrows * xrow);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(bx_rs, vx + i * xr, 0, kCacheNT);
+        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(bx_rs, vx, i * xr, kCacheNT);
     };
     // Loads are issued at the top of each step.  (Issuing the next step's
     // before this step's work needs a second set of 64 data registers, which
@@ -656,7 +659,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 if (TILE) {
                     yh0 = yh1 = tb.yh;
                     yl0 = yl1 = tb.yl;
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)tb.code, s_rs, vs + i * sr, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)tb.code, s_rs, vs, i * sr, 0);
                 } else {
                     Outer ro = rowO_t;
                     if (ROWTOK) {
@@ -665,7 +668,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                     }
                     const FastBlock f = fast_block<SAT>(bm[s], ro);
                     slow |= f.slow;
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs + i * sr, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs, i * sr, 0);
                     yh0 = from_even(f.yh); yl0 = from_even(f.yl);
                     yh1 = from_odd(f.yh);  yl1 = from_odd(f.yl);
                 }
@@ -711,8 +714,8 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 o1 = put_fp4x2<1>(o1, quot2(a1[2], yh1, yl1), quot2(a1[3], yh1, yl1));
                 o1 = put_fp4x2<2>(o1, quot2(a1[4], yh1, yl1), quot2(a1[5], yh1, yl1));
                 o1 = put_fp4x2<3>(o1, quot2(a1[6], yh1, yl1), quot2(a1[7], yh1, yl1));
-                __builtin_amdgcn_raw_buffer_store_b32(o0, q_rs, vq + i * qr, 0, kCacheNT);
-                __builtin_amdgcn_raw_buffer_store_b32(o1, q_rs, vq + (i + 1) * qr, 0, kCacheNT);
+                __builtin_amdgcn_raw_buffer_store_b32(o0, q_rs, vq, i * qr, kCacheNT);
+                __builtin_amdgcn_raw_buffer_store_b32(o1, q_rs, vq, (i + 1) * qr, kCacheNT);
             }
         }
         if (COL) {

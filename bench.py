@@ -24,8 +24,10 @@ CPU oracle on the host (test infrastructure, never on the product path).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain 256 MiB copies, for counters)
+       python bench.py --all-configs        (every named workload, one line each)
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -125,6 +127,92 @@ def copy_calibration(steps):
                       "bytes_written_per_launch": b.numel() * 2, "launches": steps}), flush=True)
 
 
+def all_configs(steps, warmup):
+    """One JSON line per named workload (not the headline line): average
+    microseconds per call over `steps` timed calls with HIP events around
+    them, inputs rotating where three fit, and algorithmic GB/s."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_bf16_amd as nv
+    from nvfp4_block_scaled_bf16_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=dev)
+    f32 = lambda n: torch.empty(n, dtype=torch.float32, device=dev)
+
+    def timed(fn, n_inputs):
+        for i in range(warmup):
+            fn(i % n_inputs)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i % n_inputs)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    def report(name, desc, us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"config": name, "workload": desc, "us_per_call": round(us, 2),
+                          "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                          "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+
+    def cast_bytes(m, k, amax_floats):
+        return 2 * m * k + m * k + m * k // 8 + 4 * amax_floats
+
+    # C1: per-tensor rowwise 256 x 1024, then the dequantize round trip
+    x1 = to_dev(W.c1())
+    o1 = dict(row_q=u8(256, 512), row_sf=u8(256, 64), row_amax=f32(1))
+    report("C1", "per-tensor rowwise quantize, 256x1024", timed(lambda i: nv.quantize_into(x1, nv.PER_TENSOR, **o1), 1),
+           2 * 256 * 1024 + 256 * 512 + 256 * 64 + 4)
+    back = f32(256 * 1024)
+    report("C1-dequant", "dequantize of the C1 output to fp32", timed(
+        lambda i: nv.lib().nvfp4_dequantize(nv._ptr(o1["row_q"]), nv._ptr(o1["row_sf"]), nv._ptr(o1["row_amax"]), 256, 1024, 0,
+                                            nv._ptr(back), nv._stream(dev)), 1),
+           256 * 512 + 256 * 64 + 4 + 4 * 256 * 1024)
+    # C2: per-token row+col 4096 x 4096 with outliers
+    x2 = [to_dev(W.row_scaled_with_outliers(4096, 4096, 1002 + 7 * t)) for t in range(3)]
+    o2 = dict(row_q=u8(4096, 2048), row_sf=u8(4096, 256), row_amax=f32(4096),
+              col_q=u8(4096, 2048), col_sf=u8(4096, 256), col_amax=f32(4096))
+    report("C2", "per-token row+col, 4096x4096", timed(lambda i: nv.quantize_into(x2[i], nv.PER_TOKEN, **o2), 3),
+           cast_bytes(4096, 4096, 8192))
+    del x2
+    # C3: per-tensor and per-token row+col 16384 x 8192, Student-t
+    x3 = [to_dev(W.c3(t)) for t in range(3)]
+    o3 = dict(row_q=u8(M, K // 2), row_sf=u8(M, K // 16), row_amax=f32(M),
+              col_q=u8(K, M // 2), col_sf=u8(K, M // 16), col_amax=f32(K))
+    buf = torch.zeros(1, dtype=torch.float32, device=dev)
+    report("C3-per-token", "per-token row+col with the decayed amax update, 16384x8192",
+           timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TOKEN, buf, 0.9, **o3), 3), cast_bytes(M, K, M + K))
+    o3t = dict(o3, row_amax=f32(1), col_amax=f32(1))
+    report("C3-per-tensor", "per-tensor row+col with the decayed amax update, 16384x8192",
+           timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3), cast_bytes(M, K, 2))
+    del x3, o3, o3t
+    # C4: grouped MoE, 64 experts, 32768 tokens x 4096
+    x4h, counts = W.c4()
+    x4 = to_dev(x4h)
+    T, K4 = x4h.shape
+    o4 = dict(row_q=u8(T, K4 // 2), row_sf=u8(T, K4 // 16), row_amax=f32(T),
+              col_q=u8(T * K4 // 2), col_sf=u8(T * K4 // 16), col_amax=f32(len(counts) * K4))
+    hc = (ctypes.c_int64 * len(counts))(*[int(c) for c in counts])
+    g = lambda i: nv.lib().nvfp4_quantize_grouped(
+        nv._ptr(x4), K4, len(counts), hc, nv._ptr(o4["row_q"]), nv._ptr(o4["row_sf"]), nv._ptr(o4["row_amax"]),
+        nv._ptr(o4["col_q"]), nv._ptr(o4["col_sf"]), nv._ptr(o4["col_amax"]), nv._stream(dev))
+    report("C4", f"grouped per-token row+col, {len(counts)} experts, {T}x{K4}", timed(g, 1),
+           cast_bytes(T, K4, T + len(counts) * K4))
+    del x4, o4
+    # C5: 16x16 tiles, 8192 x 28672 weight, per-token-layout emission
+    M5, K5 = 8192, 28672
+    x5 = to_dev(W.c5())
+    o5 = dict(row_q=u8(M5, K5 // 2), row_sf=u8(M5, K5 // 16), row_amax=f32(M5),
+              col_q=u8(K5, M5 // 2), col_sf=u8(K5, M5 // 16), col_amax=f32(K5))
+    report("C5", "16x16-tile row+col, 8192x28672 weight", timed(lambda i: nv.quantize_into(x5, nv.TILE_16x16, **o5), 1),
+           cast_bytes(M5, K5, M5 + K5))
+
+
 def cpu_baseline(inputs):
     """The oracle as it stands, single-threaded, on the full 16384 x 8192
     per-token row+col cast of each of the step inputs (about 15 s of CPU
@@ -148,6 +236,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time every named workload (one JSON line each) instead of the headline step")
     ap.add_argument("--trace-every", type=int, default=5,
                     help="time the encoding kernel with events on every N-th timed step (0: never)")
     args = ap.parse_args()
@@ -159,6 +249,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.all_configs:
+        all_configs(args.steps, args.warmup)
         return
 
     import numpy as np

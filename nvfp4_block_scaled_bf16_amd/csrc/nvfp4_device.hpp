@@ -224,6 +224,14 @@ struct GroupTable {
     int64_t cnt[kMaxGroupsPerLaunch];     // rows of each expert
 };
 
+// expert owning row r, moving forward from entry g (an entry whose offset
+// is <= r): rows only grow within a workgroup's walk, so this is usually no
+// step at all, where a fresh search costs a chain of dependent table loads
+__device__ __forceinline__ int group_advance(const GroupTable& gt, int g, int64_t r) {
+    while (g + 1 < gt.n && gt.off[g + 1] <= r) ++g;
+    return g;
+}
+
 // expert owning row r (r inside the table's span): the last entry whose
 // offset is <= r, which skips empty experts sharing that offset
 __device__ __forceinline__ int group_of_row(const GroupTable& gt, int64_t r) {

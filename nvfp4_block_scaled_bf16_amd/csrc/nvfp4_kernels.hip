@@ -134,7 +134,8 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
                                               float* __restrict__ row_amax, float* __restrict__ col_amax,
                                               float* __restrict__ t0, float* __restrict__ t1, GroupTable gt) {
     __shared__ uint32_t red[4][64][4];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar expert lookups
     // tile order: each XCD takes a contiguous run of tiles (row band major),
     // the order the encode pass walks backwards
     const uint32_t ntiles = gridDim.x * gridDim.y;
@@ -150,6 +151,29 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     uint32_t cm[4] = {0u, 0u, 0u, 0u};
     uint32_t tm = 0u;
     int cur_group = -1;
+    // Grouped: column maxima are first combined in LDS per expert present
+    // in the tile (slot = the expert's first row within the tile / 16, so at
+    // most kAmaxRows / 16 slots), then one atomic per column and expert.
+    constexpr int kSlots = kAmaxRows / 16;
+    __shared__ uint32_t gred[KIND == AMAX_GROUPED ? kSlots : 1][KIND == AMAX_GROUPED ? kTileCols : 1];
+    __shared__ int gslot[KIND == AMAX_GROUPED ? kSlots : 1];
+    const int64_t tile_r0 = row_begin + (int64_t)by * kAmaxRows;
+    if (KIND == AMAX_GROUPED) {
+        for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) gred[i / kTileCols][i % kTileCols] = 0u;
+        if (threadIdx.x < kSlots) gslot[threadIdx.x] = -1;
+        __syncthreads();
+    }
+    auto group_flush = [&](int g) {   // this wave's column maxima of expert g into its slot
+        const int64_t o = gt.off[g];
+        const int slot = o <= tile_r0 ? 0 : (int)((o - tile_r0) / 16);
+        if (lane == 0) gslot[slot] = g;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            atomicMax(&gred[slot][lane * 8 + 2 * k], cm[k] & 0xffffu);
+            atomicMax(&gred[slot][lane * 8 + 2 * k + 1], cm[k] >> 16);
+            cm[k] = 0u;
+        }
+    };
     u32x4 vnext[16];
     if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, vnext);
 #pragma unroll 1
@@ -157,17 +181,9 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         const int64_t r0 = rb + s;
         if (r0 >= row_end) break;
         if (KIND == AMAX_GROUPED) {
-            int g = group_of_row(gt, r0);
+            const int g = cur_group < 0 ? group_of_row(gt, r0) : group_advance(gt, cur_group, r0);
             if (g != cur_group) {
-                if (cur_group >= 0 && col_ok) {
-                    float* dst = col_amax + (int64_t)(gt.first + cur_group) * K + c0;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        atomic_max_mag(dst + 2 * k, cm[k] & 0xffffu);
-                        atomic_max_mag(dst + 2 * k + 1, cm[k] >> 16);
-                        cm[k] = 0u;
-                    }
-                }
+                if (cur_group >= 0) group_flush(cur_group);
                 cur_group = g;
             }
         }
@@ -212,13 +228,14 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         return;
     }
     if (KIND == AMAX_GROUPED) {
-        if (cur_group >= 0 && col_ok) {
-            float* dst = col_amax + (int64_t)(gt.first + cur_group) * K + c0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                atomic_max_mag(dst + 2 * k, cm[k] & 0xffffu);
-                atomic_max_mag(dst + 2 * k + 1, cm[k] >> 16);
-            }
+        if (cur_group >= 0) group_flush(cur_group);
+        __syncthreads();
+        const int64_t tc0 = (int64_t)bx * kTileCols;
+        for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) {
+            const int slot = i / kTileCols, c = i % kTileCols;
+            const int g = gslot[slot];
+            if (g >= 0 && tc0 + c < K)
+                atomic_max_mag(col_amax + (int64_t)(gt.first + g) * K + tc0 + c, gred[slot][c]);
         }
         return;
     }
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     constexpr bool ROWTOK = ROW && !TILE && MODE != ENC_TENSOR;   // a row amax per row
     __shared__ float row_scale[4][32][2];    // per wave: S and 1/S of the step's 32 rows
     // columnwise output of the workgroup tile, written out in whole lines
-    constexpr bool STAGE = COL && MODE != ENC_GROUPED;
+    constexpr bool STAGE = COL;
     __shared__ __attribute__((aligned(16))) uint8_t stage_q[STAGE ? kEncCols * kStageQPitch : 16];
     __shared__ __attribute__((aligned(16))) uint8_t stage_sf[STAGE ? kEncCols * kStageSfPitch : 16];
     const int lane = threadIdx.x & 63;
@@ -484,7 +501,8 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     // columnwise outer scales of this lane's 8 columns
     Outer colO[8];
     bool col_slow = false;
-    int cur_group = -1;
+    int cur_group = -1;    // the lane's expert (grouped casts)
+    int wave_group = -1;   // expert of the wave's current first row
     int64_t m_len = M, grow0 = 0;
     if (COL && !TILE && MODE != ENC_GROUPED) {
         // unconditional loads (a lane past the last column reads column 0 and
@@ -566,7 +584,13 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         uint32_t qr = qrow, sr = srow;
         asm volatile("" : "+s"(qr), "+s"(sr));
         if (COL && MODE == ENC_GROUPED) {
-            const int g = group_of_row(gt, r0);
+            // the experts of the step's two row groups, found wave-uniformly
+            // (scalar loads of the table) from the wave's cursor, then each
+            // lane takes its group's
+            wave_group = wave_group < 0 ? group_of_row(gt, wr0) : group_advance(gt, wave_group, wr0);
+            const int g0 = wave_group;
+            const int g1 = nrows > 16u ? group_advance(gt, g0, wr0 + 16) : g0;
+            const int g = rg ? g1 : g0;
             if (g != cur_group) {
                 cur_group = g;
                 m_len = gt.cnt[g];
@@ -753,54 +777,68 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     }
 
     if (STAGE) {
-        // every wave's columnwise bytes are in LDS: write whole 128-byte
-        // lines (8 lanes per column), then the scale bytes
+        // Every wave's columnwise bytes are in LDS: write them out in 16-byte
+        // pieces along each column (whole 128-byte lines for a full tile),
+        // then the scale bytes.  A grouped cast writes each expert's rows of
+        // the tile into that expert's slab, one segment per expert.
         __syncthreads();
         const int64_t tile_rows = row_end - tile_r0 < kEncRows ? row_end - tile_r0 : kEncRows;
-        const uint32_t qbytes = (uint32_t)(tile_rows / 2), sbytes = (uint32_t)(tile_rows / 16);
+        const int64_t tile_end = tile_r0 + tile_rows;
         const uint32_t cbase = bx * kEncCols;
         const uint32_t ncols = (uint32_t)(K - cbase < kEncCols ? K - cbase : kEncCols);
-        uint8_t* gq = col_q + tile_r0 / 2;
-        uint8_t* gs = col_sf + tile_r0 / 16;
         const uint32_t t = threadIdx.x;
-        // 16-byte chunks, consecutive threads along a column; qbytes is a
-        // multiple of 8, so the last chunk of a short tile may be 8 bytes
-        constexpr uint32_t kChunks = kEncRows / 32;   // per column
-        for (uint32_t k = t; k < kEncCols * kChunks; k += 256) {
-            const uint32_t c = k / kChunks, chunk = (k % kChunks) * 16;
-            if (c >= ncols || chunk >= qbytes) continue;
-            const uint8_t* src = stage_q + c * kStageQPitch + chunk;
-            uint8_t* dst = gq + (int64_t)(cbase + c) * (M / 2) + chunk;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-            if (chunk + 16 <= qbytes) {
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-                __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(dst));
-            } else {
-                __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
+        int e = MODE == ENC_GROUPED ? group_of_row(gt, tile_r0) : 0;
+        for (int64_t s0 = tile_r0; s0 < tile_end;) {
+            int64_t o = 0, m = M;   // first row and length of the vectors (the expert's for grouped)
+            if (MODE == ENC_GROUPED) {
+                while (gt.cnt[e] == 0 || gt.off[e] + gt.cnt[e] <= s0) ++e;
+                o = gt.off[e];
+                m = gt.cnt[e];
             }
-        }
-        // scale bytes: 16-byte pieces with consecutive threads along a
-        // column when the destination is aligned for them, else words or bytes
-        if (sbytes % 16 == 0 && (tile_r0 / 16) % 16 == 0 && (M / 16) % 16 == 0) {
-            const uint32_t per = sbytes / 16;
-            for (uint32_t k = t; k < ncols * per; k += 256) {
-                const uint32_t c = k / per, part = (k % per) * 16;
-                const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + c * kStageSfPitch + part);
-                __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
-                                            reinterpret_cast<u32x4*>(gs + (int64_t)(cbase + c) * (M / 16) + part));
-            }
-        } else {
-            const bool words = ((M / 16) % 4 == 0) && ((tile_r0 / 16) % 4 == 0) && (sbytes % 4 == 0);
-            for (uint32_t c = t; c < ncols; c += 256) {
-                const uint8_t* src = stage_sf + c * kStageSfPitch;
-                uint8_t* dst = gs + (int64_t)(cbase + c) * (M / 16);
-                if (words) {
-                    for (uint32_t b = 0; b < sbytes; b += 4)
-                        *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
+            const int64_t s1 = o + m < tile_end ? o + m : tile_end;
+            const uint32_t lq = (uint32_t)(s0 - tile_r0) / 2, qb = (uint32_t)(s1 - s0) / 2;    // multiples of 8
+            const uint32_t ls = (uint32_t)(s0 - tile_r0) / 16, sbn = (uint32_t)(s1 - s0) / 16;
+            uint8_t* gq = col_q + o * K / 2 + (s0 - o) / 2 + (int64_t)cbase * (m / 2);
+            uint8_t* gs = col_sf + o * K / 16 + (s0 - o) / 16 + (int64_t)cbase * (m / 16);
+            const int64_t qstride = m / 2, sstride = m / 16;
+            const uint32_t nch = (qb + 15) / 16;   // pieces per column; the last may be 8 bytes
+            for (uint32_t k = t; k < ncols * nch; k += 256) {
+                const uint32_t c = k / nch, chunk = (k % nch) * 16;
+                const uint8_t* src = stage_q + c * kStageQPitch + lq + chunk;
+                uint8_t* dst = gq + (int64_t)c * qstride + chunk;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+                if (chunk + 16 <= qb) {
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+                    __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(dst));
                 } else {
-                    for (uint32_t b = 0; b < sbytes; ++b) dst[b] = src[b];
+                    __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
                 }
             }
+            // scale bytes: 16-byte pieces along each column when source and
+            // destination are aligned for them, else words, else bytes
+            if (sbn % 16 == 0 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
+                const uint32_t per = sbn / 16;
+                for (uint32_t k = t; k < ncols * per; k += 256) {
+                    const uint32_t c = k / per, part = (k % per) * 16;
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + c * kStageSfPitch + ls + part);
+                    __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
+                                                reinterpret_cast<u32x4*>(gs + (int64_t)c * sstride + part));
+                }
+            } else {
+                const bool words = sbn % 4 == 0 && ls % 4 == 0 && sstride % 4 == 0 && reinterpret_cast<uintptr_t>(gs) % 4 == 0;
+                for (uint32_t c = t; c < ncols; c += 256) {
+                    const uint8_t* src = stage_sf + c * kStageSfPitch + ls;
+                    uint8_t* dst = gs + (int64_t)c * sstride;
+                    if (words) {
+                        for (uint32_t b = 0; b < sbn; b += 4)
+                            *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
+                    } else {
+                        for (uint32_t b = 0; b < sbn; ++b) dst[b] = src[b];
+                    }
+                }
+            }
+            s0 = s1;
+            if (MODE == ENC_GROUPED) ++e;
         }
     }
 }

@@ -19,8 +19,8 @@
 namespace nvfp4 {
 
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
-constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass
-constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass
+constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass (at most; fewer for small tensors)
+constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass (at most; 128 for small tensors)
 constexpr int kEncCols = 256;      // columns per workgroup tile in the encode pass: a wave is
                                    // two row groups of 32 lanes, each 16 rows x 256 columns
 // LDS staging of a workgroup's columnwise output: per column, kEncRows rows
@@ -132,7 +132,8 @@ template <int KIND>
 __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, int64_t K,
                                               int64_t row_begin, int64_t row_end,
                                               float* __restrict__ row_amax, float* __restrict__ col_amax,
-                                              float* __restrict__ t0, float* __restrict__ t1, GroupTable gt) {
+                                              float* __restrict__ t0, float* __restrict__ t1, GroupTable gt,
+                                              int tile_h) {
     __shared__ uint32_t red[4][64][4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar expert lookups
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     const uint32_t bx = tile % gridDim.x, by = tile / gridDim.x;
     const int64_t c0 = (int64_t)bx * kTileCols + lane * 8;
     const bool col_ok = c0 < K;
-    const int64_t rb = row_begin + (int64_t)by * kAmaxRows + wave * (kAmaxRows / 4);
+    const int64_t rb = row_begin + (int64_t)by * tile_h + wave * (tile_h / 4);   // tile_h: 64, 128 or 256 rows
     const uint32_t lane_off = col_ok ? (uint32_t)c0 * 2u : kOffOut;
     uint32_t xr = (uint32_t)K * 2u;
     asm volatile("" : "+s"(xr));   // keeps the 16 row offsets from being held in registers
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     constexpr int kSlots = kAmaxRows / 16;
     __shared__ uint32_t gred[KIND == AMAX_GROUPED ? kSlots : 1][KIND == AMAX_GROUPED ? kTileCols : 1];
     __shared__ int gslot[KIND == AMAX_GROUPED ? kSlots : 1];
-    const int64_t tile_r0 = row_begin + (int64_t)by * kAmaxRows;
+    const int64_t tile_r0 = row_begin + (int64_t)by * tile_h;
     if (KIND == AMAX_GROUPED) {
         for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) gred[i / kTileCols][i % kTileCols] = 0u;
         if (threadIdx.x < kSlots) gslot[threadIdx.x] = -1;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     u32x4 vnext[16];
     if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, vnext);
 #pragma unroll 1
-    for (int s = 0; s < kAmaxRows / 4; s += 16) {
+    for (int s = 0; s < tile_h / 4; s += 16) {
         const int64_t r0 = rb + s;
         if (r0 >= row_end) break;
         if (KIND == AMAX_GROUPED) {
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         u32x4 v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = vnext[i];
-        if (s + 16 < kAmaxRows / 4 && r0 + 16 < row_end) load_subblock(x, K, r0 + 16, row_end, lane_off, xr, vnext);
+        if (s + 16 < tile_h / 4 && r0 + 16 < row_end) load_subblock(x, K, r0 + 16, row_end, lane_off, xr, vnext);
         uint32_t rm[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                                                 uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_sf,
                                                 uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,
                                                 float* __restrict__ fill_row, float* __restrict__ fill_col,
-                                                GroupTable gt, Calib cal) {
+                                                GroupTable gt, Calib cal, int tile_h) {
     constexpr bool TILE = MODE == ENC_TILE;
     constexpr bool ROWTOK = ROW && !TILE && MODE != ENC_TENSOR;   // a row amax per row
     __shared__ float row_scale[4][32][2];    // per wave: S and 1/S of the step's 32 rows
@@ -480,8 +481,8 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     const uint32_t c0 = bx * kEncCols + (lane & 31) * 8;
     const bool col_ok = c0 < K;
     const bool odd = lane & 1;
-    const int64_t tile_r0 = row_begin + (int64_t)by * kEncRows;
-    const int64_t wbase = tile_r0 + wave * (kEncRows / 4);   // a wave covers kEncRows/4 rows in 32-row steps
+    const int64_t tile_r0 = row_begin + (int64_t)by * tile_h;   // tile_h: 128 or 256 rows
+    const int64_t wbase = tile_r0 + wave * (tile_h / 4);   // a wave covers tile_h/4 rows in 32-row steps
     float tileA = 0.0f;
     if (TILE) {
         tileA = row_amax ? row_amax[0] : col_amax[0];
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 #pragma unroll
     for (int sb = 0; sb < kSteps; ++sb) {
         const int64_t wr0 = wbase + 32 * sb;     // first row of the wave's step
-        if (wr0 >= row_end) break;
+        if (32 * sb >= tile_h / 4 || wr0 >= row_end) break;
         const uint32_t nrows = (uint32_t)(row_end - wr0 < 32 ? row_end - wr0 : 32);   // rows of the step
         const bool group_ok = 16u * rg < nrows;
         const int64_t r0 = group_ok ? wr0 + 16 * rg : wr0;
@@ -782,7 +783,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         // then the scale bytes.  A grouped cast writes each expert's rows of
         // the tile into that expert's slab, one segment per expert.
         __syncthreads();
-        const int64_t tile_rows = row_end - tile_r0 < kEncRows ? row_end - tile_r0 : kEncRows;
+        const int64_t tile_rows = row_end - tile_r0 < tile_h ? row_end - tile_r0 : tile_h;
         const int64_t tile_end = tile_r0 + tile_rows;
         const uint32_t cbase = bx * kEncCols;
         const uint32_t ncols = (uint32_t)(K - cbase < kEncCols ? K - cbase : kEncCols);
@@ -911,16 +912,19 @@ hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin
                        float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
                        hipStream_t st) {
     if (row_end <= row_begin || K <= 0) return hipSuccess;
-    dim3 grid(cdiv(K, kTileCols), cdiv(row_end - row_begin, kAmaxRows));
+    // rows per workgroup: 256, fewer when the grid would leave CUs idle
+    int tile_h = kAmaxRows;
+    while (tile_h > 64 && (int64_t)cdiv(K, kTileCols) * cdiv(row_end - row_begin, tile_h) < 1024) tile_h /= 2;
+    dim3 grid(cdiv(K, kTileCols), cdiv(row_end - row_begin, tile_h));
     switch (kind) {
     case AMAX_TENSOR:
-        hipLaunchKernelGGL(k_amax<AMAX_TENSOR>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt);
+        hipLaunchKernelGGL(k_amax<AMAX_TENSOR>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h);
         break;
     case AMAX_TOKEN:
-        hipLaunchKernelGGL(k_amax<AMAX_TOKEN>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt);
+        hipLaunchKernelGGL(k_amax<AMAX_TOKEN>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h);
         break;
     default:
-        hipLaunchKernelGGL(k_amax<AMAX_GROUPED>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt);
+        hipLaunchKernelGGL(k_amax<AMAX_GROUPED>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h);
         break;
     }
     return hipGetLastError();
@@ -932,16 +936,17 @@ template <int MODE, bool SAT>
 static void launch_encode_mode(bool row, bool col, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
                                const uint16_t* x, int64_t M, int64_t K,
                                int64_t rb, int64_t re, const float* ra, const float* ca, uint8_t* rq, uint8_t* rs,
-                               uint8_t* cq, uint8_t* cs, float* fr, float* fc, const GroupTable& gt, const Calib& cal) {
+                               uint8_t* cq, uint8_t* cs, float* fr, float* fc, const GroupTable& gt, const Calib& cal,
+                               int tile_h) {
     if (row && col)
         hipExtLaunchKernelGGL((k_encode<MODE, true, true, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
-                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal);
+                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal, tile_h);
     else if (row)
         hipExtLaunchKernelGGL((k_encode<MODE, true, false, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
-                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal);
+                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal, tile_h);
     else
         hipExtLaunchKernelGGL((k_encode<MODE, false, true, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
-                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal);
+                              x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal, tile_h);
 }
 
 hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const uint16_t* x, int64_t M, int64_t K,
@@ -950,8 +955,10 @@ hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const u
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st,
                          hipEvent_t ev0, hipEvent_t ev1, const Calib& cal) {
     if (row_end <= row_begin || K <= 0 || (!row && !col)) return hipSuccess;
-    dim3 grid(cdiv(K, kEncCols), cdiv(row_end - row_begin, kEncRows));
-#define NVFP4_ENC_ARGS row, col, grid, st, ev0, ev1, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt, cal
+    // rows per workgroup: 256, or 128 when the grid would be small
+    const int tile_h = (int64_t)cdiv(K, kEncCols) * cdiv(row_end - row_begin, kEncRows) < 768 ? 128 : kEncRows;
+    dim3 grid(cdiv(K, kEncCols), cdiv(row_end - row_begin, tile_h));
+#define NVFP4_ENC_ARGS row, col, grid, st, ev0, ev1, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt, cal, tile_h
     if (caller_amax) {
         // amax from the caller: scales may saturate
         if (mode == ENC_TENSOR) launch_encode_mode<ENC_TENSOR, true>(NVFP4_ENC_ARGS);

@@ -499,23 +499,28 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         __syncthreads();
     }
 
-    // columnwise outer scales of this lane's 8 columns
+    // columnwise outer scales of this lane's 8 columns: per-token casts keep
+    // the tile's 256 in LDS (every lane of a column reads the same entry),
+    // the others in registers
+    constexpr bool COL_LDS = COL && MODE == ENC_TOKEN;
+    __shared__ float2 col_scale[COL_LDS ? kEncCols : 1];
     Outer colO[8];
     bool col_slow = false;
     int cur_group = -1;    // the lane's expert (grouped casts)
     int wave_group = -1;   // expert of the wave's current first row
     int64_t m_len = M, grow0 = 0;
-    if (COL && !TILE && MODE != ENC_GROUPED) {
-        // unconditional loads (a lane past the last column reads column 0 and
-        // ignores it) so the eight requests are in flight together
-        float ca[8];
+    if (COL_LDS) {
+        // one column per thread; a column outside the fast range sends the
+        // whole tile to the exact path
+        const uint32_t c = bx * kEncCols + threadIdx.x;
+        const Outer o = make_outer(c < K ? col_amax[c] : 0.0f);
+        col_scale[threadIdx.x] = make_float2(o.S, o.yS);
+        col_slow = __syncthreads_or(o.slow) != 0;
+    } else if (COL && !TILE && MODE != ENC_GROUPED) {
+        const float ca = col_amax[0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ca[j] = col_amax[(MODE == ENC_TENSOR) ? 0 : (col_ok ? c0 + j : 0)];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            colO[j] = make_outer(col_ok ? ca[j] : 0.0f);
-            col_slow |= colO[j].slow;
-        }
+        for (int j = 0; j < 8; ++j) colO[j] = make_outer(ca);
+        col_slow = colO[0].slow;
     }
     // per-tensor rowwise outer scale
     const float rowA_t = (ROW && MODE == ENC_TENSOR) ? row_amax[0] : 0.0f;
@@ -553,25 +558,42 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 
     uint32_t slow_mask = 0u;
     constexpr int kSteps = kEncRows / 4 / 32;   // 32-row steps per wave
-    // loads of a step: its rowwise amax, then the 16 data words, through
-    // buffers spanning the step's valid rows, so that rows past the end read
-    // zeros (and their stores below are dropped)
-    auto issue = [&](int sb, u32x4* v, float& ra) {
-        const int64_t wr0 = wbase + 32 * sb;
-        const uint32_t nrows = (uint32_t)(row_end - wr0 < 32 ? row_end - wr0 : 32);
-        if (ROWTOK) ra = row_amax[(uint32_t)(lane & 31) < nrows ? wr0 + (lane & 31) : row_begin];
-        // the row stride is made opaque: otherwise the compiler keeps the 16
-        // per-row lane offsets live in registers instead of forming each with
-        // one add where it is used
-        uint32_t xr = xrow;
-        asm volatile("" : "+s"(xr));
-        const __amdgpu_buffer_rsrc_t bx_rs = rsrc(x + wr0 * K, nrows * xrow);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(bx_rs, vx, i * xr, kCacheNT);
+    // loads of a step issued during the step before it (grouped casts, which
+    // keep their expert's column scales in registers, load at the step's top)
+    constexpr bool kPrefetch = MODE != ENC_GROUPED;
+    // Valid rows of step sb (0 for a wave whose rows all lie past the end:
+    // its first step's loads are issued before the step loop's exit test).
+    auto step_rows = [&](int sb) -> uint32_t {
+        const int64_t left = row_end - (wbase + 32 * sb);
+        return left <= 0 ? 0u : (left < 32 ? (uint32_t)left : 32u);
     };
-    // Loads are issued at the top of each step.  (Issuing the next step's
-    // before this step's work needs a second set of 64 data registers, which
-    // costs a wave per SIMD of occupancy and measured slower.)
+    // The x buffer of a step spans its valid rows only, so that rows past the
+    // end read zeros without a memory access (and their stores below are
+    // dropped); an empty step gets an empty buffer.
+    auto x_rsrc = [&](int sb) {
+        return rsrc(x + (wbase + 32 * sb) * K, step_rows(sb) * xrow);
+    };
+    auto load_ra = [&](int sb) -> float {
+        if (!ROWTOK) return 0.0f;
+        const uint32_t l = (uint32_t)(lane & 31);
+        return row_amax[l < step_rows(sb) ? wbase + 32 * sb + l : row_begin];
+    };
+    // The row stride is made opaque: otherwise the compiler keeps the 16
+    // per-row lane offsets live in registers instead of putting each row's in
+    // the scalar offset where it is used.
+    uint32_t xr = xrow;
+    asm volatile("" : "+s"(xr));
+    // The first step's rows are loaded here; each later step's rows are loaded
+    // during the step before it, a row pair at a time, into the registers of
+    // the pair just encoded, so a wave waits for memory once per tile and
+    // needs no second set of data registers.
+    u32x4 v[16];
+    float ra = load_ra(0);
+    {
+        const __amdgpu_buffer_rsrc_t rs = x_rsrc(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, vx, i * xr, kCacheNT);
+    }
 #pragma unroll
     for (int sb = 0; sb < kSteps; ++sb) {
         const int64_t wr0 = wbase + 32 * sb;     // first row of the wave's step
@@ -579,9 +601,26 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         const uint32_t nrows = (uint32_t)(row_end - wr0 < 32 ? row_end - wr0 : 32);   // rows of the step
         const bool group_ok = 16u * rg < nrows;
         const int64_t r0 = group_ok ? wr0 + 16 * rg : wr0;
-        u32x4 v[16];
-        float ra = 0.0f;
-        issue(sb, v, ra);
+        // the next step's rows (an empty buffer when there is none: its loads
+        // then return zeros without touching memory)
+        const bool more = sb + 1 < kSteps && 32 * (sb + 1) < tile_h / 4 && wr0 + 32 < row_end;
+        if (sb > 0 && !kPrefetch) {
+            const __amdgpu_buffer_rsrc_t rs = x_rsrc(sb);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, vx, i * xr, kCacheNT);
+            ra = load_ra(sb);
+        }
+        const __amdgpu_buffer_rsrc_t nx_rs = more ? x_rsrc(sb + 1) : rsrc(x, 0u);
+        // rows i, i+1 of the next step, loaded once the outputs of the pair
+        // that held them (d0, d1: its rowwise words; dc: its columnwise
+        // words) are computed, so that they land in that pair's registers
+        auto load_next = [&](int i, uint32_t d0, uint32_t d1, const uint32_t* dc) {
+            uint32_t so = i * xr;
+            asm volatile("" : "+s"(so) : "v"(d0), "v"(d1), "v"(dc[0]), "v"(dc[2]), "v"(dc[4]), "v"(dc[6]),
+                         "v"(dc[8]), "v"(dc[10]), "v"(dc[12]), "v"(dc[14]));
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(nx_rs, vx, so, kCacheNT);
+            v[i + 1] = __builtin_amdgcn_raw_buffer_load_b128(nx_rs, vx, so + xr, kCacheNT);
+        };
         uint32_t qr = qrow, sr = srow;
         asm volatile("" : "+s"(qr), "+s"(sr));
         if (COL && MODE == ENC_GROUPED) {
@@ -618,6 +657,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         if (ROWTOK) {
             const bool row_in = (uint32_t)(lane & 31) < nrows;
             const Outer o = make_outer(row_in ? ra : 0.0f);
+            if (kPrefetch && more) ra = load_ra(sb + 1);
             if (lane < 32) {
                 row_scale[wave][lane][0] = o.S;
                 row_scale[wave][lane][1] = o.yS;
@@ -656,6 +696,12 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 bm[s] = __builtin_amdgcn_perm(m, m, own_sel);
             }
         }
+        // the rowwise block maxima are finished here, so that the 64 absolute
+        // values they come from are dead before the row pairs start (left to
+        // itself the compiler computes each pair's maximum where it is used)
+        if (ROW && !TILE)
+            asm volatile("" : "+v"(bm[0]), "+v"(bm[1]), "+v"(bm[2]), "+v"(bm[3]),
+                         "+v"(bm[4]), "+v"(bm[5]), "+v"(bm[6]), "+v"(bm[7]));
         // block parameters of the lane's column blocks (or of its 16x16 tile)
         FastBlock cb[8];
         FastBlock tb;
@@ -667,15 +713,24 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t bits = (j & 1) ? (cm[j >> 1] & 0xffff0000u) : (cm[j >> 1] << 16);
-                cb[j] = fast_block<SAT>(bits, colO[j]);
+                Outer o = colO[j];
+                if (COL_LDS) {
+                    const float2 sy = col_scale[(lane & 31) * 8 + j];
+                    o.S = sy.x;
+                    o.yS = sy.y;
+                }
+                cb[j] = fast_block<SAT>(bits, o);
                 slow |= cb[j].slow;
+                // the scale byte goes to the staging area now rather than
+                // being held through the row pairs
+                if (d.col_ok) d.lds_sf[j * kStageSfPitch] = (uint8_t)cb[j].code;
             }
         }
 
         // (3) per row pair: rowwise parameters, then both encodings
         const __amdgpu_buffer_rsrc_t q_rs = rsrc(row_q + wr0 * (K / 2), nrows * qrow);
         const __amdgpu_buffer_rsrc_t s_rs = rsrc(row_sf + wr0 * (K / 16), nrows * srow);
-        uint32_t cq[8][2];
+        uint32_t cq[8][2] = {};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int i = 2 * s;
@@ -728,24 +783,29 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                     else w = put_fp4x2<3>(w, q0, q1);
                 }
             }
+            uint32_t o0 = 0u, o1 = 0u;
             if (ROW) {
                 // as above: bytes 1..3 overwrite whatever byte 0's conversion kept
                 const float p00 = quot2(a0[0], yh0, yl0), p10 = quot2(a1[0], yh1, yl1);
-                uint32_t o0 = put_fp4x2<0>(__float_as_uint(p00), p00, quot2(a0[1], yh0, yl0));
+                o0 = put_fp4x2<0>(__float_as_uint(p00), p00, quot2(a0[1], yh0, yl0));
                 o0 = put_fp4x2<1>(o0, quot2(a0[2], yh0, yl0), quot2(a0[3], yh0, yl0));
                 o0 = put_fp4x2<2>(o0, quot2(a0[4], yh0, yl0), quot2(a0[5], yh0, yl0));
                 o0 = put_fp4x2<3>(o0, quot2(a0[6], yh0, yl0), quot2(a0[7], yh0, yl0));
-                uint32_t o1 = put_fp4x2<0>(__float_as_uint(p10), p10, quot2(a1[1], yh1, yl1));
+                o1 = put_fp4x2<0>(__float_as_uint(p10), p10, quot2(a1[1], yh1, yl1));
                 o1 = put_fp4x2<1>(o1, quot2(a1[2], yh1, yl1), quot2(a1[3], yh1, yl1));
                 o1 = put_fp4x2<2>(o1, quot2(a1[4], yh1, yl1), quot2(a1[5], yh1, yl1));
                 o1 = put_fp4x2<3>(o1, quot2(a1[6], yh1, yl1), quot2(a1[7], yh1, yl1));
                 __builtin_amdgcn_raw_buffer_store_b32(o0, q_rs, vq, i * qr, kCacheNT);
                 __builtin_amdgcn_raw_buffer_store_b32(o1, q_rs, vq, (i + 1) * qr, kCacheNT);
             }
+            if (kPrefetch && sb + 1 < kSteps) load_next(i, o0, o1, &cq[0][s >> 2]);
         }
         if (COL) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) store_col<STAGE>(d, j, cq[j][0], cq[j][1], TILE ? tb.code : cb[j].code);
+            for (int j = 0; j < 8; ++j) {
+                if (TILE) store_col<STAGE>(d, j, cq[j][0], cq[j][1], tb.code);
+                else if (d.col_ok) *reinterpret_cast<u32x2*>(d.lds_q + j * kStageQPitch) = u32x2{cq[j][0], cq[j][1]};
+            }
         }
         if (step_slow || __builtin_amdgcn_ballot_w64(slow) != 0ull) slow_mask |= 1u << sb;
         __builtin_amdgcn_wave_barrier();
@@ -802,28 +862,34 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             uint8_t* gq = col_q + o * K / 2 + (s0 - o) / 2 + (int64_t)cbase * (m / 2);
             uint8_t* gs = col_sf + o * K / 16 + (s0 - o) / 16 + (int64_t)cbase * (m / 16);
             const int64_t qstride = m / 2, sstride = m / 16;
-            const uint32_t nch = (qb + 15) / 16;   // pieces per column; the last may be 8 bytes
-            for (uint32_t k = t; k < ncols * nch; k += 256) {
-                const uint32_t c = k / nch, chunk = (k % nch) * 16;
-                const uint8_t* src = stage_q + c * kStageQPitch + lq + chunk;
-                uint8_t* dst = gq + (int64_t)c * qstride + chunk;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-                if (chunk + 16 <= qb) {
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-                    __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(dst));
-                } else {
-                    __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
+            // data: a segment is at most 128 bytes per column; thread t writes
+            // its piece t % 8 (16 bytes, the segment's last may be 8) of
+            // columns t / 8, t / 8 + 32, ...
+            const uint32_t chunk = (t & 7u) * 16u;
+            if (chunk < qb) {
+                const bool whole = chunk + 16u <= qb;
+                const uint8_t* src = stage_q + (t >> 3) * kStageQPitch + lq + chunk;
+                uint8_t* dst = gq + (int64_t)(t >> 3) * qstride + chunk;
+                for (uint32_t c = t >> 3; c < ncols; c += 32) {
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+                    if (whole) {
+                        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+                        __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(dst));
+                    } else {
+                        __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
+                    }
+                    src += 32 * kStageQPitch;
+                    dst += 32 * qstride;
                 }
             }
-            // scale bytes: 16-byte pieces along each column when source and
-            // destination are aligned for them, else words, else bytes
-            if (sbn % 16 == 0 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
-                const uint32_t per = sbn / 16;
-                for (uint32_t k = t; k < ncols * per; k += 256) {
-                    const uint32_t c = k / per, part = (k % per) * 16;
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + c * kStageSfPitch + ls + part);
+            // scale bytes: one 16-byte piece per column (thread t: column t)
+            // for a whole 256-row segment when the destination is aligned for
+            // it, else words, else bytes
+            if (sbn == 16 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
+                if (t < ncols) {
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + t * kStageSfPitch + ls);
                     __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
-                                                reinterpret_cast<u32x4*>(gs + (int64_t)c * sstride + part));
+                                                reinterpret_cast<u32x4*>(gs + (int64_t)t * sstride));
                 }
             } else {
                 const bool words = sbn % 4 == 0 && ls % 4 == 0 && sstride % 4 == 0 && reinterpret_cast<uintptr_t>(gs) % 4 == 0;

@@ -175,8 +175,11 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
             cm[k] = 0u;
         }
     };
-    u32x4 vnext[16];
-    if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, vnext);
+    // The first 16-row sub-block is loaded here; each row of the next one is
+    // loaded into the registers of the same row of the current one as soon as
+    // that row's maxima are taken, so one set of data registers suffices.
+    u32x4 v[16];
+    if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, v);
 #pragma unroll 1
     for (int s = 0; s < tile_h / 4; s += 16) {
         const int64_t r0 = rb + s;
@@ -188,19 +191,23 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
                 cur_group = g;
             }
         }
-        u32x4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = vnext[i];
-        if (s + 16 < tile_h / 4 && r0 + 16 < row_end) load_subblock(x, K, r0 + 16, row_end, lane_off, xr, vnext);
+        // the next sub-block's rows (an empty buffer when there is none)
+        const bool more = s + 16 < tile_h / 4 && r0 + 16 < row_end;
+        const int64_t left = row_end - (r0 + 16);
+        const __amdgpu_buffer_rsrc_t nrs = more ? rsrc(x + (r0 + 16) * K, (uint32_t)(left < 16 ? left : 16) * xr)
+                                                : rsrc(x, 0u);
         uint32_t rm[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            uint32_t a = pk_max_u16(pk_max_u16(abs2(v[i].x), abs2(v[i].y)), pk_max_u16(abs2(v[i].z), abs2(v[i].w)));
-            rm[i] = max_halves(a);
-            cm[0] = pk_max_u16(cm[0], abs2(v[i].x));
-            cm[1] = pk_max_u16(cm[1], abs2(v[i].y));
-            cm[2] = pk_max_u16(cm[2], abs2(v[i].z));
-            cm[3] = pk_max_u16(cm[3], abs2(v[i].w));
+            const uint32_t a0 = abs2(v[i].x), a1 = abs2(v[i].y), a2 = abs2(v[i].z), a3 = abs2(v[i].w);
+            rm[i] = max_halves(pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)));
+            cm[0] = pk_max_u16(cm[0], a0);
+            cm[1] = pk_max_u16(cm[1], a1);
+            cm[2] = pk_max_u16(cm[2], a2);
+            cm[3] = pk_max_u16(cm[3], a3);
+            uint32_t so = i * xr;
+            asm volatile("" : "+s"(so) : "v"(rm[i]), "v"(cm[0]), "v"(cm[1]), "v"(cm[2]), "v"(cm[3]));
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(nrs, lane_off, so, 0);
         }
         if ((KIND == AMAX_TOKEN || KIND == AMAX_GROUPED) && row_amax != nullptr) {
             uint32_t pair;
@@ -862,15 +869,16 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             uint8_t* gq = col_q + o * K / 2 + (s0 - o) / 2 + (int64_t)cbase * (m / 2);
             uint8_t* gs = col_sf + o * K / 16 + (s0 - o) / 16 + (int64_t)cbase * (m / 16);
             const int64_t qstride = m / 2, sstride = m / 16;
-            // data: a segment is at most 128 bytes per column; thread t writes
-            // its piece t % 8 (16 bytes, the segment's last may be 8) of
-            // columns t / 8, t / 8 + 32, ...
-            const uint32_t chunk = (t & 7u) * 16u;
+            // data: a segment is at most kEncRows/2 bytes per column, kNP
+            // 16-byte pieces; thread t writes piece t % kNP (the segment's
+            // last may be 8 bytes) of columns t / kNP, t / kNP + 256 / kNP, ...
+            constexpr uint32_t kNP = kEncRows / 32;
+            const uint32_t chunk = (t % kNP) * 16u;
             if (chunk < qb) {
                 const bool whole = chunk + 16u <= qb;
-                const uint8_t* src = stage_q + (t >> 3) * kStageQPitch + lq + chunk;
-                uint8_t* dst = gq + (int64_t)(t >> 3) * qstride + chunk;
-                for (uint32_t c = t >> 3; c < ncols; c += 32) {
+                const uint8_t* src = stage_q + (t / kNP) * kStageQPitch + lq + chunk;
+                uint8_t* dst = gq + (int64_t)(t / kNP) * qstride + chunk;
+                for (uint32_t c = t / kNP; c < ncols; c += 256 / kNP) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
                     if (whole) {
                         const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
@@ -878,18 +886,20 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                     } else {
                         __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(dst));
                     }
-                    src += 32 * kStageQPitch;
-                    dst += 32 * qstride;
+                    src += (256 / kNP) * kStageQPitch;
+                    dst += (256 / kNP) * qstride;
                 }
             }
-            // scale bytes: one 16-byte piece per column (thread t: column t)
-            // for a whole 256-row segment when the destination is aligned for
-            // it, else words, else bytes
-            if (sbn == 16 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
+            // scale bytes: 16-byte pieces along each column (thread t: column
+            // t) when the segment is a multiple of 256 rows and the destination
+            // is aligned for them, else words, else bytes
+            if (sbn % 16 == 0 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
                 if (t < ncols) {
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + t * kStageSfPitch + ls);
-                    __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
-                                                reinterpret_cast<u32x4*>(gs + (int64_t)t * sstride));
+                    for (uint32_t part = 0; part < sbn; part += 16) {
+                        const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + t * kStageSfPitch + ls + part);
+                        __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
+                                                    reinterpret_cast<u32x4*>(gs + (int64_t)t * sstride + part));
+                    }
                 }
             } else {
                 const bool words = sbn % 4 == 0 && ls % 4 == 0 && sstride % 4 == 0 && reinterpret_cast<uintptr_t>(gs) % 4 == 0;

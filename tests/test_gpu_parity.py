@@ -295,6 +295,29 @@ def test_c2_per_token_full(oracle):
         assert torch.equal(out[k], again[k]), f"run-to-run difference in {k}"
 
 
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+@pytest.mark.parametrize("M", [12032, 12288])
+def test_encode_tile_height_switch(oracle, M, mode):
+    """With K = 4096 (16 column tiles), 12032 rows give 752 workgroups of 256
+    rows, so the encode pass uses 128-row tiles; 12288 rows give 768 and keep
+    256-row tiles.  Both must match the oracle in full, and so must the
+    calibrating call's outputs and decayed buffer."""
+    x = W.row_scaled_with_outliers(M, 4096, 60 + M)
+    _announce(f"{M}x4096 mode={mode} (encode tile-height switch)")
+    d = to_dev(x)
+    out = nv.quantize(d, mode)
+    buf = torch.full((1,), 2.0, dtype=torch.float32, device="cuda:0")
+    cal = {k: torch.empty_like(v) for k, v in out.items()}
+    nv.quantize_calibrate_into(d, mode, buf, 0.5, **cal)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(x, mode)
+    compare_cast(out, ref)
+    compare_cast(cal, ref)
+    a = oracle.amax_tensor(x)
+    expect = oracle.amax_accumulate(np.array([2.0], np.float32), np.array([a], np.float32), 0.5)
+    assert_bytes_equal(host(buf), expect, "decayed buffer")
+
+
 def _sample_vectors(x, out, mode, rows, cols, oracle):
     xf = W.bf16_to_f32(x)
     if mode == nv.PER_TOKEN:

@@ -19,7 +19,8 @@
 namespace nvfp4 {
 
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
-constexpr int kAmaxRows = 256;     // rows per workgroup tile in the amax pass (at most; fewer for small tensors)
+constexpr int kAmaxRows = 512;     // rows per workgroup tile in the amax pass (at most; fewer for small tensors)
+constexpr int kAmaxGroupedRows = 256;   // at most, for grouped casts (their per-expert LDS slots scale with it)
 constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass (at most; 128 for small tensors)
 constexpr int kEncCols = 256;      // columns per workgroup tile in the encode pass: a wave is
                                    // two row groups of 32 lanes, each 16 rows x 256 columns
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     const uint32_t bx = tile % gridDim.x, by = tile / gridDim.x;
     const int64_t c0 = (int64_t)bx * kTileCols + lane * 8;
     const bool col_ok = c0 < K;
-    const int64_t rb = row_begin + (int64_t)by * tile_h + wave * (tile_h / 4);   // tile_h: 64, 128 or 256 rows
+    const int64_t rb = row_begin + (int64_t)by * tile_h + wave * (tile_h / 4);   // tile_h: 64 to 512 rows
     const uint32_t lane_off = col_ok ? (uint32_t)c0 * 2u : kOffOut;
     uint32_t xr = (uint32_t)K * 2u;
     asm volatile("" : "+s"(xr));   // keeps the 16 row offsets from being held in registers
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     int cur_group = -1;
     // Grouped: column maxima are first combined in LDS per expert present
     // in the tile (slot = the expert's first row within the tile / 16, so at
-    // most kAmaxRows / 16 slots), then one atomic per column and expert.
-    constexpr int kSlots = kAmaxRows / 16;
+    // most kAmaxGroupedRows / 16 slots), then one atomic per column and expert.
+    constexpr int kSlots = kAmaxGroupedRows / 16;
     __shared__ uint32_t gred[KIND == AMAX_GROUPED ? kSlots : 1][KIND == AMAX_GROUPED ? kTileCols : 1];
     __shared__ int gslot[KIND == AMAX_GROUPED ? kSlots : 1];
     const int64_t tile_r0 = row_begin + (int64_t)by * tile_h;
@@ -988,9 +989,11 @@ hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin
                        float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
                        hipStream_t st) {
     if (row_end <= row_begin || K <= 0) return hipSuccess;
-    // rows per workgroup: 256, fewer when the grid would leave CUs idle
+    // rows per workgroup: 512 (256 for grouped casts), fewer when the grid
+    // would leave CUs idle
     int tile_h = kAmaxRows;
-    while (tile_h > 64 && (int64_t)cdiv(K, kTileCols) * cdiv(row_end - row_begin, tile_h) < 1024) tile_h /= 2;
+    while (tile_h > 64 && (int64_t)cdiv(K, kTileCols) * cdiv(row_end - row_begin, tile_h) < 512) tile_h /= 2;
+    if (kind == AMAX_GROUPED && tile_h > kAmaxGroupedRows) tile_h = kAmaxGroupedRows;
     dim3 grid(cdiv(K, kTileCols), cdiv(row_end - row_begin, tile_h));
     switch (kind) {
     case AMAX_TENSOR:

@@ -50,6 +50,12 @@ def _load():
         "orc_dequantize": (ctypes.c_int, [_p, _p, _p, _i64, _i64, ctypes.c_int, _p]),
         "orc_amax_accumulate": (None, [_p, _p, _i64, ctypes.c_float]),
         "orc_amax_accumulate_reduce": (None, [_p, _p, _i64, ctypes.c_float]),
+        "orc_philox4x32_10_array": (None, [_p, _p, _i64, _p]),
+        "orc_e2m1_encode_sr_array": (None, [_p, _p, _i64, _p]),
+        "orc_quantize_vector_sr": (None, [_p, _i64, ctypes.c_float, _p, _p, ctypes.c_uint64, ctypes.c_uint32,
+                                          ctypes.c_uint32, ctypes.c_uint32]),
+        "orc_quantize_sr": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_int, _p, _p, _p, _p, _p, _p,
+                                           ctypes.c_uint64, ctypes.c_uint32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -193,6 +199,63 @@ def quantize(x, mode, rowwise=True, columnwise=True):
                               _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")))
     if rc != 0:
         raise ValueError("oracle: shape not supported by this mode")
+    return out
+
+
+# ----------------------------------------------------- stochastic rounding
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 blocks: ctr uint32 [n, 4], key uint32 [n, 2] -> [n, 4]."""
+    ctr = np.ascontiguousarray(ctr, np.uint32).reshape(-1, 4)
+    key = np.ascontiguousarray(key, np.uint32).reshape(-1, 2)
+    if len(ctr) != len(key):
+        raise ValueError("one key per counter")
+    out = np.empty_like(ctr)
+    _load().orc_philox4x32_10_array(_ptr(ctr), _ptr(key), len(ctr), _ptr(out))
+    return out
+
+
+def e2m1_encode_sr(q, rnd):
+    """Stochastic E2M1 codes of float32 quotients q with 32-bit randoms rnd."""
+    q = np.ascontiguousarray(q, np.float32).ravel()
+    rnd = np.ascontiguousarray(rnd, np.uint32).ravel()
+    if q.shape != rnd.shape:
+        raise ValueError("one random per quotient")
+    out = np.empty(q.shape, np.uint8)
+    _load().orc_e2m1_encode_sr_array(_ptr(q), _ptr(rnd), q.size, _ptr(out))
+    return out
+
+
+def quantize_vector_sr(v, A, seed, vec, direction, offset):
+    v = np.ascontiguousarray(v, np.float32)
+    q = np.empty(v.size // 2, np.uint8)
+    sf = np.empty(v.size // 16, np.uint8)
+    _load().orc_quantize_vector_sr(_ptr(v), v.size, float(A), _ptr(q), _ptr(sf), int(seed), int(vec),
+                                   int(direction), int(offset))
+    return q, sf
+
+
+def quantize_sr(x, mode, seed, offset, rowwise=True, columnwise=True):
+    """Stochastic-rounding cast (per-tensor or per-token); same outputs as
+    quantize()."""
+    x = _bf16(x)
+    M, K = x.shape
+    out = {}
+    if rowwise:
+        out["row_q"] = np.empty((M, K // 2), np.uint8)
+        out["row_sf"] = np.empty((M, K // 16), np.uint8)
+        out["row_amax"] = np.empty(1 if mode == PER_TENSOR else M, np.float32)
+    if columnwise:
+        out["col_q"] = np.empty((K, M // 2), np.uint8)
+        out["col_sf"] = np.empty((K, M // 16), np.uint8)
+        out["col_amax"] = np.empty(1 if mode == PER_TENSOR else K, np.float32)
+    g = out.get
+    rc = _load().orc_quantize_sr(_ptr(x), M, K, int(mode),
+                                 _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
+                                 _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")),
+                                 int(seed), int(offset))
+    if rc != 0:
+        raise ValueError("oracle: shape or mode not supported by the stochastic-rounding cast")
     return out
 
 

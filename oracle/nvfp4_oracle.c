@@ -418,3 +418,179 @@ void orc_amax_accumulate_reduce(float* buf, const float* obs, int64_t n, float d
         if (obs[i] > m) m = obs[i];
     orc_amax_accumulate(buf, &m, 1, decay);
 }
+
+/* --------------------------------------------------- stochastic rounding */
+
+/* The per-token recipe page lists a stochastic-rounding variant of the cast
+ * ("per_token_sr") without saying how its random numbers are drawn.  The
+ * reading taken here (and in the design notes):
+ *   - randoms come from Philox4x32-10, the counter-based generator of
+ *     Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+ *     1, 2, 3" (SC'11).  Key = the caller's 64-bit seed (low word first);
+ *     element i of a vector (a row for rowwise output, a column for
+ *     columnwise output) takes output word i % 4 of the counter
+ *     (i / 4, vector index, direction, offset), direction 0 rowwise and 1
+ *     columnwise, offset a 32-bit value the caller changes per call;
+ *   - rounding: block scales exactly as in the deterministic cast; the
+ *     element quotient x = |RN(v / r)| also; lo and lo + d the E2M1 grid
+ *     points around x (d = 0.5 below 2, 1 below 4, 2 below 6); with
+ *     U = (R >> 8) * 2^-24 for the element's 32-bit random R, the magnitude
+ *     rounds up iff x - lo > U * d.  Both sides of that comparison are exact
+ *     in binary32 (x - lo by Sterbenz's lemma, U * d a power-of-two scaling),
+ *     so P(up) = ceil(2^24 * (x - lo) / d) / 2^24.  x >= 6 saturates to 6
+ *     with no draw; the sign is copied; r == 0 gives sign-only nibbles. */
+
+/* One Philox4x32 block: ten rounds of the multiply-xor S-box on the counter
+ * words, with the key advanced by the two Weyl constants between rounds. */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    const uint32_t kMul0 = 0xD2511F53u, kMul1 = 0xCD9E8D57u;   /* round multipliers */
+    const uint32_t kWeyl0 = 0x9E3779B9u, kWeyl1 = 0xBB67AE85u; /* key increments */
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += kWeyl0;
+            k1 += kWeyl1;
+        }
+        uint64_t p0 = (uint64_t)kMul0 * c0;
+        uint64_t p1 = (uint64_t)kMul1 * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+void orc_philox4x32_10_array(const uint32_t* ctr, const uint32_t* key, int64_t n, uint32_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) orc_philox4x32_10(ctr + 4 * i, key + 2 * i, out + 4 * i);
+}
+
+/* E2M1 code of q rounded stochastically with the 32-bit random rnd */
+uint8_t orc_e2m1_encode_sr(float q, uint32_t rnd)
+{
+    uint8_t s = signbit(q) ? 8 : 0;
+    float x = fabsf(q);
+    if (x >= 6.0f) return (uint8_t)(s | 7);
+    float lo, d;
+    uint8_t c;
+    if (x < 2.0f) {            /* grid 0, 0.5, 1, 1.5: codes 0..3 */
+        c = (uint8_t)floorf(2.0f * x);
+        lo = 0.5f * (float)c;
+        d = 0.5f;
+    } else if (x < 4.0f) {     /* grid 2, 3: codes 4, 5 */
+        lo = floorf(x);
+        c = (uint8_t)(2 + (int)lo);
+        d = 1.0f;
+    } else {                   /* grid 4: code 6, next 6 */
+        lo = 4.0f;
+        c = 6;
+        d = 2.0f;
+    }
+    float u = (float)(rnd >> 8) * 0x1p-24f;
+    if (x - lo > u * d) c = (uint8_t)(c + 1);
+    return (uint8_t)(s | c);
+}
+
+void orc_e2m1_encode_sr_array(const float* q, const uint32_t* rnd, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode_sr(q[i], rnd[i]);
+}
+
+/* one vector, as orc_quantize_vector, with stochastic element rounding */
+void orc_quantize_vector_sr(const float* v, int64_t n, float A, uint8_t* q, uint8_t* sf,
+                            uint64_t seed, uint32_t vec, uint32_t dir, uint32_t offset)
+{
+    float S = A / kOuterDiv;
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (int64_t j = 0; j < n / 16; ++j) {
+        const float* blk = v + 16 * j;
+        float r;
+        if (S == 0.0f) {
+            sf[j] = 0x00;
+            r = 0.0f;
+        } else {
+            float b = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                float a = fabsf(blk[i]);
+                if (a > b) b = a;
+            }
+            float t = b / kE2M1Max;
+            float s = t / S;
+            uint8_t code = orc_e4m3_encode(s);
+            sf[j] = code;
+            r = orc_e4m3_decode(code) * S;
+        }
+        uint32_t rnd[16];
+        for (int g = 0; g < 4; ++g) {
+            uint32_t ctr[4] = {(uint32_t)((16 * j + 4 * g) / 4), vec, dir, offset};
+            orc_philox4x32_10(ctr, key, rnd + 4 * g);
+        }
+        uint8_t nib[16];
+        for (int i = 0; i < 16; ++i) {
+            if (r == 0.0f)
+                nib[i] = signbit(blk[i]) ? 8 : 0;
+            else
+                nib[i] = orc_e2m1_encode_sr(blk[i] / r, rnd[i]);
+        }
+        for (int i = 0; i < 8; ++i)
+            q[8 * j + i] = (uint8_t)(nib[2 * i] | (nib[2 * i + 1] << 4));
+    }
+}
+
+/* whole stochastic-rounding cast, per-tensor (mode 0) or per-token (mode 1);
+ * amax outputs as orc_quantize.  M < 2^32 (the vector index is one counter
+ * word).  Returns 0, or -1 on a shape or mode error. */
+int orc_quantize_sr(const uint16_t* x, int64_t M, int64_t K, int mode,
+                    uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                    uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                    uint64_t seed, uint32_t offset)
+{
+    int want_row = row_q != NULL, want_col = col_q != NULL;
+    if (M < 0 || K < 0 || M >= ((int64_t)1 << 32) || (mode != 0 && mode != 1)) return -1;
+    if (want_row && K % 16 != 0) return -1;
+    if (want_col && M % 16 != 0) return -1;
+    float At = mode == 0 ? orc_amax_tensor(x, M, K, K) : 0.0f;
+    if (want_row) {
+        float* ra = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+        float* v = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+        if (mode == 1) orc_amax_rows(x, M, K, K, ra);
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t k = 0; k < K; ++k) v[k] = orc_bf16_to_f32(x[m * K + k]);
+            orc_quantize_vector_sr(v, K, mode == 1 ? ra[m] : At, row_q + m * (K / 2), row_sf + m * (K / 16),
+                                   seed, (uint32_t)m, 0u, offset);
+        }
+        if (row_amax) {
+            if (mode == 1) memcpy(row_amax, ra, sizeof(float) * (size_t)M);
+            else row_amax[0] = At;
+        }
+        free(v);
+        free(ra);
+    }
+    if (want_col) {
+        float* ca = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+        float* v = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+        if (mode == 1) orc_amax_cols(x, M, K, K, ca);
+        for (int64_t k = 0; k < K; ++k) {
+            for (int64_t m = 0; m < M; ++m) v[m] = orc_bf16_to_f32(x[m * K + k]);
+            orc_quantize_vector_sr(v, M, mode == 1 ? ca[k] : At, col_q + k * (M / 2), col_sf + k * (M / 16),
+                                   seed, (uint32_t)k, 1u, offset);
+        }
+        if (col_amax) {
+            if (mode == 1) memcpy(col_amax, ca, sizeof(float) * (size_t)K);
+            else col_amax[0] = At;
+        }
+        free(v);
+        free(ca);
+    }
+    return 0;
+}

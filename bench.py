@@ -190,6 +190,8 @@ def all_configs(steps, warmup):
     o3t = dict(o3, row_amax=f32(1), col_amax=f32(1))
     report("C3-per-tensor", "per-tensor row+col with the decayed amax update, 16384x8192",
            timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3), cast_bytes(M, K, 2))
+    report("C3-per-token-SR", "per-token row+col with stochastic rounding (Philox4x32-10 randoms), 16384x8192",
+           timed(lambda i: nv.quantize_sr_into(x3[i], nv.PER_TOKEN, 2024, i, **o3), 3), cast_bytes(M, K, M + K))
     del x3, o3, o3t
     # C4: grouped MoE, 64 experts, 32768 tokens x 4096
     x4h, counts = W.c4()

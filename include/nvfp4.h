@@ -131,6 +131,29 @@ NVFP4_API nvfp4_status nvfp4_quantize_calibrate(const void* x, int64_t M, int64_
                                       uint8_t* col_q, uint8_t* col_sf, float* col_amax,
                                       float* buf, float decay, void* stream);
 
+/*
+ * nvfp4_quantize with stochastic rounding of the E2M1 element codes: the
+ * stochastic-rounding variant the per-token recipe page lists next to the
+ * per-token cast (TransformerEngine PR #3045, Changes), PER_TENSOR or
+ * PER_TOKEN scaling (TILE_16x16 is NVFP4_EINVAL).  Outer amax and block scales
+ * are those of nvfp4_quantize; each element's quotient x = |RN(v / r)| lies
+ * in [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2 below 6)
+ * and rounds up iff x - lo > U * d, U = (R >> 8) * 2^-24, R the element's
+ * 32-bit random; x >= 6 saturates.  R is word i % 4 of the Philox4x32-10
+ * block (Salmon et al., SC'11) with key (seed low word, seed high word) and
+ * counter (i / 4, vector index, 0 for rowwise / 1 for columnwise, offset),
+ * where i is the element's position along its vector (a row of x for
+ * rowwise output, a column for columnwise output).  The page does not say
+ * how its randoms are drawn; this is the library's definition, reproduced
+ * bit for bit by its CPU reference.  The same seed and offset give the same
+ * bytes; change offset per call for fresh randoms.  Needs M < 2^32
+ * (NVFP4_ESHAPE otherwise).
+ */
+NVFP4_API nvfp4_status nvfp4_quantize_sr(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                               uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                               uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                               uint64_t seed, uint32_t offset, void* stream);
+
 /* One direction only (same as nvfp4_quantize with the other direction NULL). */
 NVFP4_API nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
                                     uint8_t* row_q, uint8_t* row_sf, float* row_amax,

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_quantize_rowwise",
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
-           "nvfp4_trace_encode", "nvfp4_quantize_calibrate")
+           "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -64,6 +64,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_amax_accumulate_reduce": (st, [p, p, i64, f32, p]),
         "nvfp4_trace_encode": (st, [p, p]),
         "nvfp4_quantize_calibrate": (st, [p, i64, i64, st, p, p, p, p, p, p, p, f32, p]),
+        "nvfp4_quantize_sr": (st, [p, i64, i64, st, p, p, p, p, p, p, ctypes.c_uint64, ctypes.c_uint32, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -126,6 +127,33 @@ def quantize(x: torch.Tensor, mode="per_token", rowwise: bool = True, columnwise
     _check(lib().nvfp4_quantize(_ptr(x), M, K, mode, _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
                                 _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")), _stream(dev)))
     return out
+
+
+def quantize_sr(x: torch.Tensor, mode="per_token", seed: int = 0, offset: int = 0, rowwise: bool = True,
+                columnwise: bool = True) -> dict:
+    """Whole cast with stochastic rounding of the element codes (per-tensor or
+    per-token scaling); the same seed and offset give the same bytes."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    dev = x.device
+    out = {}
+    if rowwise:
+        out.update(row_q=_u8((M, K // 2), dev), row_sf=_u8((M, K // 16), dev), row_amax=_f32(_amax_len(mode, M), dev))
+    if columnwise:
+        out.update(col_q=_u8((K, M // 2), dev), col_sf=_u8((K, M // 16), dev), col_amax=_f32(_amax_len(mode, K), dev))
+    quantize_sr_into(x, mode, seed, offset, **out)
+    return out
+
+
+def quantize_sr_into(x, mode, seed: int, offset: int, row_q=None, row_sf=None, row_amax=None, col_q=None,
+                     col_sf=None, col_amax=None):
+    """Stochastic-rounding cast into caller-provided buffers."""
+    x = _input(x)
+    M, K = x.shape
+    _check(lib().nvfp4_quantize_sr(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
+                                   _ptr(col_q), _ptr(col_sf), _ptr(col_amax), ctypes.c_uint64(seed & (2**64 - 1)),
+                                   ctypes.c_uint32(offset & 0xFFFFFFFF), _stream(x.device)))
 
 
 def quantize_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, col_sf=None, col_amax=None):

@@ -98,12 +98,22 @@ nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
 
 // cal_buf (may be null): buf[0] = max(buf[0] * decay, tensor amax), done by
 // the encoding kernel from the amax it has just read
+// stochastic rounding of the element codes (nvfp4_quantize_sr)
+struct Rounding {
+    bool stochastic;
+    uint64_t seed;
+    uint32_t offset;
+};
+
 nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode,
                            uint8_t* row_q, uint8_t* row_sf, float* row_amax,
                            uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream,
-                           float* cal_buf = nullptr, float decay = 0.0f) {
+                           float* cal_buf = nullptr, float decay = 0.0f,
+                           Rounding rounding = Rounding{false, 0, 0}) {
     if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN && mode != NVFP4_TILE_16x16)
         return fail(NVFP4_EINVAL, "unknown scaling mode %d", (int)mode);
+    if (rounding.stochastic && mode == NVFP4_TILE_16x16)
+        return fail(NVFP4_EINVAL, "stochastic rounding is offered for per-tensor and per-token scaling only");
     Dir r = direction("row", row_q, row_sf, row_amax);
     if (r.st != NVFP4_OK) return r.st;
     Dir c = direction("col", col_q, col_sf, col_amax);
@@ -111,6 +121,8 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (!r.want && !c.want) return fail(NVFP4_EINVAL, "no output direction requested");
     nvfp4_status s = check_shape(M, K, r.want, c.want, mode);
     if (s != NVFP4_OK) return s;
+    if (rounding.stochastic && M >= ((int64_t)1 << 32))
+        return fail(NVFP4_ESHAPE, "stochastic rounding needs M < 2^32 (M = %lld)", (long long)M);
     if (xv == nullptr && M > 0 && K > 0) return fail(NVFP4_EINVAL, "x is NULL");
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     const uint16_t* x = static_cast<const uint16_t*>(xv);
@@ -134,15 +146,24 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         if ((s = zero(ra, M, ca, K, st)) != NVFP4_OK) return s;
         if (M == 0 || K == 0) return ok();
         if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
-        if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                         nullptr, nullptr, gt, st, b, a, cal); })) != NVFP4_OK) return s;
-        return ok();
+        if (rounding.stochastic)
+            s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode_sr(ENC_TOKEN, r.want, c.want, x, M, K, ra, ca, row_q, row_sf,
+                                  col_q, col_sf, rounding.seed, rounding.offset, st, b, a); });
+        else
+            s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
+                                  nullptr, nullptr, gt, st, b, a, cal); });
+        return s != NVFP4_OK ? s : ok();
     }
     // per-tensor and 16x16 tiles: one tensor amax
     if ((s = zero(ra, ra ? (mode == NVFP4_TILE_16x16 ? M : 1) : 0, ca, ca ? (mode == NVFP4_TILE_16x16 ? K : 1) : 0, st)) != NVFP4_OK) return s;
     if (M == 0 || K == 0) return ok();
     if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, st), "amax")) != NVFP4_OK) return s;
     const int emode = mode == NVFP4_TILE_16x16 ? ENC_TILE : ENC_TENSOR;
+    if (rounding.stochastic) {
+        s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode_sr(ENC_TENSOR, r.want, c.want, x, M, K, ra, ca, row_q, row_sf,
+                              col_q, col_sf, rounding.seed, rounding.offset, st, b, a); });
+        return s != NVFP4_OK ? s : ok();
+    }
     if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
                                      emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st, b, a, cal); })) != NVFP4_OK)
         return s;
@@ -178,6 +199,14 @@ nvfp4_status nvfp4_quantize_calibrate(const void* x, int64_t M, int64_t K, nvfp4
     if (!aligned(buf, 4)) return fail(NVFP4_EALIGN, "buf must be 4-byte aligned");
     if (!(decay >= 0.0f && decay <= 1.0f)) return fail(NVFP4_EINVAL, "decay must lie in [0, 1]");
     return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream, buf, decay);
+}
+
+nvfp4_status nvfp4_quantize_sr(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                               uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                               uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                               uint64_t seed, uint32_t offset, void* stream) {
+    return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream, nullptr, 0.0f,
+                         Rounding{true, seed, offset});
 }
 
 nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,

@@ -32,6 +32,11 @@ hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const u
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, const Calib& cal = Calib{nullptr, nullptr, 0, 0.0f});
+// stochastic-rounding cast (mode ENC_TENSOR or ENC_TOKEN; amax computed before)
+hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int64_t M, int64_t K,
+                            const float* row_amax, const float* col_amax, uint8_t* row_q, uint8_t* row_sf,
+                            uint8_t* col_q, uint8_t* col_sf, uint64_t seed, uint32_t offset, hipStream_t st,
+                            hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
                           int amax_per_row, float* out, hipStream_t st);
 hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);

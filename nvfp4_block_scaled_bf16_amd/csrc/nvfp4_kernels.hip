@@ -921,6 +921,160 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     }
 }
 
+// ------------------------------------------------- stochastic rounding
+
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+// Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds of
+// the two-multiplier S-box on the counter words, the key advanced by the
+// two Weyl constants between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t h0 = __umulhi(0xD2511F53u, c0), l0 = 0xD2511F53u * c0;
+        const uint32_t h1 = __umulhi(0xCD9E8D57u, c2), l1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = l1;
+        c2 = n2;
+        c3 = l0;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// Stochastic E2M1 nibble of q with the 32-bit random rnd: x = |q| lies in
+// [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2 below 6) and
+// rounds up iff x - lo > U * d with U = (rnd >> 8) * 2^-24; both sides are
+// exact in binary32.  x >= 6 saturates; the sign bit of q is copied.
+__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t rnd) {
+    const uint32_t s = (__float_as_uint(q) >> 28) & 8u;
+    const float x = __builtin_fabsf(q);
+    if (x >= 6.0f) return s | 7u;
+    float lo, d;
+    uint32_t c;
+    if (x < 2.0f) {
+        c = (uint32_t)(2.0f * x);   // truncation: floor of a non-negative value
+        lo = 0.5f * (float)c;
+        d = 0.5f;
+    } else if (x < 4.0f) {
+        const bool three = x >= 3.0f;
+        lo = three ? 3.0f : 2.0f;
+        c = three ? 5u : 4u;
+        d = 1.0f;
+    } else {
+        lo = 4.0f;
+        c = 6u;
+        d = 2.0f;
+    }
+    const float u = (float)(rnd >> 8) * 0x1p-24f;
+    return s | (c + (x - lo > u * d ? 1u : 0u));
+}
+
+// Whether every lane's block of the wave can take the three-op quotient:
+// RN(a / r) for bf16 a when r lies in [2^-64, 2^64] (fact 1 of the device
+// arithmetic; |a| / r stays below 7 in a cast whose amax covers its data, so
+// |a| * RN(1/r) is far from 2^64).  Otherwise the IEEE division.
+__device__ __forceinline__ bool sr_fast(const BlockScale& bs) {
+    const bool in_range = bs.r >= 0x1p-64f && bs.r <= 0x1p64f;
+    return __builtin_amdgcn_ballot_w64(!in_range) == 0ull;
+}
+
+// Stochastic-rounding cast (per-tensor or per-token outer amax, computed
+// beforehand).  Block scales and element quotients are the exact IEEE ones of
+// the deterministic cast; element i of a vector (a row for rowwise output, a
+// column for columnwise output) draws word i % 4 of Philox block
+// (i / 4, vector, direction, offset) under key (k0, k1), direction 0 rowwise,
+// 1 columnwise.  A lane holds a 16-row x 8-column sub-block (as in the
+// deterministic cast); a workgroup covers 128 rows x 256 columns.  Requires
+// M < 2^32 (the vector index is one counter word).
+template <int MODE, bool ROW, bool COL>
+__global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                   const float* __restrict__ row_amax, const float* __restrict__ col_amax,
+                                                   uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_sf,
+                                                   uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,
+                                                   uint32_t k0, uint32_t k1, uint32_t offset) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rg = lane >> 5;
+    const uint32_t c0 = blockIdx.x * kEncCols + (lane & 31) * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * 128 + wave * 32 + 16 * rg;
+    const bool col_ok = c0 < K;
+    const int nrows = r0 >= M ? 0 : (M - r0 < 16 ? (int)(M - r0) : 16);
+    auto load_row = [&](int i) {
+        return (col_ok && i < nrows) ? *reinterpret_cast<const u32x4*>(x + (r0 + i) * K + c0) : u32x4{0u, 0u, 0u, 0u};
+    };
+    if (ROW) {
+        const float At = MODE == ENC_TENSOR ? row_amax[0] : 0.0f;
+        // rows one at a time (a rolled loop over a register array would put
+        // the array in scratch memory)
+#pragma unroll 1
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 vi = load_row(i);
+            uint32_t hw = rowmax_word(vi);
+            hw = pk_max_u16(hw, from_pair(hw));   // the lane pair's 16 columns
+            const float A = MODE == ENC_TENSOR ? At : (i < nrows ? row_amax[r0 + i] : 0.0f);
+            const BlockScale bs = block_scale(max_halves(hw), outer_scale(A));
+            const uint32_t vec = (uint32_t)(r0 + i);
+            const u32x4 ra = philox4x32_10(c0 >> 2, vec, 0u, offset, k0, k1);
+            const u32x4 rb = philox4x32_10((c0 >> 2) + 1u, vec, 0u, offset, k0, k1);
+            const uint32_t rnd[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+            uint32_t w = 0u;
+            if (sr_fast(bs)) {
+                const float y = rcp_rn(bs.r);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) w |= e2m1_sr(div_fast(elem(vi, k), bs.r, y), rnd[k]) << (4 * k);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) w |= e2m1_sr(quotient_exact(elem(vi, k), bs), rnd[k]) << (4 * k);
+            }
+            if (col_ok && i < nrows) {
+                *reinterpret_cast<uint32_t*>(row_q + (r0 + i) * (K / 2) + c0 / 2) = w;
+                if (!(lane & 1)) row_sf[(r0 + i) * (K / 16) + c0 / 16] = (uint8_t)bs.code;
+            }
+        }
+    }
+    if (COL) {
+        u32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = load_row(i);
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t e = (__float_as_uint(elem(v[i], j)) >> 16) & 0x7fffu;
+                m = e > m ? e : m;
+            }
+            const float A = MODE == ENC_TENSOR ? col_amax[0] : (col_ok ? col_amax[c0 + j] : 0.0f);
+            const BlockScale bs = block_scale(m, outer_scale(A));
+            const uint32_t vec = c0 + (uint32_t)j, g0 = (uint32_t)(r0 >> 2);
+            uint32_t rnd[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
+                rnd[4 * g] = r.x; rnd[4 * g + 1] = r.y; rnd[4 * g + 2] = r.z; rnd[4 * g + 3] = r.w;
+            }
+            uint32_t lohi[2] = {0u, 0u};
+            if (sr_fast(bs)) {
+                const float y = rcp_rn(bs.r);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    lohi[i >> 3] |= e2m1_sr(div_fast(elem(v[i], j), bs.r, y), rnd[i]) << (4 * (i & 7));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    lohi[i >> 3] |= e2m1_sr(quotient_exact(elem(v[i], j), bs), rnd[i]) << (4 * (i & 7));
+            }
+            if (col_ok && nrows == 16) {
+                *reinterpret_cast<u32x2*>(col_q + (int64_t)(c0 + j) * (M / 2) + r0 / 2) = u32x2{lohi[0], lohi[1]};
+                col_sf[(int64_t)(c0 + j) * (M / 16) + r0 / 16] = (uint8_t)bs.code;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- dequantize
 
 // one thread per 16-element block: out = (+/-) g * (decode(sf) * (A / 2688))
@@ -1051,6 +1205,28 @@ hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const u
         }
     }
 #undef NVFP4_ENC_ARGS
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int64_t M, int64_t K,
+                            const float* row_amax, const float* col_amax, uint8_t* row_q, uint8_t* row_sf,
+                            uint8_t* col_q, uint8_t* col_sf, uint64_t seed, uint32_t offset, hipStream_t st,
+                            hipEvent_t ev0, hipEvent_t ev1) {
+    if (M <= 0 || K <= 0 || (!row && !col)) return hipSuccess;
+    const dim3 grid(cdiv(K, kEncCols), cdiv(M, 128));
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#define NVFP4_SR_LAUNCH(MD, R, C) hipExtLaunchKernelGGL((k_encode_sr<MD, R, C>), grid, dim3(256), 0, st, ev0, ev1, 0, \
+                                                      x, M, K, row_amax, col_amax, row_q, row_sf, col_q, col_sf, k0, k1, offset)
+    if (mode == ENC_TOKEN) {
+        if (row && col) NVFP4_SR_LAUNCH(ENC_TOKEN, true, true);
+        else if (row) NVFP4_SR_LAUNCH(ENC_TOKEN, true, false);
+        else NVFP4_SR_LAUNCH(ENC_TOKEN, false, true);
+    } else {
+        if (row && col) NVFP4_SR_LAUNCH(ENC_TENSOR, true, true);
+        else if (row) NVFP4_SR_LAUNCH(ENC_TENSOR, true, false);
+        else NVFP4_SR_LAUNCH(ENC_TENSOR, false, true);
+    }
+#undef NVFP4_SR_LAUNCH
     return hipGetLastError();
 }
 

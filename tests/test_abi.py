@@ -103,6 +103,19 @@ def test_quantize_calibrate_validation():
     assert q(f, 16, 16, 1, None, None, None, None, None, None, f, ctypes.c_float(0.9), None) == EINVAL
 
 
+def test_quantize_sr_validation():
+    L = nv.lib()
+    f = P(FAKE)
+    q = L.nvfp4_quantize_sr
+    seed, off = ctypes.c_uint64(1), ctypes.c_uint32(0)
+    assert q(f, 16, 16, 2, f, f, f, None, None, None, seed, off, None) == EINVAL   # 16x16 tiles: not offered
+    assert b"stochastic" in L.nvfp4_last_error()
+    assert q(f, 1 << 32, 16, 1, f, f, f, None, None, None, seed, off, None) == ESHAPE   # vector index is 32-bit
+    assert q(f, 16, 24, 0, f, f, f, None, None, None, seed, off, None) == ESHAPE
+    assert q(f, 16, 16, 1, None, None, None, None, None, None, seed, off, None) == EINVAL
+    assert q(P(FAKE + 2), 16, 16, 1, f, f, f, None, None, None, seed, off, None) == EALIGN
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

@@ -318,6 +318,70 @@ def test_encode_tile_height_switch(oracle, M, mode):
     assert_bytes_equal(host(buf), expect, "decayed buffer")
 
 
+SR_SHAPES = [(16, 16), (48, 1040), (272, 528), (1072, 544), (2048, 48)]
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+@pytest.mark.parametrize("shape", SR_SHAPES)
+def test_sr_small_shapes(oracle, mode, shape):
+    M, K = shape
+    x = _x(M, K, 300 + M + K)
+    seed, offset = 0x9E3779B97F4A7C15 ^ (M * 131 + K), M + 3 * K
+    _announce(f"quantize_sr mode={mode} shape={shape}")
+    out = nv.quantize_sr(to_dev(x), mode, seed, offset)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_sr(x, mode, seed, offset))
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+def test_sr_one_direction(oracle, mode):
+    x = _x(37, 96, 12)
+    _announce(f"quantize_sr rowwise 37x96 mode={mode}")
+    out = nv.quantize_sr(to_dev(x), mode, 5, 6, rowwise=True, columnwise=False)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_sr(x, mode, 5, 6, rowwise=True, columnwise=False))
+    x = _x(48, 24, 13)
+    _announce(f"quantize_sr columnwise 48x24 mode={mode}")
+    out = nv.quantize_sr(to_dev(x), mode, 5, 6, rowwise=False, columnwise=True)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_sr(x, mode, 5, 6, rowwise=False, columnwise=True))
+
+
+def test_sr_crafted_edges(oracle):
+    x = _crafted()
+    for mode in (nv.PER_TENSOR, nv.PER_TOKEN):
+        _announce(f"quantize_sr crafted mode={mode}")
+        out = nv.quantize_sr(to_dev(x), mode, 123, 4)
+        torch.cuda.synchronize()
+        compare_cast(out, oracle.quantize_sr(x, mode, 123, 4))
+
+
+def test_sr_c2_full_and_offsets(oracle):
+    x = W.c2()
+    d = to_dev(x)
+    _announce("quantize_sr C2 4096x4096 per-token, offsets 0 and 1")
+    a = nv.quantize_sr(d, nv.PER_TOKEN, 2024, 0)
+    b = nv.quantize_sr(d, nv.PER_TOKEN, 2024, 0)
+    c = nv.quantize_sr(d, nv.PER_TOKEN, 2024, 1)
+    torch.cuda.synchronize()
+    compare_cast(a, oracle.quantize_sr(x, nv.PER_TOKEN, 2024, 0))
+    compare_cast(c, oracle.quantize_sr(x, nv.PER_TOKEN, 2024, 1))
+    for k in a:
+        assert torch.equal(a[k], b[k]), f"same seed and offset, different {k}"
+    assert not torch.equal(a["row_q"], c["row_q"]) and not torch.equal(a["col_q"], c["col_q"])
+    # the scales and amax do not depend on the randoms
+    for k in ("row_sf", "col_sf", "row_amax", "col_amax"):
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_sr_c3_per_token_full(oracle):
+    x = W.c3(1)
+    _announce("quantize_sr C3 16384x8192 per-token (full compare)")
+    out = nv.quantize_sr(to_dev(x), nv.PER_TOKEN, 77, 9)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_sr(x, nv.PER_TOKEN, 77, 9))
+
+
 def _sample_vectors(x, out, mode, rows, cols, oracle):
     xf = W.bf16_to_f32(x)
     if mode == nv.PER_TOKEN:

@@ -56,6 +56,8 @@ def _load():
                                           ctypes.c_uint32, ctypes.c_uint32]),
         "orc_quantize_sr": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_int, _p, _p, _p, _p, _p, _p,
                                            ctypes.c_uint64, ctypes.c_uint32]),
+        "orc_gemm_nvfp4": (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64,
+                                          _p, _p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -257,6 +259,29 @@ def quantize_sr(x, mode, seed, offset, rowwise=True, columnwise=True):
     if rc != 0:
         raise ValueError("oracle: shape or mode not supported by the stochastic-rounding cast")
     return out
+
+
+# ------------------------------------------------------------ GEMM consumer
+
+def gemm_nvfp4(a_q, a_sf, a_amax, b_q, b_sf, b_amax):
+    """out[m][n] = S_a S_b sum_k (gD)_a (gD)_b for NVFP4 operands A [M][K]
+    and B [N][K] (16-element blocks along K; amax per row or [1]).  Returns
+    (out, bound) in float64, bound = S_a S_b sum_k |term|."""
+    a_q, a_sf, b_q, b_sf = (np.ascontiguousarray(t, np.uint8) for t in (a_q, a_sf, b_q, b_sf))
+    a_amax = np.ascontiguousarray(a_amax, np.float32)
+    b_amax = np.ascontiguousarray(b_amax, np.float32)
+    M, K = a_q.shape[0], a_q.shape[1] * 2
+    N = b_q.shape[0]
+    if b_q.shape[1] * 2 != K or a_sf.shape != (M, K // 16) or b_sf.shape != (N, K // 16):
+        raise ValueError("operands must be [M][K/2] / [N][K/2] with [.][K/16] scales")
+    out = np.empty((M, N), np.float64)
+    bound = np.empty((M, N), np.float64)
+    rc = _load().orc_gemm_nvfp4(_ptr(a_q), _ptr(a_sf), _ptr(a_amax), int(a_amax.size == M and M > 1),
+                                _ptr(b_q), _ptr(b_sf), _ptr(b_amax), int(b_amax.size == N and N > 1),
+                                M, N, K, _ptr(out), _ptr(bound))
+    if rc != 0:
+        raise ValueError("oracle: K must be a multiple of 16")
+    return out, bound
 
 
 def quantize_grouped(x, counts, rowwise=True, columnwise=True):

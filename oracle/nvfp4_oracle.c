@@ -594,3 +594,51 @@ int orc_quantize_sr(const uint16_t* x, int64_t M, int64_t K, int mode,
     }
     return 0;
 }
+
+/* ------------------------------------------------------ GEMM consumer */
+
+/* The per-token recipe page's GEMM consumer ("Changes": a GEMM that rescales
+ * with the per-row / per-col outer-amax vectors inside its epilogue; the
+ * sequence diagram's nvfp4_cutlass_per_token_gemm(A_data, A_sf, A_row_amax,
+ * B_data, B_sf, B_col_amax) -> output (M, N)), written for two NVFP4
+ * operands whose 16-element blocks run along the contraction dimension K:
+ *   out[m][n] = S_a(m) * S_b(n) * sum_k (g_a * D_a)[m][k] * (g_b * D_b)[n][k]
+ * with g the E2M1 value, D the decoded E4M3 block scale and S = RN(amax /
+ * 2688), per row (per_row = 1) or one per tensor.  The forward (TN), dgrad
+ * (NN) and wgrad (NT) products of the page are this form applied to the
+ * rowwise or columnwise output of the cast.  Computed here in binary64:
+ * each product of block values is exact, the sum over K rounds at most
+ * once per term at 2^-53, then the two outer scales.  bound[m][n] (may be
+ * NULL) receives S_a * S_b * sum_k |term|, the magnitude error bounds of a
+ * binary32 evaluation scale with. */
+static double deq_block_value(const uint8_t* q, const uint8_t* sf, int64_t row, int64_t K, int64_t k)
+{
+    uint8_t byte = q[row * (K / 2) + k / 2];
+    uint8_t nib = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    return (double)orc_e2m1_decode(nib) * (double)orc_e4m3_decode(sf[row * (K / 16) + k / 16]);
+}
+
+int orc_gemm_nvfp4(const uint8_t* aq, const uint8_t* asf, const float* aamax, int a_per_row,
+                   const uint8_t* bq, const uint8_t* bsf, const float* bamax, int b_per_row,
+                   int64_t M, int64_t N, int64_t K, double* out, double* bound)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return -1;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) a[k] = deq_block_value(aq, asf, m, K, k);
+        double sa = (double)(aamax[a_per_row ? m : 0] / kOuterDiv);
+        for (int64_t n = 0; n < N; ++n) {
+            double sb = (double)(bamax[b_per_row ? n : 0] / kOuterDiv);
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double t = a[k] * deq_block_value(bq, bsf, n, K, k);
+                acc += t;
+                mag += fabs(t);
+            }
+            out[m * N + n] = acc * sa * sb;
+            if (bound) bound[m * N + n] = mag * sa * sb;
+        }
+    }
+    free(a);
+    return 0;
+}

@@ -98,6 +98,13 @@ int     orc_quantize_sr(const uint16_t* x, int64_t M, int64_t K, int mode,
                         uint8_t* col_q, uint8_t* col_sf, float* col_amax,
                         uint64_t seed, uint32_t offset);
 
+
+/* GEMM consumer: out[m][n] = S_a(m) S_b(n) sum_k (gD)_a[m][k] (gD)_b[n][k] in
+ * binary64 (definition in nvfp4_oracle.c); bound may be NULL */
+int orc_gemm_nvfp4(const uint8_t* aq, const uint8_t* asf, const float* aamax, int a_per_row,
+                   const uint8_t* bq, const uint8_t* bsf, const float* bamax, int b_per_row,
+                   int64_t M, int64_t N, int64_t K, double* out, double* bound);
+
 #ifdef __cplusplus
 }
 #endif

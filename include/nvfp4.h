@@ -216,6 +216,29 @@ NVFP4_API nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, con
                               void* stream);
 
 /*
+ * NVFP4 GEMM consumer: the GEMM of the per-token recipe page (TransformerEngine
+ * PR #3045, Changes and the sequence diagram's TN forward product) that
+ * rescales with the per-row / per-column outer amax vectors in its epilogue.
+ * A and B are NVFP4 with 16-element blocks along K: a_q [M][K/2], a_sf
+ * [M][K/16], a_amax [M] (a_per_row != 0) or [1]; likewise b_* with N rows.
+ *   out[m][n] = S_a(m) * S_b(n) * sum_k (g * D)_a[m][k] * (g * D)_b[n][k]
+ * with g the E2M1 value, D the decoded block scale, S = amax / 2688 (as in the
+ * cast), out fp32 row-major [M][N], written in full (zeros when K == 0).  The
+ * page's forward (TN: x rowwise, W rowwise), dgrad (NN: dY rowwise, W
+ * columnwise) and wgrad (NT: dY columnwise, x columnwise) products are this
+ * call on the cast's outputs.  The sum runs in fp32 on bf16 matrix cores (the
+ * block values g * D are exact in bf16); against the exact value the error is
+ * within (K + 2) * 2^-24 * S_a * S_b * sum_k |term|.  K % 16 == 0 (ESHAPE);
+ * a_q, b_q 16-byte aligned, amax and out 4-byte aligned (EALIGN); at most
+ * 2^31 - 1 output tiles of 128 x 128, cdiv(M, 128) * cdiv(N, 128) (ESHAPE).
+ * M == 0 or N == 0 does nothing; negative sizes or NULL pointers (the
+ * operands may be NULL only when K == 0) give EINVAL.  Nothing is allocated.
+ */
+NVFP4_API nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                        const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                        int64_t M, int64_t N, int64_t K, float* out, void* stream);
+
+/*
  * Decayed calibration accumulator from the PTQ scaling-factor page
  * (TransformerEngine PR #3296, Description): buf[i] = max(buf[i] * decay,
  * observed[i]) for i < n, in fp32.  decay 0 keeps the latest value, decay 1

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_quantize_rowwise",
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
-           "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr")
+           "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_trace_encode": (st, [p, p]),
         "nvfp4_quantize_calibrate": (st, [p, i64, i64, st, p, p, p, p, p, p, p, f32, p]),
         "nvfp4_quantize_sr": (st, [p, i64, i64, st, p, p, p, p, p, p, ctypes.c_uint64, ctypes.c_uint32, p]),
+        "nvfp4_gemm": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -250,6 +251,35 @@ def dequantize(q, sf, amax, amax_per_row: bool):
     _check(lib().nvfp4_dequantize(_ptr(q), _ptr(sf), _ptr(amax), R, C, int(bool(amax_per_row)), _ptr(out),
                                   _stream(q.device)))
     return out
+
+
+def _operand(q, sf, amax, name):
+    if q.dim() != 2 or q.dtype != torch.uint8:
+        raise ValueError(f"{name}_q must be a 2-D uint8 tensor [rows, K/2]")
+    rows, K = q.shape[0], 2 * q.shape[1]
+    if sf.numel() != rows * (K // 16) or amax.numel() not in (1, rows):
+        raise ValueError(f"{name}_sf must hold rows*K/16 codes and {name}_amax 1 or rows values")
+    return rows, K, int(amax.numel() == rows and rows != 1)
+
+
+def gemm_into(out, a_q, a_sf, a_amax, b_q, b_sf, b_amax):
+    """out [M, N] fp32 = S_a(m) S_b(n) sum_k (g D)_a[m][k] (g D)_b[n][k] for
+    NVFP4 operands a_q [M, K/2] / a_sf [M, K/16] and b_q [N, K/2] / b_sf
+    [N, K/16]; each amax is one value (per tensor) or one per row."""
+    M, K, apr = _operand(a_q, a_sf, a_amax, "a")
+    N, Kb, bpr = _operand(b_q, b_sf, b_amax, "b")
+    if K != Kb:
+        raise ValueError(f"contraction sizes differ: {K} vs {Kb}")
+    if tuple(out.shape) != (M, N) or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [M, N]")
+    _check(lib().nvfp4_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_amax), apr, _ptr(b_q), _ptr(b_sf), _ptr(b_amax), bpr,
+                            M, N, K, _ptr(out), _stream(a_q.device)))
+    return out
+
+
+def gemm(a_q, a_sf, a_amax, b_q, b_sf, b_amax):
+    """Allocate out and run :func:`gemm_into`."""
+    return gemm_into(_f32((a_q.shape[0], b_q.shape[0]), a_q.device), a_q, a_sf, a_amax, b_q, b_sf, b_amax)
 
 
 def amax_accumulate(buf, observed, decay: float):

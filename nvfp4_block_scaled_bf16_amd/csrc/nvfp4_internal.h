@@ -37,6 +37,13 @@ hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int
                             const float* row_amax, const float* col_amax, uint8_t* row_q, uint8_t* row_sf,
                             uint8_t* col_q, uint8_t* col_sf, uint64_t seed, uint32_t offset, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1);
+// NVFP4 GEMM consumer (nvfp4_gemm.hip): out [M][N] fp32, one workgroup per
+// 128 x 128 output tile, at most kMaxGemmTiles of them
+constexpr int64_t kMaxGemmTiles = (int64_t(1) << 31) - 1;
+hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                             const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                             int64_t M, int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0,
+                             hipEvent_t ev1);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
                           int amax_per_row, float* out, hipStream_t st);
 hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);

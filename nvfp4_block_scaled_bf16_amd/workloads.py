@@ -139,6 +139,19 @@ def moe_batch(seed: int, K: int = 4096, experts: int = 64, chunks: int = 256,
     return bf16_from_f32(z), counts
 
 
+def nvfp4_operand(rows: int, K: int, seed: int, per_row: bool = True):
+    """Random NVFP4 operand bytes for the GEMM consumer: q [rows][K/2] with
+    every nibble uniform over the 16 codes, sf [rows][K/16] uniform over the
+    finite E4M3 codes 0x00..0x7E, amax ([rows] or [1]) log-uniform over
+    [2^-4, 2^12].  Raw codes, not a cast of any tensor: they span the whole
+    range of block scales (subnormal to 448) and element values."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    q = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    sf = rng.integers(0, 0x7F, size=(rows, K // 16), dtype=np.uint8)
+    amax = np.exp2(rng.uniform(-4.0, 12.0, size=rows if per_row else 1)).astype(np.float32)
+    return q, sf, amax
+
+
 # ------------------------------------------------------------ named configs
 
 def c1():

@@ -116,6 +116,20 @@ def test_quantize_sr_validation():
     assert q(P(FAKE + 2), 16, 16, 1, f, f, f, None, None, None, seed, off, None) == EALIGN
 
 
+def test_gemm_validation():
+    L = nv.lib()
+    f, g = P(FAKE), L.nvfp4_gemm
+    assert g(f, f, f, 1, f, f, f, 1, -1, 16, 16, f, None) == EINVAL
+    assert g(f, f, f, 1, f, f, f, 1, 16, 16, 24, f, None) == ESHAPE   # K % 16
+    assert b"K % 16" in L.nvfp4_last_error()
+    assert g(f, f, f, 1, f, f, f, 1, 1 << 40, 1 << 40, 16, f, None) == ESHAPE   # tile count
+    assert g(None, None, None, 1, None, None, None, 1, 0, 16, 16, None, None) == 0   # M == 0: nothing
+    assert g(None, f, f, 1, f, f, f, 1, 16, 16, 16, f, None) == EINVAL
+    assert g(None, None, f, 1, None, None, f, 1, 16, 16, 0, None, None) == EINVAL   # out NULL
+    assert g(P(FAKE + 8), f, f, 1, f, f, f, 1, 16, 16, 16, f, None) == EALIGN
+    assert g(f, f, f, 1, f, f, f, 1, 16, 16, 16, P(FAKE + 2), None) == EALIGN
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

@@ -1,0 +1,150 @@
+"""GPU parity of the NVFP4 GEMM consumer against the CPU oracle.
+
+The kernel sums exact block-value products in fp32 on bf16 matrix cores and
+then applies the two outer scales in fp32; the oracle sums in binary64.  The
+tolerance follows from that arithmetic: every fp32 addition and the two scale
+multiplications round once, each by at most 2^-24 of a magnitude no larger
+than S_a S_b sum_k |term| (the oracle's ``bound``), so
+    |gpu - exact| <= (K + 2) * 2^-24 * bound  (+ 2^-126 for fp32 underflow).
+Where every partial sum is exactly representable (unit scales, E2M1 values)
+the result must be bit-exact.  Operands come from the oracle's own cast of
+the seeded workload tensors, or are raw seeded codes spanning every block
+scale; nothing the oracle reads comes from the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_bf16_amd as nv
+from nvfp4_block_scaled_bf16_amd import workloads as W
+from tests.gpu_util import host
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _dev(*arrays):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0") for a in arrays]
+
+
+def _run(aq, asf, aa, bq, bsf, ba):
+    out = nv.gemm(*_dev(aq, asf, aa, bq, bsf, ba))
+    torch.cuda.synchronize()
+    return host(out).astype(np.float64)
+
+
+def _check(got, ref, bound, K, name):
+    tol = (K + 2) * 2.0 ** -24 * bound + 2.0 ** -126
+    err = np.abs(got - ref)
+    bad = np.nonzero(err > tol)
+    assert not bad[0].size, (f"{name}: {bad[0].size} of {got.size} outside tolerance; first at "
+                             f"{bad[0][0], bad[1][0]}: got {got[bad][0]!r} expected {ref[bad][0]!r} "
+                             f"tol {tol[bad][0]!r}")
+
+
+def _cast_operand(rows, K, seed, per_row, oracle):
+    x = W.row_scaled_with_outliers(rows, K, seed)
+    o = oracle.quantize(x, oracle.PER_TOKEN if per_row else oracle.PER_TENSOR, columnwise=False)
+    return o["row_q"], o["row_sf"], o["row_amax"]
+
+
+# several 128 x 128 tiles with ragged edges; K with a partial 64-step
+SHAPES = [(1, 1, 16), (16, 16, 16), (130, 200, 272), (256, 128, 64), (300, 520, 1040), (128, 384, 4096),
+          (64, 1000, 48)]
+
+
+@pytest.mark.parametrize("per_row", [(True, True), (True, False), (False, True), (False, False)])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm_cast_operands(oracle, shape, per_row):
+    M, N, K = shape
+    _announce(f"gemm cast operands M={M} N={N} K={K} per_row={per_row}")
+    a = _cast_operand(M, K, 11, per_row[0], oracle)
+    b = _cast_operand(N, K, 12, per_row[1], oracle)
+    ref, bound = oracle.gemm_nvfp4(*a, *b)
+    _check(_run(*a, *b), ref, bound, K, "out")
+
+
+@pytest.mark.parametrize("shape", [(96, 136, 160), (257, 129, 528)])
+def test_gemm_raw_codes_every_scale(oracle, shape):
+    M, N, K = shape
+    _announce(f"gemm raw codes M={M} N={N} K={K}")
+    a = W.nvfp4_operand(M, K, 21)
+    b = W.nvfp4_operand(N, K, 22, per_row=False)
+    ref, bound = oracle.gemm_nvfp4(*a, *b)
+    _check(_run(*a, *b), ref, bound, K, "out")
+
+
+def test_gemm_exact_when_sums_representable(oracle):
+    # unit block scales (E4M3 0x38 = 1.0) and amax = 2688 (S = 1): every
+    # product is a multiple of 1/4 below 36 and every partial sum is exact
+    M, N, K = 200, 144, 1024
+    _announce(f"gemm exact M={M} N={N} K={K}")
+    rng = np.random.Generator(np.random.PCG64(31))
+    aq = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    bq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    asf = np.full((M, K // 16), 0x38, np.uint8)
+    bsf = np.full((N, K // 16), 0x38, np.uint8)
+    aa = np.full(M, 2688.0, np.float32)
+    ba = np.full(1, 2688.0, np.float32)
+    ref, _ = oracle.gemm_nvfp4(aq, asf, aa, bq, bsf, ba)
+    got = _run(aq, asf, aa, bq, bsf, ba)
+    assert np.array_equal(got, ref)
+
+
+def test_gemm_k_zero_and_empty():
+    _announce("gemm K=0 / M=0")
+    a = [np.zeros((5, 0), np.uint8), np.zeros((5, 0), np.uint8), np.ones(5, np.float32)]
+    b = [np.zeros((7, 0), np.uint8), np.zeros((7, 0), np.uint8), np.ones(1, np.float32)]
+    out = torch.full((5, 7), 3.0, dtype=torch.float32, device="cuda:0")
+    nv.gemm_into(out, *_dev(*a), *_dev(*b))
+    torch.cuda.synchronize()
+    assert not host(out).any()
+    e = nv.gemm(*_dev(np.zeros((0, 8), np.uint8), np.zeros((0, 1), np.uint8), np.ones(1, np.float32)),
+                *_dev(*W.nvfp4_operand(4, 16, 1)))
+    torch.cuda.synchronize()
+    assert tuple(e.shape) == (0, 4)
+
+
+def test_gemm_training_products(oracle):
+    # forward Y = X W^T (TN), dgrad dX = dY W (NN: W columnwise), wgrad
+    # dW = dY^T X (NT: dY and X columnwise), all from per-token casts
+    T, K, N = 256, 192, 320
+    _announce(f"gemm TN/NN/NT T={T} K={K} N={N}")
+    X = W.row_scaled_with_outliers(T, K, 41)
+    Wt = W.weight_with_outliers(N, K, 42)
+    dY = W.row_scaled_with_outliers(T, N, 43)
+    qx = oracle.quantize(X, oracle.PER_TOKEN)
+    qw = oracle.quantize(Wt, oracle.PER_TOKEN)
+    qd = oracle.quantize(dY, oracle.PER_TOKEN)
+
+    def row(o):
+        return o["row_q"], o["row_sf"], o["row_amax"]
+
+    def col(o, R, C):   # columnwise output of an R x C tensor: C vectors of R
+        return o["col_q"].reshape(C, R // 2), o["col_sf"].reshape(C, R // 16), o["col_amax"]
+
+    for name, a, b, kk in (("TN", row(qx), row(qw), K), ("NN", row(qd), col(qw, N, K), N),
+                           ("NT", col(qd, T, N), col(qx, T, K), T)):
+        ref, bound = oracle.gemm_nvfp4(*a, *b)
+        _check(_run(*a, *b), ref, bound, kk, name)
+
+
+def test_gemm_full_size_sampled(oracle):
+    # the forward product of the 16384 x 8192 activation with an 8192 x 8192
+    # weight, in the launch configuration the benchmark times; the oracle
+    # computes sampled 64 x 64 blocks (corners, the middle, a random block)
+    M, N, K = 16384, 8192, 8192
+    _announce(f"gemm full size M={M} N={N} K={K} (sampled)")
+    a = W.nvfp4_operand(M, K, 51)
+    b = W.nvfp4_operand(N, K, 52)
+    out = host(nv.gemm(*_dev(*a), *_dev(*b)))
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(53))
+    for r0, c0 in ((0, 0), (M - 64, N - 64), (M // 2 - 32, N // 2 - 32),
+                   (int(rng.integers(0, M - 64)), int(rng.integers(0, N - 64)))):
+        rs, cs = slice(r0, r0 + 64), slice(c0, c0 + 64)
+        ref, bound = oracle.gemm_nvfp4(a[0][rs], a[1][rs], a[2][rs], b[0][cs], b[1][cs], b[2][cs])
+        _check(out[rs, cs].astype(np.float64), ref, bound, K, f"block ({r0},{c0})")

@@ -226,11 +226,12 @@ NVFP4_API nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, con
  * cast), out fp32 row-major [M][N], written in full (zeros when K == 0).  The
  * page's forward (TN: x rowwise, W rowwise), dgrad (NN: dY rowwise, W
  * columnwise) and wgrad (NT: dY columnwise, x columnwise) products are this
- * call on the cast's outputs.  The sum runs in fp32 on bf16 matrix cores (the
- * block values g * D are exact in bf16); against the exact value the error is
+ * call on the cast's outputs.  The sum runs in fp32 on fp16 matrix cores (the
+ * block values g * D are exact in fp16); against the exact value the error is
  * within (K + 2) * 2^-24 * S_a * S_b * sum_k |term|.  K % 16 == 0 (ESHAPE);
- * a_q, b_q 16-byte aligned, amax and out 4-byte aligned (EALIGN); at most
- * 2^31 - 1 output tiles of 128 x 128, cdiv(M, 128) * cdiv(N, 128) (ESHAPE).
+ * K <= 2^23 (ESHAPE); a_q, b_q 16-byte aligned, amax and out 4-byte aligned
+ * (EALIGN); at most 2^31 - 1 output tiles of 128 x 128, cdiv(M, 128) *
+ * cdiv(N, 128) (ESHAPE).
  * M == 0 or N == 0 does nothing; negative sizes or NULL pointers (the
  * operands may be NULL only when K == 0) give EINVAL.  Nothing is allocated.
  */

@@ -343,6 +343,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_
                         int64_t M, int64_t N, int64_t K, float* out, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "negative size");
     if (K % 16 != 0) return fail(NVFP4_ESHAPE, "gemm needs K %% 16 == 0 (K=%lld)", (long long)K);
+    if (K > kMaxGemmK) return fail(NVFP4_ESHAPE, "gemm needs K <= %lld (K=%lld)", (long long)kMaxGemmK, (long long)K);
     if (M > 0 && N > 0 && (M > kMaxGemmTiles || N > kMaxGemmTiles || ((M + 127) / 128) * ((N + 127) / 128) > kMaxGemmTiles))
         return fail(NVFP4_ESHAPE, "gemm needs cdiv(M, 128) * cdiv(N, 128) < 2^31 output tiles");
     if (M == 0 || N == 0) return ok();

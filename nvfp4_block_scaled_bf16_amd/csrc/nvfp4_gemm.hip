@@ -7,12 +7,19 @@
 //   out[m][n] = S_a(m) * S_b(n) * sum_k (g * D)_a[m][k] * (g * D)_b[n][k]
 // with g the E2M1 value, D the decoded E4M3 block scale and S = amax / 2688.
 //
-// g * D has at most 6 significant bits, so it is exact in bf16: each K step
-// dequantizes the operands' FP4 bytes into bf16 tiles in LDS and the
-// contraction runs on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32
-// accumulation; the outer scales multiply the accumulators in the epilogue.
-// (gfx950's scaled FP4 MFMA takes one power-of-two scale per 32 elements and
-// cannot carry an E4M3 scale per 16.)
+// g * D has at most 6 significant bits and lies in [2^-10, 2688], so it is
+// exact in fp16: each K step dequantizes the operands' FP4 bytes (hardware
+// FP4 -> fp16 conversion, then one packed fp16 multiply by D per pair) into
+// fp16 tiles in LDS, and the contraction runs on fp16 MFMA
+// (v_mfma_f32_32x32x16_f16, same rate as bf16) with fp32 accumulation; the
+// outer scales multiply the accumulators in the epilogue.  (gfx950's scaled
+// FP4 MFMA takes one power-of-two scale per 32 elements and cannot carry an
+// E4M3 scale per 16; E4M3 * E2M1 products need up to 6 significant bits, more
+// than any 8-bit format holds.)
+//
+// Every output element sees the same sequence of MFMAs (K in 16-wide chunks,
+// in order) whatever the tile shape, so the result does not depend on the
+// tile configuration chosen.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,18 +30,24 @@
 namespace nvfp4 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTileM = 128, kTileN = 128;   // output tile per workgroup (4 waves, 2 x 2, 64 x 64 each)
 constexpr int kStepK = 64;                  // K per pipeline step: 4 scale blocks
-constexpr int kPitch = kStepK + 8;          // bf16 per LDS tile row (padding spreads the rows over the banks)
+constexpr int kPitch = kStepK + 8;          // fp16 per LDS tile row (padding spreads the rows over the banks)
 
-// E4M3 code -> value (exact): subnormals m * 2^-9, else exponent + 120 in fp32
-__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
-    return code < 8u ? (float)code * 0.001953125f : __uint_as_float((code << 20) + 0x3C000000u);
+// E4M3 code -> value (exact): the code's bits placed in an fp32 exponent and
+// mantissa field are the value times 2^-120 (subnormal codes become fp32
+// subnormals, which this code keeps)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __uint_as_float(code << 20) * 0x1p120f; }
+
+// buffer descriptor over `bytes` bytes at base; loads at offsets past the end
+// return zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+constexpr uint32_t kOob = 0x80000000u;   // an offset past every descriptor's end
 
 // One thread's share of a K step for one operand: 32 consecutive elements
 // (two scale blocks) of one row.  Rows past the end and blocks past K read
@@ -44,113 +57,135 @@ struct RowPiece {
     uint32_t sf;        // two scale codes: low byte, next byte
 };
 
-__device__ __forceinline__ RowPiece load_piece(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sf,
-                                               int64_t row, int64_t rows, int64_t K, int64_t k0) {
-    RowPiece p{{0u, 0u, 0u, 0u}, 0u};
-    if (row < rows) {
-        const uint8_t* qr = q + row * (K / 2);
-        const uint8_t* sr = sf + row * (K / 16);
-        if (k0 < K) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(qr + k0 / 2);
-            p.q[0] = lo.x;
-            p.q[1] = lo.y;
-            p.sf = sr[k0 / 16];
-        }
-        if (k0 + 16 < K) {
-            const uint2 hi = *reinterpret_cast<const uint2*>(qr + k0 / 2 + 8);
-            p.q[2] = hi.x;
-            p.q[3] = hi.y;
-            p.sf |= (uint32_t)sr[k0 / 16 + 1] << 8;
-        }
-    }
-    return p;
+// row: the row within the operand tile (descriptors q_rs / s_rs start at the
+// tile's first row and end after its last valid row); k0 % 32 == 0
+__device__ __forceinline__ RowPiece load_piece(__amdgpu_buffer_rsrc_t q_rs, __amdgpu_buffer_rsrc_t s_rs, uint32_t row,
+                                               uint32_t K, uint32_t k0) {
+    const uint32_t off = row * (K / 2) + k0 / 2, soff = row * (K / 16) + k0 / 16;
+    const bool lo_ok = k0 < K, hi_ok = k0 + 16 < K;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(q_rs, lo_ok ? off : kOob, 0, 0);
+    const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(q_rs, hi_ok ? off + 8 : kOob, 0, 0);
+    const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b8(s_rs, lo_ok ? soff : kOob, 0, 0);
+    const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b8(s_rs, hi_ok ? soff + 1 : kOob, 0, 0);
+    return RowPiece{{lo.x, lo.y, hi.x, hi.y}, s0 | (s1 << 8)};
 }
 
-// dequantize a piece into 32 bf16 (g * D, exact) and store it to LDS
-__device__ __forceinline__ void store_piece(const RowPiece& p, __bf16* dst) {
-    const float d0 = e4m3_to_f32(p.sf & 0xffu), d1 = e4m3_to_f32(p.sf >> 8);
-    bf16x8 out[4];
+// dequantize a piece into 32 fp16 (g * D, exact) and store it to LDS
+__device__ __forceinline__ void store_piece(const RowPiece& p, _Float16* dst) {
+    const _Float16 d0 = (_Float16)e4m3_to_f32(p.sf & 0xffu), d1 = (_Float16)e4m3_to_f32(p.sf >> 8);
+    f16x8 out[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const float d = w < 2 ? d0 : d1;
+        const f16x2 d = w < 2 ? f16x2{d0, d0} : f16x2{d1, d1};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             // byte b of word w: elements 8w + 2b (low nibble) and 8w + 2b + 1;
-            // the conversion with scale 1.0 gives the E2M1 values exactly
-            f32x2 g;
-            if (b == 0) g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.q[w], 1.0f, 0);
-            else if (b == 1) g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.q[w], 1.0f, 1);
-            else if (b == 2) g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.q[w], 1.0f, 2);
-            else g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.q[w], 1.0f, 3);
-            out[w][2 * b] = (__bf16)(g.x * d);
-            out[w][2 * b + 1] = (__bf16)(g.y * d);
+            // the conversion with scale 1.0 gives the E2M1 values exactly and
+            // the packed product with D is exact in fp16
+            f16x2 g;
+            if (b == 0) g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p.q[w], 1.0f, 0);
+            else if (b == 1) g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p.q[w], 1.0f, 1);
+            else if (b == 2) g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p.q[w], 1.0f, 2);
+            else g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p.q[w], 1.0f, 3);
+            const f16x2 v = g * d;
+            out[w][2 * b] = v.x;
+            out[w][2 * b + 1] = v.y;
         }
     }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) *reinterpret_cast<bf16x8*>(dst + 8 * w) = out[w];
+    for (int w = 0; w < 4; ++w) *reinterpret_cast<f16x8*>(dst + 8 * w) = out[w];
 }
 
-// Grid: cdiv(M, 128) * cdiv(N, 128) workgroups (one dimension), 256 threads;
-// ntn = cdiv(N, 128).  Thread t loads row t / 2, elements 32 * (t % 2) .. + 31
-// of each K step for both operands.
-__global__ __launch_bounds__(256) void k_gemm_nvfp4(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf,
-                                                    const float* __restrict__ a_amax, int a_per_row,
-                                                    const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
-                                                    const float* __restrict__ b_amax, int b_per_row,
-                                                    int64_t M, int64_t N, int64_t K, uint32_t ntn,
-                                                    float* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) __bf16 As[2][kTileM * kPitch];
-    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][kTileN * kPitch];
+// One workgroup computes a TM x TN output tile with WM x WN waves, each wave
+// a (TM / WM) x (TN / WN) block of 32 x 32 MFMA tiles.  LDS holds the tile's
+// TM rows of A then TN rows of B, kStepK fp16 values each, double buffered.
+// Each K step a row is loaded as two 32-element pieces; piece p (p = t + NT i
+// for thread t, i < P) is row p / 2, half p % 2, so each i is all-A or all-B.
+// Grid: cdiv(M, TM) * cdiv(N, TN) workgroups (one dimension); ntn = cdiv(N, TN).
+template <int TM, int TN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4(
+    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
+    int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
+    const float* __restrict__ b_amax, int b_per_row, int64_t M, int64_t N, int64_t K, uint32_t ntn,
+    float* __restrict__ out) {
+    constexpr int NT = 64 * WM * WN, ROWS = TM + TN, P = 2 * ROWS / NT;
+    constexpr int FM = TM / WM / 32, FN = TN / WN / 32;
+    static_assert(2 * ROWS % NT == 0 && 2 * TM % NT == 0 && FM >= 1 && FN >= 1, "tile shape");
+    __shared__ __attribute__((aligned(16))) _Float16 S[2][ROWS * kPitch];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;   // the wave's 64 x 64 quarter
+    const int wm = wave / WN, wn = wave % WN;
     // XCD-aware order: each of the 8 XCDs (own L2) takes a contiguous run of
     // tiles, row band major, so a band of A is reused from one L2
     const uint32_t ntiles = gridDim.x, lin = blockIdx.x;
     const uint32_t tile = (ntiles & 7u) == 0u ? (lin & 7u) * (ntiles >> 3) + (lin >> 3) : lin;
-    const int64_t m0 = (int64_t)(tile / ntn) * kTileM, n0 = (int64_t)(tile % ntn) * kTileN;
-    const int lr = t >> 1, lh = t & 1;   // load row, half
+    const int64_t m0 = (int64_t)(tile / ntn) * TM, n0 = (int64_t)(tile % ntn) * TN;
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int64_t nk = (K + kStepK - 1) / kStepK;
-    RowPiece pa = load_piece(a_q, a_sf, m0 + lr, M, K, 32 * lh);
-    RowPiece pb = load_piece(b_q, b_sf, n0 + lr, N, K, 32 * lh);
-    store_piece(pa, &As[0][lr * kPitch + 32 * lh]);
-    store_piece(pb, &Bs[0][lr * kPitch + 32 * lh]);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int buf = (int)(kt & 1);
-        const bool more = kt + 1 < nk;
-        if (more) {   // the next step's bytes, in flight during this step's MFMAs
-            pa = load_piece(a_q, a_sf, m0 + lr, M, K, (kt + 1) * kStepK + 32 * lh);
-            pb = load_piece(b_q, b_sf, n0 + lr, N, K, (kt + 1) * kStepK + 32 * lh);
+    // descriptors over the tile's valid rows of each operand
+    const uint32_t va = (uint32_t)(M - m0 < TM ? M - m0 : TM), vb = (uint32_t)(N - n0 < TN ? N - n0 : TN);
+    const uint32_t Ku = (uint32_t)K;
+    const __amdgpu_buffer_rsrc_t aq_rs = gemm_rsrc(a_q + m0 * (K / 2), va * (Ku / 2));
+    const __amdgpu_buffer_rsrc_t as_rs = gemm_rsrc(a_sf + m0 * (K / 16), va * (Ku / 16));
+    const __amdgpu_buffer_rsrc_t bq_rs = gemm_rsrc(b_q + n0 * (K / 2), vb * (Ku / 2));
+    const __amdgpu_buffer_rsrc_t bs_rs = gemm_rsrc(b_sf + n0 * (K / 16), vb * (Ku / 16));
+
+    // pc: bytes of the next K step (dequantized into LDS during this step);
+    // pn: the step after, loaded a whole step ahead of its use
+    RowPiece pc[P], pn[P];
+    auto load_all = [&](RowPiece* dst, uint32_t kbase) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int p = t + NT * i, r = p >> 1;
+            const uint32_t k0 = kbase + 32 * (p & 1);
+            if ((NT * i) / 2 < TM) dst[i] = load_piece(aq_rs, as_rs, (uint32_t)r, Ku, k0);
+            else dst[i] = load_piece(bq_rs, bs_rs, (uint32_t)(r - TM), Ku, k0);
         }
-        const __bf16* as = As[buf];
-        const __bf16* bs = Bs[buf];
+    };
+    auto store_all = [&](const RowPiece* src, int buf) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int p = t + NT * i;
+            store_piece(src[i], &S[buf][(p >> 1) * kPitch + 32 * (p & 1)]);
+        }
+    };
+
+    const uint32_t nk = (Ku + kStepK - 1) / kStepK;
+    load_all(pc, 0);
+    store_all(pc, 0);
+    load_all(pc, kStepK);
+    __syncthreads();
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+        const int buf = (int)(kt & 1);
+        // loads past K read zeros; the buffer written in the last steps is
+        // never read
+        load_all(pn, (kt + 2) * kStepK);
+        const _Float16* as = S[buf] + (wm * (TM / WM)) * kPitch;
+        const _Float16* bs = S[buf] + (TM + wn * (TN / WN)) * kPitch;
 #pragma unroll
         for (int kc = 0; kc < kStepK / 16; ++kc) {
             const int kk = 16 * kc + 8 * (lane >> 5);
-            bf16x8 fa[2], fb[2];
+            f16x8 fa[FM], fb[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                fa[i] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + 32 * i + (lane & 31)) * kPitch + kk);
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *reinterpret_cast<const f16x8*>(as + (32 * i + (lane & 31)) * kPitch + kk);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8*>(bs + (wn * 64 + 32 * j + (lane & 31)) * kPitch + kk);
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *reinterpret_cast<const f16x8*>(bs + (32 * j + (lane & 31)) * kPitch + kk);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if (more) {
-            store_piece(pa, &As[buf ^ 1][lr * kPitch + 32 * lh]);
-            store_piece(pb, &Bs[buf ^ 1][lr * kPitch + 32 * lh]);
-        }
+        store_all(pc, buf ^ 1);
+#pragma unroll
+        for (int i = 0; i < P; ++i) pc[i] = pn[i];
         __syncthreads();
     }
 
@@ -159,15 +194,15 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(const uint8_t* __restrict__ 
     const float sa_t = a_per_row ? 0.0f : outer_scale(a_amax[0]);
     const float sb_t = b_per_row ? 0.0f : outer_scale(b_amax[0]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t col = n0 + wn * 64 + 32 * j + (lane & 31);
+    for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + wn * (TN / WN) + 32 * j + (lane & 31);
         const bool col_ok = col < N;
         const float sb = b_per_row ? (col_ok ? outer_scale(b_amax[col]) : 0.0f) : sb_t;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int a = 0; a < 16; ++a) {
-                const int64_t row = m0 + wm * 64 + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3);
+                const int64_t row = m0 + wm * (TM / WM) + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3);
                 if (row < M && col_ok) {
                     const float sa = a_per_row ? outer_scale(a_amax[row]) : sa_t;
                     out[row * N + col] = (acc[i][j][a] * sa) * sb;
@@ -177,6 +212,17 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(const uint8_t* __restrict__ 
     }
 }
 
+template <int TM, int TN, int WM, int WN>
+hipError_t launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                      const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row, int64_t M,
+                      int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const int64_t ntn = (N + TN - 1) / TN, ntiles = ntn * ((M + TM - 1) / TM);
+    if (ntiles > kMaxGemmTiles) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL(k_gemm_nvfp4<TM, TN, WM, WN>, dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, st, ev0, ev1,
+                          0, a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, (uint32_t)ntn, out);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
@@ -184,11 +230,13 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const floa
                              int64_t M, int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0,
                              hipEvent_t ev1) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const int64_t ntn = (N + kTileN - 1) / kTileN, ntiles = ntn * ((M + kTileM - 1) / kTileM);
-    if (ntiles > kMaxGemmTiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL(k_gemm_nvfp4, dim3((unsigned)ntiles), dim3(256), 0, st, ev0, ev1, 0, a_q, a_sf, a_amax,
-                          a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, (uint32_t)ntn, out);
-    return hipGetLastError();
+    // 256 x 256 tiles (8 waves of 128 x 64) once they fill the 256 CUs, else
+    // 128 x 128 tiles (4 waves of 64 x 64) for four times the workgroups
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 256)
+        return launch_cfg<256, 256, 2, 4>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out,
+                                          st, ev0, ev1);
+    return launch_cfg<128, 128, 2, 2>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, st,
+                                      ev0, ev1);
 }
 
 }  // namespace nvfp4

@@ -40,6 +40,8 @@ hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int
 // NVFP4 GEMM consumer (nvfp4_gemm.hip): out [M][N] fp32, one workgroup per
 // 128 x 128 output tile, at most kMaxGemmTiles of them
 constexpr int64_t kMaxGemmTiles = (int64_t(1) << 31) - 1;
+// the GEMM kernel addresses a tile's operand rows with 32-bit byte offsets
+constexpr int64_t kMaxGemmK = int64_t(1) << 23;
 hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                              const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                              int64_t M, int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0,

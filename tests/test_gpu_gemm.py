@@ -1,6 +1,6 @@
 """GPU parity of the NVFP4 GEMM consumer against the CPU oracle.
 
-The kernel sums exact block-value products in fp32 on bf16 matrix cores and
+The kernel sums exact block-value products in fp32 on fp16 matrix cores and
 then applies the two outer scales in fp32; the oracle sums in binary64.  The
 tolerance follows from that arithmetic: every fp32 addition and the two scale
 multiplications round once, each by at most 2^-24 of a magnitude no larger
@@ -130,6 +130,22 @@ def test_gemm_training_products(oracle):
                            ("NT", col(qd, T, N), col(qx, T, K), T)):
         ref, bound = oracle.gemm_nvfp4(*a, *b)
         _check(_run(*a, *b), ref, bound, kk, name)
+
+
+def test_gemm_large_tiles_ragged(oracle):
+    # enough output tiles for the 256 x 256 tile shape, with ragged last tiles
+    # in both directions and a partial last K step; sampled blocks including
+    # the corner tile
+    M, N, K = 4000, 4100, 272
+    _announce(f"gemm 256-tile ragged M={M} N={N} K={K} (sampled)")
+    a = W.nvfp4_operand(M, K, 61)
+    b = W.nvfp4_operand(N, K, 62, per_row=False)
+    out = host(nv.gemm(*_dev(*a), *_dev(*b)))
+    torch.cuda.synchronize()
+    for r0, c0 in ((0, 0), (M - 80, N - 70), (3800, 0), (0, 3900), (1000, 2000)):
+        rs, cs = slice(r0, min(M, r0 + 80)), slice(c0, min(N, c0 + 70))
+        ref, bound = oracle.gemm_nvfp4(a[0][rs], a[1][rs], a[2][rs], b[0][cs], b[1][cs], b[2])
+        _check(out[rs, cs].astype(np.float64), ref, bound, K, f"block ({r0},{c0})")
 
 
 def test_gemm_full_size_sampled(oracle):

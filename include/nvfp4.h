@@ -96,7 +96,10 @@ NVFP4_API const char* nvfp4_last_error(void);
  * kernel starts and `after` when it ends, so that hipEventElapsedTime gives
  * the kernel's own duration; the pair is then forgotten (one-shot).  A call
  * that fails validation leaves it pending; a grouped call times its first
- * encoding launch.  Both arguments are hipEvent_t handles created and owned
+ * encoding launch.  nvfp4_gemm and nvfp4_gemm_grouped take the pair the same
+ * way for their GEMM kernel (a grouped GEMM over more than 128 groups runs
+ * several launches: `before` at the first, `after` at the last).  Both
+ * arguments are hipEvent_t handles created and owned
  * by the caller; NULL, NULL cancels a pending pair, and exactly one NULL is
  * NVFP4_EINVAL.  Recording the events changes no result.
  */
@@ -238,6 +241,26 @@ NVFP4_API nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, con
 NVFP4_API nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                         const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                         int64_t M, int64_t N, int64_t K, float* out, void* stream);
+
+/*
+ * Grouped NVFP4 GEMM for MoE experts, one launch per 128 groups (the page's
+ * native grouped per-token GEMM over a pointer array of experts, PR #3045
+ * "Changes"): A holds the tokens of num_groups experts back to back, h_counts
+ * (a HOST array of num_groups values >= 0, any size) rows each -- the
+ * rowwise output of nvfp4_quantize_grouped has this layout -- with a_q
+ * [T][K/2], a_sf [T][K/16], a_amax [T] (a_per_row != 0) or [1].  Expert e's
+ * weight B_e is b_q + e*N*K/2 ([N][K/2]), b_sf + e*N*K/16, b_amax + e*N
+ * ([G][N], b_per_row != 0) or b_amax + e ([G], one per expert).  The rows
+ * of expert e in out [T][N] fp32 get A_e x B_e^T with the outer scales, each
+ * element exactly as nvfp4_gemm computes it.  Same limits and errors as
+ * nvfp4_gemm, plus EINVAL for num_groups < 0 or a NULL h_counts, and ESHAPE
+ * for a negative count.
+ */
+NVFP4_API nvfp4_status nvfp4_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax,
+                                int a_per_row, const uint8_t* b_q, const uint8_t* b_sf,
+                                const float* b_amax, int b_per_row, int32_t num_groups,
+                                const int64_t* h_counts, int64_t N, int64_t K, float* out,
+                                void* stream);
 
 /*
  * Decayed calibration accumulator from the PTQ scaling-factor page

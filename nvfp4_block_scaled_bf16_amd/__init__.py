@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_quantize_rowwise",
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
-           "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm")
+           "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm",
+           "nvfp4_gemm_grouped")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_quantize_calibrate": (st, [p, i64, i64, st, p, p, p, p, p, p, p, f32, p]),
         "nvfp4_quantize_sr": (st, [p, i64, i64, st, p, p, p, p, p, p, ctypes.c_uint64, ctypes.c_uint32, p]),
         "nvfp4_gemm": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
+        "nvfp4_gemm_grouped": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i32, p, i64, i64, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -280,6 +282,36 @@ def gemm_into(out, a_q, a_sf, a_amax, b_q, b_sf, b_amax):
 def gemm(a_q, a_sf, a_amax, b_q, b_sf, b_amax):
     """Allocate out and run :func:`gemm_into`."""
     return gemm_into(_f32((a_q.shape[0], b_q.shape[0]), a_q.device), a_q, a_sf, a_amax, b_q, b_sf, b_amax)
+
+
+def gemm_grouped_into(out, a_q, a_sf, a_amax, b_q, b_sf, b_amax, counts):
+    """Per expert e: out[rows of e] = A_e x B_e^T (see :func:`gemm_into`).
+    a_q [T, K/2] / a_sf [T, K/16] / a_amax ([T] or [1]) hold the experts'
+    rows back to back, counts[e] rows each; b_q [G, N, K/2], b_sf
+    [G, N, K/16], b_amax [G, N] (per row) or [G] (one per expert)."""
+    counts_t = torch.as_tensor(counts, dtype=torch.int64).cpu().contiguous()
+    G = counts_t.numel()
+    T, K, apr = _operand(a_q, a_sf, a_amax, "a")
+    if int(counts_t.sum()) != T:
+        raise ValueError("counts must sum to the rows of a_q")
+    if b_q.dim() != 3 or b_q.shape[0] != G or 2 * b_q.shape[2] != K:
+        raise ValueError("b_q must be [G, N, K/2]")
+    N = b_q.shape[1]
+    if b_sf.numel() != G * N * (K // 16) or b_amax.numel() not in (G, G * N):
+        raise ValueError("b_sf must hold G*N*K/16 codes and b_amax G or G*N values")
+    bpr = int(b_amax.numel() == G * N and N != 1)
+    if tuple(out.shape) != (T, N) or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [T, N]")
+    _check(lib().nvfp4_gemm_grouped(_ptr(a_q), _ptr(a_sf), _ptr(a_amax), apr, _ptr(b_q), _ptr(b_sf), _ptr(b_amax),
+                                    bpr, G, ctypes.c_void_p(counts_t.data_ptr()), N, K, _ptr(out),
+                                    _stream(a_q.device)))
+    return out
+
+
+def gemm_grouped(a_q, a_sf, a_amax, b_q, b_sf, b_amax, counts):
+    """Allocate out and run :func:`gemm_grouped_into`."""
+    out = _f32((a_q.shape[0], b_q.shape[1]), a_q.device)
+    return gemm_grouped_into(out, a_q, a_sf, a_amax, b_q, b_sf, b_amax, counts)
 
 
 def amax_accumulate(buf, observed, decay: float):

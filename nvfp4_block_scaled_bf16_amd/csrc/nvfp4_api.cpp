@@ -359,6 +359,35 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_
     return s != NVFP4_OK ? s : ok();
 }
 
+nvfp4_status nvfp4_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                                const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                                int32_t num_groups, const int64_t* h_counts, int64_t N, int64_t K, float* out,
+                                void* stream) {
+    if (num_groups < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "negative size");
+    if (num_groups > 0 && !h_counts) return fail(NVFP4_EINVAL, "h_counts is NULL");
+    if (K % 16 != 0) return fail(NVFP4_ESHAPE, "gemm needs K %% 16 == 0 (K=%lld)", (long long)K);
+    if (K > kMaxGemmK) return fail(NVFP4_ESHAPE, "gemm needs K <= %lld (K=%lld)", (long long)kMaxGemmK, (long long)K);
+    int64_t T = 0, tiles = 0;
+    for (int32_t e = 0; e < num_groups; ++e) {
+        if (h_counts[e] < 0) return fail(NVFP4_ESHAPE, "group %d has a negative row count", e);
+        if (h_counts[e] > kMaxGemmTiles || N > kMaxGemmTiles) return fail(NVFP4_ESHAPE, "group too large");
+        T += h_counts[e];
+        tiles += ((h_counts[e] + 127) / 128) * ((N + 127) / 128);
+        if (tiles > kMaxGemmTiles) return fail(NVFP4_ESHAPE, "gemm needs fewer than 2^31 output tiles of 128 x 128");
+    }
+    if (T == 0 || N == 0) return ok();
+    if (!out || !a_amax || !b_amax) return fail(NVFP4_EINVAL, "NULL argument");
+    if (K > 0 && (!a_q || !a_sf || !b_q || !b_sf)) return fail(NVFP4_EINVAL, "NULL argument");
+    if (!aligned(a_q, 16) || !aligned(b_q, 16)) return fail(NVFP4_EALIGN, "a_q and b_q must be 16-byte aligned");
+    if (!aligned(a_amax, 4) || !aligned(b_amax, 4) || !aligned(out, 4))
+        return fail(NVFP4_EALIGN, "amax and out must be 4-byte aligned");
+    nvfp4_status s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
+        return launch_gemm_grouped(a_q, a_sf, a_amax, a_per_row ? 1 : 0, b_q, b_sf, b_amax, b_per_row ? 1 : 0,
+                                   num_groups, h_counts, N, K, out, as_stream(stream), b, a);
+    });
+    return s != NVFP4_OK ? s : ok();
+}
+
 nvfp4_status nvfp4_amax_accumulate(float* buf, const float* observed, int64_t n, float decay, void* stream) {
     if (n < 0) return fail(NVFP4_EINVAL, "n < 0");
     if (!(decay >= 0.0f && decay <= 1.0f)) return fail(NVFP4_EINVAL, "decay must lie in [0, 1]");

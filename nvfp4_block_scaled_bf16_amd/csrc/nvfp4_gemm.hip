@@ -102,24 +102,30 @@ __device__ __forceinline__ void store_piece(const RowPiece& p, _Float16* dst) {
 // TM rows of A then TN rows of B, kStepK fp16 values each, double buffered.
 // Each K step a row is loaded as two 32-element pieces; piece p (p = t + NT i
 // for thread t, i < P) is row p / 2, half p % 2, so each i is all-A or all-B.
-// Grid: cdiv(M, TM) * cdiv(N, TN) workgroups (one dimension); ntn = cdiv(N, TN).
+template <int TM, int TN>
+using GemmLds = _Float16[2][(TM + TN) * kPitch];
+
+// XCD-aware order over a one-dimensional grid: each of the 8 XCDs (own L2)
+// takes a contiguous run of tiles, row band major, so a band of A is reused
+// from one L2
+__device__ __forceinline__ uint32_t xcd_tile() {
+    const uint32_t ntiles = gridDim.x, lin = blockIdx.x;
+    return (ntiles & 7u) == 0u ? (lin & 7u) * (ntiles >> 3) + (lin >> 3) : lin;
+}
+
+// the output tile at (m0, n0) of out [M][N] = A [M][K] x B [N][K]^T
 template <int TM, int TN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4(
-    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
-    int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
-    const float* __restrict__ b_amax, int b_per_row, int64_t M, int64_t N, int64_t K, uint32_t ntn,
-    float* __restrict__ out) {
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf,
+                                          const float* __restrict__ a_amax, int a_per_row,
+                                          const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
+                                          const float* __restrict__ b_amax, int b_per_row, int64_t M, int64_t N,
+                                          int64_t K, int64_t m0, int64_t n0, float* __restrict__ out,
+                                          GemmLds<TM, TN>& S) {
     constexpr int NT = 64 * WM * WN, ROWS = TM + TN, P = 2 * ROWS / NT;
     constexpr int FM = TM / WM / 32, FN = TN / WN / 32;
     static_assert(2 * ROWS % NT == 0 && 2 * TM % NT == 0 && FM >= 1 && FN >= 1, "tile shape");
-    __shared__ __attribute__((aligned(16))) _Float16 S[2][ROWS * kPitch];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    // XCD-aware order: each of the 8 XCDs (own L2) takes a contiguous run of
-    // tiles, row band major, so a band of A is reused from one L2
-    const uint32_t ntiles = gridDim.x, lin = blockIdx.x;
-    const uint32_t tile = (ntiles & 7u) == 0u ? (lin & 7u) * (ntiles >> 3) + (lin >> 3) : lin;
-    const int64_t m0 = (int64_t)(tile / ntn) * TM, n0 = (int64_t)(tile % ntn) * TN;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -212,6 +218,46 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     }
 }
 
+// Grid: cdiv(M, TM) * cdiv(N, TN) workgroups (one dimension); ntn = cdiv(N, TN).
+template <int TM, int TN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4(
+    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
+    int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
+    const float* __restrict__ b_amax, int b_per_row, int64_t M, int64_t N, int64_t K, uint32_t ntn,
+    float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) GemmLds<TM, TN> S;
+    const uint32_t tile = xcd_tile();
+    gemm_tile<TM, TN, WM, WN>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K,
+                              (int64_t)(tile / ntn) * TM, (int64_t)(tile % ntn) * TN, out, S);
+}
+
+// Grouped: group g (the table's entry g, expert first + g) multiplies A's
+// rows off[g] .. off[g] + cnt[g] by its own B (expert first + g of b_*),
+// writing out's same rows.  Tiles of group g are tstart[g] .. tstart[g + 1];
+// grid: tstart[n] workgroups.
+template <int TM, int TN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4_grouped(
+    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
+    int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
+    const float* __restrict__ b_amax, int b_per_row, GemmGroups gg, int64_t N, int64_t K, uint32_t ntn,
+    float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) GemmLds<TM, TN> S;
+    const uint32_t tile = xcd_tile();
+    // the last entry starting at or before this tile (skips empty groups,
+    // which share the next group's start)
+    int lo = 0, hi = gg.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (gg.tstart[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t local = tile - gg.tstart[lo];
+    const int64_t off = gg.off[lo], e = (int64_t)gg.first + lo;
+    gemm_tile<TM, TN, WM, WN>(a_q + off * (K / 2), a_sf + off * (K / 16), a_amax + (a_per_row ? off : 0), a_per_row,
+                              b_q + e * N * (K / 2), b_sf + e * N * (K / 16), b_amax + (b_per_row ? e * N : e),
+                              b_per_row, gg.cnt[lo], N, K, (int64_t)(local / ntn) * TM,
+                              (int64_t)(local % ntn) * TN, out + off * N, S);
+}
+
 template <int TM, int TN, int WM, int WN>
 hipError_t launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                       const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row, int64_t M,
@@ -237,6 +283,69 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const floa
                                           st, ev0, ev1);
     return launch_cfg<128, 128, 2, 2>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, st,
                                       ev0, ev1);
+}
+
+namespace {
+
+template <int TM, int TN, int WM, int WN>
+hipError_t launch_grouped_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                              const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                              int32_t num_groups, const int64_t* h_counts, int64_t N, int64_t K, float* out,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const int64_t ntn = (N + TN - 1) / TN;
+    // the launches that have tiles, so the trace events bracket the first and last
+    int last = -1;
+    for (int32_t e0 = 0; e0 < num_groups; e0 += kMaxGemmGroups)
+        for (int32_t e = e0; e < num_groups && e < e0 + kMaxGemmGroups; ++e)
+            if (h_counts[e] > 0) last = e0;
+    int64_t off = 0;
+    bool first_launch = true;
+    for (int32_t e0 = 0; e0 < num_groups; e0 += kMaxGemmGroups) {
+        GemmGroups gg;
+        gg.n = 0;
+        gg.first = e0;
+        int64_t tiles = 0;
+        for (int32_t e = e0; e < num_groups && e < e0 + kMaxGemmGroups; ++e) {
+            gg.off[gg.n] = off;
+            gg.cnt[gg.n] = h_counts[e];
+            gg.tstart[gg.n] = (uint32_t)tiles;
+            tiles += ntn * ((h_counts[e] + TM - 1) / TM);
+            off += h_counts[e];
+            ++gg.n;
+        }
+        gg.tstart[gg.n] = (uint32_t)tiles;
+        if (tiles == 0) continue;
+        if (tiles > kMaxGemmTiles) return hipErrorInvalidValue;
+        hipExtLaunchKernelGGL(k_gemm_nvfp4_grouped<TM, TN, WM, WN>, dim3((unsigned)tiles), dim3(64 * WM * WN), 0, st,
+                              first_launch ? ev0 : nullptr, e0 == last ? ev1 : nullptr, 0, a_q, a_sf, a_amax,
+                              a_per_row, b_q, b_sf, b_amax, b_per_row, gg, N, K, (uint32_t)ntn, out);
+        first_launch = false;
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                               const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                               int32_t num_groups, const int64_t* h_counts, int64_t N, int64_t K, float* out,
+                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    if (N <= 0) return hipSuccess;
+    // 256 x 256 tiles when they fill the CUs and each group's row padding to
+    // 256 wastes at most a fifth of the rows
+    int64_t T = 0, padded = 0, tiles256 = 0;
+    for (int32_t e = 0; e < num_groups; ++e) {
+        T += h_counts[e];
+        padded += (h_counts[e] + 255) / 256 * 256;
+        tiles256 += (h_counts[e] + 255) / 256 * ((N + 255) / 256);
+    }
+    if (tiles256 >= 256 && 4 * padded <= 5 * T)
+        return launch_grouped_cfg<256, 256, 2, 4>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row,
+                                                  num_groups, h_counts, N, K, out, st, ev0, ev1);
+    return launch_grouped_cfg<128, 128, 2, 2>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row,
+                                              num_groups, h_counts, N, K, out, st, ev0, ev1);
 }
 
 }  // namespace nvfp4

@@ -46,6 +46,20 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const floa
                              const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                              int64_t M, int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0,
                              hipEvent_t ev1);
+// grouped GEMM: groups of A's rows, each with its own B, a bounded number per
+// launch (the table travels in the kernel arguments)
+constexpr int kMaxGemmGroups = 128;
+struct GemmGroups {
+    int32_t n;                              // entries in this launch
+    int32_t first;                          // expert index of entry 0
+    int64_t off[kMaxGemmGroups];            // first row of A / out
+    int64_t cnt[kMaxGemmGroups];            // rows
+    uint32_t tstart[kMaxGemmGroups + 1];    // first output tile of each entry; tstart[n]: all tiles
+};
+hipError_t launch_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                               const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                               int32_t num_groups, const int64_t* h_counts, int64_t N, int64_t K, float* out,
+                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
                           int amax_per_row, float* out, hipStream_t st);
 hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);

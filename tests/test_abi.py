@@ -130,6 +130,21 @@ def test_gemm_validation():
     assert g(f, f, f, 1, f, f, f, 1, 16, 16, 16, P(FAKE + 2), None) == EALIGN
 
 
+def test_gemm_grouped_validation():
+    L = nv.lib()
+    f, g = P(FAKE), L.nvfp4_gemm_grouped
+    counts = (ctypes.c_int64 * 3)(16, 0, 32)
+    assert g(f, f, f, 1, f, f, f, 1, -1, counts, 16, 16, f, None) == EINVAL
+    assert g(f, f, f, 1, f, f, f, 1, 3, None, 16, 16, f, None) == EINVAL
+    assert g(f, f, f, 1, f, f, f, 1, 3, counts, 16, 24, f, None) == ESHAPE   # K % 16
+    neg = (ctypes.c_int64 * 2)(16, -1)
+    assert g(f, f, f, 1, f, f, f, 1, 2, neg, 16, 16, f, None) == ESHAPE
+    zeros = (ctypes.c_int64 * 2)(0, 0)
+    assert g(None, None, None, 1, None, None, None, 1, 2, zeros, 16, 16, None, None) == 0   # no rows
+    assert g(f, f, f, 1, f, f, f, 1, 3, counts, 16, 16, None, None) == EINVAL
+    assert g(P(FAKE + 8), f, f, 1, f, f, f, 1, 3, counts, 16, 16, f, None) == EALIGN
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

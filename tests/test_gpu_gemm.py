@@ -164,3 +164,92 @@ def test_gemm_full_size_sampled(oracle):
         rs, cs = slice(r0, r0 + 64), slice(c0, c0 + 64)
         ref, bound = oracle.gemm_nvfp4(a[0][rs], a[1][rs], a[2][rs], b[0][cs], b[1][cs], b[2][cs])
         _check(out[rs, cs].astype(np.float64), ref, bound, K, f"block ({r0},{c0})")
+
+
+# ----------------------------------------------------------------- grouped
+
+def _grouped_ref(oracle, a, b, counts, b_per_row):
+    """per group: the oracle's GEMM of the group's rows with its own B"""
+    aq, asf, aa = a
+    bq, bsf, ba = b
+    G, N = bq.shape[0], bq.shape[1]
+    refs, bounds = [], []
+    off = 0
+    for e, c in enumerate(counts):
+        rs = slice(off, off + int(c))
+        a_am = aa[rs] if aa.size != 1 else aa
+        b_am = ba.reshape(G, N)[e] if b_per_row else ba[e:e + 1]
+        if c:
+            r, bd = oracle.gemm_nvfp4(aq[rs], asf[rs], a_am, bq[e], bsf[e], b_am)
+            refs.append(r)
+            bounds.append(bd)
+        off += int(c)
+    return np.concatenate(refs), np.concatenate(bounds)
+
+
+def _grouped_b(G, N, K, seed, per_row):
+    q, sf, amax = zip(*(W.nvfp4_operand(N, K, seed + e, per_row) for e in range(G)))
+    return np.stack(q), np.stack(sf), np.concatenate(amax)
+
+
+def _run_grouped(a, b, counts):
+    out = nv.gemm_grouped(*_dev(*a), *_dev(*b), counts)
+    torch.cuda.synchronize()
+    return host(out).astype(np.float64)
+
+
+@pytest.mark.parametrize("a_per_row,b_per_row", [(True, True), (True, False), (False, False)])
+def test_gemm_grouped_ragged_counts(oracle, a_per_row, b_per_row):
+    counts = np.array([5, 0, 130, 16, 0, 64, 257, 1], np.int64)
+    N, K = 200, 272
+    _announce(f"gemm grouped counts={counts.tolist()} N={N} K={K} per_row={a_per_row},{b_per_row}")
+    a = W.nvfp4_operand(int(counts.sum()), K, 71, a_per_row)
+    b = _grouped_b(len(counts), N, K, 72, b_per_row)
+    ref, bound = _grouped_ref(oracle, a, b, counts, b_per_row)
+    _check(_run_grouped(a, b, counts), ref, bound, K, "out")
+
+
+def test_gemm_grouped_many_groups(oracle):
+    # more groups than one launch carries, with empty ones among them
+    rng = np.random.Generator(np.random.PCG64(81))
+    counts = rng.integers(0, 40, size=300).astype(np.int64)
+    counts[[0, 127, 128, 129, 299]] = 0
+    N, K = 48, 64
+    _announce(f"gemm grouped {counts.size} groups T={int(counts.sum())} N={N} K={K}")
+    a = W.nvfp4_operand(int(counts.sum()), K, 82)
+    b = _grouped_b(counts.size, N, K, 1000, True)
+    ref, bound = _grouped_ref(oracle, a, b, counts, True)
+    _check(_run_grouped(a, b, counts), ref, bound, K, "out")
+
+
+def test_gemm_grouped_moe_cast(oracle):
+    # the rowwise output of the oracle's grouped cast of an MoE batch (token
+    # counts in multiples of 16, some experts empty) times per-expert weights
+    x, counts = W.moe_batch(91, K=256, experts=12, chunks=24, align=16)
+    N, K = 96, 256
+    _announce(f"gemm grouped MoE cast counts={counts.tolist()}")
+    q = oracle.quantize_grouped(x, counts, rowwise=True, columnwise=False)
+    a = (q["row_q"], q["row_sf"], q["row_amax"])
+    Wts = [W.weight_with_outliers(N, K, 92 + e) for e in range(counts.size)]
+    qw = [oracle.quantize(w, oracle.PER_TOKEN, columnwise=False) for w in Wts]
+    b = (np.stack([o["row_q"] for o in qw]), np.stack([o["row_sf"] for o in qw]),
+         np.concatenate([o["row_amax"] for o in qw]))
+    ref, bound = _grouped_ref(oracle, a, b, counts, True)
+    _check(_run_grouped(a, b, counts), ref, bound, K, "out")
+
+
+def test_gemm_grouped_large_tiles_sampled(oracle):
+    # enough rows for the 256 x 256 tile shape; sampled blocks in each group
+    counts = np.array([1024, 768, 1280, 1024, 512, 1536, 1024, 1024], np.int64)
+    N, K = 2048, 512
+    _announce(f"gemm grouped 256-tile counts={counts.tolist()} N={N} K={K} (sampled)")
+    a = W.nvfp4_operand(int(counts.sum()), K, 101)
+    b = _grouped_b(counts.size, N, K, 200, False)
+    out = _run_grouped(a, b, counts)
+    off = 0
+    for e, c in enumerate(counts):
+        for r0, c0 in ((off, 0), (off + int(c) - 48, N - 48)):
+            rs, cs = slice(r0, r0 + 48), slice(c0, c0 + 48)
+            ref, bound = oracle.gemm_nvfp4(a[0][rs], a[1][rs], a[2][rs], b[0][e][cs], b[1][e][cs], b[2][e:e + 1])
+            _check(out[rs, cs], ref, bound, K, f"group {e} block ({r0},{c0})")
+        off += int(c)

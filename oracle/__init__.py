@@ -58,6 +58,8 @@ def _load():
                                            ctypes.c_uint64, ctypes.c_uint32]),
         "orc_gemm_nvfp4": (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64,
                                           _p, _p]),
+        "orc_rht16": (None, [_p, ctypes.c_uint32, _p]),
+        "orc_rht_columns": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_uint32, _p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -282,6 +284,36 @@ def gemm_nvfp4(a_q, a_sf, a_amax, b_q, b_sf, b_amax):
     if rc != 0:
         raise ValueError("oracle: K must be a multiple of 16")
     return out, bound
+
+
+# ------------------------------------------- random Hadamard transform
+
+def rht16(blocks, sign_mask):
+    """The transform of bf16 blocks uint16 [n, 16] (each row one block)."""
+    blocks = np.ascontiguousarray(blocks, np.uint16).reshape(-1, 16)
+    out = np.empty_like(blocks)
+    for i in range(len(blocks)):
+        _load().orc_rht16(_ptr(blocks[i]), int(sign_mask) & 0xFFFF, _ptr(out[i]))
+    return out
+
+
+def rht_columns(x, sign_mask):
+    """bf16 [M, K] (M % 16 == 0): each 16-row block of each column transformed."""
+    x = _bf16(x)
+    M, K = x.shape
+    y = np.empty_like(x)
+    if _load().orc_rht_columns(_ptr(x), M, K, int(sign_mask) & 0xFFFF, _ptr(y)) != 0:
+        raise ValueError("oracle: M must be a multiple of 16")
+    return y
+
+
+def quantize_rht(x, mode, sign_mask, rowwise=True):
+    """Cast with the random Hadamard transform on the columnwise direction:
+    rowwise outputs are the ordinary cast of x, columnwise outputs the
+    ordinary columnwise cast of rht_columns(x) (its own amax)."""
+    out = quantize(x, mode, rowwise=True, columnwise=False) if rowwise else {}
+    out.update(quantize(rht_columns(x, sign_mask), mode, rowwise=False, columnwise=True))
+    return out
 
 
 def quantize_grouped(x, counts, rowwise=True, columnwise=True):

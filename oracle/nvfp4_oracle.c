@@ -642,3 +642,62 @@ int orc_gemm_nvfp4(const uint8_t* aq, const uint8_t* asf, const float* aamax, in
     free(a);
     return 0;
 }
+
+/* ------------------------------------------ random Hadamard transform */
+
+/* The per-token recipe page lists a random Hadamard transform as an opt-in
+ * for the columnwise direction only (PR #3045, "Changes": per_token_rht, and
+ * the review's note that the row direction never uses it).  The pages fix
+ * neither its size nor its arithmetic; the readings taken here:
+ *   - size 16, one transform per 16-element block of a columnwise vector
+ *     (the block the E4M3 scale covers);
+ *   - y = (1/4) H16 D x with H16 the Sylvester Hadamard matrix,
+ *     H16[i][j] = (-1)^popcount(i & j), and D = diag(s), s_j = -1 where bit j
+ *     of a caller-given 16-bit sign mask is set, else +1;
+ *   - evaluated in binary32 as the fast Walsh-Hadamard butterfly: stages
+ *     h = 1, 2, 4, 8, each replacing the pair (v[i], v[i+h]), i & h == 0, by
+ *     (v[i] + v[i+h], v[i] - v[i+h]); then times 1/4 (exact for normal
+ *     results) and rounded to bf16, nearest-even.
+ * The transformed bf16 block then goes through the ordinary cast.  Natural
+ * (Sylvester) ordering: the butterfly above yields y_i = sum_j H16[i][j]
+ * s_j x_j / 4 up to binary32 rounding. */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+void orc_rht16(const uint16_t in[16], uint32_t sign_mask, uint16_t out[16])
+{
+    float v[16];
+    for (int j = 0; j < 16; ++j) {
+        v[j] = orc_bf16_to_f32(in[j]);
+        if ((sign_mask >> j) & 1u) v[j] = -v[j];
+    }
+    for (int h = 1; h < 16; h <<= 1)
+        for (int i = 0; i < 16; ++i)
+            if (!(i & h)) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    for (int j = 0; j < 16; ++j) out[j] = f32_to_bf16_rne(v[j] * 0.25f);
+}
+
+/* y [M][K] = the transform applied down each column of x [M][K] (M % 16 == 0),
+ * block by block of 16 rows */
+int orc_rht_columns(const uint16_t* x, int64_t M, int64_t K, uint32_t sign_mask, uint16_t* y)
+{
+    if (M < 0 || K < 0 || M % 16 != 0) return -1;
+    uint16_t in[16], out[16];
+    for (int64_t r0 = 0; r0 < M; r0 += 16)
+        for (int64_t k = 0; k < K; ++k) {
+            for (int i = 0; i < 16; ++i) in[i] = x[(r0 + i) * K + k];
+            orc_rht16(in, sign_mask, out);
+            for (int i = 0; i < 16; ++i) y[(r0 + i) * K + k] = out[i];
+        }
+    return 0;
+}

@@ -105,6 +105,12 @@ int orc_gemm_nvfp4(const uint8_t* aq, const uint8_t* asf, const float* aamax, in
                    const uint8_t* bq, const uint8_t* bsf, const float* bamax, int b_per_row,
                    int64_t M, int64_t N, int64_t K, double* out, double* bound);
 
+/* random Hadamard transform of 16 bf16 values (binary32 butterfly, 1/4,
+ * bf16 result; definition and readings in nvfp4_oracle.c), and of every
+ * 16-row block down the columns of x [M][K] */
+void orc_rht16(const uint16_t in[16], uint32_t sign_mask, uint16_t out[16]);
+int  orc_rht_columns(const uint16_t* x, int64_t M, int64_t K, uint32_t sign_mask, uint16_t* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 M, K = 16384, 8192
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F16_TFS = 2500.0   # dense fp16/bf16 matrix-core peak
 
 
 def algorithmic_bytes(M, K):
@@ -160,6 +161,12 @@ def all_configs(steps, warmup):
                           "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
                           "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
 
+    def report_mfma(name, desc, us, flops):
+        tfs = flops / (us * 1e-6) / 1e12
+        print(json.dumps({"config": name, "workload": desc, "us_per_call": round(us, 2), "flops": flops,
+                          "TFLOP_per_s": round(tfs, 1), "frac_of_peak": round(tfs / PEAK_MFMA_F16_TFS, 4),
+                          "peak": "dense fp16/bf16 MFMA"}), flush=True)
+
     def cast_bytes(m, k, amax_floats):
         return 2 * m * k + m * k + m * k // 8 + 4 * amax_floats
 
@@ -192,7 +199,18 @@ def all_configs(steps, warmup):
            timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3), cast_bytes(M, K, 2))
     report("C3-per-token-SR", "per-token row+col with stochastic rounding (Philox4x32-10 randoms), 16384x8192",
            timed(lambda i: nv.quantize_sr_into(x3[i], nv.PER_TOKEN, 2024, i, **o3), 3), cast_bytes(M, K, M + K))
-    del x3, o3, o3t
+    report("C3-per-token-RHT", "per-token row+col, columnwise through the 16-point random Hadamard transform, "
+           "16384x8192", timed(lambda i: nv.quantize_rht_into(x3[i], nv.PER_TOKEN, 0xB2E5, **o3), 3),
+           cast_bytes(M, K, M + K))
+    # the consumer: forward (TN) GEMM of the per-token C3 activation with an
+    # 8192 x 8192 weight cast per token
+    xa = nv.quantize(x3[0], nv.PER_TOKEN, columnwise=False)
+    wb = nv.quantize(to_dev(W.weight_with_outliers(K, K, 6006)), nv.PER_TOKEN, columnwise=False)
+    og = torch.empty((M, K), dtype=torch.float32, device=dev)
+    report_mfma("GEMM-TN", f"NVFP4 GEMM {M}x{K}x{K}, per-row A and B outer scales, fp32 out",
+                timed(lambda i: nv.gemm_into(og, xa["row_q"], xa["row_sf"], xa["row_amax"], wb["row_q"],
+                                             wb["row_sf"], wb["row_amax"]), 1), 2 * M * K * K)
+    del x3, o3, o3t, xa, wb, og
     # C4: grouped MoE, 64 experts, 32768 tokens x 4096
     x4h, counts = W.c4()
     x4 = to_dev(x4h)
@@ -205,7 +223,17 @@ def all_configs(steps, warmup):
         nv._ptr(o4["col_q"]), nv._ptr(o4["col_sf"]), nv._ptr(o4["col_amax"]), nv._stream(dev))
     report("C4", f"grouped per-token row+col, {len(counts)} experts, {T}x{K4}", timed(g, 1),
            cast_bytes(T, K4, T + len(counts) * K4))
-    del x4, o4
+    # the grouped consumer: each expert's tokens times its own 2048 x 4096
+    # weight (seeded NVFP4 codes), per-row outer scales
+    N4 = 2048
+    bq, bsf, ba = (torch.from_numpy(t).to(dev) for t in W.nvfp4_operand(len(counts) * N4, K4, 4040))
+    bq, bsf = bq.view(len(counts), N4, K4 // 2), bsf.view(len(counts), N4, K4 // 16)
+    og = torch.empty((T, N4), dtype=torch.float32, device=dev)
+    report_mfma("GEMM-grouped", f"grouped NVFP4 GEMM over the C4 experts' rowwise output, {len(counts)} x "
+                f"({T} tokens in all) x {N4} x {K4}",
+                timed(lambda i: nv.gemm_grouped_into(og, o4["row_q"], o4["row_sf"], o4["row_amax"], bq, bsf, ba,
+                                                     counts), 1), 2 * T * N4 * K4)
+    del x4, o4, bq, bsf, ba, og
     # C5: 16x16 tiles, 8192 x 28672 weight, per-token-layout emission
     M5, K5 = 8192, 28672
     x5 = to_dev(W.c5())

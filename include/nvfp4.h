@@ -157,6 +157,33 @@ NVFP4_API nvfp4_status nvfp4_quantize_sr(const void* x, int64_t M, int64_t K, nv
                                uint8_t* col_q, uint8_t* col_sf, float* col_amax,
                                uint64_t seed, uint32_t offset, void* stream);
 
+/*
+ * Cast with the opt-in random Hadamard transform on the columnwise direction
+ * (the per-token recipe page, PR #3045 "Changes": per_token_rht; the row
+ * direction never uses it).  Rowwise outputs (optional: all three NULL to
+ * skip) are exactly nvfp4_quantize's.  The columnwise outputs (required) are
+ * nvfp4_quantize's columnwise cast of y instead of x, where each 16-element
+ * block of a columnwise vector -- rows 16b .. 16b+15 of one column of x -- is
+ *   y = H16 D x_block / 4
+ * with H16 the Sylvester Hadamard matrix (H16[i][j] = (-1)^popcount(i & j))
+ * and D = diag(s), s_i = -1 where bit i of sign_mask is set.  The pages fix
+ * neither the size nor the arithmetic; this library evaluates y as the fast
+ * Walsh-Hadamard butterfly in binary32 (stages 1, 2, 4, 8, each pair (a, b)
+ * of entries i and i + h becoming (a + b, a - b)), multiplies by 1/4 and
+ * rounds to bf16 nearest-even, then casts y with its own amax (col_amax: max
+ * |y| per column for PER_TOKEN, over the tensor for PER_TENSOR).  Since H16 /
+ * 4 is orthonormal and its own inverse, a consumer undoes the transform with
+ * D H16 / 4 on the dequantized blocks.  mode PER_TENSOR or PER_TOKEN (else
+ * EINVAL); sign_mask < 2^16 (EINVAL); M % 16 == 0 and K % 8 == 0 (plus K % 16
+ * == 0 with rowwise output) and M <= 65535 * 128 (ESHAPE).  Reads x twice
+ * for the columnwise part (amax, then encoding).
+ */
+NVFP4_API nvfp4_status nvfp4_quantize_rht(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                uint32_t sign_mask,
+                                uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                                void* stream);
+
 /* One direction only (same as nvfp4_quantize with the other direction NULL). */
 NVFP4_API nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
                                     uint8_t* row_q, uint8_t* row_sf, float* row_amax,

@@ -29,7 +29,7 @@ EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_qua
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
            "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm",
-           "nvfp4_gemm_grouped")
+           "nvfp4_gemm_grouped", "nvfp4_quantize_rht")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_quantize_sr": (st, [p, i64, i64, st, p, p, p, p, p, p, ctypes.c_uint64, ctypes.c_uint32, p]),
         "nvfp4_gemm": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
         "nvfp4_gemm_grouped": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i32, p, i64, i64, p, p]),
+        "nvfp4_quantize_rht": (st, [p, i64, i64, st, ctypes.c_uint32, p, p, p, p, p, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -157,6 +158,31 @@ def quantize_sr_into(x, mode, seed: int, offset: int, row_q=None, row_sf=None, r
     _check(lib().nvfp4_quantize_sr(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                    _ptr(col_q), _ptr(col_sf), _ptr(col_amax), ctypes.c_uint64(seed & (2**64 - 1)),
                                    ctypes.c_uint32(offset & 0xFFFFFFFF), _stream(x.device)))
+
+
+def quantize_rht(x: torch.Tensor, mode="per_token", sign_mask: int = 0, rowwise: bool = True) -> dict:
+    """Cast with the random Hadamard transform (16-point, signs from the
+    16-bit mask) applied to the columnwise direction only; rowwise outputs
+    are the ordinary cast's."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    dev = x.device
+    out = {}
+    if rowwise:
+        out.update(row_q=_u8((M, K // 2), dev), row_sf=_u8((M, K // 16), dev), row_amax=_f32(_amax_len(mode, M), dev))
+    out.update(col_q=_u8((K, M // 2), dev), col_sf=_u8((K, M // 16), dev), col_amax=_f32(_amax_len(mode, K), dev))
+    quantize_rht_into(x, mode, sign_mask, **out)
+    return out
+
+
+def quantize_rht_into(x, mode, sign_mask: int, col_q, col_sf, col_amax, row_q=None, row_sf=None, row_amax=None):
+    """Hadamard-transform cast into caller-provided buffers."""
+    x = _input(x)
+    M, K = x.shape
+    _check(lib().nvfp4_quantize_rht(_ptr(x), M, K, _mode(mode), ctypes.c_uint32(sign_mask), _ptr(row_q),
+                                    _ptr(row_sf), _ptr(row_amax), _ptr(col_q), _ptr(col_sf), _ptr(col_amax),
+                                    _stream(x.device)))
 
 
 def quantize_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, col_sf=None, col_amax=None):

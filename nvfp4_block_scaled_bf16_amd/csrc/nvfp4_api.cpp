@@ -209,6 +209,35 @@ nvfp4_status nvfp4_quantize_sr(const void* x, int64_t M, int64_t K, nvfp4_scalin
                          Rounding{true, seed, offset});
 }
 
+nvfp4_status nvfp4_quantize_rht(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode, uint32_t sign_mask,
+                                uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+    if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN)
+        return fail(NVFP4_EINVAL, "the Hadamard transform is offered for per-tensor and per-token scaling only");
+    if (sign_mask > 0xFFFFu) return fail(NVFP4_EINVAL, "sign_mask has 16 bits (got %#x)", sign_mask);
+    Dir c = direction("col", col_q, col_sf, col_amax);
+    if (c.st != NVFP4_OK) return c.st;
+    if (!c.want) return fail(NVFP4_EINVAL, "the Hadamard transform applies to the columnwise output, which must be given");
+    Dir r = direction("row", row_q, row_sf, row_amax);
+    if (r.st != NVFP4_OK) return r.st;
+    nvfp4_status s = check_shape(M, K, r.want, true, mode);
+    if (s != NVFP4_OK) return s;
+    if (M > (int64_t)65535 * 128) return fail(NVFP4_ESHAPE, "the Hadamard transform needs M <= 65535 * 128 (M=%lld)", (long long)M);
+    if (xv == nullptr && M > 0 && K > 0) return fail(NVFP4_EINVAL, "x is NULL");
+    if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
+    if (r.want && (s = quantize_impl(xv, M, K, mode, row_q, row_sf, row_amax, nullptr, nullptr, nullptr, stream)) != NVFP4_OK)
+        return s;
+    hipStream_t st = as_stream(stream);
+    if ((s = zero(col_amax, mode == NVFP4_PER_TOKEN ? K : 1, nullptr, 0, st)) != NVFP4_OK) return s;
+    if (M == 0 || K == 0) return ok();
+    const uint16_t* x = static_cast<const uint16_t*>(xv);
+    s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
+        return launch_rht_columnwise(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, x, M, K, sign_mask, col_amax, col_q,
+                                     col_sf, st, b, a);
+    });
+    return s != NVFP4_OK ? s : ok();
+}
+
 nvfp4_status nvfp4_quantize_rowwise(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
                                     uint8_t* row_q, uint8_t* row_sf, float* row_amax, void* stream) {
     if (!row_q || !row_sf || !row_amax) return fail(NVFP4_EINVAL, "rowwise outputs must not be NULL");

@@ -145,6 +145,19 @@ def test_gemm_grouped_validation():
     assert g(P(FAKE + 8), f, f, 1, f, f, f, 1, 3, counts, 16, 16, f, None) == EALIGN
 
 
+def test_quantize_rht_validation():
+    L = nv.lib()
+    f, q = P(FAKE), L.nvfp4_quantize_rht
+    assert q(f, 16, 16, 2, 0, None, None, None, f, f, f, None) == EINVAL   # 16x16 tiles: not offered
+    assert b"per-tensor and per-token" in L.nvfp4_last_error()
+    assert q(f, 16, 16, 1, 1 << 16, None, None, None, f, f, f, None) == EINVAL   # mask has 16 bits
+    assert q(f, 16, 16, 1, 0, f, f, f, None, None, None, None) == EINVAL   # columnwise output required
+    assert q(f, 24, 16, 1, 0, None, None, None, f, f, f, None) == ESHAPE   # M % 16
+    assert q(f, 16, 24, 1, 0, f, f, f, f, f, f, None) == ESHAPE   # K % 16 with rowwise output
+    assert q(f, 65536 * 128, 16, 1, 0, None, None, None, f, f, f, None) == ESHAPE
+    assert q(P(FAKE + 2), 16, 16, 1, 0, None, None, None, f, f, f, None) == EALIGN
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

@@ -128,10 +128,11 @@ def copy_calibration(steps):
                       "bytes_written_per_launch": b.numel() * 2, "launches": steps}), flush=True)
 
 
-def all_configs(steps, warmup):
+def all_configs(steps, warmup, only=None):
     """One JSON line per named workload (not the headline line): average
     microseconds per call over `steps` timed calls with HIP events around
-    them, inputs rotating where three fit, and algorithmic GB/s."""
+    them, inputs rotating where three fit, and algorithmic GB/s (TFLOP/s for
+    the GEMM lines).  only: names of the lines to run (all if None)."""
     import numpy as np
     import torch
 
@@ -142,6 +143,8 @@ def all_configs(steps, warmup):
     to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=dev)
     f32 = lambda n: torch.empty(n, dtype=torch.float32, device=dev)
+
+    want = lambda *names: only is None or any(n in only for n in names)
 
     def timed(fn, n_inputs):
         for i in range(warmup):
@@ -171,76 +174,96 @@ def all_configs(steps, warmup):
         return 2 * m * k + m * k + m * k // 8 + 4 * amax_floats
 
     # C1: per-tensor rowwise 256 x 1024, then the dequantize round trip
-    x1 = to_dev(W.c1())
-    o1 = dict(row_q=u8(256, 512), row_sf=u8(256, 64), row_amax=f32(1))
-    report("C1", "per-tensor rowwise quantize, 256x1024", timed(lambda i: nv.quantize_into(x1, nv.PER_TENSOR, **o1), 1),
-           2 * 256 * 1024 + 256 * 512 + 256 * 64 + 4)
-    back = f32(256 * 1024)
-    report("C1-dequant", "dequantize of the C1 output to fp32", timed(
-        lambda i: nv.lib().nvfp4_dequantize(nv._ptr(o1["row_q"]), nv._ptr(o1["row_sf"]), nv._ptr(o1["row_amax"]), 256, 1024, 0,
-                                            nv._ptr(back), nv._stream(dev)), 1),
-           256 * 512 + 256 * 64 + 4 + 4 * 256 * 1024)
+    if want("C1", "C1-dequant"):
+        x1 = to_dev(W.c1())
+        o1 = dict(row_q=u8(256, 512), row_sf=u8(256, 64), row_amax=f32(1))
+        report("C1", "per-tensor rowwise quantize, 256x1024", timed(lambda i: nv.quantize_into(x1, nv.PER_TENSOR, **o1), 1),
+               2 * 256 * 1024 + 256 * 512 + 256 * 64 + 4)
+        back = f32(256 * 1024)
+        report("C1-dequant", "dequantize of the C1 output to fp32", timed(
+            lambda i: nv.lib().nvfp4_dequantize(nv._ptr(o1["row_q"]), nv._ptr(o1["row_sf"]), nv._ptr(o1["row_amax"]), 256, 1024, 0,
+                                                nv._ptr(back), nv._stream(dev)), 1),
+               256 * 512 + 256 * 64 + 4 + 4 * 256 * 1024)
     # C2: per-token row+col 4096 x 4096 with outliers
-    x2 = [to_dev(W.row_scaled_with_outliers(4096, 4096, 1002 + 7 * t)) for t in range(3)]
-    o2 = dict(row_q=u8(4096, 2048), row_sf=u8(4096, 256), row_amax=f32(4096),
-              col_q=u8(4096, 2048), col_sf=u8(4096, 256), col_amax=f32(4096))
-    report("C2", "per-token row+col, 4096x4096", timed(lambda i: nv.quantize_into(x2[i], nv.PER_TOKEN, **o2), 3),
-           cast_bytes(4096, 4096, 8192))
-    del x2
+    if want("C2"):
+        x2 = [to_dev(W.row_scaled_with_outliers(4096, 4096, 1002 + 7 * t)) for t in range(3)]
+        o2 = dict(row_q=u8(4096, 2048), row_sf=u8(4096, 256), row_amax=f32(4096),
+                  col_q=u8(4096, 2048), col_sf=u8(4096, 256), col_amax=f32(4096))
+        report("C2", "per-token row+col, 4096x4096", timed(lambda i: nv.quantize_into(x2[i], nv.PER_TOKEN, **o2), 3),
+               cast_bytes(4096, 4096, 8192))
+        del x2
     # C3: per-tensor and per-token row+col 16384 x 8192, Student-t
-    x3 = [to_dev(W.c3(t)) for t in range(3)]
-    o3 = dict(row_q=u8(M, K // 2), row_sf=u8(M, K // 16), row_amax=f32(M),
-              col_q=u8(K, M // 2), col_sf=u8(K, M // 16), col_amax=f32(K))
-    buf = torch.zeros(1, dtype=torch.float32, device=dev)
-    report("C3-per-token", "per-token row+col with the decayed amax update, 16384x8192",
-           timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TOKEN, buf, 0.9, **o3), 3), cast_bytes(M, K, M + K))
-    o3t = dict(o3, row_amax=f32(1), col_amax=f32(1))
-    report("C3-per-tensor", "per-tensor row+col with the decayed amax update, 16384x8192",
-           timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3), cast_bytes(M, K, 2))
-    report("C3-per-token-SR", "per-token row+col with stochastic rounding (Philox4x32-10 randoms), 16384x8192",
-           timed(lambda i: nv.quantize_sr_into(x3[i], nv.PER_TOKEN, 2024, i, **o3), 3), cast_bytes(M, K, M + K))
-    report("C3-per-token-RHT", "per-token row+col, columnwise through the 16-point random Hadamard transform, "
-           "16384x8192", timed(lambda i: nv.quantize_rht_into(x3[i], nv.PER_TOKEN, 0xB2E5, **o3), 3),
-           cast_bytes(M, K, M + K))
-    # the consumer: forward (TN) GEMM of the per-token C3 activation with an
-    # 8192 x 8192 weight cast per token
-    xa = nv.quantize(x3[0], nv.PER_TOKEN, columnwise=False)
-    wb = nv.quantize(to_dev(W.weight_with_outliers(K, K, 6006)), nv.PER_TOKEN, columnwise=False)
-    og = torch.empty((M, K), dtype=torch.float32, device=dev)
-    report_mfma("GEMM-TN", f"NVFP4 GEMM {M}x{K}x{K}, per-row A and B outer scales, fp32 out",
-                timed(lambda i: nv.gemm_into(og, xa["row_q"], xa["row_sf"], xa["row_amax"], wb["row_q"],
-                                             wb["row_sf"], wb["row_amax"]), 1), 2 * M * K * K)
-    del x3, o3, o3t, xa, wb, og
+    if want("C3-per-token", "C3-per-tensor", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN"):
+        x3 = [to_dev(W.c3(t)) for t in range(3)]
+        o3 = dict(row_q=u8(M, K // 2), row_sf=u8(M, K // 16), row_amax=f32(M),
+                  col_q=u8(K, M // 2), col_sf=u8(K, M // 16), col_amax=f32(K))
+        buf = torch.zeros(1, dtype=torch.float32, device=dev)
+        if want("C3-per-token"):
+            report("C3-per-token", "per-token row+col with the decayed amax update, 16384x8192",
+                   timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TOKEN, buf, 0.9, **o3), 3),
+                   cast_bytes(M, K, M + K))
+        o3t = dict(o3, row_amax=f32(1), col_amax=f32(1))
+        if want("C3-per-tensor"):
+            report("C3-per-tensor", "per-tensor row+col with the decayed amax update, 16384x8192",
+                   timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3),
+                   cast_bytes(M, K, 2))
+        if want("C3-per-token-SR"):
+            report("C3-per-token-SR", "per-token row+col with stochastic rounding (Philox4x32-10 randoms), "
+                   "16384x8192", timed(lambda i: nv.quantize_sr_into(x3[i], nv.PER_TOKEN, 2024, i, **o3), 3),
+                   cast_bytes(M, K, M + K))
+        if want("C3-per-token-RHT"):
+            report("C3-per-token-RHT", "per-token row+col, columnwise through the 16-point random Hadamard "
+                   "transform, 16384x8192", timed(lambda i: nv.quantize_rht_into(x3[i], nv.PER_TOKEN, 0xB2E5, **o3), 3),
+                   cast_bytes(M, K, M + K))
+        if want("GEMM-TN"):
+            # the consumer: forward (TN) GEMM of the per-token C3 activation
+            # with an 8192 x 8192 weight cast per token
+            xa = nv.quantize(x3[0], nv.PER_TOKEN, columnwise=False)
+            wb = nv.quantize(to_dev(W.weight_with_outliers(K, K, 6006)), nv.PER_TOKEN, columnwise=False)
+            og = torch.empty((M, K), dtype=torch.float32, device=dev)
+            report_mfma("GEMM-TN", f"NVFP4 GEMM {M}x{K}x{K}, per-row A and B outer scales, fp32 out",
+                        timed(lambda i: nv.gemm_into(og, xa["row_q"], xa["row_sf"], xa["row_amax"], wb["row_q"],
+                                                     wb["row_sf"], wb["row_amax"]), 1), 2 * M * K * K)
+            del xa, wb, og
+        del x3, o3, o3t
     # C4: grouped MoE, 64 experts, 32768 tokens x 4096
-    x4h, counts = W.c4()
-    x4 = to_dev(x4h)
-    T, K4 = x4h.shape
-    o4 = dict(row_q=u8(T, K4 // 2), row_sf=u8(T, K4 // 16), row_amax=f32(T),
-              col_q=u8(T * K4 // 2), col_sf=u8(T * K4 // 16), col_amax=f32(len(counts) * K4))
-    hc = (ctypes.c_int64 * len(counts))(*[int(c) for c in counts])
-    g = lambda i: nv.lib().nvfp4_quantize_grouped(
-        nv._ptr(x4), K4, len(counts), hc, nv._ptr(o4["row_q"]), nv._ptr(o4["row_sf"]), nv._ptr(o4["row_amax"]),
-        nv._ptr(o4["col_q"]), nv._ptr(o4["col_sf"]), nv._ptr(o4["col_amax"]), nv._stream(dev))
-    report("C4", f"grouped per-token row+col, {len(counts)} experts, {T}x{K4}", timed(g, 1),
-           cast_bytes(T, K4, T + len(counts) * K4))
-    # the grouped consumer: each expert's tokens times its own 2048 x 4096
-    # weight (seeded NVFP4 codes), per-row outer scales
-    N4 = 2048
-    bq, bsf, ba = (torch.from_numpy(t).to(dev) for t in W.nvfp4_operand(len(counts) * N4, K4, 4040))
-    bq, bsf = bq.view(len(counts), N4, K4 // 2), bsf.view(len(counts), N4, K4 // 16)
-    og = torch.empty((T, N4), dtype=torch.float32, device=dev)
-    report_mfma("GEMM-grouped", f"grouped NVFP4 GEMM over the C4 experts' rowwise output, {len(counts)} x "
-                f"({T} tokens in all) x {N4} x {K4}",
-                timed(lambda i: nv.gemm_grouped_into(og, o4["row_q"], o4["row_sf"], o4["row_amax"], bq, bsf, ba,
-                                                     counts), 1), 2 * T * N4 * K4)
-    del x4, o4, bq, bsf, ba, og
+    if want("C4", "GEMM-grouped"):
+        x4h, counts = W.c4()
+        x4 = to_dev(x4h)
+        T, K4 = x4h.shape
+        o4 = dict(row_q=u8(T, K4 // 2), row_sf=u8(T, K4 // 16), row_amax=f32(T),
+                  col_q=u8(T * K4 // 2), col_sf=u8(T * K4 // 16), col_amax=f32(len(counts) * K4))
+        hc = (ctypes.c_int64 * len(counts))(*[int(c) for c in counts])
+        g = lambda i: nv.lib().nvfp4_quantize_grouped(
+            nv._ptr(x4), K4, len(counts), hc, nv._ptr(o4["row_q"]), nv._ptr(o4["row_sf"]), nv._ptr(o4["row_amax"]),
+            nv._ptr(o4["col_q"]), nv._ptr(o4["col_sf"]), nv._ptr(o4["col_amax"]), nv._stream(dev))
+        if want("C4"):
+            report("C4", f"grouped per-token row+col, {len(counts)} experts, {T}x{K4}", timed(g, 1),
+                   cast_bytes(T, K4, T + len(counts) * K4))
+        else:
+            g(0)   # the GEMM line below consumes the cast's rowwise output
+        if want("GEMM-grouped"):
+            # the grouped consumer: each expert's tokens times its own
+            # 2048 x 4096 weight (seeded NVFP4 codes), per-row outer scales
+            N4 = 2048
+            bq, bsf, ba = (torch.from_numpy(t).to(dev) for t in W.nvfp4_operand(len(counts) * N4, K4, 4040))
+            bq, bsf = bq.view(len(counts), N4, K4 // 2), bsf.view(len(counts), N4, K4 // 16)
+            og = torch.empty((T, N4), dtype=torch.float32, device=dev)
+            report_mfma("GEMM-grouped", f"grouped NVFP4 GEMM over the C4 experts' rowwise output, {len(counts)} x "
+                        f"({T} tokens in all) x {N4} x {K4}",
+                        timed(lambda i: nv.gemm_grouped_into(og, o4["row_q"], o4["row_sf"], o4["row_amax"], bq, bsf,
+                                                             ba, counts), 1), 2 * T * N4 * K4)
+            del bq, bsf, ba, og
+        del x4, o4
     # C5: 16x16 tiles, 8192 x 28672 weight, per-token-layout emission
-    M5, K5 = 8192, 28672
-    x5 = to_dev(W.c5())
-    o5 = dict(row_q=u8(M5, K5 // 2), row_sf=u8(M5, K5 // 16), row_amax=f32(M5),
-              col_q=u8(K5, M5 // 2), col_sf=u8(K5, M5 // 16), col_amax=f32(K5))
-    report("C5", "16x16-tile row+col, 8192x28672 weight", timed(lambda i: nv.quantize_into(x5, nv.TILE_16x16, **o5), 1),
-           cast_bytes(M5, K5, M5 + K5))
+    if want("C5"):
+        M5, K5 = 8192, 28672
+        x5 = to_dev(W.c5())
+        o5 = dict(row_q=u8(M5, K5 // 2), row_sf=u8(M5, K5 // 16), row_amax=f32(M5),
+                  col_q=u8(K5, M5 // 2), col_sf=u8(K5, M5 // 16), col_amax=f32(K5))
+        report("C5", "16x16-tile row+col, 8192x28672 weight", timed(lambda i: nv.quantize_into(x5, nv.TILE_16x16, **o5), 1),
+               cast_bytes(M5, K5, M5 + K5))
+
 
 
 def cpu_baseline(inputs):
@@ -266,6 +289,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="with --all-configs: comma-separated line names to run (e.g. GEMM-TN)")
     ap.add_argument("--all-configs", action="store_true",
                     help="time every named workload (one JSON line each) instead of the headline step")
     ap.add_argument("--trace-every", type=int, default=5,
@@ -281,7 +306,7 @@ def main():
         copy_calibration(args.steps)
         return
     if args.all_configs:
-        all_configs(args.steps, args.warmup)
+        all_configs(args.steps, args.warmup, args.only.split(",") if args.only else None)
         return
 
     import numpy as np

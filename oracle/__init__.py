@@ -59,6 +59,9 @@ def _load():
         "orc_gemm_nvfp4": (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64,
                                           _p, _p]),
         "orc_rht16": (None, [_p, ctypes.c_uint32, _p]),
+        "orc_swizzled_size": (_i64, [_i64, _i64]),
+        "orc_swizzle_scales": (ctypes.c_int, [_p, _i64, _i64, _p]),
+        "orc_unswizzle_scales": (ctypes.c_int, [_p, _i64, _i64, _p]),
         "orc_rht_columns": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_uint32, _p]),
     }
     for name, (res, args) in sig.items():
@@ -314,6 +317,28 @@ def quantize_rht(x, mode, sign_mask, rowwise=True):
     out = quantize(x, mode, rowwise=True, columnwise=False) if rowwise else {}
     out.update(quantize(rht_columns(x, sign_mask), mode, rowwise=False, columnwise=True))
     return out
+
+
+# ------------------------------------------------ swizzled scale layout
+
+def swizzle_scales(sf):
+    """Plain scales uint8 [R, nb] -> the GEMM-swizzled layout, 1-D uint8 of
+    ceil(R/128)*128 * ceil(nb/4)*4 bytes (padding zero)."""
+    sf = np.ascontiguousarray(sf, np.uint8)
+    R, nb = sf.shape
+    out = np.empty(int(_load().orc_swizzled_size(R, nb)), np.uint8)
+    _load().orc_swizzle_scales(_ptr(sf), R, nb, _ptr(out))
+    return out
+
+
+def unswizzle_scales(sw, R, nb):
+    """Inverse of swizzle_scales: the [R, nb] plain scales."""
+    sw = np.ascontiguousarray(sw, np.uint8).ravel()
+    if sw.size != int(_load().orc_swizzled_size(R, nb)):
+        raise ValueError("swizzled buffer has the wrong size")
+    sf = np.empty((R, nb), np.uint8)
+    _load().orc_unswizzle_scales(_ptr(sw), R, nb, _ptr(sf))
+    return sf
 
 
 def quantize_grouped(x, counts, rowwise=True, columnwise=True):

@@ -701,3 +701,48 @@ int orc_rht_columns(const uint16_t* x, int64_t M, int64_t K, uint32_t sign_mask,
         }
     return 0;
 }
+
+/* -------------------------------------------- GEMM-swizzled scale layout */
+
+/* The per-token recipe page keeps block scales unswizzled
+ * (with_gemm_swizzled_scales off, with_swizzle=0) and leaves the swizzled
+ * layout to the GEMM consumer; the pages do not define it.  Reading: the
+ * tiled layout block-scaled GEMMs take for 16-element FP4 blocks, written
+ * here from its definition.  For a scale matrix sf [R][nb] (row r, block c):
+ *   Rp = R rounded up to 128, nbp = nb rounded up to 4;
+ *   tiles of 128 rows x 4 blocks, 512 bytes each, row-tile major:
+ *     tile(r, c) = (r / 128) * (nbp / 4) + c / 4
+ *   inside a tile, row r lands in 16-byte line r % 32 at 4-byte slot
+ *   (r / 32) % 4, block c at byte c % 4 of the slot:
+ *     offset(r, c) = 512 * tile(r, c) + 16 * (r % 32) + 4 * ((r / 32) % 4) + c % 4
+ * Bytes of the Rp * nbp layout that no (r < R, c < nb) maps to are zero. */
+int64_t orc_swizzled_size(int64_t R, int64_t nb)
+{
+    return ((R + 127) / 128 * 128) * ((nb + 3) / 4 * 4);
+}
+
+int orc_swizzle_scales(const uint8_t* sf, int64_t R, int64_t nb, uint8_t* out)
+{
+    if (R < 0 || nb < 0) return -1;
+    const int64_t nbp = (nb + 3) / 4 * 4;
+    memset(out, 0, (size_t)orc_swizzled_size(R, nb));
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < nb; ++c) {
+            int64_t tile = (r / 128) * (nbp / 4) + c / 4;
+            int64_t off = 512 * tile + 16 * (r % 32) + 4 * ((r / 32) % 4) + c % 4;
+            out[off] = sf[r * nb + c];
+        }
+    return 0;
+}
+
+int orc_unswizzle_scales(const uint8_t* in, int64_t R, int64_t nb, uint8_t* sf)
+{
+    if (R < 0 || nb < 0) return -1;
+    const int64_t nbp = (nb + 3) / 4 * 4;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < nb; ++c) {
+            int64_t tile = (r / 128) * (nbp / 4) + c / 4;
+            sf[r * nb + c] = in[512 * tile + 16 * (r % 32) + 4 * ((r / 32) % 4) + c % 4];
+        }
+    return 0;
+}

@@ -111,6 +111,12 @@ int orc_gemm_nvfp4(const uint8_t* aq, const uint8_t* asf, const float* aamax, in
 void orc_rht16(const uint16_t in[16], uint32_t sign_mask, uint16_t out[16]);
 int  orc_rht_columns(const uint16_t* x, int64_t M, int64_t K, uint32_t sign_mask, uint16_t* y);
 
+/* GEMM-swizzled scale layout (definition in nvfp4_oracle.c): size in bytes,
+ * plain [R][nb] -> swizzled (padding zeroed) and back */
+int64_t orc_swizzled_size(int64_t R, int64_t nb);
+int     orc_swizzle_scales(const uint8_t* sf, int64_t R, int64_t nb, uint8_t* out);
+int     orc_unswizzle_scales(const uint8_t* in, int64_t R, int64_t nb, uint8_t* sf);
+
 #ifdef __cplusplus
 }
 #endif

@@ -193,7 +193,7 @@ def all_configs(steps, warmup, only=None):
                cast_bytes(4096, 4096, 8192))
         del x2
     # C3: per-tensor and per-token row+col 16384 x 8192, Student-t
-    if want("C3-per-token", "C3-per-tensor", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN"):
+    if want("C3-per-token", "C3-per-tensor", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN", "GEMM-TN-swizzled"):
         x3 = [to_dev(W.c3(t)) for t in range(3)]
         o3 = dict(row_q=u8(M, K // 2), row_sf=u8(M, K // 16), row_amax=f32(M),
                   col_q=u8(K, M // 2), col_sf=u8(K, M // 16), col_amax=f32(K))
@@ -215,15 +215,28 @@ def all_configs(steps, warmup, only=None):
             report("C3-per-token-RHT", "per-token row+col, columnwise through the 16-point random Hadamard "
                    "transform, 16384x8192", timed(lambda i: nv.quantize_rht_into(x3[i], nv.PER_TOKEN, 0xB2E5, **o3), 3),
                    cast_bytes(M, K, M + K))
-        if want("GEMM-TN"):
+        if want("GEMM-TN", "GEMM-TN-swizzled"):
             # the consumer: forward (TN) GEMM of the per-token C3 activation
             # with an 8192 x 8192 weight cast per token
             xa = nv.quantize(x3[0], nv.PER_TOKEN, columnwise=False)
             wb = nv.quantize(to_dev(W.weight_with_outliers(K, K, 6006)), nv.PER_TOKEN, columnwise=False)
             og = torch.empty((M, K), dtype=torch.float32, device=dev)
-            report_mfma("GEMM-TN", f"NVFP4 GEMM {M}x{K}x{K}, per-row A and B outer scales, fp32 out",
-                        timed(lambda i: nv.gemm_into(og, xa["row_q"], xa["row_sf"], xa["row_amax"], wb["row_q"],
-                                                     wb["row_sf"], wb["row_amax"]), 1), 2 * M * K * K)
+            if want("GEMM-TN"):
+                report_mfma("GEMM-TN", f"NVFP4 GEMM {M}x{K}x{K}, per-row A and B outer scales, fp32 out",
+                            timed(lambda i: nv.gemm_into(og, xa["row_q"], xa["row_sf"], xa["row_amax"], wb["row_q"],
+                                                         wb["row_sf"], wb["row_amax"]), 1), 2 * M * K * K)
+            if want("GEMM-TN-swizzled"):
+                # the same product reading both operands' scales in the
+                # GEMM-swizzled layout, and the swizzle of the activation's scales
+                asw, bsw = nv.swizzle_scales(xa["row_sf"]), nv.swizzle_scales(wb["row_sf"])
+                report("swizzle-C3-row", f"GEMM-swizzled layout of the C3 rowwise scales ({M}x{K // 16})",
+                       timed(lambda i: nv.lib().nvfp4_swizzle_scales(nv._ptr(xa["row_sf"]), M, K // 16, nv._ptr(asw),
+                                                                     nv._stream(dev)), 1),
+                       M * (K // 16) + asw.numel())
+                report_mfma("GEMM-TN-swizzled", f"NVFP4 GEMM {M}x{K}x{K} with GEMM-swizzled scales",
+                            timed(lambda i: nv.gemm_swizzled_into(og, xa["row_q"], asw, xa["row_amax"], wb["row_q"],
+                                                                  bsw, wb["row_amax"]), 1), 2 * M * K * K)
+                del asw, bsw
             del xa, wb, og
         del x3, o3, o3t
     # C4: grouped MoE, 64 experts, 32768 tokens x 4096

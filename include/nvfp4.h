@@ -270,6 +270,36 @@ NVFP4_API nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const
                         int64_t M, int64_t N, int64_t K, float* out, void* stream);
 
 /*
+ * GEMM-swizzled scale layout.  The per-token recipe page emits unswizzled
+ * scales and leaves the swizzled layout to its GEMM (PR #3045: GEMM-swizzled
+ * scales off, with_swizzle=0) without defining it; this library takes the
+ * tiled layout of block-scaled GEMMs for 16-element FP4 blocks.  For a plain
+ * scale matrix sf [R][nb] (row r, block c; nb = C/16), with Rp = R rounded
+ * up to 128 and nbp = nb rounded up to 4, the swizzled buffer holds Rp * nbp
+ * bytes in 512-byte tiles of 128 rows x 4 blocks, row-tile major:
+ *   byte(r, c) = 512 * ((r / 128) * (nbp / 4) + c / 4)
+ *              + 16 * (r % 32) + 4 * ((r / 32) % 4) + c % 4
+ * and every byte no (r < R, c < nb) maps to is zero.  A row's four blocks of
+ * a tile sit in one 4-byte word.
+ *
+ * nvfp4_swizzle_scales writes all Rp * nbp bytes of `out` (4-byte aligned,
+ * EALIGN) from plain sf [R][nb] (e.g. the cast's row_sf with nb = K/16, or
+ * col_sf with R = K, nb = M/16).  Sizes < 0: EINVAL.
+ */
+NVFP4_API nvfp4_status nvfp4_swizzle_scales(const uint8_t* sf, int64_t R, int64_t nb, uint8_t* out,
+                                  void* stream);
+
+/*
+ * nvfp4_gemm with both operands' scales in the swizzled layout above (a_sf
+ * of R = M rows, b_sf of R = N rows, nb = K/16 each; 4-byte aligned, EALIGN).
+ * Same arithmetic, results bit-identical to nvfp4_gemm on the plain scales.
+ */
+NVFP4_API nvfp4_status nvfp4_gemm_swizzled(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax,
+                                 int a_per_row, const uint8_t* b_q, const uint8_t* b_sf,
+                                 const float* b_amax, int b_per_row, int64_t M, int64_t N, int64_t K,
+                                 float* out, void* stream);
+
+/*
  * Grouped NVFP4 GEMM for MoE experts, one launch per 128 groups (the page's
  * native grouped per-token GEMM over a pointer array of experts, PR #3045
  * "Changes"): A holds the tokens of num_groups experts back to back, h_counts

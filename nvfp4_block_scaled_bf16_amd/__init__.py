@@ -29,7 +29,8 @@ EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_qua
            "nvfp4_quantize_columnwise", "nvfp4_amax", "nvfp4_encode", "nvfp4_quantize_grouped",
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
            "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm",
-           "nvfp4_gemm_grouped", "nvfp4_quantize_rht")
+           "nvfp4_gemm_grouped", "nvfp4_quantize_rht", "nvfp4_swizzle_scales",
+           "nvfp4_gemm_swizzled")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "nvfp4_gemm": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
         "nvfp4_gemm_grouped": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i32, p, i64, i64, p, p]),
         "nvfp4_quantize_rht": (st, [p, i64, i64, st, ctypes.c_uint32, p, p, p, p, p, p, p]),
+        "nvfp4_swizzle_scales": (st, [p, i64, i64, p, p]),
+        "nvfp4_gemm_swizzled": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -302,6 +305,40 @@ def gemm_into(out, a_q, a_sf, a_amax, b_q, b_sf, b_amax):
         raise ValueError("out must be fp32 [M, N]")
     _check(lib().nvfp4_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_amax), apr, _ptr(b_q), _ptr(b_sf), _ptr(b_amax), bpr,
                             M, N, K, _ptr(out), _stream(a_q.device)))
+    return out
+
+
+def swizzled_size(R: int, nb: int) -> int:
+    """Bytes of the GEMM-swizzled layout of an [R, nb] scale matrix."""
+    return (R + 127) // 128 * 128 * ((nb + 3) // 4 * 4)
+
+
+def swizzle_scales(sf):
+    """Plain scales uint8 [R, nb] -> the GEMM-swizzled layout (1-D uint8)."""
+    if sf.dim() != 2 or sf.dtype != torch.uint8:
+        raise ValueError("sf must be a 2-D uint8 tensor [R, nb]")
+    R, nb = sf.shape
+    out = _u8(swizzled_size(R, nb), sf.device)
+    _check(lib().nvfp4_swizzle_scales(_ptr(sf.contiguous()), R, nb, _ptr(out), _stream(sf.device)))
+    return out
+
+
+def gemm_swizzled_into(out, a_q, a_sw, a_amax, b_q, b_sw, b_amax):
+    """:func:`gemm_into` with both operands' scales in the swizzled layout
+    (1-D, as :func:`swizzle_scales` returns them)."""
+    if a_q.dim() != 2 or b_q.dim() != 2:
+        raise ValueError("a_q and b_q must be 2-D [rows, K/2]")
+    M, K, N = a_q.shape[0], 2 * a_q.shape[1], b_q.shape[0]
+    if 2 * b_q.shape[1] != K:
+        raise ValueError("contraction sizes differ")
+    if a_sw.numel() != swizzled_size(M, K // 16) or b_sw.numel() != swizzled_size(N, K // 16):
+        raise ValueError("swizzled scales have the wrong size")
+    if tuple(out.shape) != (M, N) or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [M, N]")
+    apr = int(a_amax.numel() == M and M != 1)
+    bpr = int(b_amax.numel() == N and N != 1)
+    _check(lib().nvfp4_gemm_swizzled(_ptr(a_q), _ptr(a_sw), _ptr(a_amax), apr, _ptr(b_q), _ptr(b_sw),
+                                     _ptr(b_amax), bpr, M, N, K, _ptr(out), _stream(a_q.device)))
     return out
 
 

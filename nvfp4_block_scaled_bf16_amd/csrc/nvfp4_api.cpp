@@ -367,9 +367,11 @@ nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* 
     return s != NVFP4_OK ? s : ok();
 }
 
-nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
-                        const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
-                        int64_t M, int64_t N, int64_t K, float* out, void* stream) {
+namespace {
+
+nvfp4_status gemm_impl(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                       const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                       int64_t M, int64_t N, int64_t K, float* out, void* stream, bool swizzled) {
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "negative size");
     if (K % 16 != 0) return fail(NVFP4_ESHAPE, "gemm needs K %% 16 == 0 (K=%lld)", (long long)K);
     if (K > kMaxGemmK) return fail(NVFP4_ESHAPE, "gemm needs K <= %lld (K=%lld)", (long long)kMaxGemmK, (long long)K);
@@ -381,10 +383,36 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_
     if (!aligned(a_q, 16) || !aligned(b_q, 16)) return fail(NVFP4_EALIGN, "a_q and b_q must be 16-byte aligned");
     if (!aligned(a_amax, 4) || !aligned(b_amax, 4) || !aligned(out, 4))
         return fail(NVFP4_EALIGN, "amax and out must be 4-byte aligned");
+    if (swizzled && (!aligned(a_sf, 4) || !aligned(b_sf, 4)))
+        return fail(NVFP4_EALIGN, "swizzled scales must be 4-byte aligned");
     nvfp4_status s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
         return launch_gemm_nvfp4(a_q, a_sf, a_amax, a_per_row ? 1 : 0, b_q, b_sf, b_amax, b_per_row ? 1 : 0, M, N, K,
-                                 out, as_stream(stream), b, a);
+                                 out, as_stream(stream), b, a, swizzled);
     });
+    return s != NVFP4_OK ? s : ok();
+}
+
+}  // namespace
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                        const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                        int64_t M, int64_t N, int64_t K, float* out, void* stream) {
+    return gemm_impl(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, stream, false);
+}
+
+nvfp4_status nvfp4_gemm_swizzled(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
+                                 const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
+                                 int64_t M, int64_t N, int64_t K, float* out, void* stream) {
+    return gemm_impl(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, stream, true);
+}
+
+nvfp4_status nvfp4_swizzle_scales(const uint8_t* sf, int64_t R, int64_t nb, uint8_t* out, void* stream) {
+    if (R < 0 || nb < 0) return fail(NVFP4_EINVAL, "negative size");
+    if (R > ((int64_t)1 << 40) || nb > ((int64_t)1 << 24)) return fail(NVFP4_ESHAPE, "scale matrix too large");
+    if (R == 0 || nb == 0) return ok();
+    if (!sf || !out) return fail(NVFP4_EINVAL, "NULL argument");
+    if (!aligned(out, 4)) return fail(NVFP4_EALIGN, "out must be 4-byte aligned");
+    nvfp4_status s = check_hip(launch_swizzle_scales(sf, R, nb, out, as_stream(stream)), "swizzle");
     return s != NVFP4_OK ? s : ok();
 }
 

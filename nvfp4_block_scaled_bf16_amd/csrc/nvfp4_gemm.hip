@@ -57,11 +57,26 @@ struct RowPiece {
     uint32_t sf;        // two scale codes: low byte, next byte
 };
 
+// Byte offset of scale block c of row `row` (both within the operand tile,
+// whose first row is a multiple of 128).  Plain: row-major [rows][K/16].
+// Swizzled (SWZ): the GEMM layout of 128-row x 4-block tiles of 512 bytes,
+// row-tile major, row r in 16-byte line r % 32 at 4-byte slot (r / 32) % 4,
+// block c at byte c % 4; nbp = K/16 rounded up to 4.  Blocks c and c + 1 (c
+// even) are adjacent in both.
+template <bool SWZ>
+__device__ __forceinline__ uint32_t scale_offset(uint32_t row, uint32_t c, uint32_t K) {
+    if (!SWZ) return row * (K / 16) + c;
+    const uint32_t nbp = (K / 16 + 3) & ~3u;
+    return (row >> 7) * (128u * nbp) + (c >> 2) * 512u + (row & 31u) * 16u + ((row >> 5) & 3u) * 4u + (c & 3u);
+}
+
 // row: the row within the operand tile (descriptors q_rs / s_rs start at the
-// tile's first row and end after its last valid row); k0 % 32 == 0
+// tile's first row and end after its last valid row, for swizzled scales
+// after its last 128-row group); k0 % 32 == 0
+template <bool SWZ>
 __device__ __forceinline__ RowPiece load_piece(__amdgpu_buffer_rsrc_t q_rs, __amdgpu_buffer_rsrc_t s_rs, uint32_t row,
                                                uint32_t K, uint32_t k0) {
-    const uint32_t off = row * (K / 2) + k0 / 2, soff = row * (K / 16) + k0 / 16;
+    const uint32_t off = row * (K / 2) + k0 / 2, soff = scale_offset<SWZ>(row, k0 / 16, K);
     const bool lo_ok = k0 < K, hi_ok = k0 + 16 < K;
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(q_rs, lo_ok ? off : kOob, 0, 0);
@@ -114,7 +129,7 @@ __device__ __forceinline__ uint32_t xcd_tile() {
 }
 
 // the output tile at (m0, n0) of out [M][N] = A [M][K] x B [N][K]^T
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, bool SWZ>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf,
                                           const float* __restrict__ a_amax, int a_per_row,
                                           const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
@@ -137,9 +152,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
     const uint32_t va = (uint32_t)(M - m0 < TM ? M - m0 : TM), vb = (uint32_t)(N - n0 < TN ? N - n0 : TN);
     const uint32_t Ku = (uint32_t)K;
     const __amdgpu_buffer_rsrc_t aq_rs = gemm_rsrc(a_q + m0 * (K / 2), va * (Ku / 2));
-    const __amdgpu_buffer_rsrc_t as_rs = gemm_rsrc(a_sf + m0 * (K / 16), va * (Ku / 16));
     const __amdgpu_buffer_rsrc_t bq_rs = gemm_rsrc(b_q + n0 * (K / 2), vb * (Ku / 2));
-    const __amdgpu_buffer_rsrc_t bs_rs = gemm_rsrc(b_sf + n0 * (K / 16), vb * (Ku / 16));
+    // swizzled scales: the tile's whole 128-row groups (their padding bytes
+    // multiply rows that read as zeros)
+    const uint32_t nbp = (Ku / 16 + 3) & ~3u;
+    const __amdgpu_buffer_rsrc_t as_rs =
+        SWZ ? gemm_rsrc(a_sf + m0 * nbp, ((va + 127u) & ~127u) * nbp) : gemm_rsrc(a_sf + m0 * (K / 16), va * (Ku / 16));
+    const __amdgpu_buffer_rsrc_t bs_rs =
+        SWZ ? gemm_rsrc(b_sf + n0 * nbp, ((vb + 127u) & ~127u) * nbp) : gemm_rsrc(b_sf + n0 * (K / 16), vb * (Ku / 16));
 
     // pc: bytes of the next K step (dequantized into LDS during this step);
     // pn: the step after, loaded a whole step ahead of its use
@@ -149,8 +169,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
         for (int i = 0; i < P; ++i) {
             const int p = t + NT * i, r = p >> 1;
             const uint32_t k0 = kbase + 32 * (p & 1);
-            if ((NT * i) / 2 < TM) dst[i] = load_piece(aq_rs, as_rs, (uint32_t)r, Ku, k0);
-            else dst[i] = load_piece(bq_rs, bs_rs, (uint32_t)(r - TM), Ku, k0);
+            if ((NT * i) / 2 < TM) dst[i] = load_piece<SWZ>(aq_rs, as_rs, (uint32_t)r, Ku, k0);
+            else dst[i] = load_piece<SWZ>(bq_rs, bs_rs, (uint32_t)(r - TM), Ku, k0);
         }
     };
     auto store_all = [&](const RowPiece* src, int buf) {
@@ -219,7 +239,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
 }
 
 // Grid: cdiv(M, TM) * cdiv(N, TN) workgroups (one dimension); ntn = cdiv(N, TN).
-template <int TM, int TN, int WM, int WN>
+// SWZ: both operands' scales in the swizzled layout.
+template <int TM, int TN, int WM, int WN, bool SWZ>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
     int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
@@ -227,8 +248,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     float* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) GemmLds<TM, TN> S;
     const uint32_t tile = xcd_tile();
-    gemm_tile<TM, TN, WM, WN>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K,
-                              (int64_t)(tile / ntn) * TM, (int64_t)(tile % ntn) * TN, out, S);
+    gemm_tile<TM, TN, WM, WN, SWZ>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K,
+                                   (int64_t)(tile / ntn) * TM, (int64_t)(tile % ntn) * TN, out, S);
 }
 
 // Grouped: group g (the table's entry g, expert first + g) multiplies A's
@@ -252,37 +273,76 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     }
     const uint32_t local = tile - gg.tstart[lo];
     const int64_t off = gg.off[lo], e = (int64_t)gg.first + lo;
-    gemm_tile<TM, TN, WM, WN>(a_q + off * (K / 2), a_sf + off * (K / 16), a_amax + (a_per_row ? off : 0), a_per_row,
+    gemm_tile<TM, TN, WM, WN, false>(a_q + off * (K / 2), a_sf + off * (K / 16), a_amax + (a_per_row ? off : 0), a_per_row,
                               b_q + e * N * (K / 2), b_sf + e * N * (K / 16), b_amax + (b_per_row ? e * N : e),
                               b_per_row, gg.cnt[lo], N, K, (int64_t)(local / ntn) * TM,
                               (int64_t)(local % ntn) * TN, out + off * N, S);
 }
 
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, bool SWZ>
 hipError_t launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                       const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row, int64_t M,
                       int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const int64_t ntn = (N + TN - 1) / TN, ntiles = ntn * ((M + TM - 1) / TM);
     if (ntiles > kMaxGemmTiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL(k_gemm_nvfp4<TM, TN, WM, WN>, dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, st, ev0, ev1,
+    hipExtLaunchKernelGGL(k_gemm_nvfp4<TM, TN, WM, WN, SWZ>, dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, st, ev0, ev1,
                           0, a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, (uint32_t)ntn, out);
     return hipGetLastError();
 }
 
 }  // namespace
 
+namespace {
+
+// Scales [R][nb] -> the swizzled layout (see scale_offset): one thread per
+// output dword, which holds the four blocks 4 cb .. 4 cb + 3 of one row;
+// bytes for rows >= R or blocks >= nb are zero.  Grid-stride over ndw dwords.
+__global__ __launch_bounds__(256) void k_swizzle_scales(const uint8_t* __restrict__ sf, int64_t R, int64_t nb,
+                                                        uint32_t* __restrict__ out, int64_t ndw) {
+    const int64_t nbq = (nb + 3) / 4;
+    for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < ndw; d += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = d / 128, w = d % 128;
+        const int64_t r = (t / nbq) * 128 + (w & 3) * 32 + (w >> 2), c0 = (t % nbq) * 4;
+        uint32_t v = 0u;
+        if (r < R) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (c0 + j < nb) v |= (uint32_t)sf[r * nb + c0 + j] << (8 * j);
+        }
+        out[d] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_swizzle_scales(const uint8_t* sf, int64_t R, int64_t nb, uint8_t* out, hipStream_t st) {
+    const int64_t ndw = ((R + 127) / 128 * 128) * ((nb + 3) / 4 * 4) / 4;
+    if (ndw <= 0) return hipSuccess;
+    int64_t grid = (ndw + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(k_swizzle_scales, dim3((unsigned)grid), dim3(256), 0, st, sf, R, nb,
+                       reinterpret_cast<uint32_t*>(out), ndw);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                              const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                              int64_t M, int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0,
-                             hipEvent_t ev1) {
+                             hipEvent_t ev1, bool swizzled) {
     if (M <= 0 || N <= 0) return hipSuccess;
     // 256 x 256 tiles (8 waves of 128 x 64) once they fill the 256 CUs, else
     // 128 x 128 tiles (4 waves of 64 x 64) for four times the workgroups
-    if (((M + 255) / 256) * ((N + 255) / 256) >= 256)
-        return launch_cfg<256, 256, 2, 4>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out,
-                                          st, ev0, ev1);
-    return launch_cfg<128, 128, 2, 2>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, st,
-                                      ev0, ev1);
+    const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= 256;
+#define NVFP4_GEMM_LAUNCH(TM, TN, WM, WN, SW)                                                                       \
+    return launch_cfg<TM, TN, WM, WN, SW>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, \
+                                          st, ev0, ev1)
+    if (swizzled) {
+        if (big) NVFP4_GEMM_LAUNCH(256, 256, 2, 4, true);
+        NVFP4_GEMM_LAUNCH(128, 128, 2, 2, true);
+    }
+    if (big) NVFP4_GEMM_LAUNCH(256, 256, 2, 4, false);
+    NVFP4_GEMM_LAUNCH(128, 128, 2, 2, false);
+#undef NVFP4_GEMM_LAUNCH
 }
 
 namespace {

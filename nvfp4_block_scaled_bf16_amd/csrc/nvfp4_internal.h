@@ -46,10 +46,14 @@ hipError_t launch_rht_columnwise(int mode, const uint16_t* x, int64_t M, int64_t
 constexpr int64_t kMaxGemmTiles = (int64_t(1) << 31) - 1;
 // the GEMM kernel addresses a tile's operand rows with 32-bit byte offsets
 constexpr int64_t kMaxGemmK = int64_t(1) << 23;
+// swizzled: both operands' scales in the GEMM-swizzled layout
 hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                              const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                              int64_t M, int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0,
-                             hipEvent_t ev1);
+                             hipEvent_t ev1, bool swizzled);
+// plain scales [R][nb] -> GEMM-swizzled layout (out 4-byte aligned, all of
+// its ceil(R/128)*128 * ceil(nb/4)*4 bytes written)
+hipError_t launch_swizzle_scales(const uint8_t* sf, int64_t R, int64_t nb, uint8_t* out, hipStream_t st);
 // grouped GEMM: groups of A's rows, each with its own B, a bounded number per
 // launch (the table travels in the kernel arguments)
 constexpr int kMaxGemmGroups = 128;

@@ -158,6 +158,19 @@ def test_quantize_rht_validation():
     assert q(P(FAKE + 2), 16, 16, 1, 0, None, None, None, f, f, f, None) == EALIGN
 
 
+def test_swizzle_and_swizzled_gemm_validation():
+    L = nv.lib()
+    f = P(FAKE)
+    assert L.nvfp4_swizzle_scales(f, -1, 4, f, None) == EINVAL
+    assert L.nvfp4_swizzle_scales(None, 0, 4, None, None) == 0   # nothing to do
+    assert L.nvfp4_swizzle_scales(None, 4, 4, f, None) == EINVAL
+    assert L.nvfp4_swizzle_scales(f, 4, 4, P(FAKE + 2), None) == EALIGN
+    g = L.nvfp4_gemm_swizzled
+    assert g(f, f, f, 1, f, f, f, 1, 16, 16, 24, f, None) == ESHAPE
+    assert g(f, P(FAKE + 2), f, 1, f, f, f, 1, 16, 16, 16, f, None) == EALIGN   # swizzled scales 4-aligned
+    assert g(f, f, f, 1, f, f, f, 1, 0, 16, 16, None, None) == 0
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

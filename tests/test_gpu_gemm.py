@@ -17,7 +17,7 @@ import torch
 
 import nvfp4_block_scaled_bf16_amd as nv
 from nvfp4_block_scaled_bf16_amd import workloads as W
-from tests.gpu_util import host
+from tests.gpu_util import host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -253,3 +253,50 @@ def test_gemm_grouped_large_tiles_sampled(oracle):
             ref, bound = oracle.gemm_nvfp4(a[0][rs], a[1][rs], a[2][rs], b[0][e][cs], b[1][e][cs], b[2][e:e + 1])
             _check(out[rs, cs], ref, bound, K, f"group {e} block ({r0},{c0})")
         off += int(c)
+
+
+# ---------------------------------------------------- swizzled scale layout
+
+@pytest.mark.parametrize("shape", [(1, 1), (130, 5), (257, 9), (1000, 3), (4096, 512), (8192, 1024)])
+def test_swizzle_scales_bit_exact(oracle, shape):
+    rng = np.random.Generator(np.random.PCG64(sum(shape)))
+    sf = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    _announce(f"swizzle scales {shape}")
+    got = host(nv.swizzle_scales(_dev(sf)[0]))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, oracle.swizzle_scales(sf))
+
+
+def test_swizzle_of_cast_outputs(oracle):
+    # the cast's rowwise and columnwise scales, swizzled on the GPU, against
+    # the oracle's swizzle of the oracle's cast
+    x = W.row_scaled_with_outliers(272, 528, 111)
+    _announce("swizzle of the cast's scales 272x528")
+    out = nv.quantize(to_dev(x), nv.PER_TOKEN)
+    ref = oracle.quantize(x, nv.PER_TOKEN)
+    row = host(nv.swizzle_scales(out["row_sf"]))
+    col = host(nv.swizzle_scales(out["col_sf"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(row, oracle.swizzle_scales(ref["row_sf"]))
+    assert np.array_equal(col, oracle.swizzle_scales(ref["col_sf"]))
+
+
+@pytest.mark.parametrize("shape", [(130, 200, 272), (300, 520, 1040), (4000, 4100, 272)])
+def test_gemm_swizzled_equals_plain(oracle, shape):
+    # same arithmetic: bit-identical to the plain-layout GEMM; the small
+    # shape also against the oracle
+    M, N, K = shape
+    _announce(f"gemm swizzled M={M} N={N} K={K}")
+    a = W.nvfp4_operand(M, K, 121)
+    b = W.nvfp4_operand(N, K, 122, per_row=False)
+    da, db = _dev(*a), _dev(*b)
+    plain = nv.gemm(*da, *db)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    asw = _dev(oracle.swizzle_scales(a[1]))[0]
+    bsw = _dev(oracle.swizzle_scales(b[1]))[0]
+    nv.gemm_swizzled_into(out, da[0], asw, da[2], db[0], bsw, db[2])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), plain.view(torch.int32))
+    if M * N * K < 10 ** 9:
+        ref, bound = oracle.gemm_nvfp4(*a, *b)
+        _check(host(out).astype(np.float64), ref, bound, K, "out")

@@ -193,7 +193,8 @@ def all_configs(steps, warmup, only=None):
                cast_bytes(4096, 4096, 8192))
         del x2
     # C3: per-tensor and per-token row+col 16384 x 8192, Student-t
-    if want("C3-per-token", "C3-per-tensor", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN", "GEMM-TN-swizzled"):
+    if want("C3-per-token", "C3-per-tensor", "C3-per-token-swizzled", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN",
+            "GEMM-TN-swizzled"):
         x3 = [to_dev(W.c3(t)) for t in range(3)]
         o3 = dict(row_q=u8(M, K // 2), row_sf=u8(M, K // 16), row_amax=f32(M),
                   col_q=u8(K, M // 2), col_sf=u8(K, M // 16), col_amax=f32(K))
@@ -207,6 +208,12 @@ def all_configs(steps, warmup, only=None):
             report("C3-per-tensor", "per-tensor row+col with the decayed amax update, 16384x8192",
                    timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3),
                    cast_bytes(M, K, 2))
+        if want("C3-per-token-swizzled"):
+            osw = dict(o3, row_sf=u8(M * K // 16), col_sf=u8(M * K // 16))
+            report("C3-per-token-swizzled", "per-token row+col with both scale outputs in the GEMM-swizzled layout, "
+                   "16384x8192", timed(lambda i: nv.quantize_swizzled_into(x3[i], nv.PER_TOKEN, **osw), 3),
+                   cast_bytes(M, K, M + K))
+            del osw
         if want("C3-per-token-SR"):
             report("C3-per-token-SR", "per-token row+col with stochastic rounding (Philox4x32-10 randoms), "
                    "16384x8192", timed(lambda i: nv.quantize_sr_into(x3[i], nv.PER_TOKEN, 2024, i, **o3), 3),

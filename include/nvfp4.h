@@ -290,6 +290,20 @@ NVFP4_API nvfp4_status nvfp4_swizzle_scales(const uint8_t* sf, int64_t R, int64_
                                   void* stream);
 
 /*
+ * nvfp4_quantize with both scale outputs written directly in the swizzled
+ * layout above: row_sf as the [M][K/16] matrix, col_sf as [K][M/16], each
+ * M*K/16 bytes (no padding: M % 128 == 0 and K % 128 == 0, else ESHAPE; M*K/16
+ * < 2^31).  Every other output byte equals nvfp4_quantize's, and the scales
+ * equal nvfp4_swizzle_scales of its scales.  PER_TENSOR or PER_TOKEN (else
+ * EINVAL); row_sf and col_sf 4-byte aligned (EALIGN).  Each workgroup of the
+ * encoding kernel writes whole 512-byte tiles of both scale matrices.
+ */
+NVFP4_API nvfp4_status nvfp4_quantize_swizzled(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                     uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                     uint8_t* col_q, uint8_t* col_sf, float* col_amax,
+                                     void* stream);
+
+/*
  * nvfp4_gemm with both operands' scales in the swizzled layout above (a_sf
  * of R = M rows, b_sf of R = N rows, nb = K/16 each; 4-byte aligned, EALIGN).
  * Same arithmetic, results bit-identical to nvfp4_gemm on the plain scales.

@@ -30,7 +30,7 @@ EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_qua
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
            "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm",
            "nvfp4_gemm_grouped", "nvfp4_quantize_rht", "nvfp4_swizzle_scales",
-           "nvfp4_gemm_swizzled")
+           "nvfp4_gemm_swizzled", "nvfp4_quantize_swizzled")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_gemm_grouped": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i32, p, i64, i64, p, p]),
         "nvfp4_quantize_rht": (st, [p, i64, i64, st, ctypes.c_uint32, p, p, p, p, p, p, p]),
         "nvfp4_swizzle_scales": (st, [p, i64, i64, p, p]),
+        "nvfp4_quantize_swizzled": (st, [p, i64, i64, st, p, p, p, p, p, p, p]),
         "nvfp4_gemm_swizzled": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
     }
     for name, (res, args) in sig.items():
@@ -321,6 +322,30 @@ def swizzle_scales(sf):
     out = _u8(swizzled_size(R, nb), sf.device)
     _check(lib().nvfp4_swizzle_scales(_ptr(sf.contiguous()), R, nb, _ptr(out), _stream(sf.device)))
     return out
+
+
+def quantize_swizzled(x: torch.Tensor, mode="per_token", rowwise: bool = True, columnwise: bool = True) -> dict:
+    """Whole cast with both scale outputs in the GEMM-swizzled layout (1-D
+    uint8 of M*K/16 bytes each; M and K multiples of 128)."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    dev = x.device
+    out = {}
+    if rowwise:
+        out.update(row_q=_u8((M, K // 2), dev), row_sf=_u8(M * K // 16, dev), row_amax=_f32(_amax_len(mode, M), dev))
+    if columnwise:
+        out.update(col_q=_u8((K, M // 2), dev), col_sf=_u8(M * K // 16, dev), col_amax=_f32(_amax_len(mode, K), dev))
+    quantize_swizzled_into(x, mode, **out)
+    return out
+
+
+def quantize_swizzled_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, col_sf=None, col_amax=None):
+    """Swizzled-scale cast into caller-provided buffers."""
+    x = _input(x)
+    M, K = x.shape
+    _check(lib().nvfp4_quantize_swizzled(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
+                                         _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _stream(x.device)))
 
 
 def gemm_swizzled_into(out, a_q, a_sw, a_amax, b_q, b_sw, b_amax):

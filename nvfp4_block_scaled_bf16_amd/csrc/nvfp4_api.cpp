@@ -109,7 +109,7 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
                            uint8_t* row_q, uint8_t* row_sf, float* row_amax,
                            uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream,
                            float* cal_buf = nullptr, float decay = 0.0f,
-                           Rounding rounding = Rounding{false, 0, 0}) {
+                           Rounding rounding = Rounding{false, 0, 0}, bool swizzled = false) {
     if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN && mode != NVFP4_TILE_16x16)
         return fail(NVFP4_EINVAL, "unknown scaling mode %d", (int)mode);
     if (rounding.stochastic && mode == NVFP4_TILE_16x16)
@@ -123,6 +123,14 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (s != NVFP4_OK) return s;
     if (rounding.stochastic && M >= ((int64_t)1 << 32))
         return fail(NVFP4_ESHAPE, "stochastic rounding needs M < 2^32 (M = %lld)", (long long)M);
+    if (swizzled) {
+        if (mode == NVFP4_TILE_16x16) return fail(NVFP4_EINVAL, "swizzled scales are offered for per-tensor and per-token scaling only");
+        if (M % 128 != 0 || K % 128 != 0)
+            return fail(NVFP4_ESHAPE, "swizzled scales need M %% 128 == 0 and K %% 128 == 0 (M=%lld K=%lld)", (long long)M, (long long)K);
+        if (M * (K / 16) >= ((int64_t)1 << 31)) return fail(NVFP4_ESHAPE, "swizzled scales need M * K / 16 < 2^31");
+        if ((r.want && !aligned(row_sf, 4)) || (c.want && !aligned(col_sf, 4)))
+            return fail(NVFP4_EALIGN, "swizzled scales must be 4-byte aligned");
+    }
     if (xv == nullptr && M > 0 && K > 0) return fail(NVFP4_EINVAL, "x is NULL");
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
     const uint16_t* x = static_cast<const uint16_t*>(xv);
@@ -151,7 +159,7 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
                                   col_q, col_sf, rounding.seed, rounding.offset, st, b, a); });
         else
             s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_TOKEN, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                  nullptr, nullptr, gt, st, b, a, cal); });
+                                  nullptr, nullptr, gt, st, b, a, cal, swizzled); });
         return s != NVFP4_OK ? s : ok();
     }
     // per-tensor and 16x16 tiles: one tensor amax
@@ -165,7 +173,8 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         return s != NVFP4_OK ? s : ok();
     }
     if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(emode, r.want, c.want, false, x, M, K, 0, M, ra, ca, row_q, row_sf, col_q, col_sf,
-                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st, b, a, cal); })) != NVFP4_OK)
+                                     emode == ENC_TILE ? ra : nullptr, emode == ENC_TILE ? ca : nullptr, gt, st, b, a, cal,
+                                     swizzled); })) != NVFP4_OK)
         return s;
     return ok();
 }
@@ -189,6 +198,13 @@ nvfp4_status nvfp4_quantize(const void* x, int64_t M, int64_t K, nvfp4_scaling m
                             uint8_t* row_q, uint8_t* row_sf, float* row_amax,
                             uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
     return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream);
+}
+
+nvfp4_status nvfp4_quantize_swizzled(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
+                                     uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                     uint8_t* col_q, uint8_t* col_sf, float* col_amax, void* stream) {
+    return quantize_impl(x, M, K, mode, row_q, row_sf, row_amax, col_q, col_sf, col_amax, stream, nullptr, 0.0f,
+                         Rounding{false, 0, 0}, true);
 }
 
 nvfp4_status nvfp4_quantize_calibrate(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,

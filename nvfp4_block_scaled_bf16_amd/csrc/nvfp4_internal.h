@@ -31,7 +31,8 @@ hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const u
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st,
-                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, const Calib& cal = Calib{nullptr, nullptr, 0, 0.0f});
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, const Calib& cal = Calib{nullptr, nullptr, 0, 0.0f},
+                         bool swizzled = false);   // swizzled: mode ENC_TENSOR/ENC_TOKEN, M and K % 128 == 0
 // stochastic-rounding cast (mode ENC_TENSOR or ENC_TOKEN; amax computed before)
 hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int64_t M, int64_t K,
                             const float* row_amax, const float* col_amax, uint8_t* row_q, uint8_t* row_sf,

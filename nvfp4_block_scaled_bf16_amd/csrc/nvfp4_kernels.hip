@@ -287,6 +287,14 @@ __device__ __forceinline__ uint32_t rowmax_word(const u32x4& w) {
     return pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
 }
 
+// Byte offset of scale (r, c) in the GEMM-swizzled layout of a scale matrix
+// with nbp (a multiple of 4) blocks per row: 512-byte tiles of 128 rows x 4
+// blocks, row-tile major; row r in 16-byte line r % 32 at 4-byte slot
+// (r / 32) % 4, block c at byte c % 4.
+__device__ __forceinline__ int64_t swz_offset(int64_t r, uint32_t c, uint32_t nbp) {
+    return (r >> 7) * (128 * (int64_t)nbp) + (int64_t)(c >> 2) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 3);
+}
+
 // Where a lane's sub-block results go.  Row and column bases are per
 // sub-block; lane offsets are 32-bit.  Columnwise data of column c, rows
 // [r0, r0+16) of a vector of length m_len starting at row grow0.
@@ -304,18 +312,29 @@ struct SubDst {
     uint8_t* lds_q; uint8_t* lds_sf;
 };
 
+// rowwise scale byte of row i of the sub-block, block c0 / 16.  SWZ: row_sf
+// points at the swizzled position of (r0, block 0), r0 % 16 == 0, so rows
+// r0 .. r0 + 15 share their 128-row group and 32-row slot.
+template <bool SWZ>
+__device__ __forceinline__ uint8_t* row_sf_at(const SubDst& d, int i) {
+    const uint32_t c = d.c0 / 16;
+    return SWZ ? d.row_sf + i * 16 + (c >> 2) * 512 + (c & 3) : d.row_sf + i * d.row_sf_stride + c;
+}
+
+template <bool SWZ>
 __device__ __forceinline__ void store_row_pair(const SubDst& d, int i, uint32_t q0, uint32_t q1, uint32_t own_code) {
     if (!d.col_ok) return;
     if (i < d.nrows) __builtin_nontemporal_store(q0, reinterpret_cast<uint32_t*>(d.row_q + i * d.row_q_stride + d.c0 / 2));
     if (i + 1 < d.nrows) __builtin_nontemporal_store(q1, reinterpret_cast<uint32_t*>(d.row_q + (i + 1) * d.row_q_stride + d.c0 / 2));
     const int io = d.odd ? i + 1 : i;
-    if (io < d.nrows) d.row_sf[io * d.row_sf_stride + d.c0 / 16] = (uint8_t)own_code;
+    if (io < d.nrows) *row_sf_at<SWZ>(d, io) = (uint8_t)own_code;
 }
 
+template <bool SWZ>
 __device__ __forceinline__ void store_row(const SubDst& d, int i, uint32_t q, uint32_t code) {
     if (d.col_ok && i < d.nrows) {
         *reinterpret_cast<uint32_t*>(d.row_q + i * d.row_q_stride + d.c0 / 2) = q;
-        if (!d.odd) d.row_sf[i * d.row_sf_stride + d.c0 / 16] = (uint8_t)code;
+        if (!d.odd) *row_sf_at<SWZ>(d, i) = (uint8_t)code;
     }
 }
 
@@ -335,7 +354,7 @@ __device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, u
 // Exact encode and store of a sub-block with IEEE divisions throughout,
 // re-reading the data from xr (row r0, column 0; row stride K).  rowA[i]:
 // amax of row i; colA: this lane's 8 column amax; tileA: the tensor's.
-template <bool ROW, bool COL, bool TILE, bool STAGE>
+template <bool ROW, bool COL, bool TILE, bool STAGE, bool SWZ>
 __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64_t K, const float* rowA,
                                           const float* colA, float tileA, SubDst d) {
     u32x4 v[16];
@@ -351,7 +370,7 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
             for (int k = 0; k < 8; k += 2)
                 w |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], k), bs),
                                                               quotient_exact(elem(v[i], k + 1), bs), 1.0f, 0) & 0xffu) << (4 * k);
-            if (ROW) store_row(d, i, w, bs.code);
+            if (ROW) store_row<SWZ>(d, i, w, bs.code);
         }
         if (COL)
             for (int j = 0; j < 8; ++j) {
@@ -372,7 +391,7 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
             for (int k = 0; k < 8; k += 2)
                 w |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient_exact(elem(v[i], k), bs),
                                                               quotient_exact(elem(v[i], k + 1), bs), 1.0f, 0) & 0xffu) << (4 * k);
-            store_row(d, i, w, bs.code);
+            store_row<SWZ>(d, i, w, bs.code);
         }
     }
     if (COL) {
@@ -456,7 +475,11 @@ __device__ __forceinline__ float from_odd(float v) {
 // rows unpacked once and encoded both ways.  Rowwise bytes go straight to
 // memory; columnwise bytes are staged in LDS and written in whole lines at
 // the end of the workgroup's tile.
-template <int MODE, bool ROW, bool COL, bool SAT>
+// SWZ (per-tensor and per-token casts of M % 128 == 0, K % 128 == 0 only):
+// both scale outputs in the GEMM-swizzled layout (swz_offset; the rowwise
+// matrix is [M][K/16], the columnwise [K][M/16]), each workgroup writing whole
+// 512-byte tiles of it.
+template <int MODE, bool ROW, bool COL, bool SAT, bool SWZ>
 __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                 int64_t row_begin, int64_t row_end,
                                                 const float* __restrict__ row_amax, const float* __restrict__ col_amax,
@@ -539,7 +562,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     auto make_dst = [&](int64_t r0, int nrows, int64_t mlen, int64_t g0) {
         SubDst d;
         d.row_q = row_q + r0 * (K / 2);
-        d.row_sf = row_sf + r0 * (K / 16);
+        d.row_sf = SWZ ? row_sf + swz_offset(r0, 0u, (uint32_t)(K / 16)) : row_sf + r0 * (K / 16);
         d.col_q = col_q + g0 * K / 2 + (r0 - g0) / 2;
         d.col_sf = col_sf + g0 * K / 16 + (r0 - g0) / 16;
         d.row_q_stride = (uint32_t)(K / 2);
@@ -560,7 +583,11 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
     const uint32_t xrow = (uint32_t)K * 2u, qrow = (uint32_t)(K / 2), srow = (uint32_t)(K / 16);
     const uint32_t vx = col_ok ? 16u * rg * xrow + c0 * 2u : kOffOut;
     const uint32_t vq = col_ok ? 16u * rg * qrow + c0 / 2u : kOffOut;
-    const uint32_t vs = col_ok ? (16u * rg + (odd ? 1u : 0u)) * srow + c0 / 16u : kOffOut;
+    // swizzled rowwise scales: the lane's row line and block byte within the
+    // step's 128-row group (the step's 32-row slot goes in the scalar offset)
+    const uint32_t vs = !col_ok ? kOffOut
+                        : SWZ ? ((c0 / 16u) >> 2) * 512u + ((c0 / 16u) & 3u) + (16u * rg + (odd ? 1u : 0u)) * 16u
+                              : (16u * rg + (odd ? 1u : 0u)) * srow + c0 / 16u;
     // v_perm selector moving this lane's row (low half: even, high: odd) to the top half
     const uint32_t own_sel = odd ? 0x03020c0cu : 0x01000c0cu;
 
@@ -737,7 +764,10 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
 
         // (3) per row pair: rowwise parameters, then both encodings
         const __amdgpu_buffer_rsrc_t q_rs = rsrc(row_q + wr0 * (K / 2), nrows * qrow);
-        const __amdgpu_buffer_rsrc_t s_rs = rsrc(row_sf + wr0 * (K / 16), nrows * srow);
+        // (swizzled: every step is 32 whole rows, M % 128 == 0)
+        const __amdgpu_buffer_rsrc_t s_rs = SWZ ? rsrc(row_sf + (wr0 >> 7) * 128 * (K / 16), 128u * srow)
+                                                : rsrc(row_sf + wr0 * (K / 16), nrows * srow);
+        const uint32_t s_slot = SWZ ? (uint32_t)((wr0 >> 5) & 3) * 4u : 0u;
         uint32_t cq[8][2] = {};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -756,7 +786,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                     }
                     const FastBlock f = fast_block<SAT>(bm[s], ro);
                     slow |= f.slow;
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs, i * sr, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs, SWZ ? i * 16u + s_slot : i * sr, 0);
                     yh0 = from_even(f.yh); yl0 = from_even(f.yl);
                     yh1 = from_odd(f.yh);  yl1 = from_odd(f.yl);
                 }
@@ -842,7 +872,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             colA[j] = (COL && !TILE) ? (MODE == ENC_TENSOR ? col_amax[0] : (col_ok ? col_amax[cbase + c0 + j] : 0.0f)) : 0.0f;
         SubDst d = make_dst(r0, nrows, mlen, g0);
         if (!group_ok) { d.nrows = 0; d.col_ok = false; }
-        encode_exact<ROW, COL, TILE, STAGE>(x + r0 * K, K, rowA, colA, tileA, d);
+        encode_exact<ROW, COL, TILE, STAGE, SWZ>(x + r0 * K, K, rowA, colA, tileA, d);
     }
 
     if (STAGE) {
@@ -893,8 +923,19 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             }
             // scale bytes: 16-byte pieces along each column (thread t: column
             // t) when the segment is a multiple of 256 rows and the destination
-            // is aligned for them, else words, else bytes
-            if (sbn % 16 == 0 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
+            // is aligned for them, else words, else bytes.  Swizzled: column
+            // t's four blocks of each 4-block group as one word into the
+            // group's 512-byte tile (the workgroup writes whole tiles).
+            if (SWZ) {
+                if (t < ncols) {
+                    const uint32_t nbpc = (uint32_t)(M / 16);
+                    const int64_t k = (int64_t)cbase + t;
+                    for (uint32_t part = 0; part < sbn; part += 4) {
+                        const uint32_t w = *reinterpret_cast<const uint32_t*>(stage_sf + t * kStageSfPitch + ls + part);
+                        *reinterpret_cast<uint32_t*>(col_sf + swz_offset(k, (uint32_t)(s0 / 16) + part, nbpc)) = w;
+                    }
+                }
+            } else if (sbn % 16 == 0 && ls % 4 == 0 && sstride % 16 == 0 && reinterpret_cast<uintptr_t>(gs) % 16 == 0) {
                 if (t < ncols) {
                     for (uint32_t part = 0; part < sbn; part += 16) {
                         const uint32_t* src = reinterpret_cast<const uint32_t*>(stage_sf + t * kStageSfPitch + ls + part);
@@ -1165,20 +1206,20 @@ hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin
 
 // ev0 / ev1 (may be null): events the kernel's own dispatch records at its
 // start and end, for timing it alone
-template <int MODE, bool SAT>
+template <int MODE, bool SAT, bool SWZ = false>
 static void launch_encode_mode(bool row, bool col, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
                                const uint16_t* x, int64_t M, int64_t K,
                                int64_t rb, int64_t re, const float* ra, const float* ca, uint8_t* rq, uint8_t* rs,
                                uint8_t* cq, uint8_t* cs, float* fr, float* fc, const GroupTable& gt, const Calib& cal,
                                int tile_h) {
     if (row && col)
-        hipExtLaunchKernelGGL((k_encode<MODE, true, true, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
+        hipExtLaunchKernelGGL((k_encode<MODE, true, true, SAT, SWZ>), grid, dim3(256), 0, st, ev0, ev1, 0,
                               x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal, tile_h);
     else if (row)
-        hipExtLaunchKernelGGL((k_encode<MODE, true, false, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
+        hipExtLaunchKernelGGL((k_encode<MODE, true, false, SAT, SWZ>), grid, dim3(256), 0, st, ev0, ev1, 0,
                               x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal, tile_h);
     else
-        hipExtLaunchKernelGGL((k_encode<MODE, false, true, SAT>), grid, dim3(256), 0, st, ev0, ev1, 0,
+        hipExtLaunchKernelGGL((k_encode<MODE, false, true, SAT, SWZ>), grid, dim3(256), 0, st, ev0, ev1, 0,
                               x, M, K, rb, re, ra, ca, rq, rs, cq, cs, fr, fc, gt, cal, tile_h);
 }
 
@@ -1186,13 +1227,17 @@ hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const u
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,
                          float* fill_row, float* fill_col, const GroupTable& gt, hipStream_t st,
-                         hipEvent_t ev0, hipEvent_t ev1, const Calib& cal) {
+                         hipEvent_t ev0, hipEvent_t ev1, const Calib& cal, bool swizzled) {
     if (row_end <= row_begin || K <= 0 || (!row && !col)) return hipSuccess;
     // rows per workgroup: 256, or 128 when the grid would be small
     const int tile_h = (int64_t)cdiv(K, kEncCols) * cdiv(row_end - row_begin, kEncRows) < 768 ? 128 : kEncRows;
     dim3 grid(cdiv(K, kEncCols), cdiv(row_end - row_begin, tile_h));
 #define NVFP4_ENC_ARGS row, col, grid, st, ev0, ev1, x, M, K, row_begin, row_end, row_amax, col_amax, row_q, row_sf, col_q, col_sf, fill_row, fill_col, gt, cal, tile_h
-    if (caller_amax) {
+    if (swizzled) {
+        // swizzled scales: per-tensor or per-token, amax computed here
+        if (mode == ENC_TENSOR) launch_encode_mode<ENC_TENSOR, false, true>(NVFP4_ENC_ARGS);
+        else launch_encode_mode<ENC_TOKEN, false, true>(NVFP4_ENC_ARGS);
+    } else if (caller_amax) {
         // amax from the caller: scales may saturate
         if (mode == ENC_TENSOR) launch_encode_mode<ENC_TENSOR, true>(NVFP4_ENC_ARGS);
         else launch_encode_mode<ENC_TOKEN, true>(NVFP4_ENC_ARGS);

@@ -171,6 +171,16 @@ def test_swizzle_and_swizzled_gemm_validation():
     assert g(f, f, f, 1, f, f, f, 1, 0, 16, 16, None, None) == 0
 
 
+def test_quantize_swizzled_validation():
+    L = nv.lib()
+    f, q = P(FAKE), L.nvfp4_quantize_swizzled
+    assert q(f, 128, 128, 2, f, f, f, f, f, f, None) == EINVAL   # 16x16 tiles: not offered
+    assert q(f, 144, 128, 1, f, f, f, f, f, f, None) == ESHAPE   # M % 128
+    assert q(f, 128, 144, 1, f, f, f, f, f, f, None) == ESHAPE   # K % 128
+    assert q(f, 128, 128, 1, f, P(FAKE + 2), f, None, None, None, None) == EALIGN
+    assert q(f, 1 << 20, 1 << 15, 1, f, f, f, None, None, None, None) == ESHAPE   # M * K / 16 >= 2^31
+
+
 def test_trace_encode_validation():
     L = nv.lib()
     assert L.nvfp4_trace_encode(P(FAKE), None) == EINVAL

@@ -241,15 +241,15 @@ nvfp4_status nvfp4_quantize_rht(const void* xv, int64_t M, int64_t K, nvfp4_scal
     if (M > (int64_t)65535 * 128) return fail(NVFP4_ESHAPE, "the Hadamard transform needs M <= 65535 * 128 (M=%lld)", (long long)M);
     if (xv == nullptr && M > 0 && K > 0) return fail(NVFP4_EINVAL, "x is NULL");
     if (!aligned(xv, 16)) return fail(NVFP4_EALIGN, "x must be 16-byte aligned");
-    if (r.want && (s = quantize_impl(xv, M, K, mode, row_q, row_sf, row_amax, nullptr, nullptr, nullptr, stream)) != NVFP4_OK)
-        return s;
     hipStream_t st = as_stream(stream);
-    if ((s = zero(col_amax, mode == NVFP4_PER_TOKEN ? K : 1, nullptr, 0, st)) != NVFP4_OK) return s;
+    const bool tok = mode == NVFP4_PER_TOKEN;
+    float* ra = r.want ? row_amax : nullptr;
+    if ((s = zero(col_amax, tok ? K : 1, ra, ra ? (tok ? M : 1) : 0, st)) != NVFP4_OK) return s;
     if (M == 0 || K == 0) return ok();
     const uint16_t* x = static_cast<const uint16_t*>(xv);
     s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
-        return launch_rht_columnwise(mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR, x, M, K, sign_mask, col_amax, col_q,
-                                     col_sf, st, b, a);
+        return launch_rht(tok ? ENC_TOKEN : ENC_TENSOR, x, M, K, sign_mask, ra, col_amax, r.want ? row_q : nullptr,
+                          r.want ? row_sf : nullptr, col_q, col_sf, st, b, a);
     });
     return s != NVFP4_OK ? s : ok();
 }

@@ -38,10 +38,13 @@ hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int
                             const float* row_amax, const float* col_amax, uint8_t* row_q, uint8_t* row_sf,
                             uint8_t* col_q, uint8_t* col_sf, uint64_t seed, uint32_t offset, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1);
-// random Hadamard transform + columnwise cast (nvfp4_rht.hip): col_amax
-// zeroed beforehand ([K] per token, [1] per tensor); M % 16 == 0, K % 8 == 0
-hipError_t launch_rht_columnwise(int mode, const uint16_t* x, int64_t M, int64_t K, uint32_t mask, float* col_amax,
-                                 uint8_t* col_q, uint8_t* col_sf, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// random Hadamard transform + columnwise cast, with the ordinary rowwise cast
+// of x when row_q != nullptr (nvfp4_rht.hip): amax outputs zeroed beforehand
+// ([K] / [M] per token, [1] per tensor); M % 16 == 0, K % 8 == 0 (K % 16 ==
+// 0 with rows)
+hipError_t launch_rht(int mode, const uint16_t* x, int64_t M, int64_t K, uint32_t mask, float* row_amax,
+                      float* col_amax, uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf, hipStream_t st,
+                      hipEvent_t ev0, hipEvent_t ev1);
 // NVFP4 GEMM consumer (nvfp4_gemm.hip): out [M][N] fp32, one workgroup per
 // 128 x 128 output tile, at most kMaxGemmTiles of them
 constexpr int64_t kMaxGemmTiles = (int64_t(1) << 31) - 1;

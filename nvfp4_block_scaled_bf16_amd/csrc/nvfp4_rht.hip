@@ -11,11 +11,13 @@
 // bf16 result is cast exactly like any columnwise input, with its own amax
 // (per column, or one for the tensor).
 //
-// Two passes over x, like the ordinary per-token cast: the amax of the
-// transformed columns, then the transform again with the encoding.  A lane
-// holds a 16-row x 8-column sub-block (one 16-byte word per row); a
-// workgroup of 4 waves covers 128 rows x 256 columns.  Requires M % 16 == 0
-// and K % 8 == 0.
+// Two passes over x, like the ordinary per-token cast: the amaxes (of the
+// transformed columns, and of x's rows when rowwise output is wanted), then
+// the transform again with both encodings (rowwise of x, columnwise of y).
+// A lane holds a 16-row x 8-column sub-block (one 16-byte word per row); a
+// workgroup of 4 waves covers 128 rows x 256 columns; a rowwise block is a
+// lane pair.  Requires M % 16 == 0 and K % 8 == 0 (K % 16 == 0 with rowwise
+// output).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -66,32 +68,116 @@ __device__ __forceinline__ void rht_column(const u32x4 (&v)[16], int k, uint32_t
 
 __device__ __forceinline__ uint32_t mag16(uint32_t fbits) { return (fbits >> 16) & 0x7fffu; }
 
-// Pass 1: the amax of the transformed tensor, per column (col_amax [K],
-// zeroed beforehand) or for the whole tensor (col_amax [1]).  Grid:
-// (cdiv(K, 256), cdiv(M, 512)).
-template <int MODE>
+// largest bf16 magnitude (16-bit pattern) of the lane's 8 values of one row
+__device__ __forceinline__ uint32_t row8_max(const u32x4& w) {
+    return max_halves(pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w))));
+}
+
+// the same value from the neighbouring lane (lane ^ 1), by DPP
+__device__ __forceinline__ uint32_t pair_lane(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// Max over the 32 lanes of a row group of 16 per-lane 16-bit values (one
+// per row), by halving exchanges (xor 16, 8, 4 keep half the rows each, xor
+// 2 and 1 finish).  Returns j: the lane then holds rows 2j (low half) and
+// 2j + 1 (high half) in *pair.
+__device__ __forceinline__ int group_rowmax16(const uint32_t (&m)[16], uint32_t* pair) {
+    const int lane = threadIdx.x & 63;
+    uint32_t p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = m[2 * j] | (m[2 * j + 1] << 16);
+    const bool b16 = lane & 16, b8 = lane & 8, b4 = lane & 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t send = b16 ? p[j] : p[j + 4], keep = b16 ? p[j + 4] : p[j];
+        p[j] = pk_max_u16(keep, (uint32_t)__shfl_xor((int)send, 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t send = b8 ? p[j] : p[j + 2], keep = b8 ? p[j + 2] : p[j];
+        p[j] = pk_max_u16(keep, (uint32_t)__shfl_xor((int)send, 8));
+    }
+    {
+        const uint32_t send = b4 ? p[0] : p[1], keep = b4 ? p[1] : p[0];
+        p[0] = pk_max_u16(keep, (uint32_t)__shfl_xor((int)send, 4));
+    }
+    p[0] = pk_max_u16(p[0], (uint32_t)__shfl_xor((int)p[0], 2));
+    p[0] = pk_max_u16(p[0], (uint32_t)__shfl_xor((int)p[0], 1));
+    *pair = p[0];
+    return (b16 ? 4 : 0) + (b8 ? 2 : 0) + (b4 ? 1 : 0);
+}
+
+// the butterfly's largest |t| over a column block, as the magnitude of the
+// transformed block's largest bf16 value: x -> RN_bf16(x / 4) is monotonic
+// and odd, so rounding the maximum equals the maximum of the rounded values
+__device__ __forceinline__ uint32_t rht_column_max(const u32x4 (&v)[16], int k, uint32_t mask) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = __uint_as_float(col_bits(v[i], k) ^ (((mask >> i) & 1u) << 31));
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i & h) continue;
+            const float a = t[i], b = t[i + h];
+            t[i] = a + b;
+            t[i + h] = a - b;
+        }
+    }
+    float b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b = __builtin_fmaxf(b, __builtin_fabsf(t[i]));
+    return mag16(round_to_bf16(b * 0.25f));
+}
+
+// Pass 1: the amax of the transformed tensor, per column (col_amax [K]) or
+// for the whole tensor (col_amax [1]); with ROW also the amax of x's rows
+// (row_amax [M], or [1] for the tensor).  Outputs zeroed beforehand.
+// Grid: (cdiv(K, 256), cdiv(M, 512)).
+template <int MODE, bool ROW>
 __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x, int64_t M, int64_t K, uint32_t mask,
-                                                  float* __restrict__ col_amax) {
+                                                  float* __restrict__ row_amax, float* __restrict__ col_amax) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rg = lane >> 5;
     const int64_t c0 = (int64_t)blockIdx.x * kRhtCols + (lane & 31) * 8;
     const bool col_ok = c0 < K;
     uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t tm = 0u;   // ROW, per tensor: the rows' maximum
 #pragma unroll 1
     for (int step = 0; step < kRhtAmaxSteps; ++step) {
         const int64_t r0 = ((int64_t)blockIdx.y * kRhtAmaxSteps + step) * kRhtRows + wave * 32 + 16 * rg;
-        if (!col_ok || r0 >= M) continue;   // M % 16 == 0: a row group is whole or absent
+        // M % 16 == 0: a row group is whole or absent; a wave with rows
+        // still takes part in the row reduction with zeros
+        if (__builtin_amdgcn_ballot_w64(r0 < M) == 0ull) break;
+        const bool active = col_ok && r0 < M;
         u32x4 v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const u32x4*>(x + (r0 + i) * K + c0);
+        for (int i = 0; i < 16; ++i)
+            v[i] = active ? *reinterpret_cast<const u32x4*>(x + (r0 + i) * K + c0) : u32x4{0u, 0u, 0u, 0u};
+        if (ROW) {
+            uint32_t rm[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rm[i] = row8_max(v[i]);
+            if (MODE == ENC_TOKEN) {
+                uint32_t pair;
+                const int j = group_rowmax16(rm, &pair);
+                if ((lane & 3) == 0 && r0 < M) {
+                    if ((pair & 0xffffu) != 0u)
+                        atomicMax(reinterpret_cast<uint32_t*>(row_amax + r0 + 2 * j), (pair & 0xffffu) << 16);
+                    if ((pair >> 16) != 0u)
+                        atomicMax(reinterpret_cast<uint32_t*>(row_amax + r0 + 2 * j + 1), pair & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) tm = tm > rm[i] ? tm : rm[i];
+            }
+        }
+        if (!active) continue;
         // columns unrolled: a column index that varies at run time would put
         // v in scratch memory
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            uint32_t y[16];
-            rht_column(v, k, mask, y);
-            uint32_t b = 0u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) b = b > mag16(y[i]) ? b : mag16(y[i]);
+            const uint32_t b = rht_column_max(v, k, mask);
             m[k] = m[k] > b ? m[k] : b;
         }
     }
@@ -107,19 +193,30 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
         if ((int64_t)blockIdx.x * kRhtCols + t < K && b != 0u)
             atomicMax(reinterpret_cast<uint32_t*>(col_amax + (int64_t)blockIdx.x * kRhtCols + t), b << 16);
     } else {
-        // the workgroup's maximum, then one atomic
+        // the workgroup's maxima (columns of y; rows of x), then one atomic each
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
-            const uint32_t o = (uint32_t)__shfl_xor((int)b, off);
-            b = b > o ? b : o;
+            const uint32_t ob = (uint32_t)__shfl_xor((int)b, off);
+            b = b > ob ? b : ob;
+            if (ROW) {
+                const uint32_t ot = (uint32_t)__shfl_xor((int)tm, off);
+                tm = tm > ot ? tm : ot;
+            }
         }
-        __shared__ uint32_t wred[4];
-        if (lane == 0) wred[wave] = b;
+        __shared__ uint32_t wred[4][2];
+        if (lane == 0) {
+            wred[wave][0] = b;
+            wred[wave][1] = tm;
+        }
         __syncthreads();
         if (t == 0) {
-            b = wred[0];
-            for (int w = 1; w < 4; ++w) b = b > wred[w] ? b : wred[w];
-            if (b != 0u) atomicMax(reinterpret_cast<uint32_t*>(col_amax), b << 16);
+            uint32_t bc = wred[0][0], br = wred[0][1];
+            for (int w = 1; w < 4; ++w) {
+                bc = bc > wred[w][0] ? bc : wred[w][0];
+                br = br > wred[w][1] ? br : wred[w][1];
+            }
+            if (bc != 0u) atomicMax(reinterpret_cast<uint32_t*>(col_amax), bc << 16);
+            if (ROW && br != 0u) atomicMax(reinterpret_cast<uint32_t*>(row_amax), br << 16);
         }
     }
 }
@@ -172,22 +269,64 @@ __device__ __forceinline__ ColCodes encode_column(const uint32_t (&y)[16], float
     return c;
 }
 
-// Pass 2: transform and encode.  col_q [K][M/2], col_sf [K][M/16].  Grid:
-// (cdiv(K, 256), cdiv(M, 128)).
-template <int MODE>
+// E2M1 codes of the lane's 8 values of one row (a rowwise block is the lane
+// pair), one byte pair per put, and the block's E4M3 code
+__device__ __forceinline__ uint32_t encode_row8(const u32x4& w, float A, uint32_t* code) {
+    uint32_t b = row8_max(w);
+    const uint32_t ob = pair_lane(b);
+    b = b > ob ? b : ob;
+    const Outer o = make_outer(A);
+    const FastBlock fb = fast_block<false>(b << 16, o);
+    const float a[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+    float q[8];
+    if (__builtin_amdgcn_ballot_w64(o.slow || fb.slow) == 0ull) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = quot2(a[i], fb.yh, fb.yl);
+        *code = fb.code & 0xffu;
+    } else {
+        const BlockScale bs = block_scale(b, outer_scale(A));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = bs.zero ? a[i] * 0.0f : a[i] / bs.r;
+        *code = bs.code;
+    }
+    uint32_t r = put_fp4x2<0>(0u, q[0], q[1]);
+    r = put_fp4x2<1>(r, q[2], q[3]);
+    r = put_fp4x2<2>(r, q[4], q[5]);
+    return put_fp4x2<3>(r, q[6], q[7]);
+}
+
+// Pass 2: transform and encode.  col_q [K][M/2], col_sf [K][M/16]; with ROW
+// also the rowwise cast of x itself into row_q [M][K/2], row_sf [M][K/16].
+// Grid: (cdiv(K, 256), cdiv(M, 128)).
+template <int MODE, bool ROW>
 __global__ __launch_bounds__(256) void k_rht_encode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                    uint32_t mask, const float* __restrict__ col_amax,
-                                                    uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf) {
+                                                    uint32_t mask, const float* __restrict__ row_amax,
+                                                    const float* __restrict__ col_amax, uint8_t* __restrict__ row_q,
+                                                    uint8_t* __restrict__ row_sf, uint8_t* __restrict__ col_q,
+                                                    uint8_t* __restrict__ col_sf) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rg = lane >> 5;
     const int64_t c0 = (int64_t)blockIdx.x * kRhtCols + (lane & 31) * 8;
     const int64_t r0 = (int64_t)blockIdx.y * kRhtRows + wave * 32 + 16 * rg;
     // M % 16 == 0: a row group is whole or absent; inactive lanes still take
-    // part in the wave-wide path choice
+    // part in the wave-wide path choices and the lane-pair exchange
     const bool active = c0 < K && r0 < M;
     u32x4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         v[i] = active ? *reinterpret_cast<const u32x4*>(x + (r0 + i) * K + c0) : u32x4{0u, 0u, 0u, 0u};
+    if (ROW) {
+        const float Ar = MODE == ENC_TENSOR ? row_amax[0] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float A = MODE == ENC_TENSOR ? Ar : (r0 < M ? row_amax[r0 + i] : 0.0f);
+            uint32_t code;
+            const uint32_t w = encode_row8(v[i], A, &code);
+            if (active) {
+                *reinterpret_cast<uint32_t*>(row_q + (r0 + i) * (K / 2) + c0 / 2) = w;
+                if (!(lane & 1)) row_sf[(r0 + i) * (K / 16) + c0 / 16] = (uint8_t)code;
+            }
+        }
+    }
     const float At = MODE == ENC_TENSOR ? col_amax[0] : 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {   // unrolled (see k_rht_amax)
@@ -204,21 +343,28 @@ __global__ __launch_bounds__(256) void k_rht_encode(const uint16_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_rht_columnwise(int mode, const uint16_t* x, int64_t M, int64_t K, uint32_t mask, float* col_amax,
-                                 uint8_t* col_q, uint8_t* col_sf, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_rht(int mode, const uint16_t* x, int64_t M, int64_t K, uint32_t mask, float* row_amax,
+                      float* col_amax, uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf, hipStream_t st,
+                      hipEvent_t ev0, hipEvent_t ev1) {
     if (M <= 0 || K <= 0) return hipSuccess;
     const unsigned gx = (unsigned)((K + kRhtCols - 1) / kRhtCols);
     const dim3 ga(gx, (unsigned)((M + kRhtRows * kRhtAmaxSteps - 1) / (kRhtRows * kRhtAmaxSteps)));
     const dim3 ge(gx, (unsigned)((M + kRhtRows - 1) / kRhtRows));
+#define NVFP4_RHT_LAUNCH(MD, R)                                                                                     \
+    do {                                                                                                          \
+        hipLaunchKernelGGL((k_rht_amax<MD, R>), ga, dim3(256), 0, st, x, M, K, mask, row_amax, col_amax);         \
+        hipExtLaunchKernelGGL((k_rht_encode<MD, R>), ge, dim3(256), 0, st, ev0, ev1, 0, x, M, K, mask,            \
+                              (const float*)row_amax, (const float*)col_amax, row_q, row_sf, col_q, col_sf);      \
+    } while (0)
+    const bool row = row_q != nullptr;
     if (mode == ENC_TOKEN) {
-        hipLaunchKernelGGL(k_rht_amax<ENC_TOKEN>, ga, dim3(256), 0, st, x, M, K, mask, col_amax);
-        hipExtLaunchKernelGGL(k_rht_encode<ENC_TOKEN>, ge, dim3(256), 0, st, ev0, ev1, 0, x, M, K, mask,
-                              (const float*)col_amax, col_q, col_sf);
+        if (row) NVFP4_RHT_LAUNCH(ENC_TOKEN, true);
+        else NVFP4_RHT_LAUNCH(ENC_TOKEN, false);
     } else {
-        hipLaunchKernelGGL(k_rht_amax<ENC_TENSOR>, ga, dim3(256), 0, st, x, M, K, mask, col_amax);
-        hipExtLaunchKernelGGL(k_rht_encode<ENC_TENSOR>, ge, dim3(256), 0, st, ev0, ev1, 0, x, M, K, mask,
-                              (const float*)col_amax, col_q, col_sf);
+        if (row) NVFP4_RHT_LAUNCH(ENC_TENSOR, true);
+        else NVFP4_RHT_LAUNCH(ENC_TENSOR, false);
     }
+#undef NVFP4_RHT_LAUNCH
     return hipGetLastError();
 }
 

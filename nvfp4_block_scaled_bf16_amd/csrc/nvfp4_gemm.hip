@@ -161,8 +161,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
     const __amdgpu_buffer_rsrc_t bs_rs =
         SWZ ? gemm_rsrc(b_sf + n0 * nbp, ((vb + 127u) & ~127u) * nbp) : gemm_rsrc(b_sf + n0 * (K / 16), vb * (Ku / 16));
 
-    // pc: bytes of the next K step (dequantized into LDS during this step);
-    // pn: the step after, loaded a whole step ahead of its use
+    // two register sets for the raw bytes of the next two K steps
     RowPiece pc[P], pn[P];
     auto load_all = [&](RowPiece* dst, uint32_t kbase) {
 #pragma unroll
@@ -182,15 +181,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
     };
 
     const uint32_t nk = (Ku + kStepK - 1) / kStepK;
-    load_all(pc, 0);
-    store_all(pc, 0);
-    load_all(pc, kStepK);
-    __syncthreads();
-    for (uint32_t kt = 0; kt < nk; ++kt) {
+    // One K step: load the bytes of step kt + 2 into `nxt` (zeros past K),
+    // run step kt's MFMAs from its LDS buffer, dequantize step kt + 1's bytes
+    // (`cur`, loaded a step earlier) into the other buffer.  Steps alternate
+    // the two register sets, so a load stays in flight through a whole step
+    // (copying one set into the other would wait for it).  The buffer written
+    // in the last step is never read.
+    auto step = [&](uint32_t kt, RowPiece* cur, RowPiece* nxt) {
         const int buf = (int)(kt & 1);
-        // loads past K read zeros; the buffer written in the last steps is
-        // never read
-        load_all(pn, (kt + 2) * kStepK);
+        load_all(nxt, (kt + 2) * kStepK);
         const _Float16* as = S[buf] + (wm * (TM / WM)) * kPitch;
         const _Float16* bs = S[buf] + (TM + wn * (TN / WN)) * kPitch;
 #pragma unroll
@@ -209,10 +208,16 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        store_all(pc, buf ^ 1);
-#pragma unroll
-        for (int i = 0; i < P; ++i) pc[i] = pn[i];
+        store_all(cur, buf ^ 1);
         __syncthreads();
+    };
+    load_all(pc, 0);
+    store_all(pc, 0);
+    load_all(pc, kStepK);
+    __syncthreads();
+    for (uint32_t kt = 0; kt < nk; kt += 2) {
+        step(kt, pc, pn);
+        if (kt + 1 < nk) step(kt + 1, pn, pc);
     }
 
     // epilogue: out = RN(RN(acc * S_a) * S_b); accumulator a of lane l holds

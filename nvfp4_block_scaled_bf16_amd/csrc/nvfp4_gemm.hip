@@ -72,12 +72,21 @@ __device__ __forceinline__ uint32_t scale_offset(uint32_t row, uint32_t c, uint3
 
 // row: the row within the operand tile (descriptors q_rs / s_rs start at the
 // tile's first row and end after its last valid row, for swizzled scales
-// after its last 128-row group); k0 % 32 == 0
-template <bool SWZ>
+// after its last 128-row group); k0 % 32 == 0.  A64 (K % 64 == 0): every
+// K step is whole, so a piece is one 16-byte load of codes (16-byte
+// aligned) and one 4-byte load holding its two scale bytes (the step's four
+// blocks sit in one aligned word, plain or swizzled); else two 8-byte loads
+// and two byte loads, each guarded against K.
+template <bool SWZ, bool A64>
 __device__ __forceinline__ RowPiece load_piece(__amdgpu_buffer_rsrc_t q_rs, __amdgpu_buffer_rsrc_t s_rs, uint32_t row,
                                                uint32_t K, uint32_t k0) {
     const uint32_t off = row * (K / 2) + k0 / 2, soff = scale_offset<SWZ>(row, k0 / 16, K);
     const bool lo_ok = k0 < K, hi_ok = k0 + 16 < K;
+    if (A64) {
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(q_rs, lo_ok ? off : kOob, 0, 0);
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(s_rs, lo_ok ? (soff & ~3u) : kOob, 0, 0);
+        return RowPiece{{q.x, q.y, q.z, q.w}, (w >> (8 * (soff & 3u))) & 0xffffu};
+    }
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(q_rs, lo_ok ? off : kOob, 0, 0);
     const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(q_rs, hi_ok ? off + 8 : kOob, 0, 0);
@@ -129,7 +138,7 @@ __device__ __forceinline__ uint32_t xcd_tile() {
 }
 
 // the output tile at (m0, n0) of out [M][N] = A [M][K] x B [N][K]^T
-template <int TM, int TN, int WM, int WN, bool SWZ>
+template <int TM, int TN, int WM, int WN, bool SWZ, bool A64>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf,
                                           const float* __restrict__ a_amax, int a_per_row,
                                           const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
@@ -168,8 +177,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
         for (int i = 0; i < P; ++i) {
             const int p = t + NT * i, r = p >> 1;
             const uint32_t k0 = kbase + 32 * (p & 1);
-            if ((NT * i) / 2 < TM) dst[i] = load_piece<SWZ>(aq_rs, as_rs, (uint32_t)r, Ku, k0);
-            else dst[i] = load_piece<SWZ>(bq_rs, bs_rs, (uint32_t)(r - TM), Ku, k0);
+            if ((NT * i) / 2 < TM) dst[i] = load_piece<SWZ, A64>(aq_rs, as_rs, (uint32_t)r, Ku, k0);
+            else dst[i] = load_piece<SWZ, A64>(bq_rs, bs_rs, (uint32_t)(r - TM), Ku, k0);
         }
     };
     auto store_all = [&](const RowPiece* src, int buf) {
@@ -244,8 +253,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
 }
 
 // Grid: cdiv(M, TM) * cdiv(N, TN) workgroups (one dimension); ntn = cdiv(N, TN).
-// SWZ: both operands' scales in the swizzled layout.
-template <int TM, int TN, int WM, int WN, bool SWZ>
+// SWZ: both operands' scales in the swizzled layout; A64: K % 64 == 0.
+template <int TM, int TN, int WM, int WN, bool SWZ, bool A64>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
     int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     float* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) GemmLds<TM, TN> S;
     const uint32_t tile = xcd_tile();
-    gemm_tile<TM, TN, WM, WN, SWZ>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K,
+    gemm_tile<TM, TN, WM, WN, SWZ, A64>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K,
                                    (int64_t)(tile / ntn) * TM, (int64_t)(tile % ntn) * TN, out, S);
 }
 
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
 // rows off[g] .. off[g] + cnt[g] by its own B (expert first + g of b_*),
 // writing out's same rows.  Tiles of group g are tstart[g] .. tstart[g + 1];
 // grid: tstart[n] workgroups.
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, bool A64>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_nvfp4_grouped(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_amax,
     int a_per_row, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
@@ -278,19 +287,19 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     }
     const uint32_t local = tile - gg.tstart[lo];
     const int64_t off = gg.off[lo], e = (int64_t)gg.first + lo;
-    gemm_tile<TM, TN, WM, WN, false>(a_q + off * (K / 2), a_sf + off * (K / 16), a_amax + (a_per_row ? off : 0), a_per_row,
+    gemm_tile<TM, TN, WM, WN, false, A64>(a_q + off * (K / 2), a_sf + off * (K / 16), a_amax + (a_per_row ? off : 0), a_per_row,
                               b_q + e * N * (K / 2), b_sf + e * N * (K / 16), b_amax + (b_per_row ? e * N : e),
                               b_per_row, gg.cnt[lo], N, K, (int64_t)(local / ntn) * TM,
                               (int64_t)(local % ntn) * TN, out + off * N, S);
 }
 
-template <int TM, int TN, int WM, int WN, bool SWZ>
+template <int TM, int TN, int WM, int WN, bool SWZ, bool A64>
 hipError_t launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                       const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row, int64_t M,
                       int64_t N, int64_t K, float* out, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const int64_t ntn = (N + TN - 1) / TN, ntiles = ntn * ((M + TM - 1) / TM);
     if (ntiles > kMaxGemmTiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL(k_gemm_nvfp4<TM, TN, WM, WN, SWZ>, dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, st, ev0, ev1,
+    hipExtLaunchKernelGGL(k_gemm_nvfp4<TM, TN, WM, WN, SWZ, A64>, dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, st, ev0, ev1,
                           0, a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, (uint32_t)ntn, out);
     return hipGetLastError();
 }
@@ -338,9 +347,12 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const floa
     // 256 x 256 tiles (8 waves of 128 x 64) once they fill the 256 CUs, else
     // 128 x 128 tiles (4 waves of 64 x 64) for four times the workgroups
     const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= 256;
-#define NVFP4_GEMM_LAUNCH(TM, TN, WM, WN, SW)                                                                       \
-    return launch_cfg<TM, TN, WM, WN, SW>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K, out, \
-                                          st, ev0, ev1)
+    const bool a64 = K % 64 == 0;
+#define NVFP4_GEMM_LAUNCH(TM, TN, WM, WN, SW)                                                                      \
+    return a64 ? launch_cfg<TM, TN, WM, WN, SW, true>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, \
+                                                      N, K, out, st, ev0, ev1)                                     \
+               : launch_cfg<TM, TN, WM, WN, SW, false>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, \
+                                                       N, K, out, st, ev0, ev1)
     if (swizzled) {
         if (big) NVFP4_GEMM_LAUNCH(256, 256, 2, 4, true);
         NVFP4_GEMM_LAUNCH(128, 128, 2, 2, true);
@@ -352,7 +364,7 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const floa
 
 namespace {
 
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, bool A64>
 hipError_t launch_grouped_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_amax, int a_per_row,
                               const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                               int32_t num_groups, const int64_t* h_counts, int64_t N, int64_t K, float* out,
@@ -381,7 +393,7 @@ hipError_t launch_grouped_cfg(const uint8_t* a_q, const uint8_t* a_sf, const flo
         gg.tstart[gg.n] = (uint32_t)tiles;
         if (tiles == 0) continue;
         if (tiles > kMaxGemmTiles) return hipErrorInvalidValue;
-        hipExtLaunchKernelGGL(k_gemm_nvfp4_grouped<TM, TN, WM, WN>, dim3((unsigned)tiles), dim3(64 * WM * WN), 0, st,
+        hipExtLaunchKernelGGL(k_gemm_nvfp4_grouped<TM, TN, WM, WN, A64>, dim3((unsigned)tiles), dim3(64 * WM * WN), 0, st,
                               first_launch ? ev0 : nullptr, e0 == last ? ev1 : nullptr, 0, a_q, a_sf, a_amax,
                               a_per_row, b_q, b_sf, b_amax, b_per_row, gg, N, K, (uint32_t)ntn, out);
         first_launch = false;
@@ -406,11 +418,15 @@ hipError_t launch_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const fl
         padded += (h_counts[e] + 255) / 256 * 256;
         tiles256 += (h_counts[e] + 255) / 256 * ((N + 255) / 256);
     }
-    if (tiles256 >= 256 && 4 * padded <= 5 * T)
-        return launch_grouped_cfg<256, 256, 2, 4>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row,
-                                                  num_groups, h_counts, N, K, out, st, ev0, ev1);
-    return launch_grouped_cfg<128, 128, 2, 2>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row,
-                                              num_groups, h_counts, N, K, out, st, ev0, ev1);
+    const bool big = tiles256 >= 256 && 4 * padded <= 5 * T, a64 = K % 64 == 0;
+#define NVFP4_GROUPED_LAUNCH(TM, TN, WM, WN)                                                                        \
+    return a64 ? launch_grouped_cfg<TM, TN, WM, WN, true>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax,          \
+                                                          b_per_row, num_groups, h_counts, N, K, out, st, ev0, ev1) \
+               : launch_grouped_cfg<TM, TN, WM, WN, false>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax,         \
+                                                           b_per_row, num_groups, h_counts, N, K, out, st, ev0, ev1)
+    if (big) NVFP4_GROUPED_LAUNCH(256, 256, 2, 4);
+    NVFP4_GROUPED_LAUNCH(128, 128, 2, 2);
+#undef NVFP4_GROUPED_LAUNCH
 }
 
 }  // namespace nvfp4

@@ -281,7 +281,7 @@ def test_swizzle_of_cast_outputs(oracle):
     assert np.array_equal(col, oracle.swizzle_scales(ref["col_sf"]))
 
 
-@pytest.mark.parametrize("shape", [(130, 200, 272), (300, 520, 1040), (4000, 4100, 272)])
+@pytest.mark.parametrize("shape", [(130, 200, 272), (300, 520, 1040), (4000, 4100, 272), (260, 390, 1024), (4000, 4100, 320)])
 def test_gemm_swizzled_equals_plain(oracle, shape):
     # same arithmetic: bit-identical to the plain-layout GEMM; the small
     # shape also against the oracle

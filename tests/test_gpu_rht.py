@@ -92,3 +92,15 @@ def test_rht_inverse_through_dequantize(oracle):
     xf = W.bf16_to_f32(x).astype(np.float64)
     err = np.linalg.norm(back - xf) / np.linalg.norm(xf)
     assert err < 0.2
+
+
+def test_rht_empty_tensor():
+    # M == 0: nothing to read; the per-column amax comes back zero (output
+    # buffers are non-empty allocations: a NULL pointer means "not requested")
+    _announce("rht empty M=0 K=32")
+    x = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda:0")
+    dummy = lambda dt: torch.full((64,), 7, dtype=dt, device="cuda:0")
+    ca = torch.full((32,), 7.0, dtype=torch.float32, device="cuda:0")
+    nv.quantize_rht_into(x, nv.PER_TOKEN, 0x1234, col_q=dummy(torch.uint8), col_sf=dummy(torch.uint8), col_amax=ca)
+    torch.cuda.synchronize()
+    assert not host(ca).any()

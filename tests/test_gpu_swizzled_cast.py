@@ -88,3 +88,14 @@ def test_swizzled_cast_feeds_swizzled_gemm(oracle):
     plain = nv.gemm(pa["row_q"], pa["row_sf"], pa["row_amax"], pb["row_q"], pb["row_sf"], pb["row_amax"])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), plain.view(torch.int32))
+
+
+def test_swizzled_cast_empty_tensor():
+    # output buffers are non-empty allocations (NULL means "not requested")
+    _announce("swizzled cast empty M=0 K=128")
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda:0")
+    dummy = lambda dt: torch.full((64,), 7, dtype=dt, device="cuda:0")
+    ca = torch.full((128,), 7.0, dtype=torch.float32, device="cuda:0")
+    nv.quantize_swizzled_into(x, nv.PER_TOKEN, col_q=dummy(torch.uint8), col_sf=dummy(torch.uint8), col_amax=ca)
+    torch.cuda.synchronize()
+    assert not host(ca).any()

@@ -176,7 +176,7 @@ NVFP4_API nvfp4_status nvfp4_quantize_sr(const void* x, int64_t M, int64_t K, nv
  * D H16 / 4 on the dequantized blocks.  mode PER_TENSOR or PER_TOKEN (else
  * EINVAL); sign_mask < 2^16 (EINVAL); M % 16 == 0 and K % 8 == 0 (plus K % 16
  * == 0 with rowwise output) and M <= 65535 * 128 (ESHAPE).  Reads x twice
- * for the columnwise part (amax, then encoding).
+ * in all (the amaxes of both directions, then both encodings).
  */
 NVFP4_API nvfp4_status nvfp4_quantize_rht(const void* x, int64_t M, int64_t K, nvfp4_scaling mode,
                                 uint32_t sign_mask,

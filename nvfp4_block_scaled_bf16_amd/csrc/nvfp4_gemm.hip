@@ -137,6 +137,20 @@ __device__ __forceinline__ uint32_t xcd_tile() {
     return (ntiles & 7u) == 0u ? (lin & 7u) * (ntiles >> 3) + (lin >> 3) : lin;
 }
 
+// Tile t of an ntm x ntn grid in groups of kBandGroup row bands: within a
+// group, down the bands of one column of tiles, then the next column.  Runs
+// of consecutive tiles (as one XCD holds them at a time) thus share a few
+// row bands of A and a few column tiles of B instead of one band of A and
+// every tile of B, so fewer distinct operand rows stream through its L2 per
+// K step.
+constexpr uint32_t kBandGroup = 4;
+__device__ __forceinline__ void band_order(uint32_t t, uint32_t ntm, uint32_t ntn, uint32_t* by, uint32_t* bx) {
+    const uint32_t per = kBandGroup * ntn, g = t / per, first = g * kBandGroup;
+    const uint32_t gm = ntm - first < kBandGroup ? ntm - first : kBandGroup, w = t - g * per;
+    *by = first + w % gm;
+    *bx = w / gm;
+}
+
 // the output tile at (m0, n0) of out [M][N] = A [M][K] x B [N][K]^T
 template <int TM, int TN, int WM, int WN, bool SWZ, bool A64>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf,
@@ -261,9 +275,10 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     const float* __restrict__ b_amax, int b_per_row, int64_t M, int64_t N, int64_t K, uint32_t ntn,
     float* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) GemmLds<TM, TN> S;
-    const uint32_t tile = xcd_tile();
+    uint32_t by, bx;
+    band_order(xcd_tile(), gridDim.x / ntn, ntn, &by, &bx);
     gemm_tile<TM, TN, WM, WN, SWZ, A64>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, N, K,
-                                   (int64_t)(tile / ntn) * TM, (int64_t)(tile % ntn) * TN, out, S);
+                                        (int64_t)by * TM, (int64_t)bx * TN, out, S);
 }
 
 // Grouped: group g (the table's entry g, expert first + g) multiplies A's
@@ -287,10 +302,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     }
     const uint32_t local = tile - gg.tstart[lo];
     const int64_t off = gg.off[lo], e = (int64_t)gg.first + lo;
+    uint32_t by, bx;
+    band_order(local, (uint32_t)((gg.cnt[lo] + TM - 1) / TM), ntn, &by, &bx);
     gemm_tile<TM, TN, WM, WN, false, A64>(a_q + off * (K / 2), a_sf + off * (K / 16), a_amax + (a_per_row ? off : 0), a_per_row,
                               b_q + e * N * (K / 2), b_sf + e * N * (K / 16), b_amax + (b_per_row ? e * N : e),
-                              b_per_row, gg.cnt[lo], N, K, (int64_t)(local / ntn) * TM,
-                              (int64_t)(local % ntn) * TN, out + off * N, S);
+                              b_per_row, gg.cnt[lo], N, K, (int64_t)by * TM, (int64_t)bx * TN, out + off * N, S);
 }
 
 template <int TM, int TN, int WM, int WN, bool SWZ, bool A64>

@@ -212,6 +212,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
     // in the last step is never read.
     auto step = [&](uint32_t kt, RowPiece* cur, RowPiece* nxt) {
         const int buf = (int)(kt & 1);
+        // the compiler's single-wave MFMA interleave for this block: spreads
+        // the LDS reads and the dequantization between the MFMAs (measured
+        // 4-5 % faster than its default schedule)
+        __builtin_amdgcn_iglp_opt(1);
         load_all(nxt, (kt + 2) * kStepK);
         const _Float16* as = S[buf] + (wm * (TM / WM)) * kPitch;
         const _Float16* bs = S[buf] + (TM + wn * (TN / WN)) * kPitch;

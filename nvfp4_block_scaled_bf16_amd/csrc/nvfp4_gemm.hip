@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
 
@@ -95,9 +97,10 @@ __device__ __forceinline__ RowPiece load_piece(__amdgpu_buffer_rsrc_t q_rs, __am
     return RowPiece{{lo.x, lo.y, hi.x, hi.y}, s0 | (s1 << 8)};
 }
 
-// dequantize a piece into 32 fp16 (g * D, exact) and store it to LDS
-__device__ __forceinline__ void store_piece(const RowPiece& p, _Float16* dst) {
-    const _Float16 d0 = (_Float16)e4m3_to_f32(p.sf & 0xffu), d1 = (_Float16)e4m3_to_f32(p.sf >> 8);
+// dequantize a piece (its codes, and the two scale codes in sf) into 32
+// fp16 (g * D, exact) and store them to LDS
+__device__ __forceinline__ void store_piece(const RowPiece& p, uint32_t sf, _Float16* dst) {
+    const _Float16 d0 = (_Float16)e4m3_to_f32(sf & 0xffu), d1 = (_Float16)e4m3_to_f32(sf >> 8);
     f16x8 out[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -186,22 +189,52 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
 
     // two register sets for the raw bytes of the next two K steps
     RowPiece pc[P], pn[P];
-    auto load_all = [&](RowPiece* dst, uint32_t kbase) {
+    // SG (plain scale layout, K % 64 == 0): a piece's scale bytes come from
+    // one 16-byte load per four K steps (the row's blocks 16 g .. 16 g + 15
+    // for steps 4 g .. 4 g + 3; dword-aligned as K / 16 % 4 == 0), issued
+    // with the codes of step 4 g into sg_nxt and moved to sg_cur when step
+    // 4 g is dequantized, instead of one 4-byte load per step: a quarter of
+    // the scale loads, each of which touches one cache line per row.  Bytes
+    // read past a row's last block belong to steps past K and are masked.
+    constexpr bool SG = A64 && !SWZ;
+    u32x4 sg_cur[SG ? P : 1], sg_nxt[SG ? P : 1];
+    // kbase = 64 s for step s; J = s % 4
+    auto load_all = [&](RowPiece* dst, uint32_t kbase, auto J) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int p = t + NT * i, r = p >> 1;
             const uint32_t k0 = kbase + 32 * (p & 1);
-            if ((NT * i) / 2 < TM) dst[i] = load_piece<SWZ, A64>(aq_rs, as_rs, (uint32_t)r, Ku, k0);
-            else dst[i] = load_piece<SWZ, A64>(bq_rs, bs_rs, (uint32_t)(r - TM), Ku, k0);
+            const bool is_a = (NT * i) / 2 < TM;
+            const uint32_t row = (uint32_t)(is_a ? r : r - TM);
+            if (SG) {
+                const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(is_a ? aq_rs : bq_rs,
+                                                                      k0 < Ku ? row * (Ku / 2) + k0 / 2 : kOob, 0, 0);
+                dst[i] = RowPiece{{q.x, q.y, q.z, q.w}, 0u};
+                if (decltype(J)::value == 0)
+                    sg_nxt[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                        is_a ? as_rs : bs_rs, kbase < Ku ? row * (Ku / 16) + kbase / 16 : kOob, 0, 0);
+            } else {
+                dst[i] = load_piece<SWZ, A64>(is_a ? aq_rs : bq_rs, is_a ? as_rs : bs_rs, row, Ku, k0);
+            }
         }
     };
-    auto store_all = [&](const RowPiece* src, int buf) {
+    auto store_all = [&](const RowPiece* src, int buf, uint32_t kbase, auto J) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int p = t + NT * i;
-            store_piece(src[i], &S[buf][(p >> 1) * kPitch + 32 * (p & 1)]);
+            uint32_t sf = src[i].sf;
+            if (SG) {
+                constexpr int w = decltype(J)::value;
+                if (w == 0) sg_cur[i] = sg_nxt[i];
+                sf = kbase < Ku ? (sg_cur[i][w] >> (16 * (p & 1))) & 0xffffu : 0u;
+            }
+            store_piece(src[i], sf, &S[buf][(p >> 1) * kPitch + 32 * (p & 1)]);
         }
     };
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J3 = std::integral_constant<int, 3>;
 
     const uint32_t nk = (Ku + kStepK - 1) / kStepK;
     // One K step: load the bytes of step kt + 2 into `nxt` (zeros past K),
@@ -210,13 +243,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
     // the two register sets, so a load stays in flight through a whole step
     // (copying one set into the other would wait for it).  The buffer written
     // in the last step is never read.
-    auto step = [&](uint32_t kt, RowPiece* cur, RowPiece* nxt) {
+    // JN = (kt + 2) % 4, JC = (kt + 1) % 4
+    auto step = [&](uint32_t kt, RowPiece* cur, RowPiece* nxt, auto JN, auto JC) {
         const int buf = (int)(kt & 1);
         // the compiler's single-wave MFMA interleave for this block: spreads
         // the LDS reads and the dequantization between the MFMAs (measured
         // 4-5 % faster than its default schedule)
         __builtin_amdgcn_iglp_opt(1);
-        load_all(nxt, (kt + 2) * kStepK);
+        load_all(nxt, (kt + 2) * kStepK, JN);
         const _Float16* as = S[buf] + (wm * (TM / WM)) * kPitch;
         const _Float16* bs = S[buf] + (TM + wn * (TN / WN)) * kPitch;
 #pragma unroll
@@ -235,16 +269,18 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_q, const
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        store_all(cur, buf ^ 1);
+        store_all(cur, buf ^ 1, (kt + 1) * kStepK, JC);
         __syncthreads();
     };
-    load_all(pc, 0);
-    store_all(pc, 0);
-    load_all(pc, kStepK);
+    load_all(pc, 0, J0{});
+    store_all(pc, 0, 0, J0{});
+    load_all(pc, kStepK, J1{});
     __syncthreads();
-    for (uint32_t kt = 0; kt < nk; kt += 2) {
-        step(kt, pc, pn);
-        if (kt + 1 < nk) step(kt + 1, pn, pc);
+    for (uint32_t kt = 0; kt < nk; kt += 4) {
+        step(kt, pc, pn, J2{}, J1{});
+        if (kt + 1 < nk) step(kt + 1, pn, pc, J3{}, J2{});
+        if (kt + 2 < nk) step(kt + 2, pc, pn, J0{}, J3{});
+        if (kt + 3 < nk) step(kt + 3, pn, pc, J1{}, J0{});
     }
 
     // epilogue: out = RN(RN(acc * S_a) * S_b); accumulator a of lane l holds

@@ -132,11 +132,13 @@ def test_gemm_training_products(oracle):
         _check(_run(*a, *b), ref, bound, kk, name)
 
 
-def test_gemm_large_tiles_ragged(oracle):
+@pytest.mark.parametrize("K", [272, 320])
+def test_gemm_large_tiles_ragged(oracle, K):
     # enough output tiles for the 256 x 256 tile shape, with ragged last tiles
-    # in both directions and a partial last K step; sampled blocks including
-    # the corner tile
-    M, N, K = 4000, 4100, 272
+    # in both directions; K = 272: a partial last K step (two-load pieces);
+    # K = 320: whole 64-wide steps whose last 16-byte scale group (four
+    # steps) is partial; sampled blocks including the corner tile
+    M, N = 4000, 4100
     _announce(f"gemm 256-tile ragged M={M} N={N} K={K} (sampled)")
     a = W.nvfp4_operand(M, K, 61)
     b = W.nvfp4_operand(N, K, 62, per_row=False)

@@ -367,6 +367,10 @@ hipError_t launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const float* a_am
     return hipGetLastError();
 }
 
+bool sf_aligned(const uint8_t* a_sf, const uint8_t* b_sf) {
+    return ((reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf)) & 3u) == 0;
+}
+
 }  // namespace
 
 namespace {
@@ -410,7 +414,9 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const floa
     // 256 x 256 tiles (8 waves of 128 x 64) once they fill the 256 CUs, else
     // 128 x 128 tiles (4 waves of 64 x 64) for four times the workgroups
     const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= 256;
-    const bool a64 = K % 64 == 0;
+    // the wide loads also need 4-byte aligned plain scales (swizzled ones are
+    // required to be); byte-aligned plain scales take the byte loads
+    const bool a64 = K % 64 == 0 && (swizzled || sf_aligned(a_sf, b_sf));
 #define NVFP4_GEMM_LAUNCH(TM, TN, WM, WN, SW)                                                                      \
     return a64 ? launch_cfg<TM, TN, WM, WN, SW, true>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax, b_per_row, M, \
                                                       N, K, out, st, ev0, ev1)                                     \
@@ -481,7 +487,7 @@ hipError_t launch_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const fl
         padded += (h_counts[e] + 255) / 256 * 256;
         tiles256 += (h_counts[e] + 255) / 256 * ((N + 255) / 256);
     }
-    const bool big = tiles256 >= 256 && 4 * padded <= 5 * T, a64 = K % 64 == 0;
+    const bool big = tiles256 >= 256 && 4 * padded <= 5 * T, a64 = K % 64 == 0 && sf_aligned(a_sf, b_sf);
 #define NVFP4_GROUPED_LAUNCH(TM, TN, WM, WN)                                                                        \
     return a64 ? launch_grouped_cfg<TM, TN, WM, WN, true>(a_q, a_sf, a_amax, a_per_row, b_q, b_sf, b_amax,          \
                                                           b_per_row, num_groups, h_counts, N, K, out, st, ev0, ev1) \

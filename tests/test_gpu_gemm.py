@@ -77,6 +77,36 @@ def test_gemm_raw_codes_every_scale(oracle, shape):
     _check(_run(*a, *b), ref, bound, K, "out")
 
 
+def _offset_copy(t, off):
+    """the same bytes, at a device address `off` bytes past an aligned one"""
+    buf = torch.zeros(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("off", [1, 2])
+def test_gemm_unaligned_plain_scales(off):
+    # K % 64 == 0 with plain scales at byte offsets: the byte loads serve
+    # them, and the products equal the aligned call's bit for bit, single
+    # and grouped
+    M, N, K = 300, 260, 256
+    _announce(f"gemm plain scales at byte offset {off}, M={M} N={N} K={K}")
+    da, db = _dev(*W.nvfp4_operand(M, K, 31)), _dev(*W.nvfp4_operand(N, K, 32, per_row=False))
+    ref = host(nv.gemm(*da, *db))
+    da[1], db[1] = _offset_copy(da[1], off), _offset_copy(db[1], off)
+    got = host(nv.gemm(*da, *db))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    counts = np.array([100, 0, 200], np.int64)
+    ga, gb = _dev(*W.nvfp4_operand(300, K, 33)), _dev(*_grouped_b(3, N, K, 34, True))
+    gref = host(nv.gemm_grouped(*ga, *gb, counts))
+    ga[1], gb[1] = _offset_copy(ga[1], off), _offset_copy(gb[1], off)
+    ggot = host(nv.gemm_grouped(*ga, *gb, counts))
+    torch.cuda.synchronize()
+    assert np.array_equal(ggot.view(np.uint32), gref.view(np.uint32))
+
+
 def test_gemm_exact_when_sums_representable(oracle):
     # unit block scales (E4M3 0x38 = 1.0) and amax = 2688 (S = 1): every
     # product is a multiple of 1/4 below 36 and every partial sum is exact

@@ -56,7 +56,8 @@ constexpr uint32_t kOob = 0x80000000u;   // an offset past every descriptor's en
 // as zeros.
 struct RowPiece {
     uint32_t q[4];      // 16 bytes: 32 nibbles, element 2i in the low nibble
-    uint32_t sf;        // two scale codes: low byte, next byte
+    uint32_t sf;        // two scale codes: low byte, next byte (0 where the
+                        // scales come in 16-byte groups instead)
 };
 
 // Byte offset of scale block c of row `row` (both within the operand tile,
@@ -133,8 +134,8 @@ template <int TM, int TN>
 using GemmLds = _Float16[2][(TM + TN) * kPitch];
 
 // XCD-aware order over a one-dimensional grid: each of the 8 XCDs (own L2)
-// takes a contiguous run of tiles, row band major, so a band of A is reused
-// from one L2
+// takes a contiguous run of tile indices (band_order maps an index to a tile),
+// so the operand rows those tiles share are reused from one L2
 __device__ __forceinline__ uint32_t xcd_tile() {
     const uint32_t ntiles = gridDim.x, lin = blockIdx.x;
     return (ntiles & 7u) == 0u ? (lin & 7u) * (ntiles >> 3) + (lin >> 3) : lin;

@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kRhtCols = 256;        // columns per workgroup (32 lanes x 8)
 constexpr int kRhtRows = 128;        // rows per workgroup step (4 waves x 2 row groups x 16)
+constexpr int kRhtStagePitch = 72;   // LDS bytes per staged column: 64 (128 rows of codes) + 8 padding
 constexpr int kRhtAmaxSteps = 4;     // steps per workgroup in the amax pass (512 rows)
 
 // column k (0..7) of a lane's 8-column row word, as fp32 bits
@@ -337,6 +338,12 @@ __global__ __launch_bounds__(256) void k_rht_encode(const uint16_t* __restrict__
             }
         }
     }
+    // Columnwise codes are staged in LDS so that each column's 64 bytes (the
+    // tile's 128 rows) leave as whole 64-byte runs: slot k * 32 + l holds
+    // column 8 l + k of the tile, its 16-row group g = 2 wave + rg at byte
+    // 8 g (pitch 72 bytes: two-way bank conflicts at most on the writes).
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kRhtCols * kRhtStagePitch];
+    __shared__ __attribute__((aligned(8))) uint8_t sstage[kRhtCols * 8];   // scale codes, slot-major
     const float At = MODE == ENC_TENSOR ? col_amax[0] : 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {   // unrolled (see k_rht_amax)
@@ -344,10 +351,36 @@ __global__ __launch_bounds__(256) void k_rht_encode(const uint16_t* __restrict__
         rht_column(v, k, mask, y);
         const float A = MODE == ENC_TENSOR ? At : (active ? col_amax[c0 + k] : 0.0f);
         const ColCodes c = encode_column(y, A);
-        if (active) {
-            *reinterpret_cast<u32x2*>(col_q + (c0 + k) * (M / 2) + r0 / 2) = u32x2{c.lo, c.hi};
-            col_sf[(c0 + k) * (M / 16) + r0 / 16] = (uint8_t)c.code;
+        *reinterpret_cast<u32x2*>(stage + (k * 32 + (lane & 31)) * kRhtStagePitch + 8 * (2 * wave + rg)) =
+            u32x2{c.lo, c.hi};
+        sstage[(k * 32 + (lane & 31)) * 8 + 2 * wave + rg] = (uint8_t)c.code;
+    }
+    __syncthreads();
+    // thread t writes the 8 scale codes of slot t (one 8-byte store where the
+    // tile's rows are whole and the address allows it)
+    {
+        const int t = threadIdx.x;
+        const int64_t col = (int64_t)blockIdx.x * kRhtCols + 8 * (t & 31) + (t >> 5), t0 = (int64_t)blockIdx.y * kRhtRows;
+        if (col < K) {
+            uint8_t* dst = col_sf + col * (M / 16) + t0 / 16;
+            const uint8_t* src = sstage + t * 8;
+            if (t0 + kRhtRows <= M && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0)
+                *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(src);
+            else
+                for (int q = 0; q < 8; ++q)
+                    if (t0 + 16 * q < M) dst[q] = src[q];
         }
+    }
+    // thread t writes 8-byte piece g = t % 8 (rows 16 g .. 16 g + 15 of the
+    // tile) of slots t / 8 + 32 j: eight lanes cover one column's run
+    const int g = threadIdx.x & 7, l = threadIdx.x >> 3;
+    const int64_t tr = (int64_t)blockIdx.y * kRhtRows + 16 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t col = (int64_t)blockIdx.x * kRhtCols + 8 * l + j;
+        if (col < K && tr < M)
+            *reinterpret_cast<u32x2*>(col_q + col * (M / 2) + tr / 2) =
+                *reinterpret_cast<const u32x2*>(stage + (j * 32 + l) * kRhtStagePitch + 8 * g);
     }
 }
 

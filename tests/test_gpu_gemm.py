@@ -180,6 +180,39 @@ def test_gemm_large_tiles_ragged(oracle, K):
         _check(out[rs, cs].astype(np.float64), ref, bound, K, f"block ({r0},{c0})")
 
 
+def test_gemm_large_tiles_every_tile_written(oracle):
+    # 256 x 256 tiles visited in groups of row bands: the output starts as
+    # NaN and every element must come back within the bound (ragged M, N)
+    M, N, K = 4100, 4000, 128
+    _announce(f"gemm 256-tile full compare M={M} N={N} K={K}")
+    a = W.nvfp4_operand(M, K, 63)
+    b = W.nvfp4_operand(N, K, 64)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    nv.gemm_into(out, *_dev(*a), *_dev(*b))
+    torch.cuda.synchronize()
+    ref, bound = oracle.gemm_nvfp4(*a, *b)
+    got = host(out).astype(np.float64)
+    assert np.isfinite(got).all() and np.isfinite(ref).all()
+    _check(got, ref, bound, K, "out")
+
+
+def test_gemm_grouped_large_tiles_every_tile_written(oracle):
+    # the grouped kernel on 256 x 256 tiles (eight experts of 1100 rows each):
+    # NaN-filled output, full compare
+    counts = np.full(8, 1100, np.int64)
+    N, K = 2048, 64
+    _announce(f"gemm grouped 256-tile full compare counts={counts.tolist()} N={N} K={K}")
+    a = W.nvfp4_operand(int(counts.sum()), K, 65)
+    b = _grouped_b(counts.size, N, K, 66, True)
+    out = torch.full((int(counts.sum()), N), float("nan"), dtype=torch.float32, device="cuda:0")
+    nv.gemm_grouped_into(out, *_dev(*a), *_dev(*b), counts)
+    torch.cuda.synchronize()
+    ref, bound = _grouped_ref(oracle, a, b, counts, True)
+    got = host(out).astype(np.float64)
+    assert np.isfinite(got).all() and np.isfinite(ref).all()
+    _check(got, ref, bound, K, "out")
+
+
 def test_gemm_full_size_sampled(oracle):
     # the forward product of the 16384 x 8192 activation with an 8192 x 8192
     # weight, in the launch configuration the benchmark times; the oracle

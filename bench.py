@@ -181,8 +181,8 @@ def all_configs(steps, warmup, only=None):
                2 * 256 * 1024 + 256 * 512 + 256 * 64 + 4)
         back = f32(256 * 1024)
         report("C1-dequant", "dequantize of the C1 output to fp32", timed(
-            lambda i: nv.lib().nvfp4_dequantize(nv._ptr(o1["row_q"]), nv._ptr(o1["row_sf"]), nv._ptr(o1["row_amax"]), 256, 1024, 0,
-                                                nv._ptr(back), nv._stream(dev)), 1),
+            lambda i: nv.lib().nvfp4_dequantize(nv._ptr(o1["row_q"]), nv._ptr(o1["row_sf"]), nv._ptr(o1["row_amax"]), 256, 1024,
+                                                nv.PER_TENSOR, 0, nv._ptr(back), nv._stream(dev)), 1),
                256 * 512 + 256 * 64 + 4 + 4 * 256 * 1024)
     # C2: per-token row+col 4096 x 4096 with outliers
     if want("C2"):

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define NVFP4_API __attribute__((visibility("default")))
@@ -235,14 +235,24 @@ NVFP4_API nvfp4_status nvfp4_quantize_grouped(const void* x, int64_t K, int32_t 
                                     void* stream);
 
 /*
- * Dequantize R vectors of C values (C % 16 == 0) from q [R][C/2], sf
- * [R][C/16] and amax ([1] if amax_per_row == 0, else [R]) to fp32 out [R][C]:
- * out = (+/-) g * (decode(sf) * (amax / 2688)), the product computed exactly
- * as in the cast.  Columnwise buffers are passed with R = K, C = M.  This is
- * the reference dequantization the per-token page pairs with its quantizer.
+ * Dequantize R vectors of C values (C % 16 == 0, else ESHAPE) from q [R][C/2]
+ * and sf [R][C/16] to out [R][C]: this is the reference dequantization the
+ * per-token page pairs with its quantizer (TransformerEngine PR #3045,
+ * Important Files Changed: the per-token GEMM test's reference dequant).
+ *   out = (+/-) g * (decode(sf) * (A / 2688)),
+ * the product computed exactly as in the cast (one binary32 multiply by the
+ * same divisor r), with A = amax[r] for mode NVFP4_PER_TOKEN (amax holds R
+ * values) and A = amax[0] for NVFP4_PER_TENSOR and NVFP4_TILE_16x16 (a 16x16
+ * cast already replicates each tile's scale byte per vector and fills its
+ * amax vectors with the tensor amax); another mode is EINVAL.
+ * out_is_bf16 == 0: out is fp32; otherwise out is bf16, each value the
+ * round-to-nearest-even (ties to even) of that fp32 value.  Columnwise
+ * buffers are passed with R = K, C = M.  q 8-byte, out 16-byte and amax
+ * 4-byte aligned (EALIGN); NULL pointers with R, C > 0 are EINVAL; R == 0 or
+ * C == 0 does nothing.  The caller owns every buffer; nothing is allocated.
  */
 NVFP4_API nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* amax,
-                              int64_t R, int64_t C, int amax_per_row, float* out,
+                              int64_t R, int64_t C, nvfp4_scaling mode, int out_is_bf16, void* out,
                               void* stream);
 
 /*

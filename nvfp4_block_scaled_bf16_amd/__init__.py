@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_amax": (st, [p, i64, i64, st, p, p, p]),
         "nvfp4_encode": (st, [p, i64, i64, st, p, p, p, p, p, p, p]),
         "nvfp4_quantize_grouped": (st, [p, i64, i32, p, p, p, p, p, p, p, p]),
-        "nvfp4_dequantize": (st, [p, p, p, i64, i64, ctypes.c_int, p, p]),
+        "nvfp4_dequantize": (st, [p, p, p, i64, i64, st, ctypes.c_int, p, p]),
         "nvfp4_amax_accumulate": (st, [p, p, i64, f32, p]),
         "nvfp4_amax_accumulate_reduce": (st, [p, p, i64, f32, p]),
         "nvfp4_trace_encode": (st, [p, p]),
@@ -120,6 +120,55 @@ def _amax_len(mode, n):
     return 1 if mode == PER_TENSOR else n
 
 
+def _check_buf(t, dtype, numel, device, name, min_numel=None):
+    """Reject a caller tensor the library would misread: wrong dtype, another
+    device, not contiguous, or an element count other than the layout's
+    (numel; None skips that check, min_numel then gives a lower bound)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    # an empty layout accepts any buffer (the library writes nothing there,
+    # and a non-empty allocation keeps the pointer non-NULL: NULL means "not
+    # requested")
+    if numel is not None and numel > 0 and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements (got {t.numel()})")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements (got {t.numel()})")
+
+
+def _check_dir(name, q, sf, amax, dev, q_n, sf_n, amax_n):
+    """A direction's three outputs: all None (not requested) or all given
+    with the layout's sizes.  Sizes are checked only where the shape is one
+    the library accepts (q_n None otherwise), so that the library's own
+    shape error reaches the caller."""
+    given = [t is not None for t in (q, sf, amax)]
+    if not any(given):
+        return
+    if not all(given):
+        raise ValueError(f"{name}: q, sf and amax must all be given (or all None)")
+    _check_buf(q, torch.uint8, q_n, dev, f"{name}_q")
+    _check_buf(sf, torch.uint8, sf_n, dev, f"{name}_sf")
+    _check_buf(amax, torch.float32, amax_n, dev, f"{name}_amax")
+
+
+def _check_cast_outputs(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, col_sf=None, col_amax=None):
+    """Sizes of nvfp4_quantize's outputs (header layout): rowwise [M][K/2],
+    [M][K/16], amax [1] (per tensor) or [M]; columnwise [K][M/2], [K][M/16],
+    amax [1] or [K]."""
+    M, K = x.shape
+    dev = x.device
+    rok, cok = K % 16 == 0, M % 16 == 0 and K % 8 == 0
+    _check_dir("row", row_q, row_sf, row_amax, dev, M * (K // 2) if rok else None, M * (K // 16) if rok else None,
+               _amax_len(mode, M) if rok else None)
+    _check_dir("col", col_q, col_sf, col_amax, dev, K * (M // 2) if cok else None, K * (M // 16) if cok else None,
+               _amax_len(mode, K) if cok else None)
+
+
 def quantize(x: torch.Tensor, mode="per_token", rowwise: bool = True, columnwise: bool = True) -> dict:
     """Whole cast (one read of x for both directions)."""
     x = _input(x)
@@ -159,6 +208,7 @@ def quantize_sr_into(x, mode, seed: int, offset: int, row_q=None, row_sf=None, r
     """Stochastic-rounding cast into caller-provided buffers."""
     x = _input(x)
     M, K = x.shape
+    _check_cast_outputs(x, _mode(mode), row_q, row_sf, row_amax, col_q, col_sf, col_amax)
     _check(lib().nvfp4_quantize_sr(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                    _ptr(col_q), _ptr(col_sf), _ptr(col_amax), ctypes.c_uint64(seed & (2**64 - 1)),
                                    ctypes.c_uint32(offset & 0xFFFFFFFF), _stream(x.device)))
@@ -184,6 +234,7 @@ def quantize_rht_into(x, mode, sign_mask: int, col_q, col_sf, col_amax, row_q=No
     """Hadamard-transform cast into caller-provided buffers."""
     x = _input(x)
     M, K = x.shape
+    _check_cast_outputs(x, _mode(mode), row_q, row_sf, row_amax, col_q, col_sf, col_amax)
     _check(lib().nvfp4_quantize_rht(_ptr(x), M, K, _mode(mode), ctypes.c_uint32(sign_mask), _ptr(row_q),
                                     _ptr(row_sf), _ptr(row_amax), _ptr(col_q), _ptr(col_sf), _ptr(col_amax),
                                     _stream(x.device)))
@@ -193,6 +244,7 @@ def quantize_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_q=None, c
     """Whole cast into caller-provided buffers (no allocation)."""
     x = _input(x)
     M, K = x.shape
+    _check_cast_outputs(x, _mode(mode), row_q, row_sf, row_amax, col_q, col_sf, col_amax)
     _check(lib().nvfp4_quantize(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                 _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _stream(x.device)))
 
@@ -204,8 +256,8 @@ def quantize_calibrate_into(x, mode, buf, decay: float, row_q=None, row_sf=None,
     element on the same device)."""
     x = _input(x)
     M, K = x.shape
-    if buf.dtype != torch.float32 or buf.device != x.device or buf.numel() < 1:
-        raise ValueError("buf must be a float32 tensor on the input's device")
+    _check_buf(buf, torch.float32, None, x.device, "buf", min_numel=1)
+    _check_cast_outputs(x, _mode(mode), row_q, row_sf, row_amax, col_q, col_sf, col_amax)
     _check(lib().nvfp4_quantize_calibrate(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                           _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _ptr(buf),
                                           ctypes.c_float(decay), _stream(x.device)))
@@ -241,47 +293,89 @@ def amax(x, mode="per_token", rowwise=True, columnwise=True):
 
 
 def encode(x, mode="per_token", row_amax=None, col_amax=None):
-    """Block scales + E2M1 data from caller-supplied amax (split form)."""
+    """Block scales + E2M1 data from caller-supplied amax (split form): fp32
+    values, finite and >= 0, [1] per tensor or [M] / [K] per token."""
     x = _input(x)
-    mode = _mode(mode)
     M, K = x.shape
     out = {}
     if row_amax is not None:
         out.update(row_q=_u8((M, K // 2), x.device), row_sf=_u8((M, K // 16), x.device))
     if col_amax is not None:
         out.update(col_q=_u8((K, M // 2), x.device), col_sf=_u8((K, M // 16), x.device))
-    g = out.get
-    _check(lib().nvfp4_encode(_ptr(x), M, K, mode, _ptr(row_amax), _ptr(col_amax), _ptr(g("row_q")),
-                              _ptr(g("row_sf")), _ptr(g("col_q")), _ptr(g("col_sf")), _stream(x.device)))
+    encode_into(x, mode, row_amax, col_amax, **out)
     return out
+
+
+def encode_into(x, mode, row_amax=None, col_amax=None, row_q=None, row_sf=None, col_q=None, col_sf=None):
+    """:func:`encode` into caller-provided buffers (rowwise [M][K/2],
+    [M][K/16]; columnwise [K][M/2], [K][M/16])."""
+    x = _input(x)
+    mode = _mode(mode)
+    M, K = x.shape
+    dev = x.device
+    if row_amax is not None:
+        _check_buf(row_amax, torch.float32, _amax_len(mode, M), dev, "row_amax")
+    if col_amax is not None:
+        _check_buf(col_amax, torch.float32, _amax_len(mode, K), dev, "col_amax")
+    rok, cok = K % 16 == 0, M % 16 == 0 and K % 8 == 0
+    for name, t, n in (("row_q", row_q, M * (K // 2) if rok else None), ("row_sf", row_sf, M * (K // 16) if rok else None),
+                       ("col_q", col_q, K * (M // 2) if cok else None), ("col_sf", col_sf, K * (M // 16) if cok else None)):
+        if t is not None:
+            _check_buf(t, torch.uint8, n, dev, name)
+    _check(lib().nvfp4_encode(_ptr(x), M, K, mode, _ptr(row_amax), _ptr(col_amax), _ptr(row_q),
+                              _ptr(row_sf), _ptr(col_q), _ptr(col_sf), _stream(dev)))
 
 
 def quantize_grouped(x, counts, rowwise=True, columnwise=True):
     """Grouped (MoE) per-token cast; counts: host sequence of per-expert rows."""
     x = _input(x)
     T, K = x.shape
-    counts_t = torch.as_tensor(list(counts), dtype=torch.int64).contiguous()
-    G = counts_t.numel()
+    G = len(list(counts))
     dev = x.device
     out = {}
     if rowwise:
         out.update(row_q=_u8((T, K // 2), dev), row_sf=_u8((T, K // 16), dev), row_amax=_f32(T, dev))
     if columnwise:
         out.update(col_q=_u8(T * K // 2, dev), col_sf=_u8(T * K // 16, dev), col_amax=_f32((G, K), dev))
-    g = out.get
-    _check(lib().nvfp4_quantize_grouped(_ptr(x), K, G, ctypes.c_void_p(counts_t.data_ptr()),
-                                        _ptr(g("row_q")), _ptr(g("row_sf")), _ptr(g("row_amax")),
-                                        _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")), _stream(dev)))
+    quantize_grouped_into(x, counts, **out)
     return out
 
 
-def dequantize(q, sf, amax, amax_per_row: bool):
-    """fp32 [R, C] from q [R, C/2], sf [R, C/16] and amax ([1] or [R])."""
+def quantize_grouped_into(x, counts, row_q=None, row_sf=None, row_amax=None, col_q=None, col_sf=None,
+                          col_amax=None):
+    """Grouped cast into caller-provided buffers: rowwise [T][K/2], [T][K/16],
+    [T]; columnwise slabs T*K/2 and T*K/16 bytes, col_amax [G][K]."""
+    x = _input(x)
+    T, K = x.shape
+    counts_t = torch.as_tensor(list(counts), dtype=torch.int64).contiguous()
+    G = counts_t.numel()
+    dev = x.device
+    ok = K % 16 == 0
+    _check_dir("row", row_q, row_sf, row_amax, dev, T * (K // 2) if ok else None, T * (K // 16) if ok else None,
+               T if ok else None)
+    _check_dir("col", col_q, col_sf, col_amax, dev, T * (K // 2) if ok else None, T * (K // 16) if ok else None,
+               G * K if ok else None)
+    _check(lib().nvfp4_quantize_grouped(_ptr(x), K, G, ctypes.c_void_p(counts_t.data_ptr()),
+                                        _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
+                                        _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _stream(dev)))
+
+
+def dequantize(q, sf, amax, mode="per_token", out_dtype=torch.float32):
+    """[R, C] from q [R, C/2], sf [R, C/16] and amax ([R] for per-token
+    scaling, [1] otherwise): fp32, or bf16 as the round-to-nearest-even of
+    the fp32 value (out_dtype=torch.bfloat16)."""
+    mode = _mode(mode)
+    if q.dim() != 2 or q.dtype != torch.uint8 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous 2-D uint8 CUDA tensor [R, C/2]")
     R, C2 = q.shape
     C = 2 * C2
-    out = _f32((R, C), q.device)
-    _check(lib().nvfp4_dequantize(_ptr(q), _ptr(sf), _ptr(amax), R, C, int(bool(amax_per_row)), _ptr(out),
-                                  _stream(q.device)))
+    _check_buf(sf, torch.uint8, R * (C // 16), q.device, "sf")
+    _check_buf(amax, torch.float32, R if mode == PER_TOKEN else None, q.device, "amax", min_numel=1)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    out = torch.empty((R, C), dtype=out_dtype, device=q.device)
+    _check(lib().nvfp4_dequantize(_ptr(q), _ptr(sf), _ptr(amax), R, C, mode, int(out_dtype == torch.bfloat16),
+                                  _ptr(out), _stream(q.device)))
     return out
 
 
@@ -344,6 +438,8 @@ def quantize_swizzled_into(x, mode, row_q=None, row_sf=None, row_amax=None, col_
     """Swizzled-scale cast into caller-provided buffers."""
     x = _input(x)
     M, K = x.shape
+    # the swizzled scale matrices hold M*K/16 bytes each (M, K % 128 == 0)
+    _check_cast_outputs(x, _mode(mode), row_q, row_sf, row_amax, col_q, col_sf, col_amax)
     _check(lib().nvfp4_quantize_swizzled(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                          _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _stream(x.device)))
 
@@ -404,14 +500,16 @@ def gemm_grouped(a_q, a_sf, a_amax, b_q, b_sf, b_amax, counts):
 
 def amax_accumulate(buf, observed, decay: float):
     """In place: buf = max(buf * decay, observed), fp32."""
-    if buf.numel() != observed.numel():
-        raise ValueError("buf and observed must have the same length")
+    _check_buf(buf, torch.float32, None, buf.device if isinstance(buf, torch.Tensor) else None, "buf")
+    _check_buf(observed, torch.float32, buf.numel(), buf.device, "observed")
     _check(lib().nvfp4_amax_accumulate(_ptr(buf), _ptr(observed), buf.numel(), float(decay), _stream(buf.device)))
     return buf
 
 
 def amax_accumulate_reduce(buf, observed, decay: float):
     """In place: buf[0] = max(buf[0] * decay, max(observed))."""
+    _check_buf(buf, torch.float32, None, buf.device if isinstance(buf, torch.Tensor) else None, "buf", min_numel=1)
+    _check_buf(observed, torch.float32, None, buf.device, "observed")
     _check(lib().nvfp4_amax_accumulate_reduce(_ptr(buf), _ptr(observed), observed.numel(), float(decay),
                                               _stream(buf.device)))
     return buf

@@ -373,13 +373,16 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
 }
 
 nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
-                              int amax_per_row, float* out, void* stream) {
+                              nvfp4_scaling mode, int out_is_bf16, void* out, void* stream) {
+    if (mode != NVFP4_PER_TENSOR && mode != NVFP4_PER_TOKEN && mode != NVFP4_TILE_16x16)
+        return fail(NVFP4_EINVAL, "unknown scaling mode %d", (int)mode);
     if (R < 0 || C < 0) return fail(NVFP4_EINVAL, "negative size");
     if (C % 16 != 0) return fail(NVFP4_ESHAPE, "dequantize needs C %% 16 == 0 (C=%lld)", (long long)C);
     if (R == 0 || C == 0) return ok();
     if (!q || !sf || !amax || !out) return fail(NVFP4_EINVAL, "NULL argument");
     if (!aligned(q, 8) || !aligned(out, 16) || !aligned(amax, 4)) return fail(NVFP4_EALIGN, "q needs 8-byte, out 16-byte, amax 4-byte alignment");
-    nvfp4_status s = check_hip(launch_dequant(q, sf, amax, R, C, amax_per_row ? 1 : 0, out, as_stream(stream)), "dequantize");
+    nvfp4_status s = check_hip(launch_dequant(q, sf, amax, R, C, mode == NVFP4_PER_TOKEN ? 1 : 0, out_is_bf16 != 0, out,
+                                              as_stream(stream)), "dequantize");
     return s != NVFP4_OK ? s : ok();
 }
 

@@ -102,6 +102,15 @@ __device__ __forceinline__ uint32_t put_fp4x2(uint32_t old, float q0, float q1) 
 // outer scale from an outer amax
 __device__ __forceinline__ float outer_scale(float A) { return A / 2688.0f; }
 
+// two fp32 values rounded to bf16 nearest-even by the hardware's packed
+// conversion (checked against the integer rounding over every non-NaN fp32
+// pattern): a in the low half, b in the high half
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    const bf16x2_t p = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
 // ------------------------------------------------------------- fast path
 //
 // The hot loops avoid IEEE division.  Facts, each checked exhaustively (1,
@@ -130,6 +139,14 @@ __device__ __forceinline__ float rcp_rn(float r) {
     return __builtin_fmaf(e, y0, y0);
 }
 
+// RD(1/r) for normal r in [2^-64, 2^64]: the hardware reciprocal is RD or
+// RU (fact 2); step down one ulp when the residual 1 - r*y0 is negative
+__device__ __forceinline__ float rcp_rd(float r) {
+    const float y0 = __builtin_amdgcn_rcpf(r);
+    const float e = __builtin_fmaf(-r, y0, 1.0f);
+    return __uint_as_float(__float_as_uint(y0) - (__float_as_uint(e) >> 31));
+}
+
 // RN(a / r) given y = RN(1/r), under the range conditions of fact 1
 __device__ __forceinline__ float div_fast(float a, float r, float y) {
     float q0 = a * y;
@@ -143,14 +160,19 @@ struct Outer {
     bool slow;   // A outside [2^-40, 2^60] (or tiny enough for S to underflow): exact path
 };
 
-// A == 0 uses S = yS = 1: every block of such a vector is all zeros and the
-// fast block below encodes it as code 0 with sign-only nibbles.
-__device__ __forceinline__ Outer make_outer(float A) {
+// A == 0 uses S = yS = 1: when the amax was measured on the vector, every
+// block of it is all zeros and the fast block below encodes it as code 0
+// with sign-only nibbles.  SAT: the amax comes from the caller and may be 0
+// over nonzero data, where S == 0 must still give code 0 and sign-only
+// nibbles; such a vector (valid: it lies inside the tensor) takes the exact
+// path, whose block scale handles S == 0.
+template <bool SAT = false>
+__device__ __forceinline__ Outer make_outer(float A, bool valid = true) {
     Outer o;
     const bool zero = A == 0.0f;
     o.S = zero ? 1.0f : outer_scale(A);
     o.yS = rcp_rn(o.S);
-    o.slow = !zero && !(A >= 0x1p-40f && A <= 0x1p60f);
+    o.slow = zero ? (SAT && valid) : !(A >= 0x1p-40f && A <= 0x1p60f);
     return o;
 }
 
@@ -198,11 +220,7 @@ __device__ __forceinline__ FastBlock fast_block(uint32_t bbits, const Outer& o) 
     c = c < 0x400u ? 0x400u : (c > 0x47Eu ? 0x47Eu : c);
     fb.code = c;
     const float r = __uint_as_float((c << 20) - (0x40u << 20)) * o.S;   // decode(code) * S; 2^-7 * S for code 0
-    // RD(1/r): the hardware reciprocal is RD or RU (fact 2); step down one
-    // ulp when the residual 1 - r*y0 is negative
-    const float y0 = __builtin_amdgcn_rcpf(r);
-    const float e = __builtin_fmaf(-r, y0, 1.0f);
-    fb.yh = __uint_as_float(__float_as_uint(y0) - (__float_as_uint(e) >> 31));
+    fb.yh = rcp_rd(r);
     fb.yl = __builtin_fmaf(-r, fb.yh, 1.0f) * fb.yh;
     // exact path: sf in the E4M3 subnormal range (and not an all-zero
     // block), or an r with all mantissa bits set (fact 4's exception)

@@ -72,8 +72,9 @@ hipError_t launch_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const fl
                                const uint8_t* b_q, const uint8_t* b_sf, const float* b_amax, int b_per_row,
                                int32_t num_groups, const int64_t* h_counts, int64_t N, int64_t K, float* out,
                                hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// out: fp32 [R][C], or bf16 (round to nearest-even of the fp32 value) when bf16
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
-                          int amax_per_row, float* out, hipStream_t st);
+                          int amax_per_row, bool bf16, void* out, hipStream_t st);
 hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);
 hipError_t launch_accumulate_reduce(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);
 

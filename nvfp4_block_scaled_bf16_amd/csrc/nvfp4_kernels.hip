@@ -544,18 +544,18 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         // one column per thread; a column outside the fast range sends the
         // whole tile to the exact path
         const uint32_t c = bx * kEncCols + threadIdx.x;
-        const Outer o = make_outer(c < K ? col_amax[c] : 0.0f);
+        const Outer o = make_outer<SAT>(c < K ? col_amax[c] : 0.0f, c < K);
         col_scale[threadIdx.x] = make_float2(o.S, o.yS);
         col_slow = __syncthreads_or(o.slow) != 0;
     } else if (COL && !TILE && MODE != ENC_GROUPED) {
         const float ca = col_amax[0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) colO[j] = make_outer(ca);
+        for (int j = 0; j < 8; ++j) colO[j] = make_outer<SAT>(ca);
         col_slow = colO[0].slow;
     }
     // per-tensor rowwise outer scale
     const float rowA_t = (ROW && MODE == ENC_TENSOR) ? row_amax[0] : 0.0f;
-    const Outer rowO_t = make_outer(rowA_t);
+    const Outer rowO_t = make_outer<SAT>(rowA_t, ROW && MODE == ENC_TENSOR);
     const bool tile_slow = (TILE && tileO.slow) || (ROW && MODE == ENC_TENSOR && rowO_t.slow);
 
     // destinations of a sub-block (columnwise output and the exact path)
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
         bool step_slow = tile_slow;
         if (ROWTOK) {
             const bool row_in = (uint32_t)(lane & 31) < nrows;
-            const Outer o = make_outer(row_in ? ra : 0.0f);
+            const Outer o = make_outer<SAT>(row_in ? ra : 0.0f, row_in);
             if (kPrefetch && more) ra = load_ra(sb + 1);
             if (lane < 32) {
                 row_scale[wave][lane][0] = o.S;
@@ -1121,10 +1121,17 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
 
 // ---------------------------------------------------------------- dequantize
 
-// one thread per 16-element block: out = (+/-) g * (decode(sf) * (A / 2688))
+// one thread per 16-element block: out = (+/-) g * (decode(sf) * (A / 2688)),
+// fp32, or (BF16) that fp32 value rounded to nearest-even bf16
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // finite inputs (NaN cannot arise here)
+}
+
+template <bool BF16>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sf,
                                                  const float* __restrict__ amax, int64_t R, int64_t C,
-                                                 int amax_per_row, float* __restrict__ out) {
+                                                 int amax_per_row, void* __restrict__ out) {
     const int64_t nb = C / 16;
     int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -1144,9 +1151,18 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, 
             const float g = __uint_as_float(gbits | ((nib & 8u) << 28));
             o[i] = g * ratio;
         }
-        float4* dst = reinterpret_cast<float4*>(out + r * C + 16 * j);
+        if (BF16) {
+            uint32_t h[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+            for (int i = 0; i < 8; ++i) h[i] = bf16_rne(o[2 * i]) | (bf16_rne(o[2 * i + 1]) << 16);
+            u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + r * C + 16 * j);
+            dst[0] = u32x4{h[0], h[1], h[2], h[3]};
+            dst[1] = u32x4{h[4], h[5], h[6], h[7]};
+        } else {
+            float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + r * C + 16 * j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        }
     }
 }
 
@@ -1279,12 +1295,13 @@ hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int
 }
 
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
-                          int amax_per_row, float* out, hipStream_t st) {
+                          int amax_per_row, bool bf16, void* out, hipStream_t st) {
     const int64_t blocks = R * (C / 16);
     if (blocks <= 0) return hipSuccess;
     unsigned grid = cdiv(blocks, 256);
     if (grid > 16384) grid = 16384;
-    hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(256), 0, st, q, sf, amax, R, C, amax_per_row, out);
+    if (bf16) hipLaunchKernelGGL(k_dequant<true>, dim3(grid), dim3(256), 0, st, q, sf, amax, R, C, amax_per_row, out);
+    else hipLaunchKernelGGL(k_dequant<false>, dim3(grid), dim3(256), 0, st, q, sf, amax, R, C, amax_per_row, out);
     return hipGetLastError();
 }
 

@@ -39,7 +39,6 @@ __device__ __forceinline__ uint32_t col_bits(const u32x4& w, int k) {
     return (k & 1) ? (word & 0xffff0000u) : (word << 16);
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 nearest-even, returned as fp32 with a zero low half; NaN
 // stays NaN (quiet), infinities stay
@@ -65,13 +64,11 @@ __device__ __forceinline__ void rht_column(const u32x4 (&v)[16], int k, uint32_t
             t[i + h] = a - b;
         }
     }
-    // bf16 nearest-even by the hardware's packed conversion (checked equal to
-    // the integer rounding of round_to_bf16 over 2^24 fp32 patterns,
-    // subnormals included), two values per instruction
+    // bf16 nearest-even by the hardware's packed conversion, two values per
+    // instruction
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-        const bf16x2 p = {(__bf16)(t[i] * 0.25f), (__bf16)(t[i + 1] * 0.25f)};
-        const uint32_t w = __builtin_bit_cast(uint32_t, p);
+        const uint32_t w = bf16x2_rne(t[i] * 0.25f, t[i + 1] * 0.25f);
         y[i] = w << 16;
         y[i + 1] = w & 0xffff0000u;
     }

@@ -13,7 +13,7 @@ import nvfp4_block_scaled_bf16_amd as nv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 
-EINVAL, ESHAPE, EALIGN = 1, 2, 3
+OK, EINVAL, ESHAPE, EALIGN = 0, 1, 2, 3
 FAKE = 0x10000  # an aligned address that is never dereferenced: validation fails first
 
 
@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_symbol():
     L = nv.lib()
     for name in declared():
         assert hasattr(L, name), name
-    assert L.nvfp4_abi_version() == 1
+    assert L.nvfp4_abi_version() == 2
 
 
 def _q(*args):
@@ -81,8 +81,12 @@ def test_other_entry_points_validation():
     assert L.nvfp4_amax(f, 16, 12, 1, f, None, None) == ESHAPE
     assert L.nvfp4_encode(f, 16, 16, 2, f, None, f, f, None, None, None) == EINVAL
     assert L.nvfp4_encode(f, 16, 16, 1, None, None, f, f, None, None, None) == EINVAL
-    assert L.nvfp4_dequantize(f, f, f, 4, 24, 1, f, None) == ESHAPE
-    assert L.nvfp4_dequantize(None, f, f, 4, 32, 1, f, None) == EINVAL
+    assert L.nvfp4_dequantize(f, f, f, 4, 24, 1, 0, f, None) == ESHAPE
+    assert L.nvfp4_dequantize(None, f, f, 4, 32, 1, 0, f, None) == EINVAL
+    assert L.nvfp4_dequantize(f, f, f, 4, 32, 3, 0, f, None) == EINVAL      # unknown mode
+    assert L.nvfp4_dequantize(f, f, f, 4, 32, -1, 1, f, None) == EINVAL
+    assert L.nvfp4_dequantize(f, f, f, 4, 32, 1, 1, P(FAKE + 8), None) == EALIGN   # out needs 16 bytes
+    assert L.nvfp4_dequantize(f, f, f, 0, 32, 1, 1, None, None) == OK        # empty: nothing to do
     assert L.nvfp4_amax_accumulate(f, f, 4, ctypes.c_float(1.5), None) == EINVAL
     assert L.nvfp4_amax_accumulate(f, f, 4, ctypes.c_float(-0.1), None) == EINVAL
     assert L.nvfp4_amax_accumulate(f, f, 4, ctypes.c_float(float("nan")), None) == EINVAL
@@ -206,3 +210,41 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         nv.quantize(torch.zeros(16, 16, dtype=torch.bfloat16))
+
+
+def test_binding_validates_caller_buffers():
+    """The *_into wrappers check every caller tensor against the header's
+    layout before calling the library (checked here with the helpers they
+    call, on host tensors, since the wrappers themselves need a GPU)."""
+    import torch
+    M, K = 32, 64
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    good = dict(row_q=u8(M * K // 2), row_sf=u8(M * K // 16), row_amax=f32(M),
+                col_q=u8(K * M // 2), col_sf=u8(K * M // 16), col_amax=f32(K))
+    nv._check_cast_outputs(x, nv.PER_TOKEN, **good)                      # accepted
+    nv._check_cast_outputs(x, nv.PER_TENSOR, **dict(good, row_amax=f32(1), col_amax=f32(1)))
+    bad_cases = [
+        dict(good, row_amax=f32(1)),                                      # per-token row amax must be [M]
+        dict(good, col_amax=f32(M)),                                      # [K], not [M]
+        dict(good, row_q=u8(M * K // 2 - 1)),                             # short data buffer
+        dict(good, col_sf=u8(K * M // 16 + 16)),                          # wrong scale count
+        dict(good, row_amax=torch.zeros(M, dtype=torch.float64)),         # amax read as raw fp32 bits
+        dict(good, row_q=torch.zeros(M * K, dtype=torch.uint8)[::2]),    # not contiguous
+        dict(good, col_q=None),                                           # a direction half given
+        dict(good, row_sf=torch.zeros(M * K // 16, dtype=torch.uint8, device="meta")),   # another device
+    ]
+    for kw in bad_cases:
+        with pytest.raises(ValueError):
+            nv._check_cast_outputs(x, nv.PER_TOKEN, **kw)
+    with pytest.raises(ValueError):
+        nv._check_cast_outputs(x, nv.PER_TENSOR, **good)                 # per-tensor amax is [1]
+    # a shape the library rejects is left to the library (ESHAPE), not the size check
+    nv._check_cast_outputs(torch.zeros(M, 40, dtype=torch.bfloat16), nv.PER_TOKEN,
+                           row_q=u8(1), row_sf=u8(1), row_amax=f32(1))
+    with pytest.raises(ValueError):
+        nv._check_buf(f32(3), torch.float32, 4, torch.device("cpu"), "buf")
+    nv._check_buf(f32(3), torch.float32, None, torch.device("cpu"), "buf", min_numel=1)
+    with pytest.raises(ValueError):
+        nv._check_buf(f32(0), torch.float32, None, torch.device("cpu"), "buf", min_numel=1)

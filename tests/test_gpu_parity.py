@@ -1,8 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Bit-exact on every output byte (packed E2M1 data, E4M3 scale codes) and on
-the fp32 amax bit patterns.  Small shapes span several workgroup tiles and a
-ragged tail; the full-size workloads are compared in full where the oracle
+the fp32 amax bit patterns.  Every output buffer sits between canary-filled guard regions
+(tests/gpu_util.py): the guards must survive the call and the buffer is
+compared in full, so an unwritten byte or a write past an end fails.
+Small shapes span several workgroup tiles and a ragged tail; the full-size workloads are compared in full where the oracle
 finishes in seconds, otherwise on sampled rows / columns / tiles that the
 oracle computes one by one, plus the complete amax vectors.
 """
@@ -12,7 +14,8 @@ import torch
 
 import nvfp4_block_scaled_bf16_amd as nv
 from nvfp4_block_scaled_bf16_amd import workloads as W
-from tests.gpu_util import assert_bytes_equal, compare_cast, host, to_dev
+from tests.gpu_util import (Guarded, assert_bytes_equal, cast_spec, compare_cast, grouped_spec, host,
+                            quantize_guarded, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +38,7 @@ def test_cast_small_shapes(oracle, mode, shape):
     M, K = shape
     x = _x(M, K, 100 + M + K)
     _announce(f"quantize mode={mode} shape={shape}")
-    out = nv.quantize(to_dev(x), mode)
+    out = quantize_guarded(to_dev(x), mode)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, mode))
 
@@ -44,7 +47,10 @@ def test_cast_small_shapes(oracle, mode, shape):
 def test_rowwise_only_ragged_rows(oracle, mode):
     x = _x(37, 96, 7)
     _announce(f"rowwise 37x96 mode={mode}")
-    out = nv.quantize_rowwise(to_dev(x), mode)
+    d = to_dev(x)
+    out = Guarded(cast_spec(37, 96, mode, True, False))
+    nv._check(nv.lib().nvfp4_quantize_rowwise(nv._ptr(d), 37, 96, mode, nv._ptr(out["row_q"]), nv._ptr(out["row_sf"]),
+                                              nv._ptr(out["row_amax"]), nv._stream(d.device)))
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, mode, rowwise=True, columnwise=False))
 
@@ -53,7 +59,10 @@ def test_rowwise_only_ragged_rows(oracle, mode):
 def test_columnwise_only_narrow(oracle, mode):
     x = _x(48, 24, 8)
     _announce(f"columnwise 48x24 mode={mode}")
-    out = nv.quantize_columnwise(to_dev(x), mode)
+    d = to_dev(x)
+    out = Guarded(cast_spec(48, 24, mode, False, True))
+    nv._check(nv.lib().nvfp4_quantize_columnwise(nv._ptr(d), 48, 24, mode, nv._ptr(out["col_q"]), nv._ptr(out["col_sf"]),
+                                                 nv._ptr(out["col_amax"]), nv._stream(d.device)))
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, mode, rowwise=False, columnwise=True))
 
@@ -77,6 +86,14 @@ def _crafted(M=64, K=1024, seed=3):
     f[:, 7] = 0.0
     f[:, 9] = -0.0
     f[8:24, 100] = 6.0 * 448.0
+    # negative bf16 subnormals inside blocks whose scale is normal: their
+    # quotients are fp32 subnormals (or round to -0) in both directions
+    sub = np.float32(-(2.0 ** -130))
+    f[9, 0:16:3] = sub
+    f[9, 17] = np.float32(-(2.0 ** -133))
+    f[16:32, 300] = rng.standard_normal(16).astype(np.float32)
+    f[20, 300] = sub
+    f[23, 300] = np.float32(-(2.0 ** -127))
     return W.bf16_from_f32(f)
 
 
@@ -84,7 +101,7 @@ def _crafted(M=64, K=1024, seed=3):
 def test_crafted_edges(oracle, mode):
     x = _crafted()
     _announce(f"crafted 64x1024 mode={mode}")
-    out = nv.quantize(to_dev(x), mode)
+    out = quantize_guarded(to_dev(x), mode)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, mode))
 
@@ -96,38 +113,63 @@ def test_all_zero_and_single_row(oracle):
         for mode in (nv.PER_TENSOR, nv.PER_TOKEN):
             _announce(f"zeros {shape} mode={mode}")
             col = shape[0] % 16 == 0
-            out = nv.quantize(to_dev(x), mode, rowwise=True, columnwise=col)
+            out = quantize_guarded(to_dev(x), mode, rowwise=True, columnwise=col)
             torch.cuda.synchronize()
             compare_cast(out, oracle.quantize(x, mode, rowwise=True, columnwise=col))
 
 
+def _encode_guarded(d, mode, ra, ca):
+    M, K = d.shape
+    spec = {k: v for k, v in cast_spec(M, K, mode).items() if not k.endswith("amax")}
+    out = Guarded(spec)
+    nv.encode_into(d, mode, torch.from_numpy(ra).cuda(), torch.from_numpy(ca).cuda(), **out.views)
+    torch.cuda.synchronize()
+    out.check_guards()
+    return out
+
+
+def _compare_encode(oracle, x, out, ra, ca, per_token):
+    q, sf = oracle.encode_rowwise(x, ra, per_token)
+    assert_bytes_equal(host(out["row_q"]).reshape(q.shape), q, "row_q")
+    assert_bytes_equal(host(out["row_sf"]).reshape(sf.shape), sf, "row_sf")
+    q, sf = oracle.encode_colwise(x, ca, per_token)
+    assert_bytes_equal(host(out["col_q"]).reshape(q.shape), q, "col_q")
+    assert_bytes_equal(host(out["col_sf"]).reshape(sf.shape), sf, "col_sf")
+
+
 def test_encode_with_supplied_amax_saturates(oracle):
     x = _x(64, 512, 9)
+    d = to_dev(x)
     true_r, true_c = oracle.amax_rows(x), oracle.amax_cols(x)
     for fr, fc in [(1 / 64.0, 1 / 16.0), (3.0, 0.5), (1.0, 1.0)]:
         ra = (true_r * np.float32(fr)).astype(np.float32)
         ca = (true_c * np.float32(fc)).astype(np.float32)
         _announce(f"encode per-token factors {fr} {fc}")
-        out = nv.encode(to_dev(x), nv.PER_TOKEN, torch.from_numpy(ra).cuda(), torch.from_numpy(ca).cuda())
-        torch.cuda.synchronize()
-        q, sf = oracle.encode_rowwise(x, ra, True)
-        assert_bytes_equal(host(out["row_q"]), q, "row_q")
-        assert_bytes_equal(host(out["row_sf"]), sf, "row_sf")
-        q, sf = oracle.encode_colwise(x, ca, True)
-        assert_bytes_equal(host(out["col_q"]), q, "col_q")
-        assert_bytes_equal(host(out["col_sf"]), sf, "col_sf")
+        _compare_encode(oracle, x, _encode_guarded(d, nv.PER_TOKEN, ra, ca), ra, ca, True)
     # per-tensor with different rowwise / columnwise scalars
     ra = np.array([oracle.amax_tensor(x) * np.float32(0.25)], np.float32)
     ca = np.array([oracle.amax_tensor(x) * np.float32(2.0)], np.float32)
     _announce("encode per-tensor, different scalars")
-    out = nv.encode(to_dev(x), nv.PER_TENSOR, torch.from_numpy(ra).cuda(), torch.from_numpy(ca).cuda())
-    torch.cuda.synchronize()
-    q, sf = oracle.encode_rowwise(x, ra, False)
-    assert_bytes_equal(host(out["row_q"]), q, "row_q")
-    assert_bytes_equal(host(out["row_sf"]), sf, "row_sf")
-    q, sf = oracle.encode_colwise(x, ca, False)
-    assert_bytes_equal(host(out["col_q"]), q, "col_q")
-    assert_bytes_equal(host(out["col_sf"]), sf, "col_sf")
+    _compare_encode(oracle, x, _encode_guarded(d, nv.PER_TENSOR, ra, ca), ra, ca, False)
+
+
+def test_encode_with_supplied_zero_amax(oracle):
+    """A supplied amax of 0 over nonzero data (delayed scaling from a
+    zero-initialised calibration buffer) gives scale code 0 and sign-only
+    nibbles for that vector, as S == 0 does in the oracle."""
+    x = _x(64, 512, 19)
+    d = to_dev(x)
+    ra, ca = oracle.amax_rows(x).copy(), oracle.amax_cols(x).copy()
+    ra[[0, 5, 31, 32, 63]] = 0.0
+    ca[[0, 7, 8, 255, 256, 511]] = 0.0
+    _announce("encode per-token with zero entries in the supplied amax")
+    _compare_encode(oracle, x, _encode_guarded(d, nv.PER_TOKEN, ra, ca), ra, ca, True)
+    z = np.zeros(1, np.float32)
+    _announce("encode per-tensor with a supplied amax of 0")
+    _compare_encode(oracle, x, _encode_guarded(d, nv.PER_TENSOR, z, z), z, z, False)
+    ok = np.array([oracle.amax_tensor(x)], np.float32)
+    _announce("encode per-tensor: rowwise amax 0, columnwise the tensor's")
+    _compare_encode(oracle, x, _encode_guarded(d, nv.PER_TENSOR, z, ok), z, ok, False)
 
 
 @pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
@@ -160,26 +202,58 @@ def _grouped_case(counts, K, seed):
 def test_grouped_small(oracle, counts, K):
     x = _grouped_case(counts, K, len(counts))
     _announce(f"grouped experts={len(counts)} T={sum(counts)} K={K}")
-    out = nv.quantize_grouped(to_dev(x), counts)
+    out = Guarded(grouped_spec(sum(counts), K, len(counts)))
+    nv.quantize_grouped_into(to_dev(x), counts, **out.views)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_grouped(x, np.array(counts, np.int64)))
 
 
+def _bf16_rne(f32):
+    """Round-to-nearest-even of fp32 values to bf16 bit patterns, written out
+    here (a second route to what the library's bf16 output must equal)."""
+    u = np.ascontiguousarray(f32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _dequant_guarded(q, sf, amax, mode, bf16):
+    R, C = q.shape[0], 2 * q.shape[1]
+    out = Guarded({"out": (R * C, torch.bfloat16 if bf16 else torch.float32)})
+    nv._check(nv.lib().nvfp4_dequantize(nv._ptr(q), nv._ptr(sf), nv._ptr(amax), R, C, mode, int(bf16),
+                                        nv._ptr(out["out"]), nv._stream(q.device)))
+    torch.cuda.synchronize()
+    out.check_guards()
+    return host(out["out"].view(torch.int16) if bf16 else out["out"]).reshape(R, C)
+
+
 def test_dequantize_roundtrip(oracle):
+    """fp32 and bf16 outputs of every mode against the oracle's fp32
+    dequantization (bf16: its round to nearest-even)."""
     x = W.c1()
-    _announce("C1 dequantize")
+    _announce("C1 dequantize, fp32 and bf16 outputs")
     d = to_dev(x)
     out = nv.quantize(d, nv.PER_TENSOR)
-    back = nv.dequantize(out["row_q"], out["row_sf"], out["row_amax"], amax_per_row=False)
-    backc = nv.dequantize(out["col_q"], out["col_sf"], out["col_amax"], amax_per_row=False)
     tok = nv.quantize(d, nv.PER_TOKEN)
-    backt = nv.dequantize(tok["col_q"], tok["col_sf"], tok["col_amax"], amax_per_row=True)
+    til = nv.quantize(d, nv.TILE_16x16)
     torch.cuda.synchronize()
     ref = oracle.quantize(x, nv.PER_TENSOR)
-    assert_bytes_equal(host(back), oracle.dequantize(ref["row_q"], ref["row_sf"], ref["row_amax"], 256, 1024, False), "row deq")
-    assert_bytes_equal(host(backc), oracle.dequantize(ref["col_q"], ref["col_sf"], ref["col_amax"], 1024, 256, False), "col deq")
     reft = oracle.quantize(x, nv.PER_TOKEN)
-    assert_bytes_equal(host(backt), oracle.dequantize(reft["col_q"], reft["col_sf"], reft["col_amax"], 1024, 256, True), "tok deq")
+    reftl = oracle.quantize(x, nv.TILE_16x16)
+    cases = [
+        ("row per-tensor", out, "row", nv.PER_TENSOR, oracle.dequantize(ref["row_q"], ref["row_sf"], ref["row_amax"], 256, 1024, False)),
+        ("col per-tensor", out, "col", nv.PER_TENSOR, oracle.dequantize(ref["col_q"], ref["col_sf"], ref["col_amax"], 1024, 256, False)),
+        ("row per-token", tok, "row", nv.PER_TOKEN, oracle.dequantize(reft["row_q"], reft["row_sf"], reft["row_amax"], 256, 1024, True)),
+        ("col per-token", tok, "col", nv.PER_TOKEN, oracle.dequantize(reft["col_q"], reft["col_sf"], reft["col_amax"], 1024, 256, True)),
+        ("row 16x16", til, "row", nv.TILE_16x16, oracle.dequantize(reftl["row_q"], reftl["row_sf"], reftl["row_amax"], 256, 1024, False)),
+        ("col 16x16", til, "col", nv.TILE_16x16, oracle.dequantize(reftl["col_q"], reftl["col_sf"], reftl["col_amax"], 1024, 256, False)),
+    ]
+    for name, o, dr, mode, exp in cases:
+        assert_bytes_equal(_dequant_guarded(o[dr + "_q"], o[dr + "_sf"], o[dr + "_amax"], mode, False), exp, name + " fp32")
+        assert_bytes_equal(_dequant_guarded(o[dr + "_q"], o[dr + "_sf"], o[dr + "_amax"], mode, True).view(np.uint16),
+                           _bf16_rne(exp), name + " bf16")
+    # the bf16 rounding itself: ties, values just above a tie, large values
+    # that round up to the next binade, and signed zeros
+    assert list(_bf16_rne(np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20,
+                                    -0.0, 3.3895e38], np.float32))) == [0x3F80, 0x3F82, 0x3F81, 0x8000, 0x7F7F]
 
 
 @pytest.mark.parametrize("decay", [0.0, 0.9, 1.0])
@@ -220,18 +294,8 @@ def test_quantize_calibrate_matches_cast_then_accumulate(oracle, mode, shape, di
         if it == 3:
             x = (x & np.uint16(0x8000)) | ((x & np.uint16(0x7FFF)) >> np.uint16(1))   # smaller amax: decay shows
         d = to_dev(x)
-        out = {}
-        if row:
-            out.update(row_q=torch.empty(M, K // 2, dtype=torch.uint8, device="cuda:0"),
-                       row_sf=torch.empty(M, K // 16, dtype=torch.uint8, device="cuda:0"),
-                       row_amax=torch.empty(M if mode == nv.PER_TOKEN else (M if mode == nv.TILE_16x16 else 1),
-                                            dtype=torch.float32, device="cuda:0"))
-        if col:
-            out.update(col_q=torch.empty(K, M // 2, dtype=torch.uint8, device="cuda:0"),
-                       col_sf=torch.empty(K, M // 16, dtype=torch.uint8, device="cuda:0"),
-                       col_amax=torch.empty(K if mode == nv.PER_TOKEN else (K if mode == nv.TILE_16x16 else 1),
-                                            dtype=torch.float32, device="cuda:0"))
-        nv.quantize_calibrate_into(d, mode, buf, decay, **out)
+        out = Guarded(cast_spec(M, K, mode, row, col))
+        nv.quantize_calibrate_into(d, mode, buf, decay, **out.views)
         torch.cuda.synchronize()
         exp = oracle.quantize(x, mode, rowwise=row, columnwise=col)
         compare_cast(out, exp)
@@ -260,12 +324,12 @@ def test_trace_encode_brackets_the_encoding_kernel(oracle):
     d = to_dev(x)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nv.trace_encode(a, b)
-    out = nv.quantize(d, nv.PER_TOKEN)
-    again = nv.quantize(d, nv.PER_TOKEN)   # the pair was consumed by the first call
+    out = quantize_guarded(d, nv.PER_TOKEN)
+    again = quantize_guarded(d, nv.PER_TOKEN)   # the pair was consumed by the first call
     torch.cuda.synchronize()
     assert a.elapsed_time(b) > 0.0
     compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
-    for k in out:
+    for k in out.keys():
         assert torch.equal(out[k], again[k]), k
     nv.trace_encode(a, b)
     nv.trace_encode(None, None)   # cancelled: nothing is recorded
@@ -278,7 +342,7 @@ def test_trace_encode_brackets_the_encoding_kernel(oracle):
 def test_c1_per_tensor_rowwise(oracle):
     x = W.c1()
     _announce("C1 256x1024 per-tensor rowwise")
-    out = nv.quantize(to_dev(x), nv.PER_TENSOR, rowwise=True, columnwise=False)
+    out = quantize_guarded(to_dev(x), nv.PER_TENSOR, rowwise=True, columnwise=False)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, nv.PER_TENSOR, rowwise=True, columnwise=False))
 
@@ -287,11 +351,12 @@ def test_c2_per_token_full(oracle):
     x = W.c2()
     _announce("C2 4096x4096 per-token row+col")
     d = to_dev(x)
-    out = nv.quantize(d, nv.PER_TOKEN)
-    again = nv.quantize(d, nv.PER_TOKEN)
+    out = quantize_guarded(d, nv.PER_TOKEN)
+    again = quantize_guarded(d, nv.PER_TOKEN)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
-    for k in out:
+    again.check_guards()
+    for k in out.keys():
         assert torch.equal(out[k], again[k]), f"run-to-run difference in {k}"
 
 
@@ -305,10 +370,10 @@ def test_encode_tile_height_switch(oracle, M, mode):
     x = W.row_scaled_with_outliers(M, 4096, 60 + M)
     _announce(f"{M}x4096 mode={mode} (encode tile-height switch)")
     d = to_dev(x)
-    out = nv.quantize(d, mode)
+    out = quantize_guarded(d, mode)
     buf = torch.full((1,), 2.0, dtype=torch.float32, device="cuda:0")
-    cal = {k: torch.empty_like(v) for k, v in out.items()}
-    nv.quantize_calibrate_into(d, mode, buf, 0.5, **cal)
+    cal = Guarded(cast_spec(M, 4096, mode))
+    nv.quantize_calibrate_into(d, mode, buf, 0.5, **cal.views)
     torch.cuda.synchronize()
     ref = oracle.quantize(x, mode)
     compare_cast(out, ref)
@@ -321,6 +386,13 @@ def test_encode_tile_height_switch(oracle, M, mode):
 SR_SHAPES = [(16, 16), (48, 1040), (272, 528), (1072, 544), (2048, 48)]
 
 
+def _sr_guarded(d, mode, seed, offset, rowwise=True, columnwise=True):
+    M, K = d.shape
+    g = Guarded(cast_spec(M, K, mode, rowwise, columnwise))
+    nv.quantize_sr_into(d, mode, seed, offset, **g.views)
+    return g
+
+
 @pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
 @pytest.mark.parametrize("shape", SR_SHAPES)
 def test_sr_small_shapes(oracle, mode, shape):
@@ -328,7 +400,7 @@ def test_sr_small_shapes(oracle, mode, shape):
     x = _x(M, K, 300 + M + K)
     seed, offset = 0x9E3779B97F4A7C15 ^ (M * 131 + K), M + 3 * K
     _announce(f"quantize_sr mode={mode} shape={shape}")
-    out = nv.quantize_sr(to_dev(x), mode, seed, offset)
+    out = _sr_guarded(to_dev(x), mode, seed, offset)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_sr(x, mode, seed, offset))
 
@@ -337,12 +409,12 @@ def test_sr_small_shapes(oracle, mode, shape):
 def test_sr_one_direction(oracle, mode):
     x = _x(37, 96, 12)
     _announce(f"quantize_sr rowwise 37x96 mode={mode}")
-    out = nv.quantize_sr(to_dev(x), mode, 5, 6, rowwise=True, columnwise=False)
+    out = _sr_guarded(to_dev(x), mode, 5, 6, rowwise=True, columnwise=False)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_sr(x, mode, 5, 6, rowwise=True, columnwise=False))
     x = _x(48, 24, 13)
     _announce(f"quantize_sr columnwise 48x24 mode={mode}")
-    out = nv.quantize_sr(to_dev(x), mode, 5, 6, rowwise=False, columnwise=True)
+    out = _sr_guarded(to_dev(x), mode, 5, 6, rowwise=False, columnwise=True)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_sr(x, mode, 5, 6, rowwise=False, columnwise=True))
 
@@ -351,7 +423,7 @@ def test_sr_crafted_edges(oracle):
     x = _crafted()
     for mode in (nv.PER_TENSOR, nv.PER_TOKEN):
         _announce(f"quantize_sr crafted mode={mode}")
-        out = nv.quantize_sr(to_dev(x), mode, 123, 4)
+        out = _sr_guarded(to_dev(x), mode, 123, 4)
         torch.cuda.synchronize()
         compare_cast(out, oracle.quantize_sr(x, mode, 123, 4))
 
@@ -360,13 +432,14 @@ def test_sr_c2_full_and_offsets(oracle):
     x = W.c2()
     d = to_dev(x)
     _announce("quantize_sr C2 4096x4096 per-token, offsets 0 and 1")
-    a = nv.quantize_sr(d, nv.PER_TOKEN, 2024, 0)
-    b = nv.quantize_sr(d, nv.PER_TOKEN, 2024, 0)
-    c = nv.quantize_sr(d, nv.PER_TOKEN, 2024, 1)
+    a = _sr_guarded(d, nv.PER_TOKEN, 2024, 0)
+    b = _sr_guarded(d, nv.PER_TOKEN, 2024, 0)
+    c = _sr_guarded(d, nv.PER_TOKEN, 2024, 1)
     torch.cuda.synchronize()
     compare_cast(a, oracle.quantize_sr(x, nv.PER_TOKEN, 2024, 0))
     compare_cast(c, oracle.quantize_sr(x, nv.PER_TOKEN, 2024, 1))
-    for k in a:
+    b.check_guards()
+    for k in a.keys():
         assert torch.equal(a[k], b[k]), f"same seed and offset, different {k}"
     assert not torch.equal(a["row_q"], c["row_q"]) and not torch.equal(a["col_q"], c["col_q"])
     # the scales and amax do not depend on the randoms
@@ -377,7 +450,7 @@ def test_sr_c2_full_and_offsets(oracle):
 def test_sr_c3_per_token_full(oracle):
     x = W.c3(1)
     _announce("quantize_sr C3 16384x8192 per-token (full compare)")
-    out = nv.quantize_sr(to_dev(x), nv.PER_TOKEN, 77, 9)
+    out = _sr_guarded(to_dev(x), nv.PER_TOKEN, 77, 9)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_sr(x, nv.PER_TOKEN, 77, 9))
 
@@ -409,9 +482,36 @@ def _sample_vectors(x, out, mode, rows, cols, oracle):
 def test_c3_per_token_full(oracle):
     x = W.c3(0)
     _announce("C3 16384x8192 per-token row+col (full compare)")
-    out = nv.quantize(to_dev(x), nv.PER_TOKEN)
+    out = quantize_guarded(to_dev(x), nv.PER_TOKEN)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
+
+
+def test_c3_per_tensor_full(oracle):
+    x = W.c3(2)
+    _announce("C3 16384x8192 per-tensor row+col (full compare)")
+    out = quantize_guarded(to_dev(x), nv.PER_TENSOR)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.PER_TENSOR))
+
+
+def test_c3_bench_call_full(oracle):
+    """The measured step's own call -- quantize_calibrate_into, per-token
+    row+col, 16384x8192, decay 0.9 -- on the three inputs the step rotates
+    through, three calls in a row into the same buffers: every output in
+    full and the decayed buffer after each call."""
+    buf = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    ref_buf = np.zeros(1, np.float32)
+    out = Guarded(cast_spec(16384, 8192, nv.PER_TOKEN))
+    for t in range(3):
+        x = W.c3(t)
+        _announce(f"C3 bench call (quantize_calibrate per-token), input {t}")
+        nv.quantize_calibrate_into(to_dev(x), nv.PER_TOKEN, buf, 0.9, **out.views)
+        torch.cuda.synchronize()
+        ref = oracle.quantize(x, nv.PER_TOKEN)
+        compare_cast(out, ref)
+        ref_buf = oracle.amax_accumulate(ref_buf, np.array([ref["row_amax"].max()], np.float32), 0.9)
+        assert_bytes_equal(host(buf), ref_buf, f"decayed buffer after call {t}")
 
 
 def test_c3_sixteen_iterations_with_decay(oracle):
@@ -444,7 +544,8 @@ def test_c4_grouped_moe(oracle):
     x, counts = W.c4()
     assert int(counts.sum()) == 32768 and (counts % 128 == 0).all()
     _announce(f"C4 grouped 64 experts, zero-count experts: {int((counts == 0).sum())}")
-    out = nv.quantize_grouped(to_dev(x), counts.tolist())
+    out = Guarded(grouped_spec(int(counts.sum()), x.shape[1], len(counts)))
+    nv.quantize_grouped_into(to_dev(x), counts.tolist(), **out.views)
     torch.cuda.synchronize()
     ref = oracle.quantize_grouped(x, counts)
     compare_cast(out, ref)
@@ -453,6 +554,6 @@ def test_c4_grouped_moe(oracle):
 def test_c5_tile_16x16_full(oracle):
     x = W.c5()
     _announce("C5 8192x28672 16x16 tiles (full compare)")
-    out = nv.quantize(to_dev(x), nv.TILE_16x16)
+    out = quantize_guarded(to_dev(x), nv.TILE_16x16)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, nv.TILE_16x16))

@@ -9,7 +9,7 @@ import torch
 
 import nvfp4_block_scaled_bf16_amd as nv
 from nvfp4_block_scaled_bf16_amd import workloads as W
-from tests.gpu_util import compare_cast, host, to_dev
+from tests.gpu_util import Guarded, cast_spec, compare_cast, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,13 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
+def _rht_guarded(d, mode, mask, rowwise=True):
+    M, K = d.shape
+    g = Guarded(cast_spec(M, K, mode, rowwise, True))
+    nv.quantize_rht_into(d, mode, mask, **g.views)
+    return g
+
+
 @pytest.mark.parametrize("mask", MASKS)
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("shape", SHAPES)
@@ -30,7 +37,7 @@ def test_rht_small_shapes(oracle, shape, mode, mask):
     M, K = shape
     x = W.row_scaled_with_outliers(M, K, 300 + M + K)
     _announce(f"rht M={M} K={K} mode={mode} mask={mask:#06x}")
-    out = nv.quantize_rht(to_dev(x), mode, mask)
+    out = _rht_guarded(to_dev(x), mode, mask)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_rht(x, mode, mask))
 
@@ -41,7 +48,7 @@ def test_rht_columnwise_only_narrow(oracle, mode):
     M, K = 96, 24
     x = W.normal(M, K, 77)
     _announce(f"rht columnwise only M={M} K={K}")
-    out = nv.quantize_rht(to_dev(x), mode, 0x1234, rowwise=False)
+    out = _rht_guarded(to_dev(x), mode, 0x1234, rowwise=False)
     torch.cuda.synchronize()
     assert "row_q" not in out
     compare_cast(out, oracle.quantize_rht(x, mode, 0x1234, rowwise=False))
@@ -63,7 +70,7 @@ def test_rht_crafted_edges(oracle, mode):
     x[:16, 32:40] = W.bf16_from_f32(tie)
     _announce(f"rht crafted edges mode={mode}")
     for mask in (0x0000, 0x8001):
-        out = nv.quantize_rht(to_dev(x), mode, mask)
+        out = _rht_guarded(to_dev(x), mode, mask)
         torch.cuda.synchronize()
         compare_cast(out, oracle.quantize_rht(x, mode, mask))
 
@@ -72,7 +79,7 @@ def test_rht_c3_per_token_full(oracle):
     x = W.c3(0)
     mask = 0xB2E5
     _announce("rht C3 16384x8192 per-token (full compare)")
-    out = nv.quantize_rht(to_dev(x), nv.PER_TOKEN, mask)
+    out = _rht_guarded(to_dev(x), nv.PER_TOKEN, mask)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize_rht(x, nv.PER_TOKEN, mask))
 
@@ -84,7 +91,7 @@ def test_rht_inverse_through_dequantize(oracle):
     x = W.row_scaled_with_outliers(M, K, 79)
     mask = 0x0FF0
     out = nv.quantize_rht(to_dev(x), nv.PER_TOKEN, mask, rowwise=False)
-    deq = host(nv.dequantize(out["col_q"], out["col_sf"], out["col_amax"], True)).astype(np.float64)   # [K][M]
+    deq = host(nv.dequantize(out["col_q"], out["col_sf"], out["col_amax"], nv.PER_TOKEN)).astype(np.float64)   # [K][M]
     import scipy.linalg
     H = scipy.linalg.hadamard(16).astype(np.float64)
     s = np.array([-1.0 if (mask >> j) & 1 else 1.0 for j in range(16)])

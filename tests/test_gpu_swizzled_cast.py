@@ -9,7 +9,7 @@ import torch
 
 import nvfp4_block_scaled_bf16_amd as nv
 from nvfp4_block_scaled_bf16_amd import workloads as W
-from tests.gpu_util import assert_bytes_equal, host, to_dev
+from tests.gpu_util import Guarded, assert_bytes_equal, cast_spec, host, to_dev
 from tests.test_gpu_parity import _crafted
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +22,16 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
+def _swz_guarded(d, mode, rowwise=True, columnwise=True):
+    M, K = d.shape
+    g = Guarded(cast_spec(M, K, mode, rowwise, columnwise))   # swizzled matrices: M*K/16 bytes each
+    nv.quantize_swizzled_into(d, mode, **g.views)
+    return g
+
+
 def _compare(out, ref, oracle):
+    if isinstance(out, Guarded):
+        out.check_guards()
     for k in ("row_q", "row_amax", "col_q", "col_amax"):
         if k in ref:
             assert_bytes_equal(host(out[k]).reshape(ref[k].shape), ref[k], k)
@@ -38,7 +47,7 @@ def test_swizzled_cast_shapes(oracle, shape, mode):
     M, K = shape
     x = W.row_scaled_with_outliers(M, K, 500 + M + K)
     _announce(f"swizzled cast M={M} K={K} mode={mode}")
-    out = nv.quantize_swizzled(to_dev(x), mode)
+    out = _swz_guarded(to_dev(x), mode)
     torch.cuda.synchronize()
     _compare(out, oracle.quantize(x, mode), oracle)
 
@@ -49,7 +58,7 @@ def test_swizzled_cast_one_direction(oracle, mode, dirs):
     M, K = 384, 640
     x = W.normal(M, K, 501)
     _announce(f"swizzled cast one direction {dirs} mode={mode}")
-    out = nv.quantize_swizzled(to_dev(x), mode, rowwise=dirs[0], columnwise=dirs[1])
+    out = _swz_guarded(to_dev(x), mode, rowwise=dirs[0], columnwise=dirs[1])
     torch.cuda.synchronize()
     _compare(out, oracle.quantize(x, mode, rowwise=dirs[0], columnwise=dirs[1]), oracle)
 
@@ -60,7 +69,7 @@ def test_swizzled_cast_exact_path(oracle, mode):
     # its own rowwise scales
     x = _crafted(M=128, K=1024, seed=5)
     _announce(f"swizzled cast crafted edges mode={mode}")
-    out = nv.quantize_swizzled(to_dev(x), mode)
+    out = _swz_guarded(to_dev(x), mode)
     torch.cuda.synchronize()
     _compare(out, oracle.quantize(x, mode), oracle)
 
@@ -68,7 +77,7 @@ def test_swizzled_cast_exact_path(oracle, mode):
 def test_swizzled_cast_c3_full(oracle):
     x = W.c3(0)
     _announce("swizzled cast C3 16384x8192 per-token (full compare)")
-    out = nv.quantize_swizzled(to_dev(x), nv.PER_TOKEN)
+    out = _swz_guarded(to_dev(x), nv.PER_TOKEN)
     torch.cuda.synchronize()
     _compare(out, oracle.quantize(x, nv.PER_TOKEN), oracle)
 

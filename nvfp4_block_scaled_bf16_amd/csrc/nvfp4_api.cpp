@@ -7,7 +7,9 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
@@ -91,6 +93,40 @@ nvfp4_status encode_launch(Launch&& launch) {
     return check_hip(launch(before, after), "encode");
 }
 
+// ------------------------------------------------------ per-device state
+//
+// The compute-unit count of each device (the persistent row kernel's grid),
+// queried once.
+std::mutex g_dev_mu;
+std::vector<int> g_cus;
+
+nvfp4_status device_cus(hipStream_t st, int* cus) {
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(NVFP4_EDEVICE, "stream device: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    if ((int)g_cus.size() <= dev) g_cus.resize(dev + 1, 0);
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess || n <= 0)
+            return fail(NVFP4_EDEVICE, "device attribute: %s", hipGetErrorString(e));
+        g_cus[dev] = n;
+    }
+    *cus = g_cus[dev];
+    return NVFP4_OK;
+}
+
+// Rowwise-only per-token casts are served by the single-pass row kernel
+// when K is within its rounds (K <= 65536).  Grid: two 512-lane workgroups
+// per compute unit, persistent over the batches.
+bool rows_path(int64_t K) { return rows_rounds(K) != 0; }
+
+unsigned rows_grid(int cus, int64_t M, int64_t K) {
+    const int64_t nb = rows_batches(M, K);
+    const int64_t g = 2 * (int64_t)cus;
+    return (unsigned)(nb < g ? nb : g);
+}
+
 // zero-fill up to two fp32 arrays (one launch) before an atomic-max pass
 nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
     return check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
@@ -149,6 +185,21 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
     if (cal_buf) {
         if (mode == NVFP4_PER_TOKEN) { cal.obs = ca ? ca : ra; cal.n = ca ? K : M; }
         else { cal.obs = ra ? ra : ca; cal.n = 1; }
+    }
+    if (mode == NVFP4_PER_TOKEN && r.want && !c.want && M > 0 && K > 0 && !rounding.stochastic && !swizzled &&
+        rows_path(K)) {
+        // rowwise only: each row's amax is found and used on chip, x is read
+        // once
+        int cus = 0;
+        if ((s = device_cus(st, &cus)) != NVFP4_OK) return s;
+        const unsigned grid = rows_grid(cus, M, K);
+        if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
+                 return launch_rows(x, M, K, row_q, row_sf, ra, grid, st, b, a);
+             })) != NVFP4_OK)
+            return s;
+        if (cal_buf && (s = check_hip(launch_accumulate_reduce(cal_buf, ra, M, decay, st), "calibration")) != NVFP4_OK)
+            return s;
+        return ok();
     }
     if (mode == NVFP4_PER_TOKEN) {
         if ((s = zero(ra, M, ca, K, st)) != NVFP4_OK) return s;
@@ -341,6 +392,17 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
     hipStream_t st = as_stream(stream);
     float* ra = r.want ? row_amax : nullptr;
     float* ca = c.want ? col_amax : nullptr;
+    if (!c.want && T > 0 && K > 0 && rows_path(K)) {
+        // rowwise only: per-token rowwise of all T rows, one read of x
+        int cus = 0;
+        if ((s = device_cus(st, &cus)) != NVFP4_OK) return s;
+        const unsigned grid = rows_grid(cus, T, K);
+        if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
+                 return launch_rows(x, T, K, row_q, row_sf, ra, grid, st, b, a);
+             })) != NVFP4_OK)
+            return s;
+        return ok();
+    }
     if ((s = zero(ra, T, ca, (int64_t)num_groups * K, st)) != NVFP4_OK) return s;
     if (T == 0 || K == 0) return ok();
     if (!c.want) {

@@ -230,6 +230,41 @@ __device__ __forceinline__ FastBlock fast_block(uint32_t bbits, const Outer& o) 
     return fb;
 }
 
+// ------------------------------------------------ buffers and lane exchange
+
+// Buffer resources: a raw buffer over [base, base + bytes) (bytes <= 2^31).
+// Loads at an offset at or beyond `bytes` read zeros and stores there are
+// dropped, which is how rows past the end of the tensor and lanes past its
+// last column are handled.  The offset checked is the lane offset plus the
+// scalar offset (checked on gfx950 with an in-bounds probe), so the per-row
+// part of an address goes in the scalar offset at no vector-ALU cost; sums
+// stay below 2^32.  The fourth descriptor word is the raw-buffer setting of
+// the gfx9 family.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCacheNT = 2;               // nontemporal hint in the gfx940-family cache-policy bits
+constexpr uint32_t kOffOut = 0x80000000u; // lane offset beyond every buffer's extent
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// DPP: value of the neighbouring lane (lane ^ 1)
+__device__ __forceinline__ uint32_t from_pair(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t rowmax_word(const u32x4& w) {
+    return pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
+}
+
+// DPP quad permutations: the value of the even / odd lane of each pair
+__device__ __forceinline__ float from_even(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xA0, 0xF, 0xF, false));   // [0,0,2,2]
+}
+__device__ __forceinline__ float from_odd(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xF5, 0xF, 0xF, false));   // [1,1,3,3]
+}
+
 // ----------------------------------------------------------- grouped table
 
 // Experts for the grouped cast travel in the kernel arguments: row offsets

@@ -75,6 +75,14 @@ hipError_t launch_gemm_grouped(const uint8_t* a_q, const uint8_t* a_sf, const fl
 // out: fp32 [R][C], or bf16 (round to nearest-even of the fp32 value) when bf16
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sf, const float* amax, int64_t R, int64_t C,
                           int amax_per_row, bool bf16, void* out, hipStream_t st);
+// single-pass per-token rowwise cast (nvfp4_rows.hip): rounds of 4096
+// columns per row for K (1, 2, 4, 8 or 16), 0 when K is beyond the kernel
+int rows_rounds(int64_t K);
+// batches of rows for M x K (grid sizes are at most this)
+int64_t rows_batches(int64_t M, int64_t K);
+// row_q / row_sf / row_amax written in full
+hipError_t launch_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                       unsigned grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);
 hipError_t launch_accumulate_reduce(float* buf, const float* obs, int64_t n, float decay, hipStream_t st);
 

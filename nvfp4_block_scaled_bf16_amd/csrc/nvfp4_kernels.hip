@@ -47,22 +47,6 @@ __device__ __forceinline__ void atomic_max_mag(float* p, uint32_t mag16) {
     if (mag16 != 0u) atomicMax(reinterpret_cast<uint32_t*>(p), mag16 << 16);
 }
 
-// Buffer resources: a raw buffer over [base, base + bytes) (bytes <= 2^31).
-// Loads at an offset at or beyond `bytes` read zeros and stores there are
-// dropped, which is how rows past the end of the tensor and lanes past its
-// last column are handled.  The offset checked is the lane offset plus the
-// scalar offset (checked on gfx950 with an in-bounds probe), so the per-row
-// part of an address goes in the scalar offset at no vector-ALU cost; sums
-// stay below 2^32.  The fourth descriptor word is the raw-buffer setting of
-// the gfx9 family.
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kCacheNT = 2;               // nontemporal hint in the gfx940-family cache-policy bits
-constexpr uint32_t kOffOut = 0x80000000u; // lane offset beyond every buffer's extent
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
 // load 16 rows x 8 bf16 (one 16-byte word per row) of a lane's sub-block;
 // rows at or beyond row_end, and lanes past the last column (lane_off ==
 // kOffOut), read zeros.  lane_off: the lane's byte offset within a row; xr:
@@ -278,15 +262,6 @@ __device__ __forceinline__ float elem(const u32x4& w, int k) {
     return (k & 1) ? bf_hi(word) : bf_lo(word);
 }
 
-// DPP: value of the neighbouring lane (lane ^ 1)
-__device__ __forceinline__ uint32_t from_pair(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
-
-__device__ __forceinline__ uint32_t rowmax_word(const u32x4& w) {
-    return pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
-}
-
 // Byte offset of scale (r, c) in the GEMM-swizzled layout of a scale matrix
 // with nbp (a multiple of 4) blocks per row: 512-byte tiles of 128 rows x 4
 // blocks, row-tile major; row r in 16-byte line r % 32 at 4-byte slot
@@ -447,14 +422,6 @@ __device__ void wg_accumulate_reduce(float* __restrict__ buf, const float* __res
         const float t = buf[0] * decay;
         buf[0] = m > t ? m : t;
     }
-}
-
-// DPP quad permutations: the value of the even / odd lane of each pair
-__device__ __forceinline__ float from_even(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xA0, 0xF, 0xF, false));   // [0,0,2,2]
-}
-__device__ __forceinline__ float from_odd(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xF5, 0xF, 0xF, false));   // [1,1,3,3]
 }
 
 // MODE: ENC_TENSOR (row_amax[0] / col_amax[0] for every vector), ENC_TOKEN
@@ -698,6 +665,10 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                 row_scale[wave][lane][1] = o.yS;
             }
             step_slow |= __builtin_amdgcn_ballot_w64(o.slow) != 0ull;
+            // other lanes read these entries below: the fence keeps the
+            // compiler from moving those reads above the writes (a wave
+            // executes its LDS instructions in order)
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
         }
 
@@ -846,6 +817,8 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
             }
         }
         if (step_slow || __builtin_amdgcn_ballot_w64(slow) != 0ull) slow_mask |= 1u << sb;
+        // the next step's row scales overwrite entries other lanes read above
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
 

@@ -557,3 +557,87 @@ def test_c5_tile_16x16_full(oracle):
     out = quantize_guarded(to_dev(x), nv.TILE_16x16)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, nv.TILE_16x16))
+
+
+# ------------------------------------------- single-pass per-token rowwise
+
+# K values covering every round configuration of the single-pass row kernel
+# (4096 columns per round; 1, 2, 4, 8, 16 rounds, whole or with a partial
+# last round) and M values with ragged last batches
+ROWS_SHAPES = [(37, 4096), (100, 4112), (24, 12288), (40, 16384), (9, 16400), (18, 32768), (3, 65536),
+               (5, 40976), (1, 16), (300, 2064)]
+
+
+@pytest.mark.parametrize("shape", ROWS_SHAPES)
+def test_rows_single_pass_rowwise_only(oracle, shape):
+    M, K = shape
+    x = _x(M, K, 700 + M + K)
+    _announce(f"single-pass rowwise per-token M={M} K={K}")
+    out = quantize_guarded(to_dev(x), nv.PER_TOKEN, rowwise=True, columnwise=False)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.PER_TOKEN, rowwise=True, columnwise=False))
+
+
+@pytest.mark.parametrize("shape", [(48, 4096), (112, 4112), (32, 12288), (16, 16384), (4128, 1040), (4112, 8192)])
+def test_cast_row_and_col_wide_shapes(oracle, shape):
+    """Per-token row + column casts at the widths the single-pass rowwise
+    kernel covers in several round configurations (the row + column cast
+    itself takes the amax and encoding kernels)."""
+    M, K = shape
+    x = _x(M, K, 800 + M + K)
+    _announce(f"row + col per-token M={M} K={K}")
+    out = quantize_guarded(to_dev(x), nv.PER_TOKEN)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
+
+
+def test_rows_single_pass_crafted(oracle):
+    """The exact path of the row kernel: E4M3-subnormal block scales, zero
+    rows, huge rows, ties, subnormals (K = 1024: one partial round, 8 rows
+    per batch), rowwise only (and the row + column cast on the same data)."""
+    x = _crafted()
+    for col in (False, True):
+        _announce(f"single-pass crafted 64x1024 columnwise={col}")
+        out = quantize_guarded(to_dev(x), nv.PER_TOKEN, rowwise=True, columnwise=col)
+        torch.cuda.synchronize()
+        compare_cast(out, oracle.quantize(x, nv.PER_TOKEN, rowwise=True, columnwise=col))
+    # rows whose amax is outside the fast range (the whole row takes the
+    # exact path) next to ordinary rows, at K = 8192
+    rng = np.random.default_rng(41)
+    f = rng.standard_normal((24, 8192)).astype(np.float32)
+    f[3] *= np.float32(1e-13)
+    f[10] *= np.float32(1e19)
+    f[17, :100] = 0.0
+    f[17, 100] = np.float32(2.0 ** -126)
+    xx = W.bf16_from_f32(f)
+    _announce("single-pass crafted 24x8192 (outer amax outside the fast range)")
+    out = quantize_guarded(to_dev(xx), nv.PER_TOKEN, rowwise=True, columnwise=False)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize(xx, nv.PER_TOKEN, rowwise=True, columnwise=False))
+
+
+def test_rows_grouped_rowwise_only(oracle):
+    counts = [32, 0, 16, 48, 0, 16, 128, 4096]
+    K = 4096
+    x = _grouped_case(counts, K, 99)
+    _announce("grouped rowwise only (single pass)")
+    out = Guarded(grouped_spec(sum(counts), K, len(counts), rowwise=True, columnwise=False))
+    nv.quantize_grouped_into(to_dev(x), counts, **out.views)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_grouped(x, np.array(counts, np.int64))
+    compare_cast(out, ref, keys=["row_q", "row_sf", "row_amax"])
+
+
+def test_rows_calibrate_rowwise_only(oracle):
+    M, K = 520, 8192
+    buf = torch.full((1,), 5.0, dtype=torch.float32, device="cuda:0")
+    ref = np.array([5.0], np.float32)
+    for it in range(3):
+        x = _x(M, K, 900 + it)
+        _announce(f"single-pass rowwise calibrate, call {it}")
+        out = Guarded(cast_spec(M, K, nv.PER_TOKEN, True, False))
+        nv.quantize_calibrate_into(to_dev(x), nv.PER_TOKEN, buf, 0.5, **out.views)
+        torch.cuda.synchronize()
+        compare_cast(out, oracle.quantize(x, nv.PER_TOKEN, rowwise=True, columnwise=False))
+        ref = oracle.amax_accumulate(ref, np.array([oracle.amax_tensor(x)], np.float32), 0.5)
+        assert_bytes_equal(host(buf), ref, f"decayed buffer after call {it}")

@@ -20,7 +20,11 @@ not stall the stream.  "traffic" is the HBM byte count per launch measured with 
 FETCH_SIZE / WRITE_SIZE counters and calibrated against a plain copy; it is
 read from profiles/ and reported only while the kernel sources still hash to
 the value the counters were taken on (else null).  "cpu_baseline" times the
-CPU oracle on the host (test infrastructure, never on the product path).
+CPU oracle on the host's cores (test infrastructure, never on the product
+path), single-threaded and with the vectors split over every core; the same
+run checks the step's outputs for the first input against the oracle's
+("parity").  "copy_ceiling" is a plain streaming pass on the same GPU, and
+"inputs_sha256" fingerprints the three step inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain 256 MiB copies, for counters)
@@ -193,7 +197,16 @@ def all_configs(steps, warmup, only=None):
                cast_bytes(4096, 4096, 8192))
         del x2
     # C3: per-tensor and per-token row+col 16384 x 8192, Student-t
-    if want("C3-per-token", "C3-per-tensor", "C3-per-token-swizzled", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN",
+    # one GPU's share of C3 split 8 ways by rows (the shape each GPU would
+    # cast if the tokens were sharded)
+    if want("shard-2048x8192"):
+        xs8 = [to_dev(W.c3(t)[2048 * t:2048 * (t + 1)]) for t in range(3)]
+        o8 = dict(row_q=u8(2048, K // 2), row_sf=u8(2048, K // 16), row_amax=f32(2048),
+                  col_q=u8(K, 1024), col_sf=u8(K, 128), col_amax=f32(K))
+        report("shard-2048x8192", "per-token row+col, 2048x8192 (one row shard of 16384x8192 over 8 GPUs)",
+               timed(lambda i: nv.quantize_into(xs8[i], nv.PER_TOKEN, **o8), 3), cast_bytes(2048, K, 2048 + K))
+        del xs8
+    if want("C3-per-token", "C3-per-token-rowwise", "C3-per-tensor", "C3-per-token-swizzled", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN",
             "GEMM-TN-swizzled"):
         x3 = [to_dev(W.c3(t)) for t in range(3)]
         o3 = dict(row_q=u8(M, K // 2), row_sf=u8(M, K // 16), row_amax=f32(M),
@@ -204,6 +217,11 @@ def all_configs(steps, warmup, only=None):
                    timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TOKEN, buf, 0.9, **o3), 3),
                    cast_bytes(M, K, M + K))
         o3t = dict(o3, row_amax=f32(1), col_amax=f32(1))
+        if want("C3-per-token-rowwise"):
+            orow = dict(row_q=o3["row_q"], row_sf=o3["row_sf"], row_amax=o3["row_amax"])
+            report("C3-per-token-rowwise", "per-token rowwise-only cast (single pass: one read of x), 16384x8192",
+                   timed(lambda i: nv.quantize_into(x3[i], nv.PER_TOKEN, **orow), 3),
+                   2 * M * K + M * K // 2 + M * K // 16 + 4 * M)
         if want("C3-per-tensor"):
             report("C3-per-tensor", "per-tensor row+col with the decayed amax update, 16384x8192",
                    timed(lambda i: nv.quantize_calibrate_into(x3[i], nv.PER_TENSOR, buf, 0.9, **o3t), 3),
@@ -286,20 +304,75 @@ def all_configs(steps, warmup, only=None):
 
 
 
-def cpu_baseline(inputs):
-    """The oracle as it stands, single-threaded, on the full 16384 x 8192
-    per-token row+col cast of each of the step inputs (about 15 s of CPU
-    work for three)."""
+def host_cpu():
+    """Threads this process may run on, and the CPU model name."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(inputs, reps=3):
+    """The oracle as it stands on the host's cores: the full 16384 x 8192
+    per-token row+col cast of the first step input, timed single-threaded and
+    with the rows and columns split over every core the process may use (the
+    same per-vector routines), median of `reps` runs each.  Returns the
+    baseline record and the all-core run's outputs (for the parity check)."""
     import oracle
-    t0 = time.perf_counter()
-    for x in inputs:
+    cores, model = host_cpu()
+    x = inputs[0]
+    nbytes = algorithmic_bytes(*x.shape)
+    single, multi, out = [], [], None
+    for _ in range(reps):
+        t0 = time.perf_counter()
         oracle.quantize(x, oracle.PER_TOKEN)
-    dt = time.perf_counter() - t0
-    nbytes = algorithmic_bytes(*inputs[0].shape) * len(inputs)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(inputs)} full {inputs[0].shape[0]}x{inputs[0].shape[1]} per-token row+col casts "
-                      f"(the step's inputs), single thread, {dt:.2f} s",
-            "seconds": round(dt, 3)}
+        single.append(time.perf_counter() - t0)
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        out = oracle.quantize_per_token_threads(x, cores)
+        multi.append(time.perf_counter() - t0)
+    med = lambda v: sorted(v)[len(v) // 2]
+    ts, tm = med(single), med(multi)
+    rec = {"value": round(nbytes / tm / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"one full {x.shape[0]}x{x.shape[1]} per-token row+col cast (the first step input), "
+                     f"rows and columns split over {cores} threads; median of {reps} runs",
+           "seconds": round(tm, 3), "single_thread_GB_per_s": round(nbytes / ts / 1e9, 4),
+           "single_thread_seconds": round(ts, 3), "cpu_model": model,
+           "runs_seconds": {"single_thread": [round(t, 3) for t in single], "all_cores": [round(t, 3) for t in multi]}}
+    return rec, out
+
+
+def copy_ceiling(dev, reps=10):
+    """A plain streaming pass on the same GPU: c = a + b over bf16 tensors of
+    128 MiB each (256 MiB read, 128 MiB written), median of `reps` timed
+    launches -- the practical bandwidth ceiling for comparison."""
+    import torch
+    n = 64 << 20
+    a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    b = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    c = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    torch.add(a, b, out=c)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.add(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(ts)[len(ts) // 2]
+    nbytes = 3 * 2 * n
+    del a, b, c
+    return {"value": round(nbytes / t / 1e9, 1), "unit": "GB/s", "bytes": nbytes, "us": round(t * 1e6, 2),
+            "kind": "torch.add of two 128 MiB bf16 tensors (256 MiB read + 128 MiB written), median of 10"}
 
 
 def main():
@@ -396,8 +469,18 @@ def main():
         "elements_per_s": round(M * K / (ms_per_step * 1e-3), 1),
         "roofline": roofline,
     }
+    line["copy_ceiling"] = copy_ceiling(dev)
+    line["inputs_sha256"] = [hashlib.sha256(x.tobytes()).hexdigest() for x in inputs_host]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inputs_host)
+        line["cpu_baseline"], ref = cpu_baseline(inputs_host)
+        # the step's outputs for the first input, against the oracle's
+        step(0)
+        torch.cuda.synchronize()
+        ok = True
+        for k, v in ref.items():
+            got = out[k].cpu().numpy().reshape(v.shape)
+            ok = ok and bool(np.array_equal(got.view(np.uint8), v.view(np.uint8)))
+        line["parity"] = ok
     print(json.dumps(line), flush=True)
 
 

@@ -95,25 +95,119 @@ nvfp4_status encode_launch(Launch&& launch) {
 
 // ------------------------------------------------------ per-device state
 //
-// The compute-unit count of each device (the persistent row kernel's grid),
-// queried once.
+// Per device, set up on first use: the compute-unit count (grids of the
+// persistent kernels), the counts of the cross-workgroup wait slots (see
+// SyncArg: slots are handed out in turn, each advanced by its launch's
+// arrivals), and a word of pinned host memory, visible to the device, where
+// a wait that gave up records the failure; every call that takes a slot
+// checks it first and reports NVFP4_EDEVICE once for such a failure.
+struct DeviceState {
+    bool init = false;
+    int cus = 0;
+    uint64_t next_slot = 0;
+    uint64_t slot_count[kSyncSlots] = {};
+    unsigned int* err_host = nullptr;
+    unsigned int* err_dev = nullptr;
+};
 std::mutex g_dev_mu;
-std::vector<int> g_cus;
+std::vector<DeviceState> g_dev;
 
-nvfp4_status device_cus(hipStream_t st, int* cus) {
-    int dev = 0;
-    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(NVFP4_EDEVICE, "stream device: %s", hipGetErrorString(e));
-    std::lock_guard<std::mutex> lock(g_dev_mu);
-    if ((int)g_cus.size() <= dev) g_cus.resize(dev + 1, 0);
-    if (g_cus[dev] == 0) {
+nvfp4_status stream_device(hipStream_t st, int* dev) {
+    hipError_t e = st ? hipStreamGetDevice(st, dev) : hipGetDevice(dev);
+    return e == hipSuccess ? NVFP4_OK : fail(NVFP4_EDEVICE, "stream device: %s", hipGetErrorString(e));
+}
+
+// call with g_dev_mu held
+nvfp4_status device_init(int dev, DeviceState** out) {
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    DeviceState& d = g_dev[dev];
+    if (!d.init) {
+        hipError_t e;
         int n = 0;
         if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess || n <= 0)
             return fail(NVFP4_EDEVICE, "device attribute: %s", hipGetErrorString(e));
-        g_cus[dev] = n;
+        void* h = nullptr;
+        if ((e = hipHostMalloc(&h, sizeof(unsigned int), hipHostMallocMapped)) != hipSuccess)
+            return fail(NVFP4_EDEVICE, "pinned error word: %s", hipGetErrorString(e));
+        void* dp = nullptr;
+        if ((e = hipHostGetDevicePointer(&dp, h, 0)) != hipSuccess)
+            return fail(NVFP4_EDEVICE, "pinned error word: %s", hipGetErrorString(e));
+        d.cus = n;
+        d.err_host = static_cast<unsigned int*>(h);
+        d.err_dev = static_cast<unsigned int*>(dp);
+        *d.err_host = 0u;
+        d.init = true;
     }
-    *cus = g_cus[dev];
+    *out = &d;
     return NVFP4_OK;
+}
+
+nvfp4_status device_cus(hipStream_t st, int* cus) {
+    int dev = 0;
+    nvfp4_status s = stream_device(st, &dev);
+    if (s != NVFP4_OK) return s;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceState* d = nullptr;
+    if ((s = device_init(dev, &d)) != NVFP4_OK) return s;
+    *cus = d->cus;
+    return NVFP4_OK;
+}
+
+// A slot for a launch of `arrivals` arrivals on stream st.
+struct SyncTicket {
+    SyncArg arg;
+    int dev;
+    uint64_t arrivals;
+};
+
+nvfp4_status sync_take(hipStream_t st, uint64_t arrivals, SyncTicket* t) {
+    int dev = 0;
+    nvfp4_status s = stream_device(st, &dev);
+    if (s != NVFP4_OK) return s;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceState* d = nullptr;
+    if ((s = device_init(dev, &d)) != NVFP4_OK) return s;
+    if (__atomic_load_n(d->err_host, __ATOMIC_ACQUIRE) != 0u) {
+        __atomic_store_n(d->err_host, 0u, __ATOMIC_RELEASE);
+        return fail(NVFP4_EDEVICE, "an earlier call's cross-workgroup wait gave up (its outputs are invalid)");
+    }
+    const int slot = (int)(d->next_slot++ % kSyncSlots);
+    t->arg.slot = slot;
+    t->arg.base = d->slot_count[slot];
+    t->arg.err = d->err_dev;
+    t->dev = dev;
+    t->arrivals = arrivals;
+    d->slot_count[slot] += arrivals;
+    return NVFP4_OK;
+}
+
+// the launch holding ticket t did not start: its arrivals never come
+void sync_return(const SyncTicket& t) {
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    g_dev[t.dev].slot_count[t.arg.slot] -= t.arrivals;
+}
+
+// Amax launch whose first workgroups zero its outputs (a[0..na), b[0..nb))
+// before the others combine into them, in place of a separate fill launch.
+// The zeroing workgroups must exist: the grid has at least that many.
+nvfp4_status amax_zero_first(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
+                             float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
+                             float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
+    if (a == nullptr) na = 0;
+    if (b == nullptr) nb = 0;
+    ZeroFirst z{a, na, b, nb, (int)((na + nb + kZeroPerWg - 1) / kZeroPerWg)};
+    if (z.wgs == 0 || z.wgs > amax_grid_size(kind, K, row_begin, row_end)) {
+        // nothing to zero, or more than the grid has workgroups: a fill launch
+        nvfp4_status s = check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
+        if (s != NVFP4_OK) return s;
+        return check_hip(launch_amax(kind, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, st), "amax");
+    }
+    SyncTicket tk;
+    nvfp4_status s = sync_take(st, (uint64_t)z.wgs, &tk);
+    if (s != NVFP4_OK) return s;
+    s = check_hip(launch_amax(kind, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, st, z, tk.arg), "amax");
+    if (s != NVFP4_OK) sync_return(tk);
+    return s;
 }
 
 // Rowwise-only per-token casts are served by the single-pass row kernel
@@ -202,9 +296,9 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         return ok();
     }
     if (mode == NVFP4_PER_TOKEN) {
-        if ((s = zero(ra, M, ca, K, st)) != NVFP4_OK) return s;
-        if (M == 0 || K == 0) return ok();
-        if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if (M == 0 || K == 0) return zero(ra, M, ca, K, st) != NVFP4_OK ? NVFP4_EDEVICE : ok();
+        if ((s = amax_zero_first(AMAX_TOKEN, x, K, 0, M, ra, ca, nullptr, nullptr, gt, ra, M, ca, K, st)) != NVFP4_OK)
+            return s;
         if (rounding.stochastic)
             s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode_sr(ENC_TOKEN, r.want, c.want, x, M, K, ra, ca, row_q, row_sf,
                                   col_q, col_sf, rounding.seed, rounding.offset, st, b, a); });
@@ -214,9 +308,14 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         return s != NVFP4_OK ? s : ok();
     }
     // per-tensor and 16x16 tiles: one tensor amax
-    if ((s = zero(ra, ra ? (mode == NVFP4_TILE_16x16 ? M : 1) : 0, ca, ca ? (mode == NVFP4_TILE_16x16 ? K : 1) : 0, st)) != NVFP4_OK) return s;
-    if (M == 0 || K == 0) return ok();
-    if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, st), "amax")) != NVFP4_OK) return s;
+    if (M == 0 || K == 0)
+        return zero(ra, ra ? (mode == NVFP4_TILE_16x16 ? M : 1) : 0, ca, ca ? (mode == NVFP4_TILE_16x16 ? K : 1) : 0, st) != NVFP4_OK
+                   ? NVFP4_EDEVICE : ok();
+    // the tensor amax is combined into entry 0 of each vector (16x16 tiles
+    // fill the rest of theirs from it in the encoding kernel)
+    if ((s = amax_zero_first(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, ra, ca, gt, ra, ra ? 1 : 0, ca, ca ? 1 : 0, st)) !=
+        NVFP4_OK)
+        return s;
     const int emode = mode == NVFP4_TILE_16x16 ? ENC_TILE : ENC_TENSOR;
     if (rounding.stochastic) {
         s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode_sr(ENC_TENSOR, r.want, c.want, x, M, K, ra, ca, row_q, row_sf,
@@ -334,14 +433,17 @@ nvfp4_status nvfp4_amax(const void* xv, int64_t M, int64_t K, nvfp4_scaling mode
     const GroupTable gt = empty_table();
     nvfp4_status s;
     if (mode == NVFP4_PER_TOKEN) {
-        if ((s = zero(row_amax, M, col_amax, K, st)) != NVFP4_OK) return s;
-        if (M == 0 || K == 0) return ok();
-        if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, M, row_amax, col_amax, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if (M == 0 || K == 0) return zero(row_amax, M, col_amax, K, st) != NVFP4_OK ? NVFP4_EDEVICE : ok();
+        if ((s = amax_zero_first(AMAX_TOKEN, x, K, 0, M, row_amax, col_amax, nullptr, nullptr, gt, row_amax, M, col_amax, K,
+                                 st)) != NVFP4_OK)
+            return s;
         return ok();
     }
-    if ((s = zero(row_amax, row_amax ? 1 : 0, col_amax, col_amax ? 1 : 0, st)) != NVFP4_OK) return s;
-    if (M == 0 || K == 0) return ok();
-    if ((s = check_hip(launch_amax(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, row_amax, col_amax, gt, st), "amax")) != NVFP4_OK) return s;
+    if (M == 0 || K == 0)
+        return zero(row_amax, row_amax ? 1 : 0, col_amax, col_amax ? 1 : 0, st) != NVFP4_OK ? NVFP4_EDEVICE : ok();
+    if ((s = amax_zero_first(AMAX_TENSOR, x, K, 0, M, nullptr, nullptr, row_amax, col_amax, gt, row_amax,
+                             row_amax ? 1 : 0, col_amax, col_amax ? 1 : 0, st)) != NVFP4_OK)
+        return s;
     return ok();
 }
 
@@ -403,11 +505,17 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
             return s;
         return ok();
     }
-    if ((s = zero(ra, T, ca, (int64_t)num_groups * K, st)) != NVFP4_OK) return s;
-    if (T == 0 || K == 0) return ok();
+    // one amax launch (at most kMaxGroupsPerLaunch experts, or rowwise only)
+    // zeroes its own outputs; several launches take a fill first
+    const bool one_launch = !c.want || num_groups <= kMaxGroupsPerLaunch;
+    if (T == 0 || K == 0 || !one_launch) {
+        if ((s = zero(ra, T, ca, (int64_t)num_groups * K, st)) != NVFP4_OK) return s;
+        if (T == 0 || K == 0) return ok();
+    }
     if (!c.want) {
         const GroupTable gt = empty_table();
-        if ((s = check_hip(launch_amax(AMAX_TOKEN, x, K, 0, T, ra, nullptr, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if ((s = amax_zero_first(AMAX_TOKEN, x, K, 0, T, ra, nullptr, nullptr, nullptr, gt, ra, T, nullptr, 0, st)) != NVFP4_OK)
+            return s;
         if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_TOKEN, true, false, false, x, T, K, 0, T, ra, nullptr, row_q, row_sf, nullptr, nullptr,
                                          nullptr, nullptr, gt, st, b, a); })) != NVFP4_OK) return s;
         return ok();
@@ -427,7 +535,12 @@ nvfp4_status nvfp4_quantize_grouped(const void* xv, int64_t K, int32_t num_group
         }
         const int64_t end = off;
         if (end == begin) continue;
-        if ((s = check_hip(launch_amax(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, st), "amax")) != NVFP4_OK) return s;
+        if (one_launch)
+            s = amax_zero_first(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, ra, T, ca,
+                                (int64_t)num_groups * K, st);
+        else
+            s = check_hip(launch_amax(AMAX_GROUPED, x, K, begin, end, ra, ca, nullptr, nullptr, gt, st), "amax");
+        if (s != NVFP4_OK) return s;
         if ((s = encode_launch([&](hipEvent_t b, hipEvent_t a) { return launch_encode(ENC_GROUPED, r.want, true, false, x, T, K, begin, end, ra, ca, row_q, row_sf, col_q, col_sf,
                                          nullptr, nullptr, gt, st, b, a); })) != NVFP4_OK) return s;
     }

@@ -9,15 +9,44 @@ namespace nvfp4 {
 struct GroupTable;
 
 enum AmaxKind { AMAX_TENSOR = 0, AMAX_TOKEN = 1, AMAX_GROUPED = 2 };
+
+// Cross-workgroup waits (nvfp4_kernels.hip): a launch that needs them gets a
+// slot of monotonically increasing arrival counters in device memory, the
+// slot's count when it starts (base), and a word of host memory (seen by the
+// device) where a wait that gave up records the failure.  The host hands
+// out slots in turn and advances each slot's base by the launch's
+// arrivals, so a slot is shared only by launches kSyncSlots calls apart.
+constexpr int kSyncSlots = 64;
+struct SyncArg {
+    unsigned long long base;
+    unsigned int* err;
+    int slot;   // -1: the launch needs no waits
+};
 enum EncodeMode { ENC_TENSOR = 0, ENC_TOKEN = 1, ENC_TILE = 2, ENC_GROUPED = 3 };
 
 // the encoding kernel forms 32-bit byte offsets within 32 rows of x
 constexpr int64_t kMaxEncodeK = int64_t(1) << 25;
 
 hipError_t launch_fill2(float* p, int64_t n, float* q, int64_t m, float v, hipStream_t st);
+// zero (with sync.slot >= 0): the first `wgs` workgroups (in dispatch
+// order) zero a[0..na) and b[0..nb) between them, kZeroPerWg values each,
+// and arrive; every workgroup waits for those `wgs` arrivals before
+// combining into the outputs.  Without it the outputs must already hold
+// zeros.
+constexpr int64_t kZeroPerWg = 16384;
+struct ZeroFirst {
+    float* a;
+    int64_t na;
+    float* b;
+    int64_t nb;
+    int wgs;
+};
+// workgroups of the amax launch for these rows (0 when there is nothing to do)
+int64_t amax_grid_size(int kind, int64_t K, int64_t row_begin, int64_t row_end);
 hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
                        float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
-                       hipStream_t st);
+                       hipStream_t st, const ZeroFirst& zero = ZeroFirst{nullptr, 0, nullptr, 0, 0},
+                       const SyncArg& sync = SyncArg{0ull, nullptr, -1});
 // optional calibration update done by the encoding kernel: buf[0] =
 // max(buf[0] * decay, max(obs[0..n))); buf == nullptr: none
 struct Calib {

@@ -42,6 +42,50 @@ __global__ void k_fill2_u32(uint32_t* __restrict__ p, int64_t n, uint32_t* __res
     }
 }
 
+// ------------------------------------------------ cross-workgroup waits
+//
+// One workgroup's writes sometimes have to reach the others before they go
+// on: the amax pass zeroes its outputs in its first workgroups (the first
+// dispatched) while the others will combine into them with atomics.  Such a
+// launch gets a slot of g_sync_count (the count when it starts comes from
+// the host): a workgroup arrives by adding 1 with release semantics (its
+// writes reach memory first), and waits, one lane polling, until the slot
+// reaches base + n.  The poll carries no acquire fence (on this chip an
+// agent-scope acquire invalidates the caches, and one per wave costs more
+// than a separate launch), so what a waiter does next must not read through
+// the caches: device-scope atomics, which are performed beyond them, or
+// loads that bypass them.  Every wait is bounded: after kSyncWaitTicks of
+// the 100 MHz real-time clock it gives up, records the failure in the error
+// word (host memory the library checks at its next call) and returns false,
+// and the workgroup skips what depended on it.
+constexpr uint64_t kSyncWaitTicks = 20000000ull;   // 0.2 s
+__device__ unsigned long long g_sync_count[kSyncSlots];
+
+__device__ __forceinline__ void sync_arrive(const SyncArg& s) {
+    __hip_atomic_fetch_add(&g_sync_count[s.slot], 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// one lane: wait for base + n arrivals; false when the wait gave up
+__device__ __forceinline__ bool sync_poll(const SyncArg& s, unsigned long long n) {
+    const unsigned long long target = s.base + n;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(&g_sync_count[s.slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncWaitTicks) {
+            __hip_atomic_store(s.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
+// a wave waits (lane 0 polls); the result is wave-uniform
+__device__ __forceinline__ bool sync_wait_wave(const SyncArg& s, unsigned long long n) {
+    int ok = 1;
+    if ((threadIdx.x & 63) == 0) ok = sync_poll(s, n) ? 1 : 0;
+    return __builtin_amdgcn_readfirstlane(ok) != 0;
+}
+
 // max of non-negative floats through their bit patterns
 __device__ __forceinline__ void atomic_max_mag(float* p, uint32_t mag16) {
     if (mag16 != 0u) atomicMax(reinterpret_cast<uint32_t*>(p), mag16 << 16);
@@ -118,7 +162,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
                                               int64_t row_begin, int64_t row_end,
                                               float* __restrict__ row_amax, float* __restrict__ col_amax,
                                               float* __restrict__ t0, float* __restrict__ t1, GroupTable gt,
-                                              int tile_h) {
+                                              int tile_h, ZeroFirst zero, SyncArg sync) {
     __shared__ uint32_t red[4][64][4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar expert lookups
@@ -130,6 +174,26 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     const uint32_t bx = tile % gridDim.x, by = tile / gridDim.x;
     const int64_t c0 = (int64_t)bx * kTileCols + lane * 8;
     const bool col_ok = c0 < K;
+    // Zero-first: the first zero.wgs workgroups (dispatched first) clear the
+    // outputs, kZeroPerWg values each, and arrive; each wave waits for them
+    // once, before its first atomic (normally long satisfied: every
+    // workgroup reads its tile first).  A wait that gave up skips the
+    // atomics.
+    const bool sync_on = sync.slot >= 0;
+    if (sync_on && lin < (uint32_t)zero.wgs) {
+        const int64_t z0 = (int64_t)lin * kZeroPerWg, z1 = z0 + kZeroPerWg;
+        for (int64_t i = z0 + threadIdx.x; i < z1 && i < zero.na + zero.nb; i += blockDim.x) {
+            if (i < zero.na) zero.a[i] = 0.0f;
+            else zero.b[i - zero.na] = 0.0f;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) sync_arrive(sync);
+    }
+    int zero_state = sync_on ? 0 : 1;   // 0: not waited yet, 1: outputs zeroed, -1: the wait gave up
+    auto zero_ready = [&]() -> bool {
+        if (zero_state == 0) zero_state = sync_wait_wave(sync, (unsigned long long)zero.wgs) ? 1 : -1;
+        return zero_state > 0;
+    };
     const int64_t rb = row_begin + (int64_t)by * tile_h + wave * (tile_h / 4);   // tile_h: 64 to 512 rows
     const uint32_t lane_off = col_ok ? (uint32_t)c0 * 2u : kOffOut;
     uint32_t xr = (uint32_t)K * 2u;
@@ -197,7 +261,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         if ((KIND == AMAX_TOKEN || KIND == AMAX_GROUPED) && row_amax != nullptr) {
             uint32_t pair;
             int j = wave_rowmax16(rm, &pair);
-            if ((lane & 7) == 0) {
+            if (zero_ready() && (lane & 7) == 0) {
                 if (r0 + 2 * j < row_end) atomic_max_mag(row_amax + r0 + 2 * j, pair & 0xffffu);
                 if (r0 + 2 * j + 1 < row_end) atomic_max_mag(row_amax + r0 + 2 * j + 1, pair >> 16);
             }
@@ -212,7 +276,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         __shared__ uint32_t tred[4];
         if (lane == 0) tred[wave] = tm;
         __syncthreads();
-        if (threadIdx.x == 0) {
+        if (wave == 0 && zero_ready() && threadIdx.x == 0) {
             uint32_t m = tred[0];
             for (int w = 1; w < 4; ++w) m = m > tred[w] ? m : tred[w];
             if (t0) atomic_max_mag(t0, m);
@@ -224,6 +288,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         if (cur_group >= 0) group_flush(cur_group);
         __syncthreads();
         const int64_t tc0 = (int64_t)bx * kTileCols;
+        if (!zero_ready()) return;
         for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) {
             const int slot = i / kTileCols, c = i % kTileCols;
             const int g = gslot[slot];
@@ -237,7 +302,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
 #pragma unroll
         for (int k = 0; k < 4; ++k) red[wave][lane][k] = cm[k];
         __syncthreads();
-        if (wave == 0 && col_ok) {
+        if (wave == 0 && zero_ready() && col_ok) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 uint32_t m = pk_max_u16(pk_max_u16(red[0][lane][k], red[1][lane][k]),
@@ -1172,25 +1237,35 @@ hipError_t launch_fill2(float* p, int64_t n, float* q, int64_t m, float v, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
-                       float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
-                       hipStream_t st) {
-    if (row_end <= row_begin || K <= 0) return hipSuccess;
-    // rows per workgroup: 512 (256 for grouped casts), fewer when the grid
-    // would leave CUs idle
+// rows per workgroup of the amax pass: 512 (256 for grouped casts), fewer
+// when the grid would leave CUs idle
+static int amax_tile_h(int kind, int64_t K, int64_t row_begin, int64_t row_end) {
     int tile_h = kAmaxRows;
     while (tile_h > 64 && (int64_t)cdiv(K, kTileCols) * cdiv(row_end - row_begin, tile_h) < 512) tile_h /= 2;
     if (kind == AMAX_GROUPED && tile_h > kAmaxGroupedRows) tile_h = kAmaxGroupedRows;
+    return tile_h;
+}
+
+int64_t amax_grid_size(int kind, int64_t K, int64_t row_begin, int64_t row_end) {
+    if (row_end <= row_begin || K <= 0) return 0;
+    return (int64_t)cdiv(K, kTileCols) * cdiv(row_end - row_begin, amax_tile_h(kind, K, row_begin, row_end));
+}
+
+hipError_t launch_amax(int kind, const uint16_t* x, int64_t K, int64_t row_begin, int64_t row_end,
+                       float* row_amax, float* col_amax, float* t0, float* t1, const GroupTable& gt,
+                       hipStream_t st, const ZeroFirst& zero, const SyncArg& sync) {
+    if (row_end <= row_begin || K <= 0) return hipSuccess;
+    const int tile_h = amax_tile_h(kind, K, row_begin, row_end);
     dim3 grid(cdiv(K, kTileCols), cdiv(row_end - row_begin, tile_h));
     switch (kind) {
     case AMAX_TENSOR:
-        hipLaunchKernelGGL(k_amax<AMAX_TENSOR>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h);
+        hipLaunchKernelGGL(k_amax<AMAX_TENSOR>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h, zero, sync);
         break;
     case AMAX_TOKEN:
-        hipLaunchKernelGGL(k_amax<AMAX_TOKEN>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h);
+        hipLaunchKernelGGL(k_amax<AMAX_TOKEN>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h, zero, sync);
         break;
     default:
-        hipLaunchKernelGGL(k_amax<AMAX_GROUPED>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h);
+        hipLaunchKernelGGL(k_amax<AMAX_GROUPED>, grid, dim3(256), 0, st, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, tile_h, zero, sync);
         break;
     }
     return hipGetLastError();

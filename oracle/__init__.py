@@ -63,6 +63,7 @@ def _load():
         "orc_swizzle_scales": (ctypes.c_int, [_p, _i64, _i64, _p]),
         "orc_unswizzle_scales": (ctypes.c_int, [_p, _i64, _i64, _p]),
         "orc_rht_columns": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_uint32, _p]),
+        "orc_quantize_per_token_threads": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_int, _p, _p, _p, _p, _p, _p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -206,6 +207,24 @@ def quantize(x, mode, rowwise=True, columnwise=True):
                               _ptr(g("col_q")), _ptr(g("col_sf")), _ptr(g("col_amax")))
     if rc != 0:
         raise ValueError("oracle: shape not supported by this mode")
+    return out
+
+
+def quantize_per_token_threads(x, nthreads):
+    """The per-token row + column cast with rows and columns split over
+    nthreads threads (the same per-vector routines; for timing the oracle on
+    all host cores).  Same outputs as quantize(x, PER_TOKEN)."""
+    x = _bf16(x)
+    M, K = x.shape
+    out = {"row_q": np.empty((M, K // 2), np.uint8), "row_sf": np.empty((M, K // 16), np.uint8),
+           "row_amax": np.empty(M, np.float32), "col_q": np.empty((K, M // 2), np.uint8),
+           "col_sf": np.empty((K, M // 16), np.uint8), "col_amax": np.empty(K, np.float32)}
+    g = out.get
+    rc = _load().orc_quantize_per_token_threads(_ptr(x), M, K, int(nthreads), _ptr(g("row_q")), _ptr(g("row_sf")),
+                                                _ptr(g("row_amax")), _ptr(g("col_q")), _ptr(g("col_sf")),
+                                                _ptr(g("col_amax")))
+    if rc != 0:
+        raise ValueError("oracle: bad arguments")
     return out
 
 

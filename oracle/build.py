@@ -16,7 +16,7 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC, "-lm"]
+    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC, "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

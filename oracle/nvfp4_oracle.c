@@ -29,6 +29,7 @@
 
 #include <math.h>
 #include <string.h>
+#include <pthread.h>
 #include <stdlib.h>
 
 /* ---------------------------------------------------------------- codecs */
@@ -744,5 +745,70 @@ int orc_unswizzle_scales(const uint8_t* in, int64_t R, int64_t nb, uint8_t* sf)
             int64_t tile = (r / 128) * (nbp / 4) + c / 4;
             sf[r * nb + c] = in[512 * tile + 16 * (r % 32) + 4 * ((r / 32) % 4) + c % 4];
         }
+    return 0;
+}
+
+
+/* ---- CPU baseline driver: the per-token row + column cast above, with the
+ * rows and the columns partitioned over threads.  Each thread runs the same
+ * per-vector routines (orc_amax_rows / orc_encode_rowwise on its rows,
+ * orc_amax_cols / orc_encode_colwise on its columns); nothing is blocked,
+ * fused or reordered beyond that split.  Used to time the oracle on the
+ * host's cores. */
+struct orc_slice {
+    const uint16_t* x;
+    int64_t M, K, r0, r1, c0, c1;
+    uint8_t *row_q, *row_sf, *col_q, *col_sf;
+    float *row_amax, *col_amax;
+};
+
+static void* orc_slice_run(void* arg)
+{
+    struct orc_slice* a = (struct orc_slice*)arg;
+    const int64_t M = a->M, K = a->K;
+    if (a->row_q && a->r1 > a->r0) {
+        orc_amax_rows(a->x + a->r0 * K, a->r1 - a->r0, K, K, a->row_amax + a->r0);
+        orc_encode_rowwise(a->x + a->r0 * K, a->r1 - a->r0, K, K, 1, a->row_amax + a->r0,
+                           a->row_q + a->r0 * (K / 2), a->row_sf + a->r0 * (K / 16));
+    }
+    if (a->col_q && a->c1 > a->c0) {
+        orc_amax_cols(a->x + a->c0, M, a->c1 - a->c0, K, a->col_amax + a->c0);
+        orc_encode_colwise(a->x + a->c0, M, a->c1 - a->c0, K, 1, a->col_amax + a->c0,
+                           a->col_q + a->c0 * (M / 2), a->col_sf + a->c0 * (M / 16));
+    }
+    return NULL;
+}
+
+int orc_quantize_per_token_threads(const uint16_t* x, int64_t M, int64_t K, int nthreads,
+                                   uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                   uint8_t* col_q, uint8_t* col_sf, float* col_amax)
+{
+    if (M < 0 || K < 0 || nthreads < 1 || nthreads > 1024) return -1;
+    if (row_q && K % 16 != 0) return -1;
+    if (col_q && M % 16 != 0) return -1;
+    struct orc_slice* sl = (struct orc_slice*)calloc((size_t)nthreads, sizeof(struct orc_slice));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!sl || !th) { free(sl); free(th); return -1; }
+    for (int i = 0; i < nthreads; ++i) {
+        struct orc_slice* a = &sl[i];
+        a->x = x; a->M = M; a->K = K;
+        a->r0 = M * i / nthreads; a->r1 = M * (i + 1) / nthreads;
+        a->c0 = K * i / nthreads; a->c1 = K * (i + 1) / nthreads;
+        a->row_q = row_q; a->row_sf = row_sf; a->row_amax = row_amax;
+        a->col_q = col_q; a->col_sf = col_sf; a->col_amax = col_amax;
+    }
+    int started = 0, rc = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, orc_slice_run, &sl[i]) != 0) { rc = -1; break; }
+        started = i;
+    }
+    orc_slice_run(&sl[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    if (rc == 0) {
+        /* any slice a failed thread would have covered, done here */
+        for (int i = started + 1; i < nthreads; ++i) orc_slice_run(&sl[i]);
+    }
+    free(sl);
+    free(th);
     return 0;
 }

@@ -120,4 +120,12 @@ int     orc_unswizzle_scales(const uint8_t* in, int64_t R, int64_t nb, uint8_t* 
 #ifdef __cplusplus
 }
 #endif
+/* Per-token row + column cast with rows and columns partitioned over
+ * nthreads threads (1 .. 1024), each running the per-vector routines above
+ * on its share; for timing the oracle on the host's cores.  Returns 0, or
+ * -1 on bad arguments. */
+int orc_quantize_per_token_threads(const uint16_t* x, int64_t M, int64_t K, int nthreads,
+                                   uint8_t* row_q, uint8_t* row_sf, float* row_amax,
+                                   uint8_t* col_q, uint8_t* col_sf, float* col_amax);
+
 #endif

@@ -298,3 +298,16 @@ def test_decay_checkpoint_resume(oracle):
     for t in range(8, 16):
         c = oracle.amax_accumulate(c, obs[t], 0.9)
     np.testing.assert_array_equal(a, c)
+
+
+def test_threaded_driver_matches_the_oracle(oracle):
+    """The CPU-baseline driver (rows and columns split over threads, the same
+    per-vector routines) returns exactly the per-token cast, for thread
+    counts that divide the rows and columns evenly and unevenly."""
+    from nvfp4_block_scaled_bf16_amd import workloads as W
+    x = W.row_scaled_with_outliers(272, 1040, 77)
+    ref = oracle.quantize(x, oracle.PER_TOKEN)
+    for n in (1, 2, 5, 16, 300):
+        got = oracle.quantize_per_token_threads(x, n)
+        for k, v in ref.items():
+            assert np.array_equal(got[k].view(np.uint8), v.view(np.uint8)), (n, k)

@@ -132,7 +132,7 @@ def copy_calibration(steps):
                       "bytes_written_per_launch": b.numel() * 2, "launches": steps}), flush=True)
 
 
-def all_configs(steps, warmup, only=None):
+def all_configs(steps, warmup, only=None, schedule="auto"):
     """One JSON line per named workload (not the headline line): average
     microseconds per call over `steps` timed calls with HIP events around
     them, inputs rotating where three fit, and algorithmic GB/s (TFLOP/s for
@@ -149,6 +149,9 @@ def all_configs(steps, warmup, only=None):
     f32 = lambda n: torch.empty(n, dtype=torch.float32, device=dev)
 
     want = lambda *names: only is None or any(n in only for n in names)
+    # these small casts are one resident launch under the automatic schedule
+    # (every workgroup keeps its whole run of tiles in registers)
+    resident_line = lambda fn, n: ("one resident launch", kernel_us(fn, n)) if schedule != "two_pass" else None
 
     def timed(fn, n_inputs):
         for i in range(warmup):
@@ -162,11 +165,29 @@ def all_configs(steps, warmup, only=None):
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / steps
 
-    def report(name, desc, us, nbytes):
+    def kernel_us(fn, n_inputs, calls=20):
+        """Average duration of the call's encoding kernel (the whole cast when
+        it is one resident launch), from the events nvfp4_trace_encode has the
+        launch itself record: device time alone, without the host's share of
+        back-to-back calls."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for i, (a, b) in enumerate(evs):
+            nv.trace_encode(a, b)
+            fn(i % n_inputs)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) * 1e3 / calls
+
+    def report(name, desc, us, nbytes, launch=None):
         gbs = nbytes / (us * 1e-6) / 1e9
-        print(json.dumps({"config": name, "workload": desc, "us_per_call": round(us, 2),
-                          "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
-                          "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+        line = {"config": name, "workload": desc, "us_per_call": round(us, 2),
+                "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        if launch is not None:
+            # one launch does the whole cast: its own duration, and the rate on it
+            kind, kus = launch
+            line.update(launches=kind, kernel_us=round(kus, 2),
+                        kernel_frac_of_peak=round(nbytes / (kus * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+        print(json.dumps(line), flush=True)
 
     def report_mfma(name, desc, us, flops):
         tfs = flops / (us * 1e-6) / 1e12
@@ -181,8 +202,9 @@ def all_configs(steps, warmup, only=None):
     if want("C1", "C1-dequant"):
         x1 = to_dev(W.c1())
         o1 = dict(row_q=u8(256, 512), row_sf=u8(256, 64), row_amax=f32(1))
-        report("C1", "per-tensor rowwise quantize, 256x1024", timed(lambda i: nv.quantize_into(x1, nv.PER_TENSOR, **o1), 1),
-               2 * 256 * 1024 + 256 * 512 + 256 * 64 + 4)
+        c1 = nv.prepare_quantize(x1, nv.PER_TENSOR, **o1)
+        report("C1", "per-tensor rowwise quantize, 256x1024", timed(lambda i: c1(), 1),
+               2 * 256 * 1024 + 256 * 512 + 256 * 64 + 4, resident_line(lambda i: c1(), 1))
         back = f32(256 * 1024)
         report("C1-dequant", "dequantize of the C1 output to fp32", timed(
             lambda i: nv.lib().nvfp4_dequantize(nv._ptr(o1["row_q"]), nv._ptr(o1["row_sf"]), nv._ptr(o1["row_amax"]), 256, 1024,
@@ -193,8 +215,9 @@ def all_configs(steps, warmup, only=None):
         x2 = [to_dev(W.row_scaled_with_outliers(4096, 4096, 1002 + 7 * t)) for t in range(3)]
         o2 = dict(row_q=u8(4096, 2048), row_sf=u8(4096, 256), row_amax=f32(4096),
                   col_q=u8(4096, 2048), col_sf=u8(4096, 256), col_amax=f32(4096))
-        report("C2", "per-token row+col, 4096x4096", timed(lambda i: nv.quantize_into(x2[i], nv.PER_TOKEN, **o2), 3),
-               cast_bytes(4096, 4096, 8192))
+        c2 = [nv.prepare_quantize(x, nv.PER_TOKEN, **o2) for x in x2]
+        report("C2", "per-token row+col, 4096x4096", timed(lambda i: c2[i](), 3),
+               cast_bytes(4096, 4096, 8192), resident_line(lambda i: c2[i](), 3))
         del x2
     # C3: per-tensor and per-token row+col 16384 x 8192, Student-t
     # one GPU's share of C3 split 8 ways by rows (the shape each GPU would
@@ -203,8 +226,9 @@ def all_configs(steps, warmup, only=None):
         xs8 = [to_dev(W.c3(t)[2048 * t:2048 * (t + 1)]) for t in range(3)]
         o8 = dict(row_q=u8(2048, K // 2), row_sf=u8(2048, K // 16), row_amax=f32(2048),
                   col_q=u8(K, 1024), col_sf=u8(K, 128), col_amax=f32(K))
+        c8 = [nv.prepare_quantize(x, nv.PER_TOKEN, **o8) for x in xs8]
         report("shard-2048x8192", "per-token row+col, 2048x8192 (one row shard of 16384x8192 over 8 GPUs)",
-               timed(lambda i: nv.quantize_into(xs8[i], nv.PER_TOKEN, **o8), 3), cast_bytes(2048, K, 2048 + K))
+               timed(lambda i: c8[i](), 3), cast_bytes(2048, K, 2048 + K), resident_line(lambda i: c8[i](), 3))
         del xs8
     if want("C3-per-token", "C3-per-token-rowwise", "C3-per-tensor", "C3-per-token-swizzled", "C3-per-token-SR", "C3-per-token-RHT", "GEMM-TN",
             "GEMM-TN-swizzled"):
@@ -386,6 +410,8 @@ def main():
                     help="with --all-configs: comma-separated line names to run (e.g. GEMM-TN)")
     ap.add_argument("--all-configs", action="store_true",
                     help="time every named workload (one JSON line each) instead of the headline step")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "two_pass", "resident"],
+                    help="launch schedule of the per-tensor / per-token casts (nvfp4_set_schedule)")
     ap.add_argument("--trace-every", type=int, default=5,
                     help="time the encoding kernel with events on every N-th timed step (0: never)")
     args = ap.parse_args()
@@ -398,8 +424,11 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.steps)
         return
+    if args.schedule != "auto":
+        import nvfp4_block_scaled_bf16_amd as nv
+        nv.set_schedule(args.schedule)
     if args.all_configs:
-        all_configs(args.steps, args.warmup, args.only.split(",") if args.only else None)
+        all_configs(args.steps, args.warmup, args.only.split(",") if args.only else None, args.schedule)
         return
 
     import numpy as np

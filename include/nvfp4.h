@@ -23,9 +23,13 @@
  * Conventions shared by every entry point
  *   - x is bf16, contiguous row-major [M][K] (or [T][K] for grouped), on the
  *     device.  All other arrays are device memory owned by the caller; the
- *     library allocates nothing, keeps no state between calls (beyond a
- *     thread-local error string and a pending nvfp4_trace_encode pair) and
- *     never reads outputs before writing them.
+ *     library never reads outputs before writing them and allocates no
+ *     device memory per call.  Its state: a thread-local error string and
+ *     pending nvfp4_trace_encode pair, the nvfp4_set_schedule setting, and
+ *     per device (set up at the first call there) the compute-unit count,
+ *     the arrival counters of its cross-workgroup waits (a static device
+ *     array) and one word of pinned host memory where a wait that gave up
+ *     records it.
  *   - Rowwise output ("row_*"): row_q [M][K/2] bytes, row_sf [M][K/16] E4M3
  *     codes, row_amax fp32.  Columnwise output ("col_*") is the quantization
  *     of the transpose: col_q [K][M/2], col_sf [K][M/16], col_amax fp32.
@@ -49,9 +53,18 @@
  *     finite; a NaN or Inf input gives unspecified codes.
  *   - Any shape meeting these rules is accepted; all shapes give results
  *     bit-identical to the CPU reference.
- *   - The cast writes every amax output it computes: it first zero-fills the
- *     arrays in-stream, then max-combines into them, so their prior contents
- *     never matter.
+ *   - The cast writes every amax output it computes: the arrays are zeroed
+ *     on the stream (by the first workgroups of the launch that then
+ *     max-combines into them, or by a launch before it), so their prior
+ *     contents never matter.
+ *   - Calls may be recorded by stream capture: on a capturing stream the
+ *     library takes launch paths without cross-workgroup waits (whose
+ *     arrival counts come from the host at each call).
+ *   - Launches whose workgroups wait for one another bound every wait
+ *     (about 0.2 s).  A wait that gives up -- possible only when other work
+ *     holds the device's compute units for that long -- leaves that call's
+ *     outputs invalid, and the next call on the device that launches such
+ *     a kernel returns NVFP4_EDEVICE, once.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -62,7 +75,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define NVFP4_API __attribute__((visibility("default")))
@@ -104,6 +117,35 @@ NVFP4_API const char* nvfp4_last_error(void);
  * NVFP4_EINVAL.  Recording the events changes no result.
  */
 NVFP4_API nvfp4_status nvfp4_trace_encode(void* before, void* after);
+
+/*
+ * Launch schedule of the per-tensor and per-token casts whose amax the call
+ * measures (nvfp4_quantize, _rowwise, _columnwise and _calibrate; the
+ * swizzled, stochastic-rounding, Hadamard, grouped and 16x16 casts always
+ * take the two-pass one):
+ *   NVFP4_SCHEDULE_AUTO (default): resident where it applies and reads x
+ *     once (at most two tiles per workgroup), else two-pass; per-token
+ *     rowwise-only casts take their single-pass row kernel;
+ *   NVFP4_SCHEDULE_TWO_PASS: an amax launch, then an encoding launch that
+ *     reads x again;
+ *   NVFP4_SCHEDULE_RESIDENT: the resident schedule wherever it applies,
+ *     rowwise-only per-token casts included.
+ * The resident schedule is one launch of at most one workgroup per compute
+ * unit, all resident at once: an amax phase, a wait for every workgroup,
+ * then an encoding phase, with the last two 256 x 256 tiles each workgroup
+ * read in the amax phase encoded from registers (a tensor of at most two
+ * such tiles per workgroup is read from memory once).  It applies when the
+ * ceil(K/256) column strips fit that grid with runs of at most 32 tiles.
+ * Every schedule gives bit-identical results; the setting exists for timing
+ * comparisons and tests.  Process-wide, read at each call.  NVFP4_EINVAL for
+ * another value.
+ */
+typedef enum {
+    NVFP4_SCHEDULE_AUTO = 0,
+    NVFP4_SCHEDULE_TWO_PASS = 1,
+    NVFP4_SCHEDULE_RESIDENT = 2
+} nvfp4_schedule;
+NVFP4_API nvfp4_status nvfp4_set_schedule(nvfp4_schedule schedule);
 
 /*
  * Whole cast, one read of x serving both directions.  Pass NULL for all three

@@ -20,6 +20,8 @@ import os
 import torch
 
 PER_TENSOR, PER_TOKEN, TILE_16x16 = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_TWO_PASS, SCHEDULE_RESIDENT = 0, 1, 2
+_SCHEDULES = {"auto": SCHEDULE_AUTO, "two_pass": SCHEDULE_TWO_PASS, "resident": SCHEDULE_RESIDENT}
 _MODES = {"per_tensor": PER_TENSOR, "per_token": PER_TOKEN, "tile_16x16": TILE_16x16,
           PER_TENSOR: PER_TENSOR, PER_TOKEN: PER_TOKEN, TILE_16x16: TILE_16x16}
 
@@ -30,7 +32,7 @@ EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_qua
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
            "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm",
            "nvfp4_gemm_grouped", "nvfp4_quantize_rht", "nvfp4_swizzle_scales",
-           "nvfp4_gemm_swizzled", "nvfp4_quantize_swizzled")
+           "nvfp4_gemm_swizzled", "nvfp4_quantize_swizzled", "nvfp4_set_schedule")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_swizzle_scales": (st, [p, i64, i64, p, p]),
         "nvfp4_quantize_swizzled": (st, [p, i64, i64, st, p, p, p, p, p, p, p]),
         "nvfp4_gemm_swizzled": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
+        "nvfp4_set_schedule": (st, [st]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -261,6 +264,35 @@ def quantize_calibrate_into(x, mode, buf, decay: float, row_q=None, row_sf=None,
     _check(lib().nvfp4_quantize_calibrate(_ptr(x), M, K, _mode(mode), _ptr(row_q), _ptr(row_sf), _ptr(row_amax),
                                           _ptr(col_q), _ptr(col_sf), _ptr(col_amax), _ptr(buf),
                                           ctypes.c_float(decay), _stream(x.device)))
+
+
+def prepare_quantize(x, mode, buf=None, decay: float = 0.0, row_q=None, row_sf=None, row_amax=None,
+                     col_q=None, col_sf=None, col_amax=None):
+    """quantize_into (or, with buf, quantize_calibrate_into) validated and
+    marshalled once: returns a function of no arguments that issues the same
+    call on the stream current now.  For loops that repeat one call on fixed
+    buffers, where the per-call Python checks would cost more than the
+    kernels of a small tensor."""
+    x = _input(x)
+    M, K = x.shape
+    m = _mode(mode)
+    _check_cast_outputs(x, m, row_q, row_sf, row_amax, col_q, col_sf, col_amax)
+    L = lib()
+    ptrs = (_ptr(row_q), _ptr(row_sf), _ptr(row_amax), _ptr(col_q), _ptr(col_sf), _ptr(col_amax))
+    if buf is None:
+        fn, args = L.nvfp4_quantize, (_ptr(x), M, K, m) + ptrs + (_stream(x.device),)
+    else:
+        _check_buf(buf, torch.float32, None, x.device, "buf", min_numel=1)
+        fn, args = L.nvfp4_quantize_calibrate, (_ptr(x), M, K, m) + ptrs + (_ptr(buf), ctypes.c_float(decay),
+                                                                           _stream(x.device))
+    keep = (x, buf, row_q, row_sf, row_amax, col_q, col_sf, col_amax)   # alive while the call is
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            _check(st)
+    call.keep = keep
+    return call
 
 
 def quantize_rowwise(x, mode="per_token"):
@@ -529,3 +561,13 @@ def trace_encode(before, after):
             ev.record()
         return ctypes.c_void_p(ev.cuda_event)
     _check(lib().nvfp4_trace_encode(handle(before), handle(after)))
+
+
+def set_schedule(schedule):
+    """nvfp4_set_schedule: "auto", "two_pass" or "resident" (or the ints 0..2)
+    for the per-tensor and per-token casts whose amax the call measures;
+    results are identical, only the launches differ."""
+    v = _SCHEDULES.get(schedule, schedule)
+    if v not in (0, 1, 2):
+        raise ValueError(f"unknown schedule {schedule!r}")
+    _check(lib().nvfp4_set_schedule(v))

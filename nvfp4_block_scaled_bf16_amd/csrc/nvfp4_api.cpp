@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -117,26 +118,31 @@ nvfp4_status stream_device(hipStream_t st, int* dev) {
     return e == hipSuccess ? NVFP4_OK : fail(NVFP4_EDEVICE, "stream device: %s", hipGetErrorString(e));
 }
 
-// call with g_dev_mu held
-nvfp4_status device_init(int dev, DeviceState** out) {
+// call with g_dev_mu held; with_err: also the pinned error word (only the
+// launches with waits need it, and those are never made under capture)
+nvfp4_status device_init(int dev, DeviceState** out, bool with_err = false) {
     if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
     DeviceState& d = g_dev[dev];
+    hipError_t e;
     if (!d.init) {
-        hipError_t e;
         int n = 0;
         if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess || n <= 0)
             return fail(NVFP4_EDEVICE, "device attribute: %s", hipGetErrorString(e));
+        d.cus = n;
+        d.init = true;
+    }
+    if (with_err && d.err_host == nullptr) {
         void* h = nullptr;
         if ((e = hipHostMalloc(&h, sizeof(unsigned int), hipHostMallocMapped)) != hipSuccess)
             return fail(NVFP4_EDEVICE, "pinned error word: %s", hipGetErrorString(e));
         void* dp = nullptr;
-        if ((e = hipHostGetDevicePointer(&dp, h, 0)) != hipSuccess)
+        if ((e = hipHostGetDevicePointer(&dp, h, 0)) != hipSuccess) {
+            (void)hipHostFree(h);
             return fail(NVFP4_EDEVICE, "pinned error word: %s", hipGetErrorString(e));
-        d.cus = n;
-        d.err_host = static_cast<unsigned int*>(h);
+        }
+        *static_cast<unsigned int*>(h) = 0u;
         d.err_dev = static_cast<unsigned int*>(dp);
-        *d.err_host = 0u;
-        d.init = true;
+        d.err_host = static_cast<unsigned int*>(h);
     }
     *out = &d;
     return NVFP4_OK;
@@ -153,6 +159,16 @@ nvfp4_status device_cus(hipStream_t st, int* cus) {
     return NVFP4_OK;
 }
 
+// Launches with cross-workgroup waits take their slot's base count from the
+// host at the call, so they must not be recorded into a graph (a replay would
+// reuse the recorded base).  On a capturing stream the library takes the
+// paths without waits instead (a fill launch before the amax pass, the
+// two-launch schedule).
+bool capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
 // A slot for a launch of `arrivals` arrivals on stream st.
 struct SyncTicket {
     SyncArg arg;
@@ -166,7 +182,7 @@ nvfp4_status sync_take(hipStream_t st, uint64_t arrivals, SyncTicket* t) {
     if (s != NVFP4_OK) return s;
     std::lock_guard<std::mutex> lock(g_dev_mu);
     DeviceState* d = nullptr;
-    if ((s = device_init(dev, &d)) != NVFP4_OK) return s;
+    if ((s = device_init(dev, &d, true)) != NVFP4_OK) return s;
     if (__atomic_load_n(d->err_host, __ATOMIC_ACQUIRE) != 0u) {
         __atomic_store_n(d->err_host, 0u, __ATOMIC_RELEASE);
         return fail(NVFP4_EDEVICE, "an earlier call's cross-workgroup wait gave up (its outputs are invalid)");
@@ -196,8 +212,8 @@ nvfp4_status amax_zero_first(int kind, const uint16_t* x, int64_t K, int64_t row
     if (a == nullptr) na = 0;
     if (b == nullptr) nb = 0;
     ZeroFirst z{a, na, b, nb, (int)((na + nb + kZeroPerWg - 1) / kZeroPerWg)};
-    if (z.wgs == 0 || z.wgs > amax_grid_size(kind, K, row_begin, row_end)) {
-        // nothing to zero, or more than the grid has workgroups: a fill launch
+    if (z.wgs == 0 || z.wgs > amax_grid_size(kind, K, row_begin, row_end) || capturing(st)) {
+        // nothing to zero, more than the grid has workgroups, or a capture: a fill launch
         nvfp4_status s = check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
         if (s != NVFP4_OK) return s;
         return check_hip(launch_amax(kind, x, K, row_begin, row_end, row_amax, col_amax, t0, t1, gt, st), "amax");
@@ -224,6 +240,84 @@ unsigned rows_grid(int cus, int64_t M, int64_t K) {
 // zero-fill up to two fp32 arrays (one launch) before an atomic-max pass
 nvfp4_status zero(float* a, int64_t na, float* b, int64_t nb, hipStream_t st) {
     return check_hip(launch_fill2(a, na, b, nb, 0.0f, st), "fill");
+}
+
+// ------------------------------------------------------- cast schedules
+
+std::atomic<int> g_schedule{NVFP4_SCHEDULE_AUTO};
+
+// Resident schedule of an M x K cast: a grid of ceil(K / 256) strips x nband
+// bands, every workgroup resident at once (cap of them fit), each owning a
+// run of up to `run` 256-row tiles; runs over 32 tiles are not offered.
+struct ResPlan {
+    int run = 0, nband = 0;
+    unsigned grid = 0;   // 0: the schedule does not apply
+};
+
+ResPlan resident_plan(int cap, int64_t M, int64_t K) {
+    ResPlan p;
+    const int64_t tx = (K + 255) / 256, ty = (M + 255) / 256;
+    // (the columnwise output is addressed with 32-bit offsets)
+    if (cap <= 0 || M <= 0 || K <= 0 || tx > cap || M / 2 * K >= ((int64_t)1 << 31)) return p;
+    const int64_t per = cap / tx;
+    const int64_t run = (ty + per - 1) / per;
+    if (run > 32) return p;
+    p.run = (int)run;
+    p.nband = (int)((ty + run - 1) / run);
+    p.grid = (unsigned)(tx * p.nband);
+    return p;
+}
+
+// the plan for this call under the current schedule (grid 0: two passes)
+nvfp4_status resident_choice(int emode, bool row, bool col, int64_t M, int64_t K, hipStream_t st, ResPlan* out) {
+    *out = ResPlan{};
+    if (g_schedule.load(std::memory_order_relaxed) == NVFP4_SCHEDULE_TWO_PASS || capturing(st)) return NVFP4_OK;
+    int cus = 0;
+    nvfp4_status s = device_cus(st, &cus);
+    if (s != NVFP4_OK) return s;
+    const ResPlan p = resident_plan(resident_blocks_per_cu(emode, row, col) * cus, M, K);
+    // Automatic: resident when every workgroup keeps its whole run (at most
+    // two tiles) in registers, so that x is read once.  Longer runs re-read
+    // all but two tiles per workgroup, and the encoding phase, with two
+    // waves per SIMD and all the vector work of the cast, then takes longer
+    // than the separate encoding pass.
+    if (g_schedule.load(std::memory_order_relaxed) == NVFP4_SCHEDULE_RESIDENT || p.run <= 2) *out = p;
+    return NVFP4_OK;
+}
+
+// One launch: zero-first of the amax outputs, amax phase, grid-wide wait,
+// encoding phase (with the calibration update when cal.buf is set).
+nvfp4_status resident_cast(int emode, const uint16_t* x, int64_t M, int64_t K, uint8_t* rq, uint8_t* rsf, float* ra,
+                           uint8_t* cq, uint8_t* csf, float* ca, const Calib& cal, const ResPlan& p, hipStream_t st) {
+    const bool tok = emode == ENC_TOKEN;
+    const int64_t na = ra ? (tok ? M : 1) : 0, nb = ca ? (tok ? K : 1) : 0;
+    ZeroFirst z{ra, na, ca, nb, (int)((na + nb + kZeroPerWg - 1) / kZeroPerWg)};
+    nvfp4_status s;
+    if ((unsigned)z.wgs > p.grid) {
+        // more zeroing than workgroups: a fill launch first
+        if ((s = zero(ra, na, ca, nb, st)) != NVFP4_OK) return s;
+        z.wgs = 0;
+    }
+    ResArgs a{x, M, K, ra, ca, rq, rsf, cq, csf, p.run, p.nband, z, SyncArg{0ull, nullptr, -1},
+              SyncArg{0ull, nullptr, -1}, cal};
+    SyncTicket zt{}, bt{};
+    if (z.wgs > 0) {
+        if ((s = sync_take(st, (uint64_t)z.wgs, &zt)) != NVFP4_OK) return s;
+        a.zsync = zt.arg;
+    }
+    if ((s = sync_take(st, p.grid, &bt)) != NVFP4_OK) {
+        if (z.wgs > 0) sync_return(zt);
+        return s;
+    }
+    a.bar = bt.arg;
+    s = encode_launch([&](hipEvent_t b, hipEvent_t e) {
+        return launch_resident(emode, ra != nullptr, ca != nullptr, a, p.grid, st, b, e);
+    });
+    if (s != NVFP4_OK) {
+        sync_return(bt);
+        if (z.wgs > 0) sync_return(zt);
+    }
+    return s;
 }
 
 // cal_buf (may be null): buf[0] = max(buf[0] * decay, tensor amax), done by
@@ -281,7 +375,7 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         else { cal.obs = ra ? ra : ca; cal.n = 1; }
     }
     if (mode == NVFP4_PER_TOKEN && r.want && !c.want && M > 0 && K > 0 && !rounding.stochastic && !swizzled &&
-        rows_path(K)) {
+        rows_path(K) && g_schedule.load(std::memory_order_relaxed) != NVFP4_SCHEDULE_RESIDENT) {
         // rowwise only: each row's amax is found and used on chip, x is read
         // once
         int cus = 0;
@@ -294,6 +388,17 @@ nvfp4_status quantize_impl(const void* xv, int64_t M, int64_t K, nvfp4_scaling m
         if (cal_buf && (s = check_hip(launch_accumulate_reduce(cal_buf, ra, M, decay, st), "calibration")) != NVFP4_OK)
             return s;
         return ok();
+    }
+    if ((mode == NVFP4_PER_TOKEN || mode == NVFP4_PER_TENSOR) && M > 0 && K > 0 && !rounding.stochastic && !swizzled) {
+        // amax and encoding in one resident launch, where it applies
+        const int emode = mode == NVFP4_PER_TOKEN ? ENC_TOKEN : ENC_TENSOR;
+        ResPlan p;
+        if ((s = resident_choice(emode, r.want, c.want, M, K, st, &p)) != NVFP4_OK) return s;
+        if (p.grid != 0) {
+            s = resident_cast(emode, x, M, K, r.want ? row_q : nullptr, r.want ? row_sf : nullptr, ra,
+                              c.want ? col_q : nullptr, c.want ? col_sf : nullptr, ca, cal, p, st);
+            return s != NVFP4_OK ? s : ok();
+        }
     }
     if (mode == NVFP4_PER_TOKEN) {
         if (M == 0 || K == 0) return zero(ra, M, ca, K, st) != NVFP4_OK ? NVFP4_EDEVICE : ok();
@@ -341,6 +446,14 @@ nvfp4_status nvfp4_trace_encode(void* before, void* after) {
     if ((before == nullptr) != (after == nullptr)) return fail(NVFP4_EINVAL, "give both trace events or neither");
     g_trace_before = static_cast<hipEvent_t>(before);
     g_trace_after = static_cast<hipEvent_t>(after);
+    return ok();
+}
+
+nvfp4_status nvfp4_set_schedule(nvfp4_schedule schedule) {
+    const int v = (int)schedule;
+    if (v != NVFP4_SCHEDULE_AUTO && v != NVFP4_SCHEDULE_TWO_PASS && v != NVFP4_SCHEDULE_RESIDENT)
+        return fail(NVFP4_EINVAL, "unknown schedule %d", v);
+    g_schedule.store(v, std::memory_order_relaxed);
     return ok();
 }
 

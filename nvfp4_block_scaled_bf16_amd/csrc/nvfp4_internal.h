@@ -56,6 +56,31 @@ struct Calib {
     float decay;
 };
 
+// Resident one-launch cast (per-tensor or per-token, amax measured in the
+// same launch; nvfp4_kernels.hip): 256 x 256 tiles, workgroup w takes a
+// vertical run of up to `run` tiles of strip w / nband, band w % nband; the
+// grid (ceil(K / 256) * nband workgroups of 512 lanes) must be resident at
+// once.  zero / zsync: zero-first of the amax outputs (zsync.slot < 0: they
+// hold zeros already); bar: the grid-wide wait.
+struct ResArgs {
+    const uint16_t* x;
+    int64_t M, K;
+    float* row_amax;
+    float* col_amax;
+    uint8_t* row_q;
+    uint8_t* row_sf;
+    uint8_t* col_q;
+    uint8_t* col_sf;
+    int run, nband;
+    ZeroFirst zero;
+    SyncArg zsync, bar;
+    Calib cal;
+};
+// workgroups of the resident kernel one compute unit holds (0 when unknown)
+int resident_blocks_per_cu(int mode, bool row, bool col);
+hipError_t launch_resident(int mode, bool row, bool col, const ResArgs& a, unsigned grid, hipStream_t st,
+                           hipEvent_t ev0, hipEvent_t ev1);
+
 hipError_t launch_encode(int mode, bool row, bool col, bool caller_amax, const uint16_t* x, int64_t M, int64_t K,
                          int64_t row_begin, int64_t row_end, const float* row_amax, const float* col_amax,
                          uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf,

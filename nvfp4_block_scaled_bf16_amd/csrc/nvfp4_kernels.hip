@@ -29,6 +29,8 @@ constexpr int kEncCols = 256;      // columns per workgroup tile in the encode p
 // spread the lanes' writes over the banks
 constexpr int kStageQPitch = kEncRows / 2 + 4;
 constexpr int kStageSfPitch = kEncRows / 16 + 4;
+// longest run of 256-row tiles per workgroup in the resident cast
+constexpr int kResMaxRun = 32;
 
 // --------------------------------------------------------------- utilities
 
@@ -63,6 +65,12 @@ __device__ unsigned long long g_sync_count[kSyncSlots];
 
 __device__ __forceinline__ void sync_arrive(const SyncArg& s) {
     __hip_atomic_fetch_add(&g_sync_count[s.slot], 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// arrival for a workgroup whose prior writes are device-scope atomics or
+// stores already complete (s_waitcnt): no cache write-back is needed
+__device__ __forceinline__ void sync_arrive_relaxed(const SyncArg& s) {
+    __hip_atomic_fetch_add(&g_sync_count[s.slot], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // one lane: wait for base + n arrivals; false when the wait gave up
@@ -395,8 +403,8 @@ __device__ __forceinline__ void store_col(const SubDst& d, int j, uint32_t lo, u
 // re-reading the data from xr (row r0, column 0; row stride K).  rowA[i]:
 // amax of row i; colA: this lane's 8 column amax; tileA: the tensor's.
 template <bool ROW, bool COL, bool TILE, bool STAGE, bool SWZ>
-__device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64_t K, const float* rowA,
-                                          const float* colA, float tileA, SubDst d) {
+__device__ __forceinline__ void encode_exact_body(const uint16_t* __restrict__ xr, int64_t K, const float* rowA,
+                                                  const float* colA, float tileA, const SubDst& d) {
     u32x4 v[16];
     for (int i = 0; i < 16; ++i)
         v[i] = (d.col_ok && i < d.nrows) ? *reinterpret_cast<const u32x4*>(xr + i * K + d.c0) : u32x4{0u, 0u, 0u, 0u};
@@ -449,6 +457,13 @@ __device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64
             store_col<STAGE>(d, j, lohi[0], lohi[1], bs.code);
         }
     }
+}
+
+// the same, out of line (kept out of the hot loops' register allocation)
+template <bool ROW, bool COL, bool TILE, bool STAGE, bool SWZ>
+__device__ __noinline__ void encode_exact(const uint16_t* __restrict__ xr, int64_t K, const float* rowA,
+                                          const float* colA, float tileA, SubDst d) {
+    encode_exact_body<ROW, COL, TILE, STAGE, SWZ>(xr, K, rowA, colA, tileA, d);
 }
 
 // One workgroup (blockDim.x a multiple of 64, at most 1024): m = max(obs),
@@ -1204,6 +1219,531 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, 
     }
 }
 
+// ------------------------------------------------ resident one-launch cast
+//
+// Per-tensor and per-token casts whose amax is measured on x, in a single
+// launch of at most one workgroup per compute unit, all resident at once.
+// Phase A reads the workgroup's tiles and combines their maxima into the
+// amax outputs (zeroed first, as in the amax pass); then a grid-wide wait;
+// phase B encodes.  The last two tiles a wave reads in phase A stay in its
+// registers and are encoded in phase B without a second read: a tensor of at
+// most two tiles per workgroup crosses HBM once, a larger one re-reads the
+// rest (nontemporal, most recently read first).  With two waves per SIMD
+// and all of the cast's vector work in phase B, runs longer than two tiles
+// are slower than the two-launch schedule; the host uses this kernel for
+// them only when asked to.
+//
+// Work: 256-row x 256-column tiles.  Workgroup w (8 waves) owns a vertical
+// run of up to `run` tiles of strip w / nband (256 columns), band w % nband
+// (so the strips of a band share an XCD when nband % 8 == 0, and write the
+// same rowwise scale lines through one L2).  Its column maxima accumulate in
+// registers over the run and the strip's column scales are set once in
+// phase B.  Wave v covers rows 32v .. 32v+31 of each tile, laid out as a
+// step of the encode pass (two 32-lane row groups, a 16-row x 8-column
+// sub-block per lane).
+//
+// Phase A walks the run from its last tile down: tile t sits in register set
+// t % 2, and tile t - 2 is loaded into that set once tile t's maxima are
+// taken.  Phase B walks up from tile 0 and loads tile t + 2 into the set of
+// tile t as that one is encoded.  Phase B reads the amax outputs with
+// coherent (atomic) loads: the grid-wide wait carries no acquire, and a
+// cache may still hold the zeros written before phase A.
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Max over each 32-lane half of the wave of 16 per-lane 16-bit values (one
+// per row), by halving exchanges: after the xor-16/8/4 steps each lane holds
+// a pair of rows, the xor-2/1 steps finish.  Returns the pair index j (rows
+// 2j, 2j+1 in the low / high half of *pair) this lane holds.
+__device__ __forceinline__ int half_rowmax16(const uint32_t m[16], uint32_t* pair) {
+    const int lane = threadIdx.x & 63;
+    uint32_t p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = m[2 * j] | (m[2 * j + 1] << 16);
+    const bool b16 = lane & 16, b8 = lane & 8, b4 = lane & 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t send = b16 ? p[j] : p[j + 4], keep = b16 ? p[j + 4] : p[j];
+        p[j] = pk_max_u16(keep, (uint32_t)__shfl_xor((int)send, 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t send = b8 ? p[j] : p[j + 2], keep = b8 ? p[j + 2] : p[j];
+        p[j] = pk_max_u16(keep, (uint32_t)__shfl_xor((int)send, 8));
+    }
+    {
+        const uint32_t send = b4 ? p[0] : p[1], keep = b4 ? p[1] : p[0];
+        p[0] = pk_max_u16(keep, (uint32_t)__shfl_xor((int)send, 4));
+    }
+    p[0] = pk_max_u16(p[0], (uint32_t)__shfl_xor((int)p[0], 2));
+    p[0] = pk_max_u16(p[0], (uint32_t)__shfl_xor((int)p[0], 1));
+    *pair = p[0];
+    return (b16 ? 4 : 0) + (b8 ? 2 : 0) + (b4 ? 1 : 0);
+}
+
+// wg_accumulate_reduce over amax values other workgroups of the same launch
+// combined: obs is read with coherent loads
+__device__ void wg_accumulate_reduce_coherent(float* __restrict__ buf, const float* obs, int64_t n, float decay,
+                                              float* red) {
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const float o = load_coherent(obs + i);
+        m = o > m ? o : m;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float o = __shfl_xor(m, d);
+        m = o > m ? o : m;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nw = (int)(blockDim.x >> 6);
+        for (int w = 1; w < nw; ++w) m = red[w] > m ? red[w] : m;
+        const float t = buf[0] * decay;
+        buf[0] = m > t ? m : t;
+    }
+}
+
+template <int MODE, bool ROW, bool COL>
+__global__ __launch_bounds__(512) void k_resident(ResArgs a) {
+    constexpr bool TOK = MODE == ENC_TOKEN;
+    constexpr bool ROWTOK = ROW && TOK;
+    constexpr bool COL_LDS = COL && TOK;
+    __shared__ float row_scale[8][32][2];    // per wave: S and 1/S of the step's 32 rows
+    __shared__ float2 col_scale[COL_LDS ? kEncCols : 1];
+    __shared__ uint32_t red[8][32][4];
+    __shared__ int bar_ok;
+    // per-token rowwise: the amax of the band's rows, read once after the
+    // grid-wide wait (LDS reads in the steps keep memory waits for x alone)
+    __shared__ float band_amax[ROWTOK ? kResMaxRun * kEncRows : 1];
+
+    const uint16_t* __restrict__ x = a.x;
+    const int64_t M = a.M, K = a.K;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lin = blockIdx.x;
+    const uint32_t strip = lin / (uint32_t)a.nband, band = lin % (uint32_t)a.nband;
+    const int64_t ty = (M + kEncRows - 1) / kEncRows;
+    const int64_t t_first = (int64_t)band * a.run;
+    const int tcount = (int)(ty - t_first < a.run ? ty - t_first : a.run);   // >= 1
+    const int rg = lane >> 5;
+    const uint32_t c0 = strip * kEncCols + (lane & 31) * 8;
+    const bool col_ok = c0 < K;
+    const bool odd = lane & 1;
+    const uint32_t xrow = (uint32_t)K * 2u, qrow = (uint32_t)(K / 2), srow = (uint32_t)(K / 16);
+    const uint32_t vx = col_ok ? 16u * rg * xrow + c0 * 2u : kOffOut;
+    auto tile_r0 = [&](int t) -> int64_t { return (t_first + t) * kEncRows; };
+    // valid rows of the wave's step of tile t (0 outside the run)
+    auto step_rows = [&](int t) -> uint32_t {
+        if (t < 0 || t >= tcount) return 0u;
+        const int64_t left = M - (tile_r0(t) + 32 * wave);
+        return left <= 0 ? 0u : (left < 32 ? (uint32_t)left : 32u);
+    };
+    auto x_rsrc = [&](int t) {
+        const uint32_t n = step_rows(t);
+        return n ? rsrc(x + (tile_r0(t) + 32 * wave) * K, n * xrow) : rsrc(x, 0u);
+    };
+
+    // Zero-first as in the amax pass, but with device-scope stores (performed
+    // beyond the caches, like the atomics that follow) and a relaxed arrival
+    // once they are complete: a release here would write back the whole L2.
+    const bool zon = a.zsync.slot >= 0;
+    if (zon && lin < (uint32_t)a.zero.wgs) {
+        const int64_t z0 = (int64_t)lin * kZeroPerWg, z1 = z0 + kZeroPerWg;
+        for (int64_t i = z0 + threadIdx.x; i < z1 && i < a.zero.na + a.zero.nb; i += blockDim.x) {
+            float* p = i < a.zero.na ? a.zero.a + i : a.zero.b + (i - a.zero.na);
+            __hip_atomic_store(p, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) sync_arrive_relaxed(a.zsync);
+    }
+    int zero_state = zon ? 0 : 1;
+    auto zero_ready = [&]() -> bool {
+        if (zero_state == 0) zero_state = sync_wait_wave(a.zsync, (unsigned long long)a.zero.wgs) ? 1 : -1;
+        return zero_state > 0;
+    };
+
+    uint32_t xr = xrow;
+    asm volatile("" : "+s"(xr));   // keeps the 16 row offsets out of vector registers
+
+    // ---------------------------------------------------------- phase A
+    u32x4 v0[16], v1[16];
+    uint32_t cm[4] = {0u, 0u, 0u, 0u};   // column maxima over the run (columns 2k | 2k+1 << 16)
+    uint32_t tm = 0u;                    // tensor maximum (two halves)
+    const int tpad = (tcount + 1) & ~1;
+    {
+        const __amdgpu_buffer_rsrc_t r1 = x_rsrc(tpad - 1), r0 = x_rsrc(tpad - 2);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v1[i] = __builtin_amdgcn_raw_buffer_load_b128(r1, vx, i * xr, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v0[i] = __builtin_amdgcn_raw_buffer_load_b128(r0, vx, i * xr, 0);
+    }
+    // (load: tile t - 2 follows into v; false for the kept tiles 0 and 1)
+    auto amax_step = [&](u32x4(&v)[16], int t, bool load) {
+        const __amdgpu_buffer_rsrc_t nrs = x_rsrc(t - 2);
+        uint32_t rm[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t a0 = abs2(v[i].x), a1 = abs2(v[i].y), a2 = abs2(v[i].z), a3 = abs2(v[i].w);
+            if (COL && TOK) {
+                cm[0] = pk_max_u16(cm[0], a0);
+                cm[1] = pk_max_u16(cm[1], a1);
+                cm[2] = pk_max_u16(cm[2], a2);
+                cm[3] = pk_max_u16(cm[3], a3);
+            }
+            const uint32_t r = pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3));
+            if (TOK) rm[i] = max_halves(r);
+            else tm = pk_max_u16(tm, r);
+            if (load) {
+                uint32_t so = i * xr;
+                asm volatile("" : "+s"(so) : "v"(r), "v"(cm[0]), "v"(cm[1]), "v"(cm[2]), "v"(cm[3]), "v"(tm));
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(nrs, vx, so, 0);
+            }
+        }
+        if (ROWTOK && t < tcount) {
+            uint32_t pair;
+            const int j = half_rowmax16(rm, &pair);
+            if (zero_ready() && (lane & 3) == 0) {
+                const int64_t r = tile_r0(t) + 32 * wave + 16 * rg + 2 * j;
+                if (r < M) atomic_max_mag(a.row_amax + r, pair & 0xffffu);
+                if (r + 1 < M) atomic_max_mag(a.row_amax + r + 1, pair >> 16);
+            }
+        }
+    };
+    // The memory-wait counts the compiler derives across the loop's back
+    // edge are exact only when every pass issues the same loads: the last
+    // pair, which loads nothing, is peeled off.
+#pragma unroll 1
+    for (int t = tpad - 2; t >= 2; t -= 2) {
+        amax_step(v1, t + 1, true);
+        amax_step(v0, t, true);
+    }
+    amax_step(v1, 1, false);
+    amax_step(v0, 0, false);
+    if (COL && TOK) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cm[k] = pk_max_u16(cm[k], (uint32_t)__shfl_xor((int)cm[k], 32));
+        if (lane < 32) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) red[wave][lane][k] = cm[k];
+        }
+    }
+    if (!TOK) {
+        const uint32_t w = wave_max(max_halves(tm));
+        if (lane == 0) red[wave][0][0] = w;
+    }
+    __syncthreads();
+    if (COL && TOK) {
+        // one atomic per column: threads 0..127 take a column pair each
+        if (wave < 2 && zero_ready()) {
+            const int l = threadIdx.x >> 2, k = threadIdx.x & 3;
+            uint32_t m = 0u;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) m = pk_max_u16(m, red[w][l][k]);
+            const uint32_t c = strip * kEncCols + l * 8 + 2 * k;
+            if (c < K) {
+                atomic_max_mag(a.col_amax + c, m & 0xffffu);
+                atomic_max_mag(a.col_amax + c + 1, m >> 16);
+            }
+        }
+    }
+    if (!TOK && wave == 0 && zero_ready() && threadIdx.x == 0) {
+        uint32_t m = 0u;
+        for (int w = 0; w < 8; ++w) m = m > red[w][0][0] ? m : red[w][0][0];
+        if (ROW) atomic_max_mag(a.row_amax, m);
+        if (COL) atomic_max_mag(a.col_amax, m);
+    }
+
+    // ------------------------------------------------ grid-wide wait
+    // Every wave's atomics are complete before its workgroup arrives (they
+    // are performed beyond the caches, so no release is needed: one would
+    // write back the whole L2, per workgroup).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        sync_arrive_relaxed(a.bar);
+        bar_ok = sync_poll(a.bar, gridDim.x) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!bar_ok) return;
+
+    // ---------------------------------------------------------- phase B
+    // outer scales: the strip's columns (per token, in LDS) or the tensor's
+    // (all loads issued before any is used: one memory round trip)
+    bool col_slow = false;
+    float rowA_t = 0.0f, colA_t = 0.0f;
+    Outer rowO_t{1.0f, 1.0f, false}, colO_t{1.0f, 1.0f, false};
+    {
+        const uint32_t c = strip * kEncCols + (threadIdx.x & (kEncCols - 1));
+        const float ca = (COL_LDS && threadIdx.x < kEncCols && c < K) ? load_coherent(a.col_amax + c) : 0.0f;
+        constexpr int kPer = ROWTOK ? kResMaxRun * kEncRows / 512 : 1;
+        float ba[kPer];
+        const int64_t b0 = tile_r0(0);
+        const int64_t nb = M - b0 < (int64_t)tcount * kEncRows ? M - b0 : (int64_t)tcount * kEncRows;
+        if (ROWTOK) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int64_t i = threadIdx.x + 512 * k;
+                ba[k] = i < nb ? load_coherent(a.row_amax + b0 + i) : 0.0f;
+            }
+        }
+        if (!TOK) {
+            if (ROW) rowA_t = load_coherent(a.row_amax);
+            if (COL) colA_t = load_coherent(a.col_amax);
+        }
+        bool sl = false;
+        if (COL_LDS && threadIdx.x < kEncCols) {
+            const Outer o = make_outer(ca, c < K);
+            col_scale[threadIdx.x] = make_float2(o.S, o.yS);
+            sl = o.slow;
+        }
+        if (ROWTOK) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                if (threadIdx.x + 512 * k < nb) band_amax[threadIdx.x + 512 * k] = ba[k];
+        }
+        col_slow = __syncthreads_or(sl) != 0;
+    }
+    if (!TOK) {
+        rowO_t = make_outer(rowA_t, ROW);
+        colO_t = make_outer(colA_t, COL);
+    }
+    const bool tensor_slow = !TOK && ((ROW && rowO_t.slow) || (COL && colO_t.slow));
+    // the calibration update: one workgroup reduces the finished amax
+    if (a.cal.buf != nullptr && lin == 0u) {
+        wg_accumulate_reduce_coherent(a.cal.buf, a.cal.obs, a.cal.n, a.cal.decay, &row_scale[0][0][0]);
+        __syncthreads();
+    }
+
+    const uint32_t vq = col_ok ? 16u * rg * qrow + c0 / 2u : kOffOut;
+    const uint32_t vs = col_ok ? (16u * rg + (odd ? 1u : 0u)) * srow + c0 / 16u : kOffOut;
+    const uint32_t own_sel = odd ? 0x03020c0cu : 0x01000c0cu;
+    uint32_t slow_mask = 0u;   // tiles of the run this wave must encode again (run <= 32)
+
+    // Columnwise output goes straight to memory (no LDS staging, so phase B
+    // has no workgroup barrier): a lane's 8 columns x 16 rows are 8 bytes of
+    // data and one scale byte per column; the lane part of each offset is
+    // fixed, the tile and column parts are scalar.  Lanes l and l + 32 write
+    // adjacent halves of 16 bytes, the 8 waves a tile's 128 bytes of each
+    // column, merged in the L2 (ordinary stores: nontemporal ones reach
+    // memory in pieces and measured slower).
+    const __amdgpu_buffer_rsrc_t cq_rs = rsrc(a.col_q, COL ? (uint32_t)(M / 2 * K) : 0u);
+    const __amdgpu_buffer_rsrc_t cs_rs = rsrc(a.col_sf, COL ? (uint32_t)(M / 16 * K) : 0u);
+    const uint32_t vcq = col_ok ? c0 * (uint32_t)(M / 2) + (32u * wave + 16u * rg) / 2u : kOffOut;
+    const uint32_t vcs = col_ok ? c0 * (uint32_t)(M / 16) + (32u * wave + 16u * rg) / 16u : kOffOut;
+    const uint32_t mq = (uint32_t)(M / 2), ms = (uint32_t)(M / 16);
+
+    auto enc_step = [&](u32x4(&v)[16], int t) {
+        const int64_t wr0 = tile_r0(t) + 32 * wave;
+        const uint32_t nrows = step_rows(t);
+        const bool group_ok = 16u * rg < nrows;
+        const int64_t r0 = group_ok ? wr0 + 16 * rg : wr0;
+        uint32_t qr = qrow, sr = srow;
+        asm volatile("" : "+s"(qr), "+s"(sr));
+        SubDst d;
+        d.row_q = a.row_q + r0 * (K / 2);
+        d.row_sf = a.row_sf + r0 * (K / 16);
+        d.col_q = nullptr;
+        d.col_sf = nullptr;
+        d.row_q_stride = qrow;
+        d.row_sf_stride = srow;
+        d.col_q_stride = (uint32_t)(M / 2);
+        d.col_sf_stride = (uint32_t)(M / 16);
+        d.c0 = c0;
+        d.nrows = group_ok ? (int)(nrows - 16u * rg < 16u ? nrows - 16u * rg : 16u) : 0;
+        d.col_ok = col_ok && group_ok;
+        d.odd = odd;
+        d.lds_q = nullptr;
+        d.lds_sf = nullptr;
+        // the sub-block's columnwise offsets (16-row groups past the end store nothing)
+        const uint32_t tq = (uint32_t)(tile_r0(t) / 2), ts = (uint32_t)(tile_r0(t) / 16);
+        const uint32_t lq = group_ok ? vcq : kOffOut, ls = group_ok ? vcs : kOffOut;
+
+        // rowwise outer scales of the step's rows: lanes 0..31 one row each
+        bool step_slow = tensor_slow;
+        if (ROWTOK) {
+            const bool row_in = (uint32_t)(lane & 31) < nrows;
+            const Outer o = make_outer(row_in ? band_amax[t * kEncRows + 32 * wave + (lane & 31)] : 0.0f, row_in);
+            if (lane < 32) {
+                row_scale[wave][lane][0] = o.S;
+                row_scale[wave][lane][1] = o.yS;
+            }
+            step_slow |= __builtin_amdgcn_ballot_w64(o.slow) != 0ull;
+            // other lanes read these entries below: keep the reads after the writes
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+
+        // maxima from the packed words
+        bool slow = col_slow;
+        uint32_t bcm[4] = {0u, 0u, 0u, 0u};   // column block maxima (columns 2k | 2k+1 << 16)
+        uint32_t bm[8];                        // rowwise block max of the own row of pair s
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            uint32_t rw[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 w = v[2 * s + h];
+                const uint32_t a0 = abs2(w.x), a1 = abs2(w.y), a2 = abs2(w.z), a3 = abs2(w.w);
+                if (COL) {
+                    bcm[0] = pk_max_u16(bcm[0], a0);
+                    bcm[1] = pk_max_u16(bcm[1], a1);
+                    bcm[2] = pk_max_u16(bcm[2], a2);
+                    bcm[3] = pk_max_u16(bcm[3], a3);
+                }
+                rw[h] = pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3));
+            }
+            if (ROW) {
+                uint32_t m = pk_max_u16(__builtin_amdgcn_perm(rw[1], rw[0], 0x05040100u),
+                                        __builtin_amdgcn_perm(rw[1], rw[0], 0x07060302u));
+                m = pk_max_u16(m, from_pair(m));
+                bm[s] = __builtin_amdgcn_perm(m, m, own_sel);
+            }
+        }
+        if (ROW)
+            asm volatile("" : "+v"(bm[0]), "+v"(bm[1]), "+v"(bm[2]), "+v"(bm[3]),
+                         "+v"(bm[4]), "+v"(bm[5]), "+v"(bm[6]), "+v"(bm[7]));
+        FastBlock cb[8];
+        if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t bits = (j & 1) ? (bcm[j >> 1] & 0xffff0000u) : (bcm[j >> 1] << 16);
+                Outer o = colO_t;
+                if (COL_LDS) {
+                    const float2 sy = col_scale[(lane & 31) * 8 + j];
+                    o.S = sy.x;
+                    o.yS = sy.y;
+                }
+                cb[j] = fast_block<false>(bits, o);
+                slow |= cb[j].slow;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)cb[j].code, cs_rs, ls, ts + j * ms, 0);
+            }
+        }
+
+        // per row pair: rowwise parameters, then both encodings
+        const __amdgpu_buffer_rsrc_t q_rs = rsrc(a.row_q + wr0 * (K / 2), nrows * qrow);
+        const __amdgpu_buffer_rsrc_t s_rs = rsrc(a.row_sf + wr0 * (K / 16), nrows * srow);
+        uint32_t cq[8][2] = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int i = 2 * s;
+            float yh0 = 0.0f, yl0 = 0.0f, yh1 = 0.0f, yl1 = 0.0f;
+            if (ROW) {
+                Outer ro = rowO_t;
+                if (ROWTOK) {
+                    ro.S = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][0];
+                    ro.yS = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][1];
+                }
+                const FastBlock f = fast_block<false>(bm[s], ro);
+                slow |= f.slow;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs, i * sr, 0);
+                yh0 = from_even(f.yh); yl0 = from_even(f.yl);
+                yh1 = from_odd(f.yh);  yl1 = from_odd(f.yl);
+            }
+            // pair s is unpacked only after pair s-1's outputs are done
+            u32x4 w0 = v[i], w1 = v[i + 1];
+            if (COL && s > 0)
+                asm volatile("" : "+v"(w0), "+v"(w1), "+v"(cq[0][(s - 1) >> 2]), "+v"(cq[1][(s - 1) >> 2]),
+                             "+v"(cq[2][(s - 1) >> 2]), "+v"(cq[3][(s - 1) >> 2]), "+v"(cq[4][(s - 1) >> 2]),
+                             "+v"(cq[5][(s - 1) >> 2]), "+v"(cq[6][(s - 1) >> 2]), "+v"(cq[7][(s - 1) >> 2]));
+            else
+                asm volatile("" : "+v"(w0), "+v"(w1));
+            const float a0[8] = {bf_lo(w0.x), bf_hi(w0.x), bf_lo(w0.y), bf_hi(w0.y),
+                                 bf_lo(w0.z), bf_hi(w0.z), bf_lo(w0.w), bf_hi(w0.w)};
+            const float a1[8] = {bf_lo(w1.x), bf_hi(w1.x), bf_lo(w1.y), bf_hi(w1.y),
+                                 bf_lo(w1.z), bf_hi(w1.z), bf_lo(w1.w), bf_hi(w1.w)};
+            if (COL) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float q0 = quot2(a0[j], cb[j].yh, cb[j].yl), q1 = quot2(a1[j], cb[j].yh, cb[j].yl);
+                    uint32_t& w = cq[j][s >> 2];
+                    if ((s & 3) == 0) w = put_fp4x2<0>(__float_as_uint(q0), q0, q1);
+                    else if ((s & 3) == 1) w = put_fp4x2<1>(w, q0, q1);
+                    else if ((s & 3) == 2) w = put_fp4x2<2>(w, q0, q1);
+                    else w = put_fp4x2<3>(w, q0, q1);
+                }
+            }
+            uint32_t o0 = 0u, o1 = 0u;
+            if (ROW) {
+                const float p00 = quot2(a0[0], yh0, yl0), p10 = quot2(a1[0], yh1, yl1);
+                o0 = put_fp4x2<0>(__float_as_uint(p00), p00, quot2(a0[1], yh0, yl0));
+                o0 = put_fp4x2<1>(o0, quot2(a0[2], yh0, yl0), quot2(a0[3], yh0, yl0));
+                o0 = put_fp4x2<2>(o0, quot2(a0[4], yh0, yl0), quot2(a0[5], yh0, yl0));
+                o0 = put_fp4x2<3>(o0, quot2(a0[6], yh0, yl0), quot2(a0[7], yh0, yl0));
+                o1 = put_fp4x2<0>(__float_as_uint(p10), p10, quot2(a1[1], yh1, yl1));
+                o1 = put_fp4x2<1>(o1, quot2(a1[2], yh1, yl1), quot2(a1[3], yh1, yl1));
+                o1 = put_fp4x2<2>(o1, quot2(a1[4], yh1, yl1), quot2(a1[5], yh1, yl1));
+                o1 = put_fp4x2<3>(o1, quot2(a1[6], yh1, yl1), quot2(a1[7], yh1, yl1));
+                __builtin_amdgcn_raw_buffer_store_b32(o0, q_rs, vq, i * qr, kCacheNT);
+                __builtin_amdgcn_raw_buffer_store_b32(o1, q_rs, vq, (i + 1) * qr, kCacheNT);
+            }
+        }
+        if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{cq[j][0], cq[j][1]}, cq_rs, lq, tq + j * mq, 0);
+        }
+        // a block outside the fast path's range: the sub-block is encoded
+        // again, exactly, after the last tile
+        if ((step_slow || __builtin_amdgcn_ballot_w64(slow) != 0ull) && t < tcount) slow_mask |= 1u << t;
+        // tile t + 2 into this register set, encoded two steps on (past the
+        // run: an empty buffer, zeros without a memory access; issued either
+        // way so that every step issues the same loads)
+        {
+            const __amdgpu_buffer_rsrc_t nx_rs = x_rsrc(t + 2);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(nx_rs, vx, i * xr, kCacheNT);
+        }
+        // the next step's row scales overwrite entries other lanes read above
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // whole pairs in the loop (every pass issues the same loads), then the
+    // odd tile
+#pragma unroll 1
+    for (int t = 0; t + 1 < tcount; t += 2) {
+        enc_step(v0, t);
+        enc_step(v1, t + 1);
+    }
+    if (tcount & 1) enc_step(v0, tcount - 1);
+
+    // Exact pass over the flagged steps (by the lanes that stored them: a
+    // wave's stores to one address land in order).
+    while (slow_mask != 0u) {
+        const int t = __builtin_ctz(slow_mask);
+        slow_mask &= slow_mask - 1u;
+        const uint32_t nrows = step_rows(t);
+        const bool group_ok = 16u * rg < nrows;
+        const int64_t r0 = tile_r0(t) + 32 * wave + (group_ok ? 16 * rg : 0);
+        SubDst d;
+        d.row_q = a.row_q + r0 * (K / 2);
+        d.row_sf = a.row_sf + r0 * (K / 16);
+        d.col_q = a.col_q + r0 / 2;
+        d.col_sf = a.col_sf + r0 / 16;
+        d.row_q_stride = qrow;
+        d.row_sf_stride = srow;
+        d.col_q_stride = (uint32_t)(M / 2);
+        d.col_sf_stride = (uint32_t)(M / 16);
+        d.c0 = c0;
+        d.nrows = group_ok ? (int)(nrows - 16u * rg < 16u ? nrows - 16u * rg : 16u) : 0;
+        d.col_ok = col_ok && group_ok;
+        d.odd = odd;
+        d.lds_q = nullptr;
+        d.lds_sf = nullptr;
+        float rowA[16], colA[8];
+        for (int i = 0; i < 16; ++i)
+            rowA[i] = !ROW ? 0.0f : !TOK ? rowA_t : (i < d.nrows ? load_coherent(a.row_amax + r0 + i) : 0.0f);
+        for (int j = 0; j < 8; ++j)
+            colA[j] = !COL ? 0.0f : !TOK ? colA_t : (col_ok ? load_coherent(a.col_amax + c0 + j) : 0.0f);
+        encode_exact<ROW, COL, false, false, false>(x + r0 * K, K, rowA, colA, 0.0f, d);
+    }
+}
+
 // --------------------------------------------------------- decayed maximum
 
 __global__ void k_accumulate(float* __restrict__ buf, const float* __restrict__ obs, int64_t n, float decay) {
@@ -1363,6 +1903,49 @@ hipError_t launch_accumulate(float* buf, const float* obs, int64_t n, float deca
 
 hipError_t launch_accumulate_reduce(float* buf, const float* obs, int64_t n, float decay, hipStream_t st) {
     hipLaunchKernelGGL(k_accumulate_reduce, dim3(1), dim3(1024), 0, st, buf, obs, n, decay);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- resident launcher
+
+template <int MODE, bool ROW, bool COL>
+static int resident_blocks_per_cu() {
+    static int cached = -1;
+    if (cached < 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k_resident<MODE, ROW, COL>),
+                                                         512, 0) != hipSuccess)
+            n = 0;
+        cached = n;
+    }
+    return cached;
+}
+
+int resident_blocks_per_cu(int mode, bool row, bool col) {
+    if (mode == ENC_TOKEN) {
+        if (row && col) return resident_blocks_per_cu<ENC_TOKEN, true, true>();
+        if (row) return resident_blocks_per_cu<ENC_TOKEN, true, false>();
+        return resident_blocks_per_cu<ENC_TOKEN, false, true>();
+    }
+    if (row && col) return resident_blocks_per_cu<ENC_TENSOR, true, true>();
+    if (row) return resident_blocks_per_cu<ENC_TENSOR, true, false>();
+    return resident_blocks_per_cu<ENC_TENSOR, false, true>();
+}
+
+hipError_t launch_resident(int mode, bool row, bool col, const ResArgs& a, unsigned grid, hipStream_t st,
+                           hipEvent_t ev0, hipEvent_t ev1) {
+    if (grid == 0 || (!row && !col)) return hipSuccess;
+#define NVFP4_RES_LAUNCH(MD, R, C) hipExtLaunchKernelGGL((k_resident<MD, R, C>), dim3(grid), dim3(512), 0, st, ev0, ev1, 0, a)
+    if (mode == ENC_TOKEN) {
+        if (row && col) NVFP4_RES_LAUNCH(ENC_TOKEN, true, true);
+        else if (row) NVFP4_RES_LAUNCH(ENC_TOKEN, true, false);
+        else NVFP4_RES_LAUNCH(ENC_TOKEN, false, true);
+    } else {
+        if (row && col) NVFP4_RES_LAUNCH(ENC_TENSOR, true, true);
+        else if (row) NVFP4_RES_LAUNCH(ENC_TENSOR, true, false);
+        else NVFP4_RES_LAUNCH(ENC_TENSOR, false, true);
+    }
+#undef NVFP4_RES_LAUNCH
     return hipGetLastError();
 }
 

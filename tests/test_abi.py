@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_symbol():
     L = nv.lib()
     for name in declared():
         assert hasattr(L, name), name
-    assert L.nvfp4_abi_version() == 2
+    assert L.nvfp4_abi_version() == 3
 
 
 def _q(*args):
@@ -191,6 +191,17 @@ def test_trace_encode_validation():
     assert b"trace" in L.nvfp4_last_error()
     assert L.nvfp4_trace_encode(None, P(FAKE)) == EINVAL
     assert L.nvfp4_trace_encode(None, None) == 0   # cancels; nothing pending
+
+
+def test_set_schedule_validation():
+    L = nv.lib()
+    assert L.nvfp4_set_schedule(3) == EINVAL
+    assert b"schedule" in L.nvfp4_last_error()
+    assert L.nvfp4_set_schedule(-1) == EINVAL
+    for v in (1, 2, 0):   # ends on the default
+        assert L.nvfp4_set_schedule(v) == 0
+    with pytest.raises(ValueError):
+        nv.set_schedule("fastest")
 
 
 def test_grouped_validation():

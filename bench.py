@@ -46,6 +46,7 @@ if ROOT not in sys.path:
 M, K = 16384, 8192
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_F16_TFS = 2500.0   # dense fp16/bf16 matrix-core peak
+PEAK_MFMA_FP4_TFS = 10100.0   # MI355X dense FP4 MFMA
 
 
 def algorithmic_bytes(M, K):
@@ -170,12 +171,14 @@ def all_configs(steps, warmup, only=None, schedule="auto"):
         it is one resident launch), from the events nvfp4_trace_encode has the
         launch itself record: device time alone, without the host's share of
         back-to-back calls."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-        for i, (a, b) in enumerate(evs):
-            nv.trace_encode(a, b)
+        evs = TimingEvents(calls)
+        for i in range(calls):
+            nv.trace_encode(*evs.pairs[i])
             fn(i % n_inputs)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) * 1e3 / calls
+        us = sum(evs.elapsed_ms(i) for i in range(calls)) * 1e3 / calls
+        evs.close()
+        return us
 
     def report(name, desc, us, nbytes, launch=None):
         gbs = nbytes / (us * 1e-6) / 1e9
@@ -190,10 +193,16 @@ def all_configs(steps, warmup, only=None, schedule="auto"):
         print(json.dumps(line), flush=True)
 
     def report_mfma(name, desc, us, flops):
+        # frac_of_peak: against the dense fp16 MFMA peak the kernel runs on
+        # (it dequantizes both operands to fp16 in LDS); frac_of_fp4_peak:
+        # against the dense FP4 MFMA peak, which this block format cannot use
+        # directly (gfx950's scaled FP4 MFMA takes one power-of-two scale per
+        # 32 elements, NVFP4 one E4M3 scale per 16)
         tfs = flops / (us * 1e-6) / 1e12
         print(json.dumps({"config": name, "workload": desc, "us_per_call": round(us, 2), "flops": flops,
                           "TFLOP_per_s": round(tfs, 1), "frac_of_peak": round(tfs / PEAK_MFMA_F16_TFS, 4),
-                          "peak": "dense fp16/bf16 MFMA"}), flush=True)
+                          "peak": "dense fp16/bf16 MFMA",
+                          "frac_of_fp4_peak": round(tfs / PEAK_MFMA_FP4_TFS, 4)}), flush=True)
 
     def cast_bytes(m, k, amax_floats):
         return 2 * m * k + m * k + m * k // 8 + 4 * amax_floats

@@ -148,6 +148,18 @@ typedef enum {
 NVFP4_API nvfp4_status nvfp4_set_schedule(nvfp4_schedule schedule);
 
 /*
+ * Testing hook for the failure path of the cross-workgroup waits: the next
+ * launch on this process that waits on other workgroups gets an arrival
+ * target no launch reaches, so each of its waits gives up at its bound
+ * (about 0.2 s per waiting wave group, all in parallel) and the kernel
+ * finishes without the work that depended on them.  That call returns
+ * NVFP4_OK (its outputs are invalid); the next call on the device that
+ * launches such a kernel returns NVFP4_EDEVICE once; calls after it are
+ * normal.  Process-wide, one-shot; not for production use.
+ */
+NVFP4_API nvfp4_status nvfp4_test_fail_next_wait(void);
+
+/*
  * Whole cast, one read of x serving both directions.  Pass NULL for all three
  * pointers of a direction that is not wanted (at least one must be wanted).
  * PER_TENSOR / PER_TOKEN follow the Description of the per-token recipe page;

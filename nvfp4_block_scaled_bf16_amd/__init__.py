@@ -32,7 +32,8 @@ EXPORTS = ("nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize", "nvfp4_qua
            "nvfp4_dequantize", "nvfp4_amax_accumulate", "nvfp4_amax_accumulate_reduce",
            "nvfp4_trace_encode", "nvfp4_quantize_calibrate", "nvfp4_quantize_sr", "nvfp4_gemm",
            "nvfp4_gemm_grouped", "nvfp4_quantize_rht", "nvfp4_swizzle_scales",
-           "nvfp4_gemm_swizzled", "nvfp4_quantize_swizzled", "nvfp4_set_schedule")
+           "nvfp4_gemm_swizzled", "nvfp4_quantize_swizzled", "nvfp4_set_schedule",
+           "nvfp4_test_fail_next_wait")
 
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EALIGN", 4: "EDEVICE"}
 
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_quantize_swizzled": (st, [p, i64, i64, st, p, p, p, p, p, p, p]),
         "nvfp4_gemm_swizzled": (st, [p, p, p, ctypes.c_int, p, p, p, ctypes.c_int, i64, i64, i64, p, p]),
         "nvfp4_set_schedule": (st, [st]),
+        "nvfp4_test_fail_next_wait": (st, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

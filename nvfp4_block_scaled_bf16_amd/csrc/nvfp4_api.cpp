@@ -112,6 +112,9 @@ struct DeviceState {
 };
 std::mutex g_dev_mu;
 std::vector<DeviceState> g_dev;
+// nvfp4_test_fail_next_wait: the next slot handed out gets a base no launch
+// reaches (its waits give up at their bound)
+std::atomic<bool> g_fail_next_wait{false};
 
 nvfp4_status stream_device(hipStream_t st, int* dev) {
     hipError_t e = st ? hipStreamGetDevice(st, dev) : hipGetDevice(dev);
@@ -190,6 +193,7 @@ nvfp4_status sync_take(hipStream_t st, uint64_t arrivals, SyncTicket* t) {
     const int slot = (int)(d->next_slot++ % kSyncSlots);
     t->arg.slot = slot;
     t->arg.base = d->slot_count[slot];
+    if (g_fail_next_wait.exchange(false)) t->arg.base += (uint64_t)1 << 40;
     t->arg.err = d->err_dev;
     t->dev = dev;
     t->arrivals = arrivals;
@@ -446,6 +450,11 @@ nvfp4_status nvfp4_trace_encode(void* before, void* after) {
     if ((before == nullptr) != (after == nullptr)) return fail(NVFP4_EINVAL, "give both trace events or neither");
     g_trace_before = static_cast<hipEvent_t>(before);
     g_trace_after = static_cast<hipEvent_t>(after);
+    return ok();
+}
+
+nvfp4_status nvfp4_test_fail_next_wait(void) {
+    g_fail_next_wait.store(true);
     return ok();
 }
 

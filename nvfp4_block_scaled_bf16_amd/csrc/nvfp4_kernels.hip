@@ -335,6 +335,14 @@ __device__ __forceinline__ float elem(const u32x4& w, int k) {
     return (k & 1) ? bf_hi(word) : bf_lo(word);
 }
 
+// the same for a k known only at run time: the word is picked first and
+// then shifted by an amount that depends on k, so that a loop over k does
+// not get all eight unpacked values of every word hoisted out of it
+__device__ __forceinline__ float elem_rt(const u32x4& w, int k) {
+    const uint32_t word = (k >> 1) == 0 ? w.x : (k >> 1) == 1 ? w.y : (k >> 1) == 2 ? w.z : w.w;
+    return __uint_as_float((word >> (16 * (k & 1))) << 16);
+}
+
 // Byte offset of scale (r, c) in the GEMM-swizzled layout of a scale matrix
 // with nbp (a multiple of 4) blocks per row: 512-byte tiles of 128 rows x 4
 // blocks, row-tile major; row r in 16-byte line r % 32 at 4-byte slot
@@ -1034,7 +1042,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
         const uint32_t h0 = (uint32_t)(p0 >> 32), l0 = (uint32_t)p0;
         const uint32_t h1 = (uint32_t)(p1 >> 32), l1 = (uint32_t)p1;
-        const uint32_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
+        // each three-way xor as one v_bitop3_b32 (truth table 0x96)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32(h1, c1, k0, 0x96), n2 = __builtin_amdgcn_bitop3_b32(h0, c3, k1, 0x96);
         c0 = n0;
         c1 = l1;
         c2 = n2;
@@ -1047,28 +1056,25 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2 below 6) and
 // rounds up iff x - lo > U * d with U = (rnd >> 8) * 2^-24; both sides are
 // exact in binary32.  x >= 6 saturates; the sign bit of q is copied.
+// Without branches, from the bit pattern of x: at or above 1, lo keeps x's
+// exponent and first mantissa bit, d is half its binade and the code is
+// lo's top 10 bits less 252 (1 -> 2, 1.5 -> 3, ..., 4 -> 6); below 1, lo is
+// 0.5 or 0 (codes 1, 0) and d is 0.5.  U * d is formed as (rnd >> 8) times
+// the power of two d * 2^-24.  (tests/native/sr_round_check.c compares
+// this form with the oracle's rule over every fp32 q.)
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t rnd) {
-    const uint32_t s = (__float_as_uint(q) >> 28) & 8u;
-    const float x = __builtin_fabsf(q);
-    if (x >= 6.0f) return s | 7u;
-    float lo, d;
-    uint32_t c;
-    if (x < 2.0f) {
-        c = (uint32_t)(2.0f * x);   // truncation: floor of a non-negative value
-        lo = 0.5f * (float)c;
-        d = 0.5f;
-    } else if (x < 4.0f) {
-        const bool three = x >= 3.0f;
-        lo = three ? 3.0f : 2.0f;
-        c = three ? 5u : 4u;
-        d = 1.0f;
-    } else {
-        lo = 4.0f;
-        c = 6u;
-        d = 2.0f;
-    }
-    const float u = (float)(rnd >> 8) * 0x1p-24f;
-    return s | (c + (x - lo > u * d ? 1u : 0u));
+    const uint32_t b = __float_as_uint(q);
+    const uint32_t s = (b >> 28) & 8u;
+    const uint32_t xb = b & 0x7fffffffu;
+    const bool ge1 = xb >= 0x3f800000u;
+    const uint32_t half = xb >= 0x3f000000u ? 0x3f000000u : 0u;
+    const uint32_t lob = ge1 ? (xb & 0xffc00000u) : half;
+    const uint32_t db24 = ge1 ? (xb & 0x7f800000u) - (25u << 23) : 0x33000000u;   // d * 2^-24
+    const uint32_t c = ge1 ? (lob >> 22) - 252u : (half >> 29);
+    const float diff = __uint_as_float(xb) - __uint_as_float(lob);
+    const float ud = (float)(rnd >> 8) * __uint_as_float(db24);
+    const uint32_t r = c + (diff > ud ? 1u : 0u);
+    return s | (xb >= 0x40c00000u ? 7u : r);
 }
 
 // Whether every lane's block of the wave can take the three-op quotient:
@@ -1105,10 +1111,13 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
     if (ROW) {
         const float At = MODE == ENC_TENSOR ? row_amax[0] : 0.0f;
         // rows one at a time (a rolled loop over a register array would put
-        // the array in scratch memory)
+        // the array in scratch memory), the next row's load issued before
+        // this one is encoded
+        u32x4 vnext = load_row(0);
 #pragma unroll 1
         for (int i = 0; i < 16; ++i) {
-            const u32x4 vi = load_row(i);
+            const u32x4 vi = vnext;
+            if (i + 1 < 16) vnext = load_row(i + 1);
             uint32_t hw = rowmax_word(vi);
             hw = pk_max_u16(hw, from_pair(hw));   // the lane pair's 16 columns
             const float A = MODE == ENC_TENSOR ? At : (i < nrows ? row_amax[r0 + i] : 0.0f);
@@ -1141,28 +1150,42 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
             uint32_t m = 0u;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint32_t e = (__float_as_uint(elem(v[i], j)) >> 16) & 0x7fffu;
+                const uint32_t e = (__float_as_uint(elem_rt(v[i], j)) >> 16) & 0x7fffu;
                 m = e > m ? e : m;
             }
             const float A = MODE == ENC_TENSOR ? col_amax[0] : (col_ok ? col_amax[c0 + j] : 0.0f);
             const BlockScale bs = block_scale(m, outer_scale(A));
             const uint32_t vec = c0 + (uint32_t)j, g0 = (uint32_t)(r0 >> 2);
-            uint32_t rnd[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
-                rnd[4 * g] = r.x; rnd[4 * g + 1] = r.y; rnd[4 * g + 2] = r.z; rnd[4 * g + 3] = r.w;
-            }
+            // one Philox block (four words) per four rows, each used as soon
+            // as it is drawn, so that at most one block is live
             uint32_t lohi[2] = {0u, 0u};
             if (sr_fast(bs)) {
                 const float y = rcp_rn(bs.r);
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    lohi[i >> 3] |= e2m1_sr(div_fast(elem(v[i], j), bs.r, y), rnd[i]) << (4 * (i & 7));
+                for (int g = 0; g < 4; ++g) {
+                    const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
+                    const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int i = 4 * g + k;
+                        lohi[i >> 3] |= e2m1_sr(div_fast(elem_rt(v[i], j), bs.r, y), rr[k]) << (4 * (i & 7));
+                        // one element at a time: the rounding has no branches,
+                        // and sixteen of it in flight would cost registers
+                        asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
+                    }
+                }
             } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    lohi[i >> 3] |= e2m1_sr(quotient_exact(elem(v[i], j), bs), rnd[i]) << (4 * (i & 7));
+                for (int g = 0; g < 4; ++g) {
+                    const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
+                    const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int i = 4 * g + k;
+                        lohi[i >> 3] |= e2m1_sr(quotient_exact(elem_rt(v[i], j), bs), rr[k]) << (4 * (i & 7));
+                        asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
+                    }
+                }
             }
             if (col_ok && nrows == 16) {
                 *reinterpret_cast<u32x2*>(col_q + (int64_t)(c0 + j) * (M / 2) + r0 / 2) = u32x2{lohi[0], lohi[1]};

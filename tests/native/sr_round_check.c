@@ -1,0 +1,86 @@
+/* The stochastic E2M1 rounding of the SR encoding kernel (nvfp4_kernels.hip,
+ * e2m1_sr: a branch-free form on the bits of |q|) against the oracle's rule
+ * (orc_e2m1_encode_sr), for every fp32 bit pattern q that is not a NaN, each
+ * with a random word drawn from a hash of q.  The two forms compute the same
+ * two exact binary32 values x - lo and U*d wherever they pick the same (lo, d,
+ * code), so one random word per q checks the pick; the hash still varies
+ * which side of the threshold each q falls.  Prints "<n> checked, <m>
+ * mismatches". */
+#include <pthread.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+uint8_t orc_e2m1_encode_sr(float q, uint32_t rnd);
+
+static float f_of(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+
+/* the kernel's form, transcribed */
+static uint32_t kernel_sr(float q, uint32_t rnd)
+{
+    uint32_t b;
+    memcpy(&b, &q, 4);
+    const uint32_t s = (b >> 28) & 8u;
+    const uint32_t xb = b & 0x7fffffffu;
+    const int ge1 = xb >= 0x3f800000u;
+    const uint32_t half = xb >= 0x3f000000u ? 0x3f000000u : 0u;
+    const uint32_t lob = ge1 ? (xb & 0xffc00000u) : half;
+    const uint32_t db24 = ge1 ? (xb & 0x7f800000u) - (25u << 23) : 0x33000000u;
+    const uint32_t c = ge1 ? (lob >> 22) - 252u : (half >> 29);
+    const float diff = f_of(xb) - f_of(lob);
+    const float ud = (float)(rnd >> 8) * f_of(db24);
+    const uint32_t r = c + (diff > ud ? 1u : 0u);
+    return s | (xb >= 0x40c00000u ? 7u : r);
+}
+
+static uint32_t hash(uint32_t x)
+{
+    x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+    return x;
+}
+
+#define NT 8
+static uint64_t bad[NT], seen[NT];
+
+static void* work(void* arg)
+{
+    const int t = (int)(intptr_t)arg;
+    for (uint64_t i = (uint64_t)t; i < ((uint64_t)1 << 32); i += NT) {
+        const uint32_t b = (uint32_t)i;
+        if ((b & 0x7fffffffu) > 0x7f800000u) continue;   /* NaN */
+        const float q = f_of(b);
+        const uint32_t rnd = hash(b);
+        ++seen[t];
+        if (kernel_sr(q, rnd) != orc_e2m1_encode_sr(q, rnd)) {
+            if (bad[t] < 3) printf("mismatch q=%08x rnd=%08x kernel %u oracle %u\n", b, rnd, kernel_sr(q, rnd),
+                                   orc_e2m1_encode_sr(q, rnd));
+            ++bad[t];
+        }
+    }
+    return NULL;
+}
+
+int main(void)
+{
+    pthread_t th[NT];
+    for (int t = 0; t < NT; ++t) pthread_create(&th[t], NULL, work, (void*)(intptr_t)t);
+    uint64_t n = 0, m = 0;
+    for (int t = 0; t < NT; ++t) {
+        pthread_join(th[t], NULL);
+        n += seen[t];
+        m += bad[t];
+    }
+    /* the extremes of the random word at the grid's midpoints and ends */
+    const float pts[] = {0.0f, 0.25f, 0.5f, 0.75f, 1.0f, 1.25f, 1.5f, 1.75f, 2.0f, 2.5f, 3.0f, 3.5f, 4.0f, 5.0f, 6.0f,
+                         5.9999995f, 1.9999999f, 0.49999997f, 0.99999994f};
+    const uint32_t rs[] = {0u, 0xffu, 0x100u, 0x7fffffffu, 0x80000000u, 0xffffff00u, 0xffffffffu};
+    for (size_t i = 0; i < sizeof pts / sizeof pts[0]; ++i)
+        for (size_t j = 0; j < sizeof rs / sizeof rs[0]; ++j)
+            for (int sg = 0; sg < 2; ++sg) {
+                const float q = sg ? -pts[i] : pts[i];
+                ++n;
+                if (kernel_sr(q, rs[j]) != orc_e2m1_encode_sr(q, rs[j])) ++m;
+            }
+    printf("%llu checked, %llu mismatches\n", (unsigned long long)n, (unsigned long long)m);
+    return m != 0;
+}

@@ -15,9 +15,10 @@
 // parameters of the pair's even-numbered loads, the odd lane those of the
 // odd-numbered ones, and DPP hands them across.  Row maxima: lane, then wave
 // (xor exchanges), then the 8 waves through LDS (one barrier per batch); the
-// row scales reach the other lanes by readlane.  Workgroups are persistent:
-// workgroup g takes batches g, g + G, ..., and loads the next batch's rows
-// while it encodes the current one.  x is read with the nontemporal hint:
+// row scales reach the other lanes by readlane.  Workgroup g takes batches
+// g, g + G, ... and loads the next batch's rows while it encodes the current
+// one (the host launches one workgroup per batch unless there are more than
+// 2^20 batches, so that the dispatcher balances the load).  x is read with the nontemporal hint:
 // nothing in the cast reads it again.
 #include <hip/hip_ext.h>
 

@@ -520,13 +520,27 @@ nvfp4_status nvfp4_quantize_rht(const void* xv, int64_t M, int64_t K, nvfp4_scal
     hipStream_t st = as_stream(stream);
     const bool tok = mode == NVFP4_PER_TOKEN;
     float* ra = r.want ? row_amax : nullptr;
-    if ((s = zero(col_amax, tok ? K : 1, ra, ra ? (tok ? M : 1) : 0, st)) != NVFP4_OK) return s;
-    if (M == 0 || K == 0) return ok();
+    const int64_t na = tok ? K : 1, nb = ra ? (tok ? M : 1) : 0;
+    if (M == 0 || K == 0) return (s = zero(col_amax, na, ra, nb, st)) != NVFP4_OK ? s : ok();
+    // the amax launch's first workgroups zero its outputs (a fill launch
+    // instead under stream capture, or when the grid is too small for them)
+    ZeroFirst z{col_amax, na, ra, nb, (int)((na + nb + kZeroPerWg - 1) / kZeroPerWg)};
+    SyncTicket tk;
+    const bool zero_first = z.wgs <= rht_amax_grid_size(M, K) && !capturing(st);
+    if (zero_first) {
+        if ((s = sync_take(st, (uint64_t)z.wgs, &tk)) != NVFP4_OK) return s;
+    } else if ((s = zero(col_amax, na, ra, nb, st)) != NVFP4_OK) {
+        return s;
+    }
     const uint16_t* x = static_cast<const uint16_t*>(xv);
+    bool amax_launched = false;
     s = encode_launch([&](hipEvent_t b, hipEvent_t a) {
         return launch_rht(tok ? ENC_TOKEN : ENC_TENSOR, x, M, K, sign_mask, ra, col_amax, r.want ? row_q : nullptr,
-                          r.want ? row_sf : nullptr, col_q, col_sf, st, b, a);
+                          r.want ? row_sf : nullptr, col_q, col_sf, st, b, a,
+                          zero_first ? z : ZeroFirst{nullptr, 0, nullptr, 0, 0},
+                          zero_first ? tk.arg : SyncArg{0ull, nullptr, -1}, &amax_launched);
     });
+    if (zero_first && !amax_launched) sync_return(tk);
     return s != NVFP4_OK ? s : ok();
 }
 

@@ -93,12 +93,16 @@ hipError_t launch_encode_sr(int mode, bool row, bool col, const uint16_t* x, int
                             uint8_t* col_q, uint8_t* col_sf, uint64_t seed, uint32_t offset, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1);
 // random Hadamard transform + columnwise cast, with the ordinary rowwise cast
-// of x when row_q != nullptr (nvfp4_rht.hip): amax outputs zeroed beforehand
-// ([K] / [M] per token, [1] per tensor); M % 16 == 0, K % 8 == 0 (K % 16 ==
-// 0 with rows)
+// of x when row_q != nullptr (nvfp4_rht.inc): amax outputs ([K] / [M] per
+// token, [1] per tensor) zeroed beforehand, or by the amax launch's first
+// workgroups (zero, sync as for launch_amax); M % 16 == 0, K % 8 == 0 (K %
+// 16 == 0 with rows)
 hipError_t launch_rht(int mode, const uint16_t* x, int64_t M, int64_t K, uint32_t mask, float* row_amax,
                       float* col_amax, uint8_t* row_q, uint8_t* row_sf, uint8_t* col_q, uint8_t* col_sf, hipStream_t st,
-                      hipEvent_t ev0, hipEvent_t ev1);
+                      hipEvent_t ev0, hipEvent_t ev1, const ZeroFirst& zero = ZeroFirst{nullptr, 0, nullptr, 0, 0},
+                      const SyncArg& sync = SyncArg{0ull, nullptr, -1}, bool* amax_launched = nullptr);
+// workgroups of the Hadamard amax launch
+int64_t rht_amax_grid_size(int64_t M, int64_t K);
 // NVFP4 GEMM consumer (nvfp4_gemm.hip): out [M][N] fp32, one workgroup per
 // 128 x 128 output tile, at most kMaxGemmTiles of them
 constexpr int64_t kMaxGemmTiles = (int64_t(1) << 31) - 1;

@@ -1973,3 +1973,7 @@ hipError_t launch_resident(int mode, bool row, bool col, const ResArgs& a, unsig
 }
 
 }  // namespace nvfp4
+
+// The Hadamard-transform cast, in this translation unit for its amax pass's
+// cross-workgroup waits (the counters above).
+#include "nvfp4_rht.inc"

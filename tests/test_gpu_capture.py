@@ -72,3 +72,25 @@ def test_capture_calibrate_replays_accumulate(oracle):
         compare_cast(out, ref)
         ref_buf = oracle.amax_accumulate(ref_buf, A, 0.5)
         assert_bytes_equal(host(buf), ref_buf, f"buf after replay {rep}")
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+def test_capture_rht_replays(oracle, mode):
+    """The Hadamard-transform cast under capture: a fill launch zeroes its
+    amax outputs (no waits), and every replay gives the oracle's result."""
+    M, K, mask = 1072, 544, 0xA5C3
+    x = W.row_scaled_with_outliers(M, K, 1400)
+    _announce(f"capture quantize_rht mode={mode} {M}x{K}")
+    d = to_dev(x)
+    out = Guarded(cast_spec(M, K, mode, True, True))
+    ref = oracle.quantize_rht(x, mode, mask)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.quantize_rht_into(d, mode, mask, **out.views)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _refill(out)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare_cast(out, ref)

@@ -44,3 +44,27 @@ def test_wait_gives_up_and_is_reported(oracle, schedule, shape):
         compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
     finally:
         nv.set_schedule("auto")
+
+
+def test_rht_wait_gives_up_and_is_reported(oracle):
+    """The Hadamard-transform cast's amax pass waits for the workgroups that
+    zero its outputs: forced to give up, it records the failure, the next
+    call reports it, and the call after that is bit-exact."""
+    M, K, mask = 1072, 544, 0x1234
+    print(f"\n[case] forced wait failure, quantize_rht {M}x{K}", flush=True)
+    x = W.row_scaled_with_outliers(M, K, 4343)
+    d = to_dev(x)
+    out = Guarded(cast_spec(M, K, nv.PER_TOKEN, True, True))
+    nv._check(nv.lib().nvfp4_test_fail_next_wait())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    nv.quantize_rht_into(d, nv.PER_TOKEN, mask, **out.views)   # enqueued: OK, outputs invalid
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert 0.15 < dt < 10.0, f"the forced waits took {dt:.3f} s"
+    with pytest.raises(nv.NVFP4Error) as err:
+        nv.quantize_rht_into(d, nv.PER_TOKEN, mask, **out.views)
+    assert err.value.status == 4 and "gave up" in str(err.value)
+    nv.quantize_rht_into(d, nv.PER_TOKEN, mask, **out.views)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_rht(x, nv.PER_TOKEN, mask))

@@ -87,13 +87,6 @@ __device__ __forceinline__ bool sync_poll(const SyncArg& s, unsigned long long n
     return true;
 }
 
-// a wave waits (lane 0 polls); the result is wave-uniform
-__device__ __forceinline__ bool sync_wait_wave(const SyncArg& s, unsigned long long n) {
-    int ok = 1;
-    if ((threadIdx.x & 63) == 0) ok = sync_poll(s, n) ? 1 : 0;
-    return __builtin_amdgcn_readfirstlane(ok) != 0;
-}
-
 // max of non-negative floats through their bit patterns
 __device__ __forceinline__ void atomic_max_mag(float* p, uint32_t mag16) {
     if (mag16 != 0u) atomicMax(reinterpret_cast<uint32_t*>(p), mag16 << 16);
@@ -183,9 +176,9 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     const int64_t c0 = (int64_t)bx * kTileCols + lane * 8;
     const bool col_ok = c0 < K;
     // Zero-first: the first zero.wgs workgroups (dispatched first) clear the
-    // outputs, kZeroPerWg values each, and arrive; each wave waits for them
-    // once, before its first atomic (normally long satisfied: every
-    // workgroup reads its tile first).  A wait that gave up skips the
+    // outputs, kZeroPerWg values each, and arrive.  Every atomic of a
+    // workgroup comes after its loop, behind one wait for those arrivals (one
+    // lane polls, normally long satisfied); a wait that gave up skips the
     // atomics.
     const bool sync_on = sync.slot >= 0;
     if (sync_on && lin < (uint32_t)zero.wgs) {
@@ -197,11 +190,9 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         __syncthreads();
         if (threadIdx.x == 0) sync_arrive(sync);
     }
-    int zero_state = sync_on ? 0 : 1;   // 0: not waited yet, 1: outputs zeroed, -1: the wait gave up
-    auto zero_ready = [&]() -> bool {
-        if (zero_state == 0) zero_state = sync_wait_wave(sync, (unsigned long long)zero.wgs) ? 1 : -1;
-        return zero_state > 0;
-    };
+    // one lane's wait for the zeroing workgroups (true: the outputs hold zeros)
+    auto zeroed = [&]() -> bool { return !sync_on || sync_poll(sync, (unsigned long long)zero.wgs); };
+    __shared__ int zero_ok;
     const int64_t rb = row_begin + (int64_t)by * tile_h + wave * (tile_h / 4);   // tile_h: 64 to 512 rows
     const uint32_t lane_off = col_ok ? (uint32_t)c0 * 2u : kOffOut;
     uint32_t xr = (uint32_t)K * 2u;
@@ -235,6 +226,21 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     // The first 16-row sub-block is loaded here; each row of the next one is
     // loaded into the registers of the same row of the current one as soon as
     // that row's maxima are taken, so one set of data registers suffices.
+    // per-token and grouped: the row-pair maxima of each sub-block of each
+    // wave, combined into row_amax after the loop (thread t: wave t / 64,
+    // sub-block (t / 8) % 8, pair t % 8)
+    constexpr bool kRows = KIND == AMAX_TOKEN || KIND == AMAX_GROUPED;
+    __shared__ uint32_t rowred[kRows ? 4 : 1][kRows ? kAmaxRows / 64 : 1][8];
+    auto flush_rows = [&]() {
+        if (row_amax == nullptr) return;
+        const int t = threadIdx.x, w = t >> 6, si = (t >> 3) & 7, jj = t & 7;
+        const int64_t r0 = row_begin + (int64_t)by * tile_h + w * (tile_h / 4) + 16 * si;
+        if (16 * si < tile_h / 4 && r0 < row_end) {
+            const uint32_t pair = rowred[w][si][jj];
+            if (r0 + 2 * jj < row_end) atomic_max_mag(row_amax + r0 + 2 * jj, pair & 0xffffu);
+            if (r0 + 2 * jj + 1 < row_end) atomic_max_mag(row_amax + r0 + 2 * jj + 1, pair >> 16);
+        }
+    };
     u32x4 v[16];
     if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, v);
 #pragma unroll 1
@@ -266,13 +272,10 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
             asm volatile("" : "+s"(so) : "v"(rm[i]), "v"(cm[0]), "v"(cm[1]), "v"(cm[2]), "v"(cm[3]));
             v[i] = __builtin_amdgcn_raw_buffer_load_b128(nrs, lane_off, so, 0);
         }
-        if ((KIND == AMAX_TOKEN || KIND == AMAX_GROUPED) && row_amax != nullptr) {
+        if (kRows && row_amax != nullptr) {
             uint32_t pair;
-            int j = wave_rowmax16(rm, &pair);
-            if (zero_ready() && (lane & 7) == 0) {
-                if (r0 + 2 * j < row_end) atomic_max_mag(row_amax + r0 + 2 * j, pair & 0xffffu);
-                if (r0 + 2 * j + 1 < row_end) atomic_max_mag(row_amax + r0 + 2 * j + 1, pair >> 16);
-            }
+            const int j = wave_rowmax16(rm, &pair);
+            if ((lane & 7) == 0) rowred[wave][s >> 4][j] = pair;
         }
         if (KIND == AMAX_TENSOR) {
 #pragma unroll
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         __shared__ uint32_t tred[4];
         if (lane == 0) tred[wave] = tm;
         __syncthreads();
-        if (wave == 0 && zero_ready() && threadIdx.x == 0) {
+        if (threadIdx.x == 0 && zeroed()) {
             uint32_t m = tred[0];
             for (int w = 1; w < 4; ++w) m = m > tred[w] ? m : tred[w];
             if (t0) atomic_max_mag(t0, m);
@@ -294,9 +297,11 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     }
     if (KIND == AMAX_GROUPED) {
         if (cur_group >= 0) group_flush(cur_group);
+        if (threadIdx.x == 0) zero_ok = zeroed();
         __syncthreads();
+        if (!zero_ok) return;
+        flush_rows();
         const int64_t tc0 = (int64_t)bx * kTileCols;
-        if (!zero_ready()) return;
         for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) {
             const int slot = i / kTileCols, c = i % kTileCols;
             const int g = gslot[slot];
@@ -305,12 +310,18 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         }
         return;
     }
+    // per token: the four waves' column maxima combined in LDS, then one
+    // atomic per row and per column
     if (col_amax != nullptr) {
-        // combine the four waves' column maxima, then one atomic per column
 #pragma unroll
         for (int k = 0; k < 4; ++k) red[wave][lane][k] = cm[k];
-        __syncthreads();
-        if (wave == 0 && zero_ready() && col_ok) {
+    }
+    if (threadIdx.x == 0) zero_ok = zeroed();
+    __syncthreads();
+    if (!zero_ok) return;
+    flush_rows();
+    if (col_amax != nullptr) {
+        if (wave == 0 && col_ok) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 uint32_t m = pk_max_u16(pk_max_u16(red[0][lane][k], red[1][lane][k]),
@@ -1384,11 +1395,14 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
         __syncthreads();
         if (threadIdx.x == 0) sync_arrive_relaxed(a.zsync);
     }
-    int zero_state = zon ? 0 : 1;
-    auto zero_ready = [&]() -> bool {
-        if (zero_state == 0) zero_state = sync_wait_wave(a.zsync, (unsigned long long)a.zero.wgs) ? 1 : -1;
-        return zero_state > 0;
-    };
+    // Phase A's atomics all come after its loop, behind one wait for the
+    // zeroing workgroups (one lane polls for the workgroup).  Until then the
+    // per-token row-pair maxima of each tile and wave sit in LDS, in the
+    // space band_amax takes after the grid-wide wait: entry (t * 8 + wave) *
+    // 16 + e holds rows 16 (e >> 3) + 2 (e & 7) and the next of the wave's 32.
+    __shared__ int zero_ok;
+    uint32_t* const rowred = reinterpret_cast<uint32_t*>(band_amax);
+    static_assert(!ROWTOK || kResMaxRun * kEncRows >= kResMaxRun * 8 * 16, "row-pair maxima fit in band_amax");
 
     uint32_t xr = xrow;
     asm volatile("" : "+s"(xr));   // keeps the 16 row offsets out of vector registers
@@ -1429,12 +1443,8 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
         }
         if (ROWTOK && t < tcount) {
             uint32_t pair;
-            const int j = half_rowmax16(rm, &pair);
-            if (zero_ready() && (lane & 3) == 0) {
-                const int64_t r = tile_r0(t) + 32 * wave + 16 * rg + 2 * j;
-                if (r < M) atomic_max_mag(a.row_amax + r, pair & 0xffffu);
-                if (r + 1 < M) atomic_max_mag(a.row_amax + r + 1, pair >> 16);
-            }
+            half_rowmax16(rm, &pair);   // lane 4e: pair e & 7 of row group e >> 3
+            if ((lane & 3) == 0) rowred[(t * 8 + wave) * 16 + (lane >> 2)] = pair;
         }
     };
     // The memory-wait counts the compiler derives across the loop's back
@@ -1459,10 +1469,22 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
         const uint32_t w = wave_max(max_halves(tm));
         if (lane == 0) red[wave][0][0] = w;
     }
+    if (threadIdx.x == 0) zero_ok = !zon || sync_poll(a.zsync, (unsigned long long)a.zero.wgs);
     __syncthreads();
+    // (a workgroup whose wait gave up skips the atomics but still arrives
+    // at the grid-wide wait below)
+    if (ROWTOK && zero_ok) {
+        for (int i = threadIdx.x; i < tcount * 128; i += blockDim.x) {
+            const int t = i >> 7, w = (i >> 4) & 7, e = i & 15;
+            const uint32_t pair = rowred[i];
+            const int64_t r = tile_r0(t) + 32 * w + 16 * (e >> 3) + 2 * (e & 7);
+            if (r < M) atomic_max_mag(a.row_amax + r, pair & 0xffffu);
+            if (r + 1 < M) atomic_max_mag(a.row_amax + r + 1, pair >> 16);
+        }
+    }
     if (COL && TOK) {
         // one atomic per column: threads 0..127 take a column pair each
-        if (wave < 2 && zero_ready()) {
+        if (wave < 2 && zero_ok) {
             const int l = threadIdx.x >> 2, k = threadIdx.x & 3;
             uint32_t m = 0u;
 #pragma unroll
@@ -1474,7 +1496,7 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
             }
         }
     }
-    if (!TOK && wave == 0 && zero_ready() && threadIdx.x == 0) {
+    if (!TOK && threadIdx.x == 0 && zero_ok) {
         uint32_t m = 0u;
         for (int w = 0; w < 8; ++w) m = m > red[w][0][0] ? m : red[w][0][0];
         if (ROW) atomic_max_mag(a.row_amax, m);

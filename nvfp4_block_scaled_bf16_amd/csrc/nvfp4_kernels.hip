@@ -193,7 +193,22 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     // one lane's wait for the zeroing workgroups (true: the outputs hold zeros)
     auto zeroed = [&]() -> bool { return !sync_on || sync_poll(sync, (unsigned long long)zero.wgs); };
     __shared__ int zero_ok;
-    const int64_t rb = row_begin + (int64_t)by * tile_h + wave * (tile_h / 4);   // tile_h: 64 to 512 rows
+    // Rows of the workgroup (tile_h: 64 to 512).  Per token, the four row
+    // tiles of a group (by / 4, one strip) share the group's rows so that,
+    // together, they read it from the top down in stripes of 256 rows:
+    // workgroup k = by % 4, wave w, step j take rows 16 (16 j + 4 w + k) ..
+    // + 15 of the group.  At the end of the pass the last-level cache then
+    // holds each group's lower rows most recently, which the encode pass
+    // (walking the tiles backwards) reads first.  Other kinds, and a group
+    // that is not four whole tiles, keep one contiguous tile per workgroup
+    // (wave w: rows w tile_h / 4 ..).
+    const int64_t grp0 = row_begin + (int64_t)(by & ~3u) * tile_h;
+    const bool spread = KIND == AMAX_TOKEN && (by | 3u) < gridDim.y && grp0 + 4 * (int64_t)tile_h <= row_end;
+    const int64_t rstride = spread ? 256 : 16;   // rows from one step of a wave to its next
+    auto wave_row0 = [&](int w) -> int64_t {
+        return spread ? grp0 + 16 * (4 * w + (int)(by & 3u)) : row_begin + (int64_t)by * tile_h + w * (tile_h / 4);
+    };
+    const int64_t rb = wave_row0(wave);
     const uint32_t lane_off = col_ok ? (uint32_t)c0 * 2u : kOffOut;
     uint32_t xr = (uint32_t)K * 2u;
     asm volatile("" : "+s"(xr));   // keeps the 16 row offsets from being held in registers
@@ -223,9 +238,6 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
             cm[k] = 0u;
         }
     };
-    // The first 16-row sub-block is loaded here; each row of the next one is
-    // loaded into the registers of the same row of the current one as soon as
-    // that row's maxima are taken, so one set of data registers suffices.
     // per-token and grouped: the row-pair maxima of each sub-block of each
     // wave, combined into row_amax after the loop (thread t: wave t / 64,
     // sub-block (t / 8) % 8, pair t % 8)
@@ -234,18 +246,21 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     auto flush_rows = [&]() {
         if (row_amax == nullptr) return;
         const int t = threadIdx.x, w = t >> 6, si = (t >> 3) & 7, jj = t & 7;
-        const int64_t r0 = row_begin + (int64_t)by * tile_h + w * (tile_h / 4) + 16 * si;
+        const int64_t r0 = wave_row0(w) + si * rstride;
         if (16 * si < tile_h / 4 && r0 < row_end) {
             const uint32_t pair = rowred[w][si][jj];
             if (r0 + 2 * jj < row_end) atomic_max_mag(row_amax + r0 + 2 * jj, pair & 0xffffu);
             if (r0 + 2 * jj + 1 < row_end) atomic_max_mag(row_amax + r0 + 2 * jj + 1, pair >> 16);
         }
     };
+    // The first 16-row sub-block is loaded here; each row of the next one is
+    // loaded into the registers of the same row of the current one as soon as
+    // that row's maxima are taken, so one set of data registers suffices.
     u32x4 v[16];
     if (rb < row_end) load_subblock(x, K, rb, row_end, lane_off, xr, v);
 #pragma unroll 1
     for (int s = 0; s < tile_h / 4; s += 16) {
-        const int64_t r0 = rb + s;
+        const int64_t r0 = rb + (s >> 4) * rstride;
         if (r0 >= row_end) break;
         if (KIND == AMAX_GROUPED) {
             const int g = cur_group < 0 ? group_of_row(gt, r0) : group_advance(gt, cur_group, r0);
@@ -255,9 +270,9 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
             }
         }
         // the next sub-block's rows (an empty buffer when there is none)
-        const bool more = s + 16 < tile_h / 4 && r0 + 16 < row_end;
-        const int64_t left = row_end - (r0 + 16);
-        const __amdgpu_buffer_rsrc_t nrs = more ? rsrc(x + (r0 + 16) * K, (uint32_t)(left < 16 ? left : 16) * xr)
+        const bool more = s + 16 < tile_h / 4 && r0 + rstride < row_end;
+        const int64_t left = row_end - (r0 + rstride);
+        const __amdgpu_buffer_rsrc_t nrs = more ? rsrc(x + (r0 + rstride) * K, (uint32_t)(left < 16 ? left : 16) * xr)
                                                 : rsrc(x, 0u);
         uint32_t rm[16];
 #pragma unroll

@@ -176,6 +176,21 @@ __device__ __forceinline__ Outer make_outer(float A, bool valid = true) {
     return o;
 }
 
+// Outer scale of a vector as kept in LDS: S and 1/S, the reciprocal negated
+// when the vector needs the exact path (an amax outside the fast range)
+__device__ __forceinline__ float2 outer_entry(float A) {
+    const Outer o = make_outer(A);
+    return make_float2(o.S, o.slow ? -o.yS : o.yS);
+}
+
+__device__ __forceinline__ Outer outer_from(float2 e) {
+    Outer o;
+    o.S = e.x;
+    o.yS = __builtin_fabsf(e.y);
+    o.slow = e.y < 0.0f;
+    return o;
+}
+
 // Per-block parameters on the fast path: the split reciprocal yh = RD(1/r),
 // yl = RN((1 - r*yh) * yh) >= 0 of the divisor r = decode(code) * S, used
 // by the two-op element quotient, and the E4M3 scale byte in the low 8 bits

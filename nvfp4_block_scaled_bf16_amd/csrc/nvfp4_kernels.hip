@@ -1103,13 +1103,32 @@ __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t rnd) {
     return s | (xb >= 0x40c00000u ? 7u : r);
 }
 
-// Whether every lane's block of the wave can take the three-op quotient:
-// RN(a / r) for bf16 a when r lies in [2^-64, 2^64] (fact 1 of the device
-// arithmetic; |a| / r stays below 7 in a cast whose amax covers its data, so
-// |a| * RN(1/r) is far from 2^64).  Otherwise the IEEE division.
-__device__ __forceinline__ bool sr_fast(const BlockScale& bs) {
-    const bool in_range = bs.r >= 0x1p-64f && bs.r <= 0x1p64f;
-    return __builtin_amdgcn_ballot_w64(!in_range) == 0ull;
+// Block parameters of the stochastic-rounding cast on the fast path: the
+// exact block scale (code = E4M3(RN(RN(b / 6) / S)), r = decode(code) * S)
+// from the division shortcut of fact 1 and 1b, and y = RN(1/r) for the
+// element quotients RN(a / r) (fact 1).  slow: the vector's outer scale is
+// outside the fast range, the scale falls in the E4M3 subnormal range, or r
+// lies outside [2^-64, 2^64]; that block takes IEEE divisions throughout.
+// An all-zero block gets code 0 and some normal r: its quotients are +/-0.
+struct SrBlock {
+    float r, y;
+    uint32_t code;
+    bool slow;
+};
+
+__device__ __forceinline__ SrBlock sr_block(uint32_t bbits, const Outer& o) {
+    SrBlock f;
+    const float t = div_fast(__uint_as_float(bbits), 6.0f, kRcp6);   // RN(b / 6)
+    const float sf = div_fast(t, o.S, o.yS);                         // RN(t / S)
+    const uint32_t u = __float_as_uint(sf);
+    // E4M3 code by rounding sf's encoding (as in fast_block): the low byte
+    uint32_t c = (u + (0x7FFFFu + (0x40u << 20)) + ((u >> 20) & 1u)) >> 20;
+    c = c < 0x400u ? 0x400u : (c > 0x47Eu ? 0x47Eu : c);
+    f.code = c & 0xffu;
+    f.r = __uint_as_float((c << 20) - (0x40u << 20)) * o.S;
+    f.y = rcp_rn(f.r);
+    f.slow = o.slow || (u - 1u) < (0x3C800000u - 1u) || !(f.r >= 0x1p-64f && f.r <= 0x1p64f);
+    return f;
 }
 
 // Stochastic-rounding cast (per-tensor or per-token outer amax, computed
@@ -1118,7 +1137,10 @@ __device__ __forceinline__ bool sr_fast(const BlockScale& bs) {
 // column for columnwise output) draws word i % 4 of Philox block
 // (i / 4, vector, direction, offset) under key (k0, k1), direction 0 rowwise,
 // 1 columnwise.  A lane holds a 16-row x 8-column sub-block (as in the
-// deterministic cast); a workgroup covers 128 rows x 256 columns.  Requires
+// deterministic cast); a workgroup covers 128 rows x 256 columns.  Per-token
+// outer scales are computed once per workgroup into LDS; rows go two at a
+// time, the lane pair splitting their block parameters (the even lane the
+// even row's, the odd lane the odd row's, handed across by DPP).  Requires
 // M < 2^32 (the vector index is one counter word).
 template <int MODE, bool ROW, bool COL>
 __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
@@ -1127,43 +1149,82 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
                                                    uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,
                                                    uint32_t k0, uint32_t k1, uint32_t offset) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rg = lane >> 5;
-    const uint32_t c0 = blockIdx.x * kEncCols + (lane & 31) * 8;
-    const int64_t r0 = (int64_t)blockIdx.y * 128 + wave * 32 + 16 * rg;
+    const bool odd = lane & 1;
+    const uint32_t tc0 = blockIdx.x * kEncCols;
+    const int64_t tr0 = (int64_t)blockIdx.y * 128;
+    const uint32_t c0 = tc0 + (lane & 31) * 8;
+    const int rl0 = wave * 32 + 16 * rg;   // the lane's first row within the tile
+    const int64_t r0 = tr0 + rl0;
     const bool col_ok = c0 < K;
     const int nrows = r0 >= M ? 0 : (M - r0 < 16 ? (int)(M - r0) : 16);
     auto load_row = [&](int i) {
         return (col_ok && i < nrows) ? *reinterpret_cast<const u32x4*>(x + (r0 + i) * K + c0) : u32x4{0u, 0u, 0u, 0u};
     };
+    constexpr bool TOK = MODE == ENC_TOKEN;
+    __shared__ float2 rsc[(TOK && ROW) ? 128 : 1];
+    __shared__ float2 csc[(TOK && COL) ? kEncCols : 1];
+    if (TOK) {
+        const int t = threadIdx.x;
+        if (COL) csc[t] = outer_entry(tc0 + t < K ? col_amax[tc0 + t] : 0.0f);
+        if (ROW && t < 128) rsc[t] = outer_entry(tr0 + t < M ? row_amax[tr0 + t] : 0.0f);
+        __syncthreads();
+    }
     if (ROW) {
-        const float At = MODE == ENC_TENSOR ? row_amax[0] : 0.0f;
-        // rows one at a time (a rolled loop over a register array would put
-        // the array in scratch memory), the next row's load issued before
-        // this one is encoded
-        u32x4 vnext = load_row(0);
+        const Outer rot = make_outer(TOK ? 0.0f : row_amax[0]);
+        const uint32_t own_sel = odd ? 0x03020c0cu : 0x01000c0cu;   // own row's half to the top
+        // rows two at a time (a rolled loop: unrolled, its register arrays
+        // would go to scratch memory), the next pair's loads issued before
+        // this pair is encoded
+        u32x4 n0 = load_row(0), n1 = load_row(1);
 #pragma unroll 1
-        for (int i = 0; i < 16; ++i) {
-            const u32x4 vi = vnext;
-            if (i + 1 < 16) vnext = load_row(i + 1);
-            uint32_t hw = rowmax_word(vi);
-            hw = pk_max_u16(hw, from_pair(hw));   // the lane pair's 16 columns
-            const float A = MODE == ENC_TENSOR ? At : (i < nrows ? row_amax[r0 + i] : 0.0f);
-            const BlockScale bs = block_scale(max_halves(hw), outer_scale(A));
-            const uint32_t vec = (uint32_t)(r0 + i);
-            const u32x4 ra = philox4x32_10(c0 >> 2, vec, 0u, offset, k0, k1);
-            const u32x4 rb = philox4x32_10((c0 >> 2) + 1u, vec, 0u, offset, k0, k1);
-            const uint32_t rnd[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-            uint32_t w = 0u;
-            if (sr_fast(bs)) {
-                const float y = rcp_rn(bs.r);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) w |= e2m1_sr(div_fast(elem(vi, k), bs.r, y), rnd[k]) << (4 * k);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) w |= e2m1_sr(quotient_exact(elem(vi, k), bs), rnd[k]) << (4 * k);
+        for (int i = 0; i < 16; i += 2) {
+            const u32x4 w0 = n0, w1 = n1;
+            if (i + 2 < 16) {
+                n0 = load_row(i + 2);
+                n1 = load_row(i + 3);
             }
-            if (col_ok && i < nrows) {
-                *reinterpret_cast<uint32_t*>(row_q + (r0 + i) * (K / 2) + c0 / 2) = w;
-                if (!(lane & 1)) row_sf[(r0 + i) * (K / 16) + c0 / 16] = (uint8_t)bs.code;
+            const uint32_t rw0 = rowmax_word(w0), rw1 = rowmax_word(w1);
+            // (row i | row i+1 << 16) over the lane's 8 columns, then the pair's 16
+            uint32_t m = pk_max_u16(__builtin_amdgcn_perm(rw1, rw0, 0x05040100u),
+                                    __builtin_amdgcn_perm(rw1, rw0, 0x07060302u));
+            m = pk_max_u16(m, from_pair(m));
+            const Outer ro = TOK ? outer_from(rsc[rl0 + i + (odd ? 1 : 0)]) : rot;
+            const SrBlock f = sr_block(__builtin_amdgcn_perm(m, m, own_sel), ro);
+            const bool fast = __builtin_amdgcn_ballot_w64(f.slow) == 0ull;
+            const float rr0 = from_even(f.r), ry0 = from_even(f.y), rr1 = from_odd(f.r), ry1 = from_odd(f.y);
+            BlockScale b0, b1;
+            if (!fast) {
+                const float A0 = TOK ? (i < nrows ? row_amax[r0 + i] : 0.0f) : row_amax[0];
+                const float A1 = TOK ? (i + 1 < nrows ? row_amax[r0 + i + 1] : 0.0f) : row_amax[0];
+                b0 = block_scale(m & 0xffffu, outer_scale(A0));
+                b1 = block_scale(m >> 16, outer_scale(A1));
+            }
+            uint32_t wq[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 vi = h ? w1 : w0;
+                const uint32_t vec = (uint32_t)(r0 + i + h);
+                const u32x4 ra = philox4x32_10(c0 >> 2, vec, 0u, offset, k0, k1);
+                const u32x4 rb = philox4x32_10((c0 >> 2) + 1u, vec, 0u, offset, k0, k1);
+                const uint32_t rnd[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+                uint32_t w = 0u;
+                if (fast) {
+                    const float r = h ? rr1 : rr0, y = h ? ry1 : ry0;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) w |= e2m1_sr(div_fast(elem(vi, k), r, y), rnd[k]) << (4 * k);
+                } else {
+                    const BlockScale& bs = h ? b1 : b0;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) w |= e2m1_sr(quotient_exact(elem(vi, k), bs), rnd[k]) << (4 * k);
+                }
+                wq[h] = w;
+            }
+            const uint32_t code = fast ? f.code : (odd ? b1.code : b0.code);
+            if (col_ok) {
+                if (i < nrows) *reinterpret_cast<uint32_t*>(row_q + (r0 + i) * (K / 2) + c0 / 2) = wq[0];
+                if (i + 1 < nrows) *reinterpret_cast<uint32_t*>(row_q + (r0 + i + 1) * (K / 2) + c0 / 2) = wq[1];
+                const int io = i + (odd ? 1 : 0);
+                if (io < nrows) row_sf[(r0 + io) * (K / 16) + c0 / 16] = (uint8_t)code;
             }
         }
     }
@@ -1171,6 +1232,7 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
         u32x4 v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = load_row(i);
+        const Outer cot = make_outer(TOK ? 0.0f : col_amax[0]);
 #pragma unroll 1
         for (int j = 0; j < 8; ++j) {
             uint32_t m = 0u;
@@ -1179,14 +1241,15 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
                 const uint32_t e = (__float_as_uint(elem_rt(v[i], j)) >> 16) & 0x7fffu;
                 m = e > m ? e : m;
             }
-            const float A = MODE == ENC_TENSOR ? col_amax[0] : (col_ok ? col_amax[c0 + j] : 0.0f);
-            const BlockScale bs = block_scale(m, outer_scale(A));
+            const Outer co = TOK ? outer_from(csc[(lane & 31) * 8 + j]) : cot;
+            const SrBlock f = sr_block(m << 16, co);
             const uint32_t vec = c0 + (uint32_t)j, g0 = (uint32_t)(r0 >> 2);
             // one Philox block (four words) per four rows, each used as soon
             // as it is drawn, so that at most one block is live
             uint32_t lohi[2] = {0u, 0u};
-            if (sr_fast(bs)) {
-                const float y = rcp_rn(bs.r);
+            uint32_t code;
+            if (__builtin_amdgcn_ballot_w64(f.slow) == 0ull) {
+                code = f.code;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
@@ -1194,13 +1257,16 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int i = 4 * g + k;
-                        lohi[i >> 3] |= e2m1_sr(div_fast(elem_rt(v[i], j), bs.r, y), rr[k]) << (4 * (i & 7));
+                        lohi[i >> 3] |= e2m1_sr(div_fast(elem_rt(v[i], j), f.r, f.y), rr[k]) << (4 * (i & 7));
                         // one element at a time: the rounding has no branches,
                         // and sixteen of it in flight would cost registers
                         asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
                     }
                 }
             } else {
+                const float A = TOK ? (col_ok ? col_amax[c0 + j] : 0.0f) : col_amax[0];
+                const BlockScale bs = block_scale(m, outer_scale(A));
+                code = bs.code;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
@@ -1215,7 +1281,7 @@ __global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ 
             }
             if (col_ok && nrows == 16) {
                 *reinterpret_cast<u32x2*>(col_q + (int64_t)(c0 + j) * (M / 2) + r0 / 2) = u32x2{lohi[0], lohi[1]};
-                col_sf[(int64_t)(c0 + j) * (M / 16) + r0 / 16] = (uint8_t)bs.code;
+                col_sf[(int64_t)(c0 + j) * (M / 16) + r0 / 16] = (uint8_t)code;
             }
         }
     }

@@ -1140,10 +1140,13 @@ __device__ __forceinline__ SrBlock sr_block(uint32_t bbits, const Outer& o) {
 // deterministic cast); a workgroup covers 128 rows x 256 columns.  Per-token
 // outer scales are computed once per workgroup into LDS; rows go two at a
 // time, the lane pair splitting their block parameters (the even lane the
-// even row's, the odd lane the odd row's, handed across by DPP).  Requires
-// M < 2^32 (the vector index is one counter word).
+// even row's, the odd lane the odd row's, handed across by DPP).  Built for
+// four waves per SIMD (at most 128 VGPRs; one 8-byte value spills, outside
+// the element loops): the Philox rounds are chains of dependent operations
+// that more waves hide better.  Requires M < 2^32 (the vector index is one
+// counter word).
 template <int MODE, bool ROW, bool COL>
-__global__ __launch_bounds__(256) void k_encode_sr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+__global__ __launch_bounds__(256, 4) void k_encode_sr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                    const float* __restrict__ row_amax, const float* __restrict__ col_amax,
                                                    uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_sf,
                                                    uint8_t* __restrict__ col_q, uint8_t* __restrict__ col_sf,

@@ -20,7 +20,8 @@ namespace nvfp4 {
 
 constexpr int kTileCols = 512;     // columns per workgroup tile (64 lanes x 8)
 constexpr int kAmaxRows = 512;     // rows per workgroup tile in the amax pass (at most; fewer for small tensors)
-constexpr int kAmaxGroupedRows = 256;   // at most, for grouped casts (their per-expert LDS slots scale with it)
+constexpr int kAmaxGroupedRows = 512;   // at most, for grouped casts (their per-expert LDS slots scale with it:
+                                         // 32 slots x 512 columns, 64 KB)
 constexpr int kEncRows = 256;      // rows per workgroup tile in the encode pass (at most; 128 for small tensors)
 constexpr int kEncCols = 256;      // columns per workgroup tile in the encode pass: a wave is
                                    // two row groups of 32 lanes, each 16 rows x 256 columns
@@ -222,15 +223,23 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     __shared__ uint32_t gred[KIND == AMAX_GROUPED ? kSlots : 1][KIND == AMAX_GROUPED ? kTileCols : 1];
     __shared__ int gslot[KIND == AMAX_GROUPED ? kSlots : 1];
     const int64_t tile_r0 = row_begin + (int64_t)by * tile_h;
+    // the slots the tile's experts take (the experts overlapping a tile are
+    // consecutive table entries): only those are cleared and combined
+    uint32_t used = 0u;
     if (KIND == AMAX_GROUPED) {
-        for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) gred[i / kTileCols][i % kTileCols] = 0u;
-        if (threadIdx.x < kSlots) gslot[threadIdx.x] = -1;
+        const int64_t tile_end = row_end - tile_r0 < tile_h ? row_end : tile_r0 + tile_h;
+        for (int g = group_of_row(gt, tile_r0); g < gt.n && gt.off[g] < tile_end; ++g)
+            if (gt.cnt[g] > 0) used |= 1u << (gt.off[g] <= tile_r0 ? 0 : (int)((gt.off[g] - tile_r0) / 16));
+        for (uint32_t m = used; m != 0u; m &= m - 1u) {
+            const int slot = __builtin_ctz(m);
+            for (int i = threadIdx.x; i < kTileCols; i += 256) gred[slot][i] = 0u;
+        }
         __syncthreads();
     }
     auto group_flush = [&](int g) {   // this wave's column maxima of expert g into its slot
         const int64_t o = gt.off[g];
         const int slot = o <= tile_r0 ? 0 : (int)((o - tile_r0) / 16);
-        if (lane == 0) gslot[slot] = g;
+        if (lane == 0) gslot[slot] = g;   // (the same g from every wave)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             atomicMax(&gred[slot][lane * 8 + 2 * k], cm[k] & 0xffffu);
@@ -317,11 +326,11 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
         if (!zero_ok) return;
         flush_rows();
         const int64_t tc0 = (int64_t)bx * kTileCols;
-        for (int i = threadIdx.x; i < kSlots * kTileCols; i += 256) {
-            const int slot = i / kTileCols, c = i % kTileCols;
+        for (uint32_t m = used; m != 0u; m &= m - 1u) {
+            const int slot = __builtin_ctz(m);
             const int g = gslot[slot];
-            if (g >= 0 && tc0 + c < K)
-                atomic_max_mag(col_amax + (int64_t)(gt.first + g) * K + tc0 + c, gred[slot][c]);
+            for (int c = threadIdx.x; c < kTileCols; c += 256)
+                if (tc0 + c < K) atomic_max_mag(col_amax + (int64_t)(gt.first + g) * K + tc0 + c, gred[slot][c]);
         }
         return;
     }

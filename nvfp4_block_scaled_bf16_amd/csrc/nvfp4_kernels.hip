@@ -345,14 +345,13 @@ __global__ __launch_bounds__(256) void k_amax(const uint16_t* __restrict__ x, in
     if (!zero_ok) return;
     flush_rows();
     if (col_amax != nullptr) {
-        if (wave == 0 && col_ok) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t m = pk_max_u16(pk_max_u16(red[0][lane][k], red[1][lane][k]),
-                                        pk_max_u16(red[2][lane][k], red[3][lane][k]));
-                atomic_max_mag(col_amax + c0 + 2 * k, m & 0xffffu);
-                atomic_max_mag(col_amax + c0 + 2 * k + 1, m >> 16);
-            }
+        // thread t: the column pair 8 (t / 4) + 2 (t % 4) of the tile
+        const int t = threadIdx.x, l = t >> 2, k = t & 3;
+        const uint32_t m = pk_max_u16(pk_max_u16(red[0][l][k], red[1][l][k]), pk_max_u16(red[2][l][k], red[3][l][k]));
+        const int64_t c = (int64_t)bx * kTileCols + 8 * l + 2 * k;
+        if (c < K) {
+            atomic_max_mag(col_amax + c, m & 0xffffu);
+            atomic_max_mag(col_amax + c + 1, m >> 16);
         }
     }
 }

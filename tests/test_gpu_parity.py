@@ -551,6 +551,21 @@ def test_c4_grouped_moe(oracle):
     compare_cast(out, ref)
 
 
+def test_grouped_many_experts_per_amax_tile(oracle):
+    """Thirty-two 16-row experts in each of the first two 512-row tiles of
+    the amax pass (4096 x 32768 gives 512 workgroups of 512 rows, so every
+    LDS slot of the per-expert column maxima is taken), then 48-row experts
+    straddling tile boundaries."""
+    counts = [16] * 64 + [48] * 64
+    K = 32768
+    x = _grouped_case(counts, K, 4097)
+    _announce(f"grouped 128 experts (16 and 48 rows), T={sum(counts)} K={K}")
+    out = Guarded(grouped_spec(sum(counts), K, len(counts)))
+    nv.quantize_grouped_into(to_dev(x), counts, **out.views)
+    torch.cuda.synchronize()
+    compare_cast(out, oracle.quantize_grouped(x, np.array(counts, np.int64)))
+
+
 def test_c5_tile_16x16_full(oracle):
     x = W.c5()
     _announce("C5 8192x28672 16x16 tiles (full compare)")

@@ -195,12 +195,13 @@ NVFP4_API nvfp4_status nvfp4_quantize_calibrate(const void* x, int64_t M, int64_
  * PER_TOKEN scaling (TILE_16x16 is NVFP4_EINVAL).  Outer amax and block scales
  * are those of nvfp4_quantize; each element's quotient x = |RN(v / r)| lies
  * in [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2 below 6)
- * and rounds up iff x - lo > U * d, U = (R >> 8) * 2^-24, R the element's
- * 32-bit random; x >= 6 saturates.  R is word i % 4 of the Philox4x32-10
- * block (Salmon et al., SC'11) with key (seed low word, seed high word) and
- * counter (i / 4, vector index, 0 for rowwise / 1 for columnwise, offset),
- * where i is the element's position along its vector (a row of x for
- * rowwise output, a column for columnwise output).  The page does not say
+ * and rounds up iff x - lo > U * d, U = R * 2^-8, R the element's 8-bit
+ * random; x >= 6 saturates.  R is byte i % 16 of the Philox4x32-10 block
+ * (Salmon et al., SC'11) with key (seed low word, seed high word) and
+ * counter (i / 16, vector index, 0 for rowwise / 1 for columnwise, offset),
+ * its four output words read as 16 little-endian bytes, where i is the
+ * element's position along its vector (a row of x for rowwise output, a
+ * column for columnwise output).  The page does not say
  * how its randoms are drawn; this is the library's definition, reproduced
  * bit for bit by its CPU reference.  The same seed and offset give the same
  * bytes; change offset per call for fresh randoms.  Needs M < 2^32

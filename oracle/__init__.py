@@ -242,9 +242,12 @@ def philox4x32_10(ctr, key):
 
 
 def e2m1_encode_sr(q, rnd):
-    """Stochastic E2M1 codes of float32 quotients q with 32-bit randoms rnd."""
+    """Stochastic E2M1 codes of float32 quotients q with 8-bit randoms rnd."""
     q = np.ascontiguousarray(q, np.float32).ravel()
-    rnd = np.ascontiguousarray(rnd, np.uint32).ravel()
+    rnd = np.asarray(rnd)
+    if rnd.dtype != np.uint8:
+        raise ValueError("rnd: one uint8 random per quotient")
+    rnd = np.ascontiguousarray(rnd).ravel()
     if q.shape != rnd.shape:
         raise ValueError("one random per quotient")
     out = np.empty(q.shape, np.uint8)

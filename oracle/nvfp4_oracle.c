@@ -429,17 +429,21 @@ void orc_amax_accumulate_reduce(float* buf, const float* obs, int64_t n, float d
  *     Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
  *     1, 2, 3" (SC'11).  Key = the caller's 64-bit seed (low word first);
  *     element i of a vector (a row for rowwise output, a column for
- *     columnwise output) takes output word i % 4 of the counter
- *     (i / 4, vector index, direction, offset), direction 0 rowwise and 1
- *     columnwise, offset a 32-bit value the caller changes per call;
+ *     columnwise output) takes byte i % 16 of the block with counter
+ *     (i / 16, vector index, direction, offset), the block's four output
+ *     words read as 16 little-endian bytes (byte k = bits 8(k % 4) ..
+ *     8(k % 4) + 7 of word k / 4); direction 0 rowwise and 1 columnwise,
+ *     offset a 32-bit value the caller changes per call.  One block thus
+ *     serves one 16-element block of the cast, eight random bits per element;
  *   - rounding: block scales exactly as in the deterministic cast; the
  *     element quotient x = |RN(v / r)| also; lo and lo + d the E2M1 grid
  *     points around x (d = 0.5 below 2, 1 below 4, 2 below 6); with
- *     U = (R >> 8) * 2^-24 for the element's 32-bit random R, the magnitude
- *     rounds up iff x - lo > U * d.  Both sides of that comparison are exact
- *     in binary32 (x - lo by Sterbenz's lemma, U * d a power-of-two scaling),
- *     so P(up) = ceil(2^24 * (x - lo) / d) / 2^24.  x >= 6 saturates to 6
- *     with no draw; the sign is copied; r == 0 gives sign-only nibbles. */
+ *     U = R * 2^-8 for the element's 8-bit random R, the magnitude rounds up
+ *     iff x - lo > U * d.  Both sides of that comparison are exact in
+ *     binary32 (x - lo by Sterbenz's lemma, U * d a power-of-two scaling), so
+ *     P(up) = ceil(2^8 * (x - lo) / d) / 2^8: the rounding's mean exceeds x
+ *     by less than d / 256.  x >= 6 saturates to 6 with no draw; the sign is
+ *     copied; r == 0 gives sign-only nibbles. */
 
 /* One Philox4x32 block: ten rounds of the multiply-xor S-box on the counter
  * words, with the key advanced by the two Weyl constants between rounds. */
@@ -476,8 +480,8 @@ void orc_philox4x32_10_array(const uint32_t* ctr, const uint32_t* key, int64_t n
     for (int64_t i = 0; i < n; ++i) orc_philox4x32_10(ctr + 4 * i, key + 2 * i, out + 4 * i);
 }
 
-/* E2M1 code of q rounded stochastically with the 32-bit random rnd */
-uint8_t orc_e2m1_encode_sr(float q, uint32_t rnd)
+/* E2M1 code of q rounded stochastically with the 8-bit random rnd */
+uint8_t orc_e2m1_encode_sr(float q, uint8_t rnd)
 {
     uint8_t s = signbit(q) ? 8 : 0;
     float x = fabsf(q);
@@ -497,12 +501,12 @@ uint8_t orc_e2m1_encode_sr(float q, uint32_t rnd)
         c = 6;
         d = 2.0f;
     }
-    float u = (float)(rnd >> 8) * 0x1p-24f;
+    float u = (float)rnd * 0x1p-8f;
     if (x - lo > u * d) c = (uint8_t)(c + 1);
     return (uint8_t)(s | c);
 }
 
-void orc_e2m1_encode_sr_array(const float* q, const uint32_t* rnd, int64_t n, uint8_t* out)
+void orc_e2m1_encode_sr_array(const float* q, const uint8_t* rnd, int64_t n, uint8_t* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode_sr(q[i], rnd[i]);
 }
@@ -531,17 +535,17 @@ void orc_quantize_vector_sr(const float* v, int64_t n, float A, uint8_t* q, uint
             sf[j] = code;
             r = orc_e4m3_decode(code) * S;
         }
-        uint32_t rnd[16];
-        for (int g = 0; g < 4; ++g) {
-            uint32_t ctr[4] = {(uint32_t)((16 * j + 4 * g) / 4), vec, dir, offset};
-            orc_philox4x32_10(ctr, key, rnd + 4 * g);
-        }
+        /* elements 16 j .. 16 j + 15: bytes 0 .. 15 of block (j, vec, dir, offset) */
+        uint32_t words[4];
+        uint32_t ctr[4] = {(uint32_t)j, vec, dir, offset};
+        orc_philox4x32_10(ctr, key, words);
         uint8_t nib[16];
         for (int i = 0; i < 16; ++i) {
+            uint8_t rnd = (uint8_t)(words[i / 4] >> (8 * (i % 4)));
             if (r == 0.0f)
                 nib[i] = signbit(blk[i]) ? 8 : 0;
             else
-                nib[i] = orc_e2m1_encode_sr(blk[i] / r, rnd[i]);
+                nib[i] = orc_e2m1_encode_sr(blk[i] / r, rnd);
         }
         for (int i = 0; i < 8; ++i)
             q[8 * j + i] = (uint8_t)(nib[2 * i] | (nib[2 * i + 1] << 4));

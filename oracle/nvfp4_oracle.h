@@ -89,8 +89,8 @@ void orc_amax_accumulate_reduce(float* buf, const float* obs, int64_t n, float d
 /* stochastic-rounding variant (definition and readings in nvfp4_oracle.c) */
 void    orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 void    orc_philox4x32_10_array(const uint32_t* ctr, const uint32_t* key, int64_t n, uint32_t* out);
-uint8_t orc_e2m1_encode_sr(float q, uint32_t rnd);
-void    orc_e2m1_encode_sr_array(const float* q, const uint32_t* rnd, int64_t n, uint8_t* out);
+uint8_t orc_e2m1_encode_sr(float q, uint8_t rnd);
+void    orc_e2m1_encode_sr_array(const float* q, const uint8_t* rnd, int64_t n, uint8_t* out);
 void    orc_quantize_vector_sr(const float* v, int64_t n, float A, uint8_t* q, uint8_t* sf,
                                uint64_t seed, uint32_t vec, uint32_t dir, uint32_t offset);
 int     orc_quantize_sr(const uint16_t* x, int64_t M, int64_t K, int mode,

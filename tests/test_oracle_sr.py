@@ -9,8 +9,8 @@ tests tie the oracle to things other than itself:
     ROCm headers;
   - its E2M1 stochastic rounding against the rule evaluated in exact rational
     arithmetic;
-  - the exact round-up frequency over all 2^24 values of U, which makes the
-    rounding unbiased to within 2^-24 of a grid step;
+  - the exact round-up frequency over all 2^8 values of U, which puts the
+    rounding's mean within 2^-8 of a grid step above the quotient;
   - the cast's structure against the deterministic cast: the same amax and
     block scales, and every element code one of the two grid neighbours of
     the exact quotient.
@@ -68,14 +68,14 @@ def test_philox_matches_rocrand_block_function():
 
 def _sr_rational(q, rnd):
     """The rounding rule in exact arithmetic: lo <= x < hi on the grid,
-    up iff x - lo > U * (hi - lo), U = (rnd >> 8) / 2^24."""
+    up iff x - lo > U * (hi - lo), U = rnd / 2^8 (rnd the 8-bit random)."""
     sign = 8 if np.signbit(q) else 0
     x = Fraction(abs(float(q)))
     if x >= 6:
         return sign | 7
     c = max(i for i, g in enumerate(GRID) if g <= x)
     lo, hi = GRID[c], GRID[c + 1]
-    u = Fraction(int(rnd) >> 8, 2**24)
+    u = Fraction(int(rnd), 2**8)
     return sign | (c + 1 if x - lo > u * (hi - lo) else c)
 
 
@@ -88,17 +88,17 @@ def test_sr_matches_rational_definition():
     qs += list(rng.uniform(-7, 7, 3000).astype(np.float32))
     qs += list((rng.standard_normal(500) * 1e-3).astype(np.float32))
     q = np.array(qs, np.float32)
-    rnd = rng.integers(0, 2**32, size=q.size, dtype=np.uint64).astype(np.uint32)
+    rnd = rng.integers(0, 256, size=q.size, dtype=np.int64).astype(np.uint8)
     # randoms at the edges, and ones that make U * d land exactly on x - lo
     rnd[:50] = 0
-    rnd[50:100] = 2**32 - 1
+    rnd[50:100] = 255
     got = oracle.e2m1_encode_sr(q, rnd)
     want = np.array([_sr_rational(a, r) for a, r in zip(q, rnd)], np.uint8)
     assert np.array_equal(got, want)
     # ties: U * d == x - lo exactly rounds down, one step of U more rounds up
     for x, lo, d in [(0.25, 0.0, 0.5), (1.25, 1.0, 0.5), (2.5, 2.0, 1.0), (5.0, 4.0, 2.0), (3.75, 3.0, 1.0)]:
-        k = int(Fraction(x - lo) / Fraction(d) * 2**24)
-        r = np.array([k << 8, (k - 1) << 8], np.uint32)
+        k = int(Fraction(x - lo) / Fraction(d) * 2**8)
+        r = np.array([k, k - 1], np.uint8)
         codes = oracle.e2m1_encode_sr(np.array([x, x], np.float32), r)
         base = GRID.index(Fraction(lo))
         assert codes[0] == base and codes[1] == base + 1, (x, codes)
@@ -106,21 +106,21 @@ def test_sr_matches_rational_definition():
 
 @pytest.mark.parametrize("x", [0.1, 0.3, 0.6, 1.3, 1.9999999, 2.2, 3.7, 4.4, 5.9, 1.0, 4.0])
 def test_sr_round_up_count_is_exact(x):
-    """Over all 2^24 values of U, rounding up happens exactly
-    ceil(2^24 (x - lo) / d) times, so E[code value] = x within 2^-24 d."""
+    """Over all 2^8 values of U, rounding up happens exactly
+    ceil(2^8 (x - lo) / d) times, so E[code value] lies in [x, x + 2^-8 d)."""
     xf = np.float32(x)
     X = Fraction(float(xf))
     c = max(i for i, g in enumerate(GRID) if g <= X)
     lo, d = GRID[c], GRID[c + 1] - GRID[c]
-    t = (X - lo) / d * 2**24
+    t = (X - lo) / d * 2**8
     expect = -((-t.numerator) // t.denominator)   # ceil
-    rnd = (np.arange(2**24, dtype=np.uint64) << np.uint64(8)).astype(np.uint32)
-    codes = oracle.e2m1_encode_sr(np.full(2**24, xf, np.float32), rnd)
+    rnd = np.arange(2**8, dtype=np.int64).astype(np.uint8)
+    codes = oracle.e2m1_encode_sr(np.full(2**8, xf, np.float32), rnd)
     ups = int(np.count_nonzero(codes == c + 1))
     assert int(np.count_nonzero((codes != c) & (codes != c + 1))) == 0
     assert ups == expect
-    mean = lo + d * Fraction(ups, 2**24)
-    assert abs(mean - X) <= d / 2**24
+    mean = lo + d * Fraction(ups, 2**8)
+    assert X <= mean < X + d / 2**8
 
 
 @pytest.mark.parametrize("mode", [oracle.PER_TENSOR, oracle.PER_TOKEN])
@@ -170,9 +170,10 @@ def test_sr_seed_and_offset():
 
 @pytest.mark.parametrize("mode", [oracle.PER_TENSOR, oracle.PER_TOKEN])
 def test_sr_counter_layout(mode):
-    """Every element's random is word i % 4 of the Philox block with counter
-    (i / 4, vector, direction, offset) and key (seed low, seed high): rebuild
-    each element's code from the two pinned pieces above and compare."""
+    """Every element's random is byte i % 16 of the Philox block with counter
+    (i / 16, vector, direction, offset) and key (seed low, seed high), the
+    block's four words read as 16 little-endian bytes: rebuild each element's
+    code from the two pinned pieces above and compare."""
     from nvfp4_block_scaled_bf16_amd import workloads as W
     M, K, seed, offset = 48, 96, 0xFEDCBA9876543210, 77
     x = W.row_scaled_with_outliers(M, K, 21)
@@ -190,9 +191,10 @@ def test_sr_counter_layout(mode):
         with np.errstate(divide="ignore", invalid="ignore"):
             qv = np.where(rr == 0, np.float32(0) * v, v / rr).astype(np.float32)
         vec, i = np.meshgrid(np.arange(n_vec), np.arange(n), indexing="ij")
-        ctr = np.stack([i // 4, vec, np.full_like(i, dflag), np.full_like(i, offset)], -1).reshape(-1, 4).astype(np.uint32)
+        ctr = np.stack([i // 16, vec, np.full_like(i, dflag), np.full_like(i, offset)], -1).reshape(-1, 4).astype(np.uint32)
         words = oracle.philox4x32_10(ctr, np.tile(key, (ctr.shape[0], 1)))
-        rnd = words[np.arange(ctr.shape[0]), (i % 4).ravel()]
+        k = (i % 16).ravel()
+        rnd = ((words[np.arange(ctr.shape[0]), k // 4] >> (8 * (k % 4)).astype(np.uint32)) & 0xFF).astype(np.uint8)
         want = oracle.e2m1_encode_sr(qv.ravel(), rnd).reshape(n_vec, n)
         zero = (rr == 0)
         want = np.where(zero, np.where(np.signbit(v), 8, 0), want).astype(np.uint8)

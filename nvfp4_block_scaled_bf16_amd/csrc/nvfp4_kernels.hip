@@ -1085,29 +1085,38 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     return u32x4{c0, c1, c2, c3};
 }
 
-// Stochastic E2M1 nibble of q with the 32-bit random rnd: x = |q| lies in
-// [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2 below 6) and
-// rounds up iff x - lo > U * d with U = (rnd >> 8) * 2^-24; both sides are
-// exact in binary32.  x >= 6 saturates; the sign bit of q is copied.
-// Without branches, from the bit pattern of x: at or above 1, lo keeps x's
-// exponent and first mantissa bit, d is half its binade and the code is
-// lo's top 10 bits less 252 (1 -> 2, 1.5 -> 3, ..., 4 -> 6); below 1, lo is
-// 0.5 or 0 (codes 1, 0) and d is 0.5.  U * d is formed as (rnd >> 8) times
-// the power of two d * 2^-24.  (tests/native/sr_round_check.c compares
-// this form with the oracle's rule over every fp32 q.)
-__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t rnd) {
+// Stochastic E2M1 nibble of q with the 8-bit random byte K of word w: x = |q|
+// lies in [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2
+// below 6) and rounds up iff x - lo > U * d with U = R * 2^-8, R that byte;
+// both sides are exact in binary32.  x >= 6 saturates; the sign bit of q is
+// copied.  Without branches, from the bit pattern of x: at or above 1, lo
+// keeps x's exponent and first mantissa bit, d is half its binade and the
+// code is lo's top 10 bits less 252 (1 -> 2, 1.5 -> 3, ..., 4 -> 6); below
+// 1, lo is 0.5 or 0 (codes 1, 0) and d is 0.5.  U * d is formed as R (one
+// byte-to-float conversion) times the power of two d * 2^-8.
+// (tests/native/sr_round_check.c compares this form with the oracle's rule
+// over every fp32 q.)
+template <int K>
+__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t w) {
     const uint32_t b = __float_as_uint(q);
     const uint32_t s = (b >> 28) & 8u;
     const uint32_t xb = b & 0x7fffffffu;
     const bool ge1 = xb >= 0x3f800000u;
     const uint32_t half = xb >= 0x3f000000u ? 0x3f000000u : 0u;
     const uint32_t lob = ge1 ? (xb & 0xffc00000u) : half;
-    const uint32_t db24 = ge1 ? (xb & 0x7f800000u) - (25u << 23) : 0x33000000u;   // d * 2^-24
+    const uint32_t db8 = ge1 ? (xb & 0x7f800000u) - (9u << 23) : 0x3b000000u;   // d * 2^-8
     const uint32_t c = ge1 ? (lob >> 22) - 252u : (half >> 29);
     const float diff = __uint_as_float(xb) - __uint_as_float(lob);
-    const float ud = (float)(rnd >> 8) * __uint_as_float(db24);
+    const float ud = (float)((w >> (8 * K)) & 0xffu) * __uint_as_float(db8);
     const uint32_t r = c + (diff > ud ? 1u : 0u);
     return s | (xb >= 0x40c00000u ? 7u : r);
+}
+
+// the nibble of element k (0..7) of a lane's row from the row's two random
+// words (bytes 0..3 of w0, then of w1)
+template <int k>
+__device__ __forceinline__ uint32_t e2m1_sr8(float q, uint32_t w0, uint32_t w1) {
+    return e2m1_sr<k & 3>(q, k < 4 ? w0 : w1);
 }
 
 // Block parameters of the stochastic-rounding cast on the fast path: the
@@ -1141,13 +1150,17 @@ __device__ __forceinline__ SrBlock sr_block(uint32_t bbits, const Outer& o) {
 // Stochastic-rounding cast (per-tensor or per-token outer amax, computed
 // beforehand).  Block scales and element quotients are the exact IEEE ones of
 // the deterministic cast; element i of a vector (a row for rowwise output, a
-// column for columnwise output) draws word i % 4 of Philox block
-// (i / 4, vector, direction, offset) under key (k0, k1), direction 0 rowwise,
-// 1 columnwise.  A lane holds a 16-row x 8-column sub-block (as in the
-// deterministic cast); a workgroup covers 128 rows x 256 columns.  Per-token
-// outer scales are computed once per workgroup into LDS; rows go two at a
-// time, the lane pair splitting their block parameters (the even lane the
-// even row's, the odd lane the odd row's, handed across by DPP).  Built for
+// column for columnwise output) draws byte i % 16 of Philox block
+// (i / 16, vector, direction, offset) under key (k0, k1), direction 0
+// rowwise, 1 columnwise, the block's words read as little-endian bytes.  A
+// lane holds a 16-row x 8-column sub-block (as in the deterministic cast); a
+// workgroup covers 128 rows x 256 columns.  Per-token outer scales are
+// computed once per workgroup into LDS; rows go two at a time, the lane pair
+// splitting their block parameters (the even lane the even row's, the odd
+// lane the odd row's, handed across by DPP) and their Philox blocks (the
+// even lane draws the even row's block, whose 16 bytes cover both lanes'
+// columns, the odd lane the odd row's; each hands the other the two words it
+// needs).  A column's 16 rows take one block.  Built for
 // four waves per SIMD (at most 128 VGPRs; one 8-byte value spills, outside
 // the element loops): the Philox rounds are chains of dependent operations
 // that more waves hide better.  Requires M < 2^32 (the vector index is one
@@ -1209,25 +1222,30 @@ __global__ __launch_bounds__(256, 4) void k_encode_sr(const uint16_t* __restrict
                 b0 = block_scale(m & 0xffffu, outer_scale(A0));
                 b1 = block_scale(m >> 16, outer_scale(A1));
             }
+            // the pair's randoms: the lane's columns c0 .. c0+7 are bytes
+            // (c0 % 16) .. +7, two words, of each row's block (c0 / 16, row)
+            const u32x4 P = philox4x32_10(c0 >> 4, (uint32_t)(r0 + i + (odd ? 1 : 0)), 0u, offset, k0, k1);
+            const uint32_t t0 = from_pair(odd ? P.x : P.z), t1 = from_pair(odd ? P.y : P.w);
+            const uint32_t rw[2][2] = {{odd ? t0 : P.x, odd ? t1 : P.y}, {odd ? P.z : t0, odd ? P.w : t1}};
             uint32_t wq[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const u32x4 vi = h ? w1 : w0;
-                const uint32_t vec = (uint32_t)(r0 + i + h);
-                const u32x4 ra = philox4x32_10(c0 >> 2, vec, 0u, offset, k0, k1);
-                const u32x4 rb = philox4x32_10((c0 >> 2) + 1u, vec, 0u, offset, k0, k1);
-                const uint32_t rnd[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-                uint32_t w = 0u;
+                const uint32_t g0 = rw[h][0], g1 = rw[h][1];
+                float qv[8];
                 if (fast) {
                     const float r = h ? rr1 : rr0, y = h ? ry1 : ry0;
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) w |= e2m1_sr(div_fast(elem(vi, k), r, y), rnd[k]) << (4 * k);
+                    for (int k = 0; k < 8; ++k) qv[k] = div_fast(elem(vi, k), r, y);
                 } else {
                     const BlockScale& bs = h ? b1 : b0;
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) w |= e2m1_sr(quotient_exact(elem(vi, k), bs), rnd[k]) << (4 * k);
+                    for (int k = 0; k < 8; ++k) qv[k] = quotient_exact(elem(vi, k), bs);
                 }
-                wq[h] = w;
+                wq[h] = e2m1_sr8<0>(qv[0], g0, g1) | e2m1_sr8<1>(qv[1], g0, g1) << 4 |
+                        e2m1_sr8<2>(qv[2], g0, g1) << 8 | e2m1_sr8<3>(qv[3], g0, g1) << 12 |
+                        e2m1_sr8<4>(qv[4], g0, g1) << 16 | e2m1_sr8<5>(qv[5], g0, g1) << 20 |
+                        e2m1_sr8<6>(qv[6], g0, g1) << 24 | e2m1_sr8<7>(qv[7], g0, g1) << 28;
             }
             const uint32_t code = fast ? f.code : (odd ? b1.code : b0.code);
             if (col_ok) {
@@ -1253,41 +1271,34 @@ __global__ __launch_bounds__(256, 4) void k_encode_sr(const uint16_t* __restrict
             }
             const Outer co = TOK ? outer_from(csc[(lane & 31) * 8 + j]) : cot;
             const SrBlock f = sr_block(m << 16, co);
-            const uint32_t vec = c0 + (uint32_t)j, g0 = (uint32_t)(r0 >> 2);
-            // one Philox block (four words) per four rows, each used as soon
-            // as it is drawn, so that at most one block is live
+            // the column's 16 rows take bytes 0..15 of one block (r0 / 16, column)
+            const u32x4 P = philox4x32_10((uint32_t)(r0 >> 4), c0 + (uint32_t)j, 1u, offset, k0, k1);
+            const uint32_t rr[4] = {P.x, P.y, P.z, P.w};
             uint32_t lohi[2] = {0u, 0u};
             uint32_t code;
-            if (__builtin_amdgcn_ballot_w64(f.slow) == 0ull) {
-                code = f.code;
+            // one element at a time (the empty asm): the rounding has no
+            // branches, and sixteen of it in flight would cost registers
+            auto col_codes = [&](auto quot) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
-                    const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int i = 4 * g + k;
-                        lohi[i >> 3] |= e2m1_sr(div_fast(elem_rt(v[i], j), f.r, f.y), rr[k]) << (4 * (i & 7));
-                        // one element at a time: the rounding has no branches,
-                        // and sixteen of it in flight would cost registers
-                        asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
-                    }
+                    lohi[g >> 1] |= e2m1_sr<0>(quot(4 * g), rr[g]) << (4 * ((4 * g) & 7));
+                    asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
+                    lohi[g >> 1] |= e2m1_sr<1>(quot(4 * g + 1), rr[g]) << (4 * ((4 * g + 1) & 7));
+                    asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
+                    lohi[g >> 1] |= e2m1_sr<2>(quot(4 * g + 2), rr[g]) << (4 * ((4 * g + 2) & 7));
+                    asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
+                    lohi[g >> 1] |= e2m1_sr<3>(quot(4 * g + 3), rr[g]) << (4 * ((4 * g + 3) & 7));
+                    asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
                 }
+            };
+            if (__builtin_amdgcn_ballot_w64(f.slow) == 0ull) {
+                code = f.code;
+                col_codes([&](int i) { return div_fast(elem_rt(v[i], j), f.r, f.y); });
             } else {
                 const float A = TOK ? (col_ok ? col_amax[c0 + j] : 0.0f) : col_amax[0];
                 const BlockScale bs = block_scale(m, outer_scale(A));
                 code = bs.code;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x4 r = philox4x32_10(g0 + (uint32_t)g, vec, 1u, offset, k0, k1);
-                    const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int i = 4 * g + k;
-                        lohi[i >> 3] |= e2m1_sr(quotient_exact(elem_rt(v[i], j), bs), rr[k]) << (4 * (i & 7));
-                        asm volatile("" : "+v"(lohi[0]), "+v"(lohi[1]));
-                    }
-                }
+                col_codes([&](int i) { return quotient_exact(elem_rt(v[i], j), bs); });
             }
             if (col_ok && nrows == 16) {
                 *reinterpret_cast<u32x2*>(col_q + (int64_t)(c0 + j) * (M / 2) + r0 / 2) = u32x2{lohi[0], lohi[1]};

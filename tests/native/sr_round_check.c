@@ -1,21 +1,22 @@
 /* The stochastic E2M1 rounding of the SR encoding kernel (nvfp4_kernels.hip,
  * e2m1_sr: a branch-free form on the bits of |q|) against the oracle's rule
  * (orc_e2m1_encode_sr), for every fp32 bit pattern q that is not a NaN, each
- * with a random word drawn from a hash of q.  The two forms compute the same
- * two exact binary32 values x - lo and U*d wherever they pick the same (lo, d,
- * code), so one random word per q checks the pick; the hash still varies
- * which side of the threshold each q falls.  Prints "<n> checked, <m>
+ * with an 8-bit random drawn from a hash of q.  The two forms compute the
+ * same two exact binary32 values x - lo and U*d wherever they pick the same
+ * (lo, d, code), so one random per q checks the pick; the hash still varies
+ * which side of the threshold each q falls.  Then every random value at the
+ * grid points, midpoints and their neighbours.  Prints "<n> checked, <m>
  * mismatches". */
 #include <pthread.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
-uint8_t orc_e2m1_encode_sr(float q, uint32_t rnd);
+uint8_t orc_e2m1_encode_sr(float q, uint8_t rnd);
 
 static float f_of(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
 
-/* the kernel's form, transcribed */
+/* the kernel's form, transcribed (rnd: the element's 8-bit random) */
 static uint32_t kernel_sr(float q, uint32_t rnd)
 {
     uint32_t b;
@@ -25,10 +26,10 @@ static uint32_t kernel_sr(float q, uint32_t rnd)
     const int ge1 = xb >= 0x3f800000u;
     const uint32_t half = xb >= 0x3f000000u ? 0x3f000000u : 0u;
     const uint32_t lob = ge1 ? (xb & 0xffc00000u) : half;
-    const uint32_t db24 = ge1 ? (xb & 0x7f800000u) - (25u << 23) : 0x33000000u;
+    const uint32_t db8 = ge1 ? (xb & 0x7f800000u) - (9u << 23) : 0x3b000000u;
     const uint32_t c = ge1 ? (lob >> 22) - 252u : (half >> 29);
     const float diff = f_of(xb) - f_of(lob);
-    const float ud = (float)(rnd >> 8) * f_of(db24);
+    const float ud = (float)(rnd & 0xffu) * f_of(db8);
     const uint32_t r = c + (diff > ud ? 1u : 0u);
     return s | (xb >= 0x40c00000u ? 7u : r);
 }
@@ -49,7 +50,7 @@ static void* work(void* arg)
         const uint32_t b = (uint32_t)i;
         if ((b & 0x7fffffffu) > 0x7f800000u) continue;   /* NaN */
         const float q = f_of(b);
-        const uint32_t rnd = hash(b);
+        const uint8_t rnd = (uint8_t)(hash(b) >> 24);
         ++seen[t];
         if (kernel_sr(q, rnd) != orc_e2m1_encode_sr(q, rnd)) {
             if (bad[t] < 3) printf("mismatch q=%08x rnd=%08x kernel %u oracle %u\n", b, rnd, kernel_sr(q, rnd),
@@ -70,16 +71,16 @@ int main(void)
         n += seen[t];
         m += bad[t];
     }
-    /* the extremes of the random word at the grid's midpoints and ends */
+    /* every random value at the grid's points, midpoints, ends and their
+       neighbours */
     const float pts[] = {0.0f, 0.25f, 0.5f, 0.75f, 1.0f, 1.25f, 1.5f, 1.75f, 2.0f, 2.5f, 3.0f, 3.5f, 4.0f, 5.0f, 6.0f,
-                         5.9999995f, 1.9999999f, 0.49999997f, 0.99999994f};
-    const uint32_t rs[] = {0u, 0xffu, 0x100u, 0x7fffffffu, 0x80000000u, 0xffffff00u, 0xffffffffu};
+                         5.9999995f, 1.9999999f, 0.49999997f, 0.99999994f, 0.25000003f, 2.5000002f, 4.9999995f};
     for (size_t i = 0; i < sizeof pts / sizeof pts[0]; ++i)
-        for (size_t j = 0; j < sizeof rs / sizeof rs[0]; ++j)
+        for (uint32_t r = 0; r < 256; ++r)
             for (int sg = 0; sg < 2; ++sg) {
                 const float q = sg ? -pts[i] : pts[i];
                 ++n;
-                if (kernel_sr(q, rs[j]) != orc_e2m1_encode_sr(q, rs[j])) ++m;
+                if (kernel_sr(q, r) != orc_e2m1_encode_sr(q, (uint8_t)r)) ++m;
             }
     printf("%llu checked, %llu mismatches\n", (unsigned long long)n, (unsigned long long)m);
     return m != 0;

@@ -2,7 +2,7 @@
 branches on the bits of |q|; tests/native/sr_round_check.c transcribes that
 form and compares it with the oracle's rule (orc_e2m1_encode_sr, compiled
 from oracle/nvfp4_oracle.c) for every non-NaN fp32 q, each with a hashed
-random word, plus the random word's extremes at the grid points.  Zero
+8-bit random, plus every random value at the grid points.  Zero
 mismatches required.  (The GPU parity tests then compare the kernel itself
 with the oracle.)"""
 import os

@@ -198,8 +198,14 @@ def _grouped_case(counts, K, seed):
 @pytest.mark.parametrize("counts,K", [([32, 0, 16, 48, 0, 16, 128], 96),
                                       ([0, 0, 64], 512),
                                       ([16] * 70 + [0] * 40 + [32] * 30, 48),
-                                      ([256, 512, 0, 128], 1040)])
+                                      ([256, 512, 0, 128], 1040),
+                                      ([64, 0, 32, 32] + [128] * 31, 256),
+                                      ([64, 0, 32, 32] + [128] * 30 + [144], 512),
+                                      ([32, 0, 32, 32, 32] + [128] * 31, 256)])
 def test_grouped_small(oracle, counts, K):
+    """Grouped casts of a few shapes, among them 128-row encode tiles owned
+    by four and by five consecutive table entries with an empty expert among
+    them, and a ragged last tile."""
     x = _grouped_case(counts, K, len(counts))
     _announce(f"grouped experts={len(counts)} T={sum(counts)} K={K}")
     out = Guarded(grouped_spec(sum(counts), K, len(counts)))

@@ -74,6 +74,39 @@ __device__ __forceinline__ void sync_arrive_relaxed(const SyncArg& s) {
     __hip_atomic_fetch_add(&g_sync_count[s.slot], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Grid-wide wait of a resident launch (one lane per workgroup): arrive with
+// a fetch-and-add; the workgroup whose arrival is the last (the count it
+// returns is base + n - 1) publishes base + n to kFlagLines flag words, one
+// per 128-byte line, and goes on; every other workgroup polls the flag of
+// line lin % kFlagLines.  All workgroups polling the arrival counter itself
+// keep that one address busy at the memory side and delay the arrivals they
+// wait for; spread over the lines, the wait passes about 4.5 us sooner.  The
+// flags only grow (each launch on a slot publishes a larger count than the
+// one before), so they are never cleared.  Bounded as sync_poll.
+constexpr int kFlagLines = 16;
+__device__ unsigned long long g_sync_flag[kSyncSlots][kFlagLines][16];
+
+__device__ __forceinline__ bool sync_grid_wait(const SyncArg& s, unsigned long long n, uint32_t lin) {
+    const unsigned long long target = s.base + n;
+    const unsigned long long old =
+        __hip_atomic_fetch_add(&g_sync_count[s.slot], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1ull == target) {
+        for (int i = 0; i < kFlagLines; ++i)
+            __hip_atomic_store(&g_sync_flag[s.slot][i][0], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
+    unsigned long long* f = &g_sync_flag[s.slot][lin % kFlagLines][0];
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncWaitTicks) {
+            __hip_atomic_store(s.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
 // one lane: wait for base + n arrivals; false when the wait gave up
 __device__ __forceinline__ bool sync_poll(const SyncArg& s, unsigned long long n) {
     const unsigned long long target = s.base + n;
@@ -1611,10 +1644,7 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
     // write back the whole L2, per workgroup).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        sync_arrive_relaxed(a.bar);
-        bar_ok = sync_poll(a.bar, gridDim.x) ? 1 : 0;
-    }
+    if (threadIdx.x == 0) bar_ok = sync_grid_wait(a.bar, gridDim.x, lin) ? 1 : 0;
     __syncthreads();
     if (!bar_ok) return;
 

@@ -3,7 +3,9 @@
 // nvfp4_api.cpp), run with one thread per workgroup to check the protocol's
 // logic: zero-first (the first workgroups clear the outputs and arrive; the
 // others wait for them before their first atomic max), the grid-wide wait
-// (every workgroup arrives after its atomics and waits for all), slots reused
+// (every workgroup arrives after its atomics; the last arrival publishes the
+// slot's final count to flag words, which the others poll, one of several
+// per workgroup), slots reused
 // by later launches with host-tracked bases, and the bounded wait that gives
 // up and records the failure in an error word the next call reports.
 //
@@ -25,6 +27,8 @@ namespace {
 constexpr int kSlots = 4;                  // few slots, so they are reused often
 std::atomic<uint64_t> g_count[kSlots];     // the device counters (never reset)
 std::atomic<uint32_t> g_err{0};            // the pinned error word
+constexpr int kFlagLines = 4;              // flag words per slot (fewer than workgroups)
+std::atomic<uint64_t> g_flag[kSlots][kFlagLines];   // published final counts (never reset)
 
 struct SyncArg { uint64_t base; int slot; };
 
@@ -47,6 +51,24 @@ void arrive(const SyncArg& s) { g_count[s.slot].fetch_add(1, std::memory_order_r
 bool poll(const SyncArg& s, uint64_t n, std::chrono::milliseconds bound) {
     const auto t0 = std::chrono::steady_clock::now();
     while (g_count[s.slot].load(std::memory_order_acquire) < s.base + n) {
+        if (std::chrono::steady_clock::now() - t0 > bound) { g_err.store(1); return false; }
+        std::this_thread::yield();
+    }
+    return true;
+}
+
+// the grid-wide wait: arrive; the last arrival publishes base + n to every
+// flag word of the slot, the others poll word g % kFlagLines; false when the
+// bound passed (the error word is then set)
+bool grid_wait(const SyncArg& s, uint64_t n, int g, std::chrono::milliseconds bound) {
+    const uint64_t target = s.base + n;
+    const uint64_t old = g_count[s.slot].fetch_add(1, std::memory_order_acq_rel);
+    if (old + 1 == target) {
+        for (auto& f : g_flag[s.slot]) f.store(target, std::memory_order_release);
+        return true;
+    }
+    const auto t0 = std::chrono::steady_clock::now();
+    while (g_flag[s.slot][g % kFlagLines].load(std::memory_order_acquire) < target) {
         if (std::chrono::steady_clock::now() - t0 > bound) { g_err.store(1); return false; }
         std::this_thread::yield();
     }
@@ -83,8 +105,7 @@ bool launch(Host& host, int G, int zw, std::vector<std::atomic<uint32_t>>& out, 
         } else {
             gave_up.fetch_add(1);
         }
-        arrive(bs);
-        if (!poll(bs, (uint64_t)G, bound)) { gave_up.fetch_add(1); return; }
+        if (!grid_wait(bs, (uint64_t)G, g, bound)) { gave_up.fetch_add(1); return; }
         for (int i = 0; i < n; ++i)
             if (out[i].load(std::memory_order_relaxed) != expect - (uint32_t)(i % 3)) bad.fetch_add(1);
     };

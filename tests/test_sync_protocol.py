@@ -1,6 +1,6 @@
 """The cross-workgroup wait protocol (arrival counters with host-issued
-bases, zero-first, the grid-wide wait, the bounded give-up and its error
-word), checked on a CPU build: tests/native/sync_protocol_check.cpp models
+bases, zero-first, the grid-wide wait with its published flag words, the
+bounded give-up and its error word), checked on a CPU build: tests/native/sync_protocol_check.cpp models
 it with one thread per workgroup over many launches that reuse a few slots,
 with shuffled start times, and one forced give-up every 20 launches."""
 import os

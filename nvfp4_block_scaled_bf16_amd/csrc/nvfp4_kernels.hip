@@ -1282,8 +1282,9 @@ __global__ __launch_bounds__(256, 4) void k_encode_sr(const uint16_t* __restrict
             }
             const uint32_t code = fast ? f.code : (odd ? b1.code : b0.code);
             if (col_ok) {
-                if (i < nrows) *reinterpret_cast<uint32_t*>(row_q + (r0 + i) * (K / 2) + c0 / 2) = wq[0];
-                if (i + 1 < nrows) *reinterpret_cast<uint32_t*>(row_q + (r0 + i + 1) * (K / 2) + c0 / 2) = wq[1];
+                // a row's 32 lanes write one whole 128-byte line: nontemporal
+                if (i < nrows) __builtin_nontemporal_store(wq[0], reinterpret_cast<uint32_t*>(row_q + (r0 + i) * (K / 2) + c0 / 2));
+                if (i + 1 < nrows) __builtin_nontemporal_store(wq[1], reinterpret_cast<uint32_t*>(row_q + (r0 + i + 1) * (K / 2) + c0 / 2));
                 const int io = i + (odd ? 1 : 0);
                 if (io < nrows) row_sf[(r0 + io) * (K / 16) + c0 / 16] = (uint8_t)code;
             }

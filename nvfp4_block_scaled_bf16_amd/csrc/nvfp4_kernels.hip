@@ -1121,28 +1121,26 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // Stochastic E2M1 nibble of q with the 8-bit random byte K of word w: x = |q|
 // lies in [lo, lo + d) of the E2M1 grid (d = 0.5 below 2, 1 below 4, 2
 // below 6) and rounds up iff x - lo > U * d with U = R * 2^-8, R that byte;
-// both sides are exact in binary32.  x >= 6 saturates; the sign bit of q is
-// copied.  Without branches, from the bit pattern of x: at or above 1, lo
-// keeps x's exponent and first mantissa bit, d is half its binade and the
-// code is lo's top 10 bits less 252 (1 -> 2, 1.5 -> 3, ..., 4 -> 6); below
-// 1, lo is 0.5 or 0 (codes 1, 0) and d is 0.5.  U * d is formed as R (one
-// byte-to-float conversion) times the power of two d * 2^-8.
-// (tests/native/sr_round_check.c compares this form with the oracle's rule
-// over every fp32 q.)
+// x >= 6 saturates; the sign bit of q is copied.  Without branches, through
+// t = code(lo) * 2^22 + (x - lo) / d * 2^22 rounded up to an integer: at or
+// above 1 that is exactly x's bit pattern less 252 * 2^22 (the exponent and
+// first mantissa bit give the code, the other 22 bits (x - lo) / d); below 1
+// it is ceil(x * 2^23) (lo = 0 or 0.5, d = 0.5).  Rounding up to the integer
+// keeps the strict comparison exact, as R * 2^14 is an integer: x - lo >
+// U * d iff t's low 22 bits exceed R * 2^14, compared here as t << 10 >
+// R << 24; a carry into the code bits is a round-up, which the rule also
+// takes there.  (tests/native/sr_round_check.c compares this form with the
+// oracle's rule over every fp32 q.)
 template <int K>
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t w) {
     const uint32_t b = __float_as_uint(q);
-    const uint32_t s = (b >> 28) & 8u;
     const uint32_t xb = b & 0x7fffffffu;
-    const bool ge1 = xb >= 0x3f800000u;
-    const uint32_t half = xb >= 0x3f000000u ? 0x3f000000u : 0u;
-    const uint32_t lob = ge1 ? (xb & 0xffc00000u) : half;
-    const uint32_t db8 = ge1 ? (xb & 0x7f800000u) - (9u << 23) : 0x3b000000u;   // d * 2^-8
-    const uint32_t c = ge1 ? (lob >> 22) - 252u : (half >> 29);
-    const float diff = __uint_as_float(xb) - __uint_as_float(lob);
-    const float ud = (float)((w >> (8 * K)) & 0xffu) * __uint_as_float(db8);
-    const uint32_t r = c + (diff > ud ? 1u : 0u);
-    return s | (xb >= 0x40c00000u ? 7u : r);
+    const uint32_t ta = xb - 0x3f000000u;
+    const uint32_t tb = (uint32_t)__builtin_ceilf(__builtin_fminf(__uint_as_float(xb), 1.0f) * 0x1p23f);
+    const uint32_t t = xb >= 0x3f800000u ? ta : tb;
+    const uint32_t r24 = __builtin_amdgcn_perm(0u, w, ((uint32_t)K << 24) | 0x000c0c0cu);   // byte K, shifted to the top
+    const uint32_t c = (t >> 22) + ((t << 10) > r24 ? 1u : 0u);
+    return ((b >> 28) & 8u) | (c < 7u ? c : 7u);
 }
 
 // the nibble of element k (0..7) of a lane's row from the row's two random

@@ -4,9 +4,11 @@
  * with an 8-bit random drawn from a hash of q.  The two forms compute the
  * same two exact binary32 values x - lo and U*d wherever they pick the same
  * (lo, d, code), so one random per q checks the pick; the hash still varies
- * which side of the threshold each q falls.  Then every random value at the
- * grid points, midpoints and their neighbours.  Prints "<n> checked, <m>
+ * which side of the threshold each q falls.  Then every random value for a
+ * dense set of q (see main) and at the grid points, midpoints and their
+ * neighbours.  Prints "<n> checked, <m>
  * mismatches". */
+#include <math.h>
 #include <pthread.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -21,17 +23,13 @@ static uint32_t kernel_sr(float q, uint32_t rnd)
 {
     uint32_t b;
     memcpy(&b, &q, 4);
-    const uint32_t s = (b >> 28) & 8u;
     const uint32_t xb = b & 0x7fffffffu;
-    const int ge1 = xb >= 0x3f800000u;
-    const uint32_t half = xb >= 0x3f000000u ? 0x3f000000u : 0u;
-    const uint32_t lob = ge1 ? (xb & 0xffc00000u) : half;
-    const uint32_t db8 = ge1 ? (xb & 0x7f800000u) - (9u << 23) : 0x3b000000u;
-    const uint32_t c = ge1 ? (lob >> 22) - 252u : (half >> 29);
-    const float diff = f_of(xb) - f_of(lob);
-    const float ud = (float)(rnd & 0xffu) * f_of(db8);
-    const uint32_t r = c + (diff > ud ? 1u : 0u);
-    return s | (xb >= 0x40c00000u ? 7u : r);
+    const uint32_t ta = xb - 0x3f000000u;
+    const uint32_t tb = (uint32_t)ceilf(fminf(f_of(xb), 1.0f) * 0x1p23f);
+    const uint32_t t = xb >= 0x3f800000u ? ta : tb;
+    const uint32_t r24 = (rnd & 0xffu) << 24;
+    const uint32_t c = (t >> 22) + ((t << 10) > r24 ? 1u : 0u);
+    return ((b >> 28) & 8u) | (c < 7u ? c : 7u);
 }
 
 static uint32_t hash(uint32_t x)
@@ -65,12 +63,36 @@ int main(void)
 {
     pthread_t th[NT];
     for (int t = 0; t < NT; ++t) pthread_create(&th[t], NULL, work, (void*)(intptr_t)t);
-    uint64_t n = 0, m = 0;
+    uint64_t n = 0, m = 0, m_all = 0;
     for (int t = 0; t < NT; ++t) {
         pthread_join(th[t], NULL);
         n += seen[t];
         m += bad[t];
     }
+    /* every random value for: every q whose mantissa has at most its top 9
+       bits set (its position between grid neighbours is then a multiple of
+       1/256 of a step at most binades, where ties with U*d fall), and every
+       97th mantissa of the binades from 2^-30 up to 8, both signs */
+    for (uint32_t e = 0; e < 256; ++e)
+        for (uint32_t m = 0; m < 512; ++m)
+            for (uint32_t sg = 0; sg < 2; ++sg) {
+                const uint32_t bb = (sg << 31) | (e << 23) | (m << 14);
+                if ((bb & 0x7fffffffu) > 0x7f800000u) continue;
+                for (uint32_t r = 0; r < 256; ++r) {
+                    ++n;
+                    if (kernel_sr(f_of(bb), r) != orc_e2m1_encode_sr(f_of(bb), (uint8_t)r)) ++m_all;
+                }
+            }
+    for (uint32_t e = 97; e < 130; ++e)
+        for (uint32_t m = 0; m < (1u << 23); m += 97)
+            for (uint32_t sg = 0; sg < 2; ++sg) {
+                const uint32_t bb = (sg << 31) | (e << 23) | m;
+                for (uint32_t r = 0; r < 256; ++r) {
+                    ++n;
+                    if (kernel_sr(f_of(bb), r) != orc_e2m1_encode_sr(f_of(bb), (uint8_t)r)) ++m_all;
+                }
+            }
+    m += m_all;
     /* every random value at the grid's points, midpoints, ends and their
        neighbours */
     const float pts[] = {0.0f, 0.25f, 0.5f, 0.75f, 1.0f, 1.25f, 1.5f, 1.75f, 2.0f, 2.5f, 3.0f, 3.5f, 4.0f, 5.0f, 6.0f,

@@ -1136,7 +1136,7 @@ __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t w) {
     const uint32_t b = __float_as_uint(q);
     const uint32_t xb = b & 0x7fffffffu;
     const uint32_t ta = xb - 0x3f000000u;
-    const uint32_t tb = (uint32_t)__builtin_ceilf(__builtin_fminf(__uint_as_float(xb), 1.0f) * 0x1p23f);
+    const uint32_t tb = (uint32_t)__builtin_ceilf(__uint_as_float(xb < 0x3f800000u ? xb : 0x3f800000u) * 0x1p23f);
     const uint32_t t = xb >= 0x3f800000u ? ta : tb;
     const uint32_t r24 = __builtin_amdgcn_perm(0u, w, ((uint32_t)K << 24) | 0x000c0c0cu);   // byte K, shifted to the top
     const uint32_t c = (t >> 22) + ((t << 10) > r24 ? 1u : 0u);

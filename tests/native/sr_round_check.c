@@ -25,7 +25,7 @@ static uint32_t kernel_sr(float q, uint32_t rnd)
     memcpy(&b, &q, 4);
     const uint32_t xb = b & 0x7fffffffu;
     const uint32_t ta = xb - 0x3f000000u;
-    const uint32_t tb = (uint32_t)ceilf(fminf(f_of(xb), 1.0f) * 0x1p23f);
+    const uint32_t tb = (uint32_t)ceilf(f_of(xb < 0x3f800000u ? xb : 0x3f800000u) * 0x1p23f);
     const uint32_t t = xb >= 0x3f800000u ? ta : tb;
     const uint32_t r24 = (rnd & 0xffu) << 24;
     const uint32_t c = (t >> 22) + ((t << 10) > r24 ? 1u : 0u);

@@ -112,3 +112,26 @@ def test_schedule_c3_per_token_full(oracle, schedule):
     out = quantize_guarded(to_dev(x), nv.PER_TOKEN)
     torch.cuda.synchronize()
     compare_cast(out, oracle.quantize(x, nv.PER_TOKEN))
+
+
+@pytest.mark.parametrize("mode", [nv.PER_TENSOR, nv.PER_TOKEN])
+def test_resident_wait_slots_wrap(oracle, mode):
+    """140 resident casts queued back to back with no synchronization between
+    them (more than twice the 64 wait slots, so every slot's arrival counter
+    and flag words are taken again, with larger targets, by later launches),
+    each into its own guarded outputs; then every output against the
+    oracle."""
+    nv.set_schedule("resident")
+    try:
+        M, K, n = 64, 1024, 140
+        _announce(f"resident x{n} mode={mode} {M}x{K}")
+        xs = [W.row_scaled_with_outliers(M, K, 5000 + i) for i in range(n)]
+        dx = [to_dev(x) for x in xs]
+        outs = [Guarded(cast_spec(M, K, mode)) for _ in range(n)]
+        for d, o in zip(dx, outs):
+            nv.quantize_into(d, mode, **o.views)
+        torch.cuda.synchronize()
+        for x, o in zip(xs, outs):
+            compare_cast(o, oracle.quantize(x, mode))
+    finally:
+        nv.set_schedule("auto")

@@ -216,8 +216,10 @@ constexpr float kRcp6 = 0x1.555556p-3f;   // RN(1/6)
 // bbits: the block's largest magnitude as fp32 bits (a bf16 magnitude in the
 // high half, zeros below).  SAT: the outer amax may be smaller than the data
 // (caller-supplied amax), so the block scale may saturate and quotients
-// exceed 6.
-template <bool SAT>
+// exceed 6.  SUB: blocks with a scale in the E4M3 subnormal range stay on
+// the fast path (below); without it they go to the exact path, which costs
+// the kernels that rarely meet them nothing on their common path.
+template <bool SAT, bool SUB = false>
 __device__ __forceinline__ FastBlock fast_block(uint32_t bbits, const Outer& o) {
     FastBlock fb;
     const float b = __uint_as_float(bbits);
@@ -234,12 +236,31 @@ __device__ __forceinline__ FastBlock fast_block(uint32_t bbits, const Outer& o) 
     uint32_t c = (u + (0x7FFFFu + (0x40u << 20)) + ((u >> 20) & 1u)) >> 20;
     c = c < 0x400u ? 0x400u : (c > 0x47Eu ? 0x47Eu : c);
     fb.code = c;
-    const float r = __uint_as_float((c << 20) - (0x40u << 20)) * o.S;   // decode(code) * S; 2^-7 * S for code 0
+    float r = __uint_as_float((c << 20) - (0x40u << 20)) * o.S;   // decode(code) * S; 2^-7 * S for code 0
     fb.yh = rcp_rd(r);
     fb.yl = __builtin_fmaf(-r, fb.yh, 1.0f) * fb.yh;
-    // exact path: sf in the E4M3 subnormal range (and not an all-zero
-    // block), or an r with all mantissa bits set (fact 4's exception)
-    bool slow = (u - 1u) < (0x3C800000u - 1u) || (__float_as_uint(r) & 0x7FFFFFu) == 0x7FFFFFu;
+    // 0 < sf < 2^-6 (rare: a block far below its vector's amax) is the E4M3
+    // subnormal range: code = RNE(sf * 2^9) in 0..8 (8 is 2^-6, the smallest
+    // normal; sf * 2^9 < 8 is exact and adding 2^23 leaves a unit spacing,
+    // so the addition rounds), r = code * 2^-9 * S.  Code 0 (sf < 2^-10) has
+    // r = 0: yh = yl = 0 make every quotient a zero of the element's sign,
+    // the sign-only nibbles the definition gives.  Taken by the whole wave
+    // when any lane needs it (a uniform branch costs the common case less
+    // than a divergent one).
+    const bool sub = (u - 1u) < (0x3C800000u - 1u);
+    if (SUB && __builtin_amdgcn_ballot_w64(sub) != 0ull) {
+        const uint32_t m = __float_as_uint(sf * 512.0f + 8388608.0f) - 0x4B000000u;
+        const float rs = ((float)m * 0x1p-9f) * o.S;
+        const float yhs = m == 0u ? 0.0f : rcp_rd(rs);
+        const float yls = __builtin_fmaf(-rs, yhs, 1.0f) * yhs;
+        fb.code = sub ? m : fb.code;
+        r = sub ? rs : r;
+        fb.yh = sub ? yhs : fb.yh;
+        fb.yl = sub ? yls : fb.yl;
+    }
+    // exact path: an r with all mantissa bits set (fact 4's exception), and
+    // without SUB a scale in the E4M3 subnormal range
+    bool slow = (!SUB && sub) || (__float_as_uint(r) & 0x7FFFFFu) == 0x7FFFFFu;
     if (SAT) slow |= !(r <= 0x1p64f && b * fb.yh <= 0x1p64f);
     fb.slow = slow;
     return fb;

@@ -1794,7 +1794,7 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
                     o.S = sy.x;
                     o.yS = sy.y;
                 }
-                cb[j] = fast_block<false>(bits, o);
+                cb[j] = fast_block<false, true>(bits, o);
                 slow |= cb[j].slow;
                 __builtin_amdgcn_raw_buffer_store_b8((uint8_t)cb[j].code, cs_rs, ls, ts + j * ms, 0);
             }
@@ -1814,7 +1814,7 @@ __global__ __launch_bounds__(512) void k_resident(ResArgs a) {
                     ro.S = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][0];
                     ro.yS = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][1];
                 }
-                const FastBlock f = fast_block<false>(bm[s], ro);
+                const FastBlock f = fast_block<false, true>(bm[s], ro);
                 slow |= f.slow;
                 __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs, i * sr, 0);
                 yh0 = from_even(f.yh); yl0 = from_even(f.yl);

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kRowsThreads, L == 8 ? 5 : 4) void k_rows(const uin
                 o.S = odd ? lane_f(ov.S, fo / NR) : lane_f(ov.S, fe / NR);
                 o.yS = odd ? lane_f(ov.yS, fo / NR) : lane_f(ov.yS, fe / NR);
             }
-            const FastBlock fb = fast_block<false>(bm[k], o);
+            const FastBlock fb = fast_block<false, true>(bm[k], o);
             const bool bslow = fb.slow || ((oslow >> rown) & 1ull);
             slow |= (bslow ? 1u : 0u) << (odd ? fo : fe);
             const uint32_t vo = odd ? sv(fo % NR) + ss(fo % NR) + (uint32_t)(fo / NR) * srow

@@ -879,7 +879,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                     o.S = sy.x;
                     o.yS = sy.y;
                 }
-                cb[j] = fast_block<SAT>(bits, o);
+                cb[j] = fast_block<SAT, !SAT>(bits, o);
                 slow |= cb[j].slow;
                 // the scale byte goes to the staging area now rather than
                 // being held through the row pairs
@@ -909,7 +909,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ x, 
                         ro.S = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][0];
                         ro.yS = row_scale[wave][16 * rg + i + (odd ? 1 : 0)][1];
                     }
-                    const FastBlock f = fast_block<SAT>(bm[s], ro);
+                    const FastBlock f = fast_block<SAT, !SAT>(bm[s], ro);
                     slow |= f.slow;
                     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f.code, s_rs, vs, SWZ ? i * 16u + s_slot : i * sr, 0);
                     yh0 = from_even(f.yh); yl0 = from_even(f.yl);
